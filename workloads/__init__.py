@@ -1,0 +1,8 @@
+"""Seeded synthetic inputs for the paged decode step.
+
+The oracle and the HIP path both read these inputs. This module holds none of
+the attention arithmetic. It draws lengths, hands out physical blocks, writes
+block tables, and fills pools and queries with N(0, 1) values.
+"""
+
+from .configs import CONFIG_NAMES, Case, build_case, make_case  # noqa: F401

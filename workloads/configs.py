@@ -1,0 +1,212 @@
+"""The five synthetic decode workloads plus a general case builder.
+
+Each workload has the shapes, sizes and length mix of the pages' examples:
+
+* ``tiny``: fp32; 4 q heads / 2 kv heads; head_dim 64; b = 16; lengths
+  {1, 17, 33, 64}; a 32-block pool handed out as a seeded permutation.
+  ``tiny_b4`` replays the worked example of [P1] "Paging": b = 4, table
+  [5, 1, 7], and the token at position 9 written and attended, so L = 10.
+* ``batch64``: bf16; a Llama-3-8B-shaped layer (32 q / 8 kv heads, head_dim
+  128, b = 16); 64 sequences with L ~ U{20..500}. This scales up the chapter
+  demo's mix of 32 requests of 20-500 tokens ([P1] "Reserved memory is wasted
+  memory"). The pool has 4096 shuffled blocks.
+* ``long``: bf16; same heads; 16 sequences with L log-uniform on
+  [4096, 32768]; the pool holds every block the sequences need plus 10%,
+  shuffled.
+* ``prefix``: bf16; 128 sequences share their first 2048 tokens (128 physical
+  blocks), each followed by a private suffix of U{64..1024} tokens.
+* ``spec``: bf16; 4 query tokens per sequence; 64 q / 8 kv heads;
+  256 sequences with L ~ U{1024..8192}.
+
+No public dataset is involved; every value is drawn from a seeded
+``torch.Generator``. Floating values are N(0, 1) drawn in fp32, then rounded to
+the case dtype. For bf16 that rounding is torch's round-to-nearest-even.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+CONFIG_NAMES = ("tiny", "tiny_b4", "batch64", "long", "prefix", "spec")
+INT32_MAX = 2**31 - 1
+_SEEDS = {"tiny": 1000, "batch64": 1001, "long": 1002, "prefix": 1003, "spec": 1004, "tiny_b4": 1005}
+_FILL_CHUNK = 1 << 25  # elements drawn per randn call when filling big pools
+
+
+@dataclass
+class Case:
+    """One decode step's inputs, as CPU tensors.
+
+    Layouts: ``q [B, T, Hq, D]``; ``k_new``/``v_new [B, T, Hkv, D]``;
+    ``k_pool``/``v_pool [N, Hkv, b, D]``; ``block_tables [B, MB]`` int32, where
+    entries past a sequence's block count are ``table_pad``;
+    ``seq_lens [B]`` int32, counting the T new tokens; ``positions [B, T]``
+    int32, holding the new tokens' positions L - T .. L - 1.
+    """
+
+    name: str
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    positions: torch.Tensor
+    block_size: int
+    scale: float
+    table_rows: list = field(default_factory=list)  # per sequence: its physical blocks
+    unused_blocks: torch.Tensor | None = None        # physical blocks no table references
+
+    @property
+    def dims(self):
+        b, t, hq, d = self.q.shape
+        return dict(num_seqs=b, q_tokens=t, num_q_heads=hq, num_kv_heads=self.k_pool.shape[1],
+                    head_dim=d, block_size=self.block_size, num_blocks=self.k_pool.shape[0],
+                    max_blocks_per_seq=self.block_tables.shape[1])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.numel() else 0
+
+    def kv_tokens(self) -> int:
+        """Total positions attended over: sum of L_i."""
+        return int(self.seq_lens.to(torch.int64).sum())
+
+
+def _randn(shape, gen, dtype):
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(dtype)
+
+
+def _fill_pool(shape, gen, dtype):
+    """N(0,1) pool, drawn in bounded chunks so big pools never need a full fp32 copy."""
+    out = torch.empty(shape, dtype=dtype)
+    flat = out.view(-1)
+    for start in range(0, flat.numel(), _FILL_CHUNK):
+        n = min(_FILL_CHUNK, flat.numel() - start)
+        flat[start:start + n] = torch.randn(n, generator=gen, dtype=torch.float32).to(dtype)
+    return out
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def build_case(*, name="custom", lengths, num_q_heads, num_kv_heads, head_dim, block_size,
+               q_tokens=1, dtype=torch.bfloat16, seed=0, num_blocks=None, shared_prefix_blocks=0,
+               table_pad=INT32_MAX, pool_slack=0.0, explicit_tables=None, poison_unused=True):
+    """General builder used by every named workload.
+
+    Blocks are handed out like a free list over a seeded permutation of the
+    pool: each sequence takes the next ``ceil(L/b)`` entries, as in [P1] "The
+    allocator". If ``shared_prefix_blocks`` > 0, the first that many logical
+    blocks of every sequence map to the same physical blocks. Their refcount
+    equals the number of sequences, as in a forked or prefix-cached prompt
+    ([P1] "Sharing blocks"). When ``explicit_tables`` is given, those rows are
+    used as they are.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    lengths = [int(x) for x in lengths]
+    n_seq = len(lengths)
+    need = [_ceil_div(max(L, 0), block_size) for L in lengths]
+    if explicit_tables is not None:
+        rows = [list(map(int, r)) for r in explicit_tables]
+        if num_blocks is None:
+            num_blocks = max(max(r) for r in rows if r) + 1
+        perm_unused = sorted(set(range(num_blocks)) - {b for r in rows for b in r})
+    else:
+        private = [n - shared_prefix_blocks for n in need]
+        if min(private) < 0:
+            raise ValueError("a sequence is shorter than the shared prefix")
+        used = shared_prefix_blocks + sum(private)
+        if num_blocks is None:
+            num_blocks = max(1, math.ceil(used * (1.0 + pool_slack)))
+        if used > num_blocks:
+            raise MemoryError("KV block pool exhausted")
+        perm = torch.randperm(num_blocks, generator=gen).tolist()
+        prefix = perm[:shared_prefix_blocks]
+        cursor = shared_prefix_blocks
+        rows = []
+        for n in private:
+            rows.append(prefix + perm[cursor:cursor + n])
+            cursor += n
+        perm_unused = perm[cursor:]
+    width = max(1, max(len(r) for r in rows))
+    tables = torch.full((n_seq, width), table_pad, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        if r:
+            tables[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+
+    hq, hkv, d, t = num_q_heads, num_kv_heads, head_dim, q_tokens
+    q = _randn((n_seq, t, hq, d), gen, dtype)
+    k_new = _randn((n_seq, t, hkv, d), gen, dtype)
+    v_new = _randn((n_seq, t, hkv, d), gen, dtype)
+    pool_shape = (num_blocks, hkv, block_size, d)
+    k_pool = _fill_pool(pool_shape, gen, dtype)
+    v_pool = _fill_pool(pool_shape, gen, dtype)
+    unused = torch.tensor(perm_unused, dtype=torch.int64)
+    if poison_unused and unused.numel():
+        k_pool[unused] = float("nan")
+        v_pool[unused] = float("nan")
+    seq_lens = torch.tensor(lengths, dtype=torch.int32)
+    positions = torch.stack([torch.arange(L - t, L, dtype=torch.int32) for L in lengths]) \
+        if n_seq else torch.empty((0, t), dtype=torch.int32)
+    return Case(name=name, q=q, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool,
+                block_tables=tables, seq_lens=seq_lens, positions=positions,
+                block_size=block_size, scale=1.0 / math.sqrt(d), table_rows=rows,
+                unused_blocks=unused)
+
+
+def config_lengths(name: str, gen: torch.Generator, num_seqs: int | None = None):
+    """Draw the length mix of a named workload (its first ``num_seqs`` sequences if given)."""
+    if name == "tiny":
+        lens = [1, 17, 33, 64]
+    elif name == "tiny_b4":
+        lens = [10]
+    elif name == "batch64":
+        lens = torch.randint(20, 501, (64,), generator=gen).tolist()
+    elif name == "long":
+        u = torch.rand(16, generator=gen, dtype=torch.float64)
+        lo, hi = math.log(4096.0), math.log(32768.0)
+        lens = [int(round(math.exp(lo + float(x) * (hi - lo)))) for x in u]
+    elif name == "prefix":
+        lens = [2048 + int(s) for s in torch.randint(64, 1025, (128,), generator=gen)]
+    elif name == "spec":
+        lens = torch.randint(1024, 8193, (256,), generator=gen).tolist()
+    else:
+        raise KeyError(name)
+    if num_seqs is not None:
+        lens = lens[:num_seqs]
+    return lens
+
+
+def make_case(name: str, *, num_seqs: int | None = None, seed: int | None = None,
+              table_pad: int = INT32_MAX, poison_unused: bool = True) -> Case:
+    """Build a named workload; ``num_seqs`` keeps only its first sequences."""
+    seed = _SEEDS[name] if seed is None else seed
+    gen = torch.Generator().manual_seed(seed)
+    lens = config_lengths(name, gen, num_seqs)
+    common = dict(name=name, lengths=lens, seed=seed + 7919, table_pad=table_pad,
+                  poison_unused=poison_unused)
+    if name == "tiny":
+        return build_case(num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                          dtype=torch.float32, num_blocks=32, **common)
+    if name == "tiny_b4":
+        return build_case(num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=4,
+                          dtype=torch.float32, num_blocks=8, explicit_tables=[[5, 1, 7]], **common)
+    if name == "batch64":
+        return build_case(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                          dtype=torch.bfloat16, num_blocks=4096, **common)
+    if name == "long":
+        return build_case(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                          dtype=torch.bfloat16, pool_slack=0.10, **common)
+    if name == "prefix":
+        return build_case(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                          dtype=torch.bfloat16, shared_prefix_blocks=128, pool_slack=0.10, **common)
+    if name == "spec":
+        return build_case(num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+                          q_tokens=4, dtype=torch.bfloat16, **common)
+    raise KeyError(name)
