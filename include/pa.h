@@ -1,0 +1,175 @@
+/*
+ * pa.h: C ABI of libpa.so, a paged-KV-cache decode step for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The KV cache of one attention layer is two pools, K and V, each shaped
+ * [num_blocks, num_kv_heads, block_size, head_dim] and row-major (head_dim is
+ * fastest). A sequence's logical position p lives in physical block
+ * block_tables[seq][p / block_size] at offset p % block_size ([P1] "25. Paged
+ * attention and prefix caching", section "Paging"; [P5] "Chapter 7 Paged KV
+ * Cache and Memory Management", sections 3.1-3.2).
+ *
+ * Conventions that apply to every entry point:
+ *  - Every data pointer is device memory owned by the caller: a tensor that is
+ *    contiguous in the stated layout, 16-byte aligned for q, k_new, v_new, the
+ *    pools and out.
+ *  - The library allocates nothing and keeps no state between calls. It is
+ *    re-entrant. All work is enqueued on `stream` (0 is the null stream), and
+ *    nothing synchronises with the host.
+ *  - Return value: PA_OK, or a negative pa_status. On error nothing is
+ *    launched, except for PA_ERR_LAUNCH, which reports a failed launch.
+ *  - Preconditions the library does not check (breaking them is undefined
+ *    behaviour):
+ *      * 1 <= seq_lens[i] <= max_blocks_per_seq * block_size, and
+ *        seq_lens[i] >= q_tokens;
+ *      * block_tables[i][j] is in [0, num_blocks) for j < ceil(seq_lens[i] /
+ *        block_size). Entries past that point are never read, so any padding
+ *        value is allowed;
+ *      * the slots written by pa_write_kv are distinct, and no other sequence
+ *        reads them (copy-on-write is the caller's job: [P1] section
+ *        "Sharing blocks: forks and copy-on-write").
+ *
+ * Sources: [P1] "25. Paged attention and prefix caching"
+ *          (inference.shantanugoel.com); [P2] "Модуль 09: PagedAttention:
+ *          пейджинг KV-кэша" (hermes-agent.ru); [P4] "PagedAttention and the
+ *          KV Cache" (kanthi.in); [P5] "Chapter 7 Paged KV Cache and Memory
+ *          Management" (zero-to-sglang).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; declared here so the header needs no HIP include. */
+typedef struct ihipStream_t* pa_stream_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, bad dtype code, workspace too small */
+  PA_ERR_UNSUPPORTED = -2, /* valid arguments, but no kernel for this (dtype, head_dim, block, rows) */
+  PA_ERR_LAUNCH = -3       /* the HIP runtime reported an error for the launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Kernel choice for the attention entry points. PA_VARIANT_AUTO picks the
+ * fastest kernel this library has for the shape. The other values force one
+ * kernel family and return PA_ERR_UNSUPPORTED if it cannot serve the shape. */
+typedef enum {
+  PA_VARIANT_AUTO = 0,
+  PA_VARIANT_VALU = 1, /* vector-ALU kernel: up to 8 query rows per kv head in one workgroup */
+  PA_VARIANT_MFMA = 2  /* matrix-core kernel: bf16, 16 or 32 query rows per kv head */
+} pa_variant;
+
+/* Problem dimensions.
+ * B = num_seqs; T = q_tokens, the new tokens per sequence, which are causal
+ * among themselves; Hq = num_q_heads; Hkv = num_kv_heads; G = Hq / Hkv is the
+ * GQA group (query head h reads kv head h / G: [P1] section "Attention that
+ * reads through the table"); D = head_dim; b = block_size; N = num_blocks;
+ * MB = max_blocks_per_seq, the width of block_tables. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t q_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t q_dtype;   /* pa_dtype of q and of k_new/v_new */
+  int32_t kv_dtype;  /* pa_dtype of the pools; must equal q_dtype */
+  int32_t out_dtype; /* pa_dtype of out */
+  int32_t variant;   /* pa_variant */
+} pa_dims;
+
+/* pa_write_kv: the KV-append scatter.
+ * For every sequence i < B and new token t < T, with pos = positions[i*T + t]:
+ *   k_pool[block_tables[i*MB + pos / b]][h][pos % b][:] = k_new[i][t][h][:]
+ *   v_pool[...same slot...]                               = v_new[i][t][h][:]
+ * for every kv head h. This is the scatter half of `update` in [P1] section
+ * "The paged cache"; [P2] `Sequence.append`; and the "write k_t, v_t" step of
+ * the decode-step sketch in [P4] section "Block table and allocator".
+ *   k_new, v_new : [B, T, Hkv, D], dtype q_dtype (== kv_dtype)
+ *   k_pool, v_pool : [N, Hkv, b, D], written in place, bit-exact copies
+ *   block_tables : int32 [B, MB];  positions : int32 [B, T], each in
+ *                  [0, MB * b)
+ * Requires D * sizeof(dtype) to be a multiple of 16 bytes. Each copied row
+ * is bit-for-bit identical to its source. */
+int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool,
+                void* v_pool, const int32_t* block_tables, const int32_t* positions,
+                pa_stream_t stream);
+
+/* pa_decode: single-pass paged decode attention.
+ * For every sequence i, query token t < T and query head h, with
+ * L = seq_lens[i], kv head g = h / G and visible positions
+ * p = 0 .. L - T + t (the T new tokens are the last T positions; causal mask
+ * from [P5] section 4.1):
+ *   s_p = scale * dot(q[i][t][h][:], K[p])     K[p] = k_pool[table(i,p)][g][p % b][:]
+ *   out[i][t][h][:] = sum_p softmax(s)_p * V[p]
+ * This is [P1] section "Attention that reads through the table", [P2]
+ * section 5 and [P5] sections 4.1-4.2. It is exact softmax attention, computed
+ * with a blockwise online softmax and an fp32 running max, sum and
+ * accumulator.
+ *   q : [B, T, Hq, D], q_dtype;  out : [B, T, Hq, D], out_dtype
+ *   k_pool, v_pool : [N, Hkv, b, D], kv_dtype (read only)
+ *   block_tables : int32 [B, MB];  seq_lens : int32 [B]
+ * One workgroup runs per (sequence, kv head), and loops over the whole
+ * sequence. Use pa_decode_partitioned for long contexts.
+ * Supported: (kv dtype, D) in {(PA_BF16, 128), (PA_F32, 64)}; b in
+ * {4, 8, 16, 32}. The VALU kernel serves any T * G: groups of up to 8 query
+ * rows share one workgroup. The MFMA kernel serves PA_BF16 with T * G = 16 or
+ * 32. */
+int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+              pa_stream_t stream);
+
+/* Bytes of device workspace pa_decode_partitioned needs for these dims:
+ * B * T * Hq * P * (D + 2) * 4 plus alignment, with
+ * P = ceil(max_seq_len / partition_tokens). Returns 0 for invalid
+ * arguments. */
+size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
+                                             int32_t partition_tokens);
+
+/* pa_decode_partitioned: split-context decode (flash-decoding) with a merge pass.
+ * Each sequence's positions are cut into partitions of partition_tokens.
+ * Workgroup (i, kv head, k) writes the fp32 partial (m_k, l_k, acc_k[D]) of
+ * partition k for its query rows. A second kernel on the same stream merges
+ * them exactly ([P5] section 4.2, block merging in three steps):
+ *   M = max_k m_k;  l = sum_k l_k e^(m_k - M);
+ *   out = sum_k acc_k e^(m_k - M) / l.
+ * Partitions with no visible position (l_k = 0) are skipped. Partitioning
+ * long sequences across programs with a final merge is the production
+ * technique named in [P1] section "Attention that reads through the table";
+ * [P2] section 5 also names it.
+ *   max_seq_len : host-known upper bound of seq_lens (the host keeps a copy of
+ *                 the tables: [P5] section 3.1). It sizes the grid. Every
+ *                 seq_lens[i] must be <= max_seq_len.
+ *   partition_tokens : > 0, and a multiple of 16 and of b
+ *   workspace : device scratch of >= pa_decode_partitioned_workspace_bytes()
+ *               bytes, 256-byte aligned, owned by the caller; its contents on
+ *               entry are irrelevant.
+ * Other arguments and the supported shapes are as for pa_decode. Two calls
+ * that share one workspace must be ordered by the caller, for example by
+ * using the same stream. */
+int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
+                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                          pa_stream_t stream);
+
+/* Static text for a status code. Never NULL. */
+const char* pa_status_string(int status);
+
+/* ABI version: bumped when a signature or a struct layout changes. */
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,213 @@
+"""paged_kv_cache_69_amd: a paged-KV-cache decode step for AMD MI355X (gfx950).
+
+This module is a thin ctypes binding over ``libpa.so``, whose C ABI is declared
+in ``include/pa.h``. It only marshals arguments: every step of the path runs in
+the library's HIP kernels, and PyTorch supplies device memory and streams. If
+the library is missing, every call raises. There is no fallback path.
+
+Entry points, with the same names as the C ABI:
+
+* :func:`write_kv`: the KV-append scatter (``pa_write_kv``).
+* :func:`decode`: single-pass paged decode attention (``pa_decode``).
+* :func:`decode_partitioned`: split-context decode plus its merge pass
+  (``pa_decode_partitioned``).
+* :func:`workspace_bytes`: workspace size for :func:`decode_partitioned`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB_PATH
+
+PA_F32, PA_BF16 = 0, 1
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+EXPORTS = (
+    "pa_write_kv",
+    "pa_decode",
+    "pa_decode_partitioned_workspace_bytes",
+    "pa_decode_partitioned",
+    "pa_status_string",
+    "pa_abi_version",
+)
+ABI_VERSION = 1
+
+_DIM_FIELDS = ("num_seqs", "q_tokens", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+               "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "variant")
+
+
+class PaDims(ctypes.Structure):
+    """Mirror of ``pa_dims`` in include/pa.h."""
+
+    _fields_ = [(name, ctypes.c_int32) for name in _DIM_FIELDS]
+
+
+class PaError(RuntimeError):
+    """A libpa entry point returned a non-zero status."""
+
+    def __init__(self, func: str, status: int, text: str):
+        super().__init__(f"{func} failed: {text} (status {status})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libpa.so (once) and declare its signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m paged_kv_cache_69_amd._build, "
+                           "or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    dims_p = ctypes.POINTER(PaDims)
+    lib.pa_write_kv.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P]
+    lib.pa_write_kv.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_partitioned_workspace_bytes.argtypes = [dims_p, _I32, _I32]
+    lib.pa_decode_partitioned_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
+                                          ctypes.c_size_t, _P]
+    lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_abi_version.argtypes = []
+    lib.pa_abi_version.restype = ctypes.c_int
+    if lib.pa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libpa.so ABI {lib.pa_abi_version()} != binding ABI {ABI_VERSION}; rebuild")
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(lib, func: str, status: int):
+    if status != 0:
+        raise PaError(func, status, lib.pa_status_string(status).decode())
+
+
+def dtype_code(dtype) -> int:
+    import torch
+
+    if dtype == torch.float32:
+        return PA_F32
+    if dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16")
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(**tensors):
+    devs = {t.device for t in tensors.values()}
+    _require(len(devs) == 1, f"all tensors must share one device, got {devs}")
+    dev = next(iter(devs))
+    _require(dev.type == "cuda", "tensors must live on the GPU")
+    for name, t in tensors.items():
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+    return dev
+
+
+def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT_AUTO) -> PaDims:
+    """Dims for q ``[B, T, Hq, D]``, pools ``[N, Hkv, b, D]`` and tables ``[B, MB]``."""
+    _require(q.dim() == 4 and k_pool.dim() == 4 and block_tables.dim() == 2, "bad tensor ranks")
+    b, t, hq, d = q.shape
+    n, hkv, bs, d2 = k_pool.shape
+    _require(d == d2, "head_dim of q and pools differ")
+    _require(block_tables.shape[0] == b, "block_tables rows != num_seqs")
+    return PaDims(b, t, hq, hkv, d, bs, n, block_tables.shape[1], dtype_code(q.dtype), dtype_code(k_pool.dtype),
+                  dtype_code(out_dtype if out_dtype is not None else q.dtype), int(variant))
+
+
+def write_kv(k_new, v_new, k_pool, v_pool, block_tables, positions, *, stream=None):
+    """``pa_write_kv``: scatter ``k_new``/``v_new [B, T, Hkv, D]`` into the pools at ``positions [B, T]``."""
+    import torch
+
+    lib = load_library()
+    dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                         positions=positions)
+    _require(block_tables.dtype == torch.int32 and positions.dtype == torch.int32, "tables/positions must be int32")
+    _require(k_new.shape == v_new.shape and k_pool.shape == v_pool.shape, "K/V shapes differ")
+    bsz, t, hkv, d = k_new.shape
+    _require(positions.shape == (bsz, t), "positions must be [B, T]")
+    _require(k_pool.shape[1] == hkv and k_pool.shape[3] == d, "pool and new rows disagree")
+    code = dtype_code(k_pool.dtype)
+    _require(dtype_code(k_new.dtype) == code, "new rows and pools must share a dtype")
+    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, code, code, 0)
+    st = lib.pa_write_kv(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                         v_pool.data_ptr(), block_tables.data_ptr(), positions.data_ptr(),
+                         _stream_handle(stream, dev))
+    _check(lib, "pa_write_kv", st)
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, *, out_dtype=None,
+           variant: int = VARIANT_AUTO, stream=None):
+    """``pa_decode``: returns ``out [B, T, Hq, D]`` (fp32 unless ``out``/``out_dtype`` says otherwise)."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant)
+    st = lib.pa_decode(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                       block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                       _stream_handle(stream, dev))
+    _check(lib, "pa_decode", st)
+    return out
+
+
+def workspace_bytes(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int,
+                    *, variant: int = VARIANT_AUTO) -> int:
+    """``pa_decode_partitioned_workspace_bytes`` for these tensors."""
+    lib = load_library()
+    dims = make_dims(q, k_pool, block_tables, variant=variant)
+    n = lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
+    if n == 0:
+        raise PaError("pa_decode_partitioned_workspace_bytes", -1, "invalid argument")
+    return int(n)
+
+
+def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
+                       partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                       variant: int = VARIANT_AUTO, stream=None):
+    """``pa_decode_partitioned``: split-context decode + merge. ``workspace`` is a uint8 device tensor
+    of at least :func:`workspace_bytes` bytes (allocated here if omitted)."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out,
+                         workspace=workspace)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant)
+    st = lib.pa_decode_partitioned(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                   block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                   int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(lib, "pa_decode_partitioned", st)
+    return out

@@ -1,0 +1,191 @@
+// extern "C" entry points of libpa.so: argument checks, kernel choice, launches.
+// The declarations, and their citations of the pages, are in include/pa.h.
+#include <math.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::DecodeParams;
+
+constexpr int kAbiVersion = 1;
+constexpr int32_t kSinglePassTokens = 0x7ffffff0;  // one partition that covers any length
+
+bool valid_dtype(int32_t t) { return t == PA_F32 || t == PA_BF16; }
+int dtype_size(int32_t t) { return t == PA_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point. Returns PA_OK when the dims describe a valid problem.
+int check_dims(const pa_dims* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  if (d->num_seqs < 0 || d->q_tokens < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+      d->head_dim < 1 || d->block_size < 1 || d->num_blocks < 1 || d->max_blocks_per_seq < 1)
+    return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype) || !valid_dtype(d->out_dtype))
+    return PA_ERR_INVALID_ARG;
+  if (d->q_dtype != d->kv_dtype) return PA_ERR_UNSUPPORTED;
+  if (d->variant < PA_VARIANT_AUTO || d->variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+// Which kernel family serves these dims, or PA_ERR_UNSUPPORTED.
+int choose_variant(const pa_dims* d, int* variant) {
+  const bool mfma = pa::mfma_supported(*d);
+  const bool valu = pa::valu_supported(*d);
+  switch (d->variant) {
+    case PA_VARIANT_MFMA:
+      if (!mfma) return PA_ERR_UNSUPPORTED;
+      *variant = PA_VARIANT_MFMA;
+      return PA_OK;
+    case PA_VARIANT_VALU:
+      if (!valu) return PA_ERR_UNSUPPORTED;
+      *variant = PA_VARIANT_VALU;
+      return PA_OK;
+    default:
+      if (mfma) {
+        *variant = PA_VARIANT_MFMA;
+        return PA_OK;
+      }
+      if (valu) {
+        *variant = PA_VARIANT_VALU;
+        return PA_OK;
+      }
+      return PA_ERR_UNSUPPORTED;
+  }
+}
+
+DecodeParams base_params(const pa_dims* d, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out) {
+  DecodeParams p = {};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.qk_scale_log2 = scale * pa::kLog2eHost;
+  p.B = d->num_seqs;
+  p.T = d->q_tokens;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.G = d->num_q_heads / d->num_kv_heads;
+  p.D = d->head_dim;
+  p.MB = d->max_blocks_per_seq;
+  p.block_size = d->block_size;
+  p.rows = p.T * p.G;
+  p.out_dtype = d->out_dtype;
+  return p;
+}
+
+int launch_attention(const pa_dims* d, int variant, DecodeParams& p, hipStream_t stream) {
+  if (variant == PA_VARIANT_MFMA) {
+    p.row_groups = 1;
+    return launch_status(pa::launch_decode_mfma(p, stream));
+  }
+  p.row_groups = (p.rows + pa::valu_rows_per_group(p.rows) - 1) / pa::valu_rows_per_group(p.rows);
+  return launch_status(pa::launch_decode_valu(p, d->kv_dtype, stream));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace split: (m, l) pairs first, then the accumulators, each 256-byte aligned.
+void workspace_layout(const pa_dims* d, int32_t parts, size_t* ml_bytes, size_t* acc_bytes) {
+  const size_t rows = (size_t)d->num_seqs * d->q_tokens * d->num_q_heads;
+  *ml_bytes = align256(rows * (size_t)parts * 2 * sizeof(float));
+  *acc_bytes = align256(rows * (size_t)parts * d->head_dim * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                const int32_t* block_tables, const int32_t* positions, pa_stream_t stream) {
+  const int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !positions) return PA_ERR_INVALID_ARG;
+  if ((int64_t)dims->head_dim * dtype_size(dims->kv_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_INVALID_ARG;
+  return launch_status(pa::launch_write_kv(*dims, k_new, v_new, k_pool, v_pool, block_tables, positions,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+              pa_stream_t stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  int variant = 0;
+  st = choose_variant(dims, &variant);
+  if (st != PA_OK) return st;
+  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
+  p.parts = 1;
+  p.part_tokens = kSinglePassTokens;
+  p.partial = 0;
+  return launch_attention(dims, variant, p, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
+                                             int32_t partition_tokens) {
+  if (check_dims(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return 0;
+  const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
+  size_t ml = 0, acc = 0;
+  workspace_layout(dims, parts, &ml, &acc);
+  return ml + acc;
+}
+
+int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                          int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, pa_stream_t stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
+  if (partition_tokens % 16 != 0 || partition_tokens % dims->block_size != 0) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < pa_decode_partitioned_workspace_bytes(dims, max_seq_len, partition_tokens))
+    return PA_ERR_INVALID_ARG;
+  int variant = 0;
+  st = choose_variant(dims, &variant);
+  if (st != PA_OK) return st;
+
+  const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
+  size_t ml_bytes = 0, acc_bytes = 0;
+  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
+  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
+  p.parts = parts;
+  p.part_tokens = partition_tokens;
+  p.partial = 1;
+  p.part_ml = static_cast<float*>(workspace);
+  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = launch_attention(dims, variant, p, s);
+  if (st != PA_OK) return st;
+  return launch_status(pa::launch_merge_partials(p, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,405 @@
+// Paged decode attention on the vector ALUs (gfx950, wave64).
+//
+// What is computed. For each query row (token t, head h) of a sequence of
+// length L, scores s_p = scale * q . K[p] over the visible positions
+// p <= L - T + t. K[p] and V[p] are read through the block table (physical
+// block table[p / b], offset p % b). The result is o = sum_p softmax(s)_p V[p]
+// ([P1] "25. Paged attention and prefix caching", section "Attention that
+// reads through the table"; [P5] "Chapter 7 Paged KV Cache and Memory
+// Management", sections 4.1-4.2). Softmax is online, per [P5] section 4.2: a
+// running reference max m, a sum l and an accumulator acc that always share
+// that reference, merged exactly at the end.
+//
+// Mapping onto the hardware. One workgroup of NW waves handles one
+// (sequence, kv head, context partition, group of up to 8 query rows). All
+// query rows of the GQA group share every K/V byte the workgroup loads. The
+// partition's positions are cut into tiles of 16. A kv head's row is 256
+// bytes (128 bf16 or 64 fp32), so one tile of K is 4 KiB. Wave w takes tiles
+// w, w + NW, ... and, while it computes tile i, its loads for tile i + 1 are
+// already in flight. Physical block ids for a wave's tiles are fetched up
+// front, one per lane, and read with v_readlane, so no table lookup sits on
+// the critical path.
+//  * K layout: lane = 4*ts + j holds token ts of the tile, 16-byte chunks
+//    4*r + j (r = 0..3). Four adjacent lanes read 64 contiguous bytes.
+//    q . k is 16 v_dot2_f32_bf16 per row (fp32: 16 FMAs), then a 2-step DPP
+//    quad reduction.
+//  * V layout: lane = 16*R + cv holds chunk cv of tokens 4R + r. Each lane
+//    accumulates a contiguous 8-element (bf16) or 4-element (fp32) slice of
+//    head_dim for every row, so P.V needs no cross-lane reduction. The
+//    probabilities move from the K lanes to the V lanes through 16 * NR
+//    floats of LDS per wave.
+//  * Lazy max: the reference max of a row is only raised when a score
+//    exceeds it by more than 2^8 (base-2 units). That happens once per row in
+//    practice, so the common path rescales nothing. acc and l stay within
+//    fp32 range (p <= 256), and o = acc / l is unchanged because both share
+//    the same reference ([P5] section 4.2).
+//  * Masking: only tiles that reach past the fully visible prefix, and row
+//    groups with absent rows, take the masked path. There, invisible scores
+//    become -inf, and V chunks of positions >= L are zeroed before use, since
+//    those slots may hold any bits (a 0 * NaN product would otherwise leak).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kTile = 16;             // positions per wave tile
+constexpr int kRowBytes = 256;        // one kv head's K or V row
+constexpr float kRescaleSlack = 8.0f; // lazy-max slack, base-2 exponent units
+constexpr int kWaves = 4;             // waves per workgroup
+
+template <bool BF16>
+struct KvFmt {
+  static constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+};
+
+struct Tile {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+template <bool BF16, int NR, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams p) {
+  constexpr int E = KvFmt<BF16>::E;
+  constexpr int D = 16 * E;
+  constexpr int NPL = NR >= 4 ? NR / 4 : 1;  // rows each K lane turns into probabilities
+
+  __shared__ float p_lds[NW][kTile][NR];
+  __shared__ float red_acc[NW][NR][D];
+  __shared__ float red_m[NW][NR];
+  __shared__ float red_l[NW][NR];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // Block id = ((seq * parts + part) * row_groups + rg) * Hkv + kvh: workgroups are dealt
+  // round-robin to the 8 XCDs, so with Hkv = 8 every workgroup of one kv head shares an L2.
+  int bid = blockIdx.x;
+  const int kvh = bid % p.Hkv;
+  bid /= p.Hkv;
+  const int rg = bid % p.row_groups;
+  bid /= p.row_groups;
+  const int part = bid % p.parts;
+  const int seq = bid / p.parts;
+
+  const int L = p.seq_lens[seq];
+  const int T = p.T;
+  const int p_begin = part * p.part_tokens;
+  if (p.partial && p_begin >= L) return;  // empty partition: the merge pass never reads it
+  const int p_end = min(L, p_begin + p.part_tokens);
+  const int ntiles = p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
+  const int vis_all = L - T + 1;  // positions below this are visible to every query row
+
+  const int ts = lane >> 2, j = lane & 3;  // K lanes
+  const int R = lane >> 4, cv = lane & 15; // V lanes
+
+  // ---- query rows: row n of this group is global row rg*NR + n = t*G + g
+  int row_lim[NR];  // last visible position; -1 for an absent row
+  bool rows_all_present = true;
+  u32x4 qv[NR][4];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int r = rg * NR + n;
+    if (r < p.rows) {
+      const int t = r / p.G, g = r % p.G;
+      row_lim[n] = L - T + t;
+      const char* qrow =
+          static_cast<const char*>(p.q) + ((int64_t)(seq * T + t) * p.Hq + kvh * p.G + g) * kRowBytes;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[n][c] = load16(qrow + (c * 4 + j) * 16);
+    } else {
+      row_lim[n] = -1;
+      rows_all_present = false;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[n][c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
+  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
+  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
+  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
+  const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
+
+  // Physical block of the wave's i-th tile (blocks of >= 16 positions): lane i - tab_base of tab_v.
+  int tab_base = -64;
+  int tab_v = 0;
+  auto refill_table = [&](int base) {
+    tab_base = base;
+    const int i = base + lane;
+    tab_v = 0;
+    if (i < my_tiles) tab_v = trow[(p_begin + (wave + i * NW) * kTile) / BS];
+  };
+
+  auto load_tile = [&](int i, Tile& tl) {
+    const int tile_p0 = p_begin + (wave + i * NW) * kTile;
+    if constexpr (BS >= kTile) {
+      if (i - tab_base >= 64) refill_table(i);
+      const int64_t phys = __builtin_amdgcn_readlane(tab_v, i - tab_base);
+      const int64_t off = phys * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
+      const char* kb = kbase + off;
+      const char* vb = vbase + off;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tl.k[c] = load16(kb + ts * kRowBytes + (c * 4 + j) * 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tl.v[c] = load16(vb + (4 * R + c) * kRowBytes + cv * 16);
+    } else {
+      // Blocks shorter than a tile: each lane finds its own block. Positions past the
+      // sequence are clamped to its last position (a valid slot), then masked.
+      const int pk = min(tile_p0 + ts, L - 1);
+      const char* kb = kbase + (int64_t)trow[pk / BS] * block_bytes + (int64_t)(pk % BS) * kRowBytes;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tl.k[c] = load16(kb + (c * 4 + j) * 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int pv = min(tile_p0 + 4 * R + c, L - 1);
+        tl.v[c] = load16(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * kRowBytes +
+                         cv * 16);
+      }
+    }
+  };
+
+  float m_ref[NR];
+  float l_part[NPL];
+  float acc[NR][E];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    m_ref[n] = kNegInf;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[n][e] = 0.f;
+  }
+#pragma unroll
+  for (int nl = 0; nl < NPL; ++nl) l_part[nl] = 0.f;
+
+  auto row_of = [&](int nl) { return NR >= 4 ? nl * 4 + j : j; };
+
+  auto compute_tile = [&](int i, const Tile& tl) {
+    const int tile_p0 = p_begin + (wave + i * NW) * kTile;
+    const bool masked = !rows_all_present || (tile_p0 + kTile > vis_all);
+
+    // ---- scores of token ts for every row (all four lanes of the quad end up with them)
+    float s[NR];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (BF16)
+            a = dot2_bf16(qv[n][c][w], tl.k[c][w], a);
+          else
+            a = fmaf(__uint_as_float(qv[n][c][w]), __uint_as_float(tl.k[c][w]), a);
+        }
+      }
+      a += quad_xor1(a);
+      a += quad_xor2(a);
+      s[n] = a * p.qk_scale_log2;
+    }
+    if (masked) {
+      const int pk = tile_p0 + ts;
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+        if (pk > row_lim[n]) s[n] = kNegInf;
+    }
+
+    // ---- lazy reference max (wave-uniform per row)
+    bool over = false;
+#pragma unroll
+    for (int n = 0; n < NR; ++n) over |= s[n] > m_ref[n] + kRescaleSlack;
+    if (__builtin_expect(__any(over), 0)) {
+#pragma unroll
+      for (int n = 0; n < NR; ++n) {
+        const float m_new = fmaxf(m_ref[n], wave_max(s[n]));
+        if (m_new > m_ref[n]) {
+          const float alpha = exp2_fast(m_ref[n] - m_new);  // 0 when m_ref was -inf
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[n][e] *= alpha;
+#pragma unroll
+          for (int nl = 0; nl < NPL; ++nl)
+            if (row_of(nl) == n) l_part[nl] *= alpha;
+          m_ref[n] = m_new;
+        }
+      }
+    }
+
+    // ---- probabilities of this lane's rows, handed to the V lanes through LDS
+#pragma unroll
+    for (int nl = 0; nl < NPL; ++nl) {
+      constexpr int kSel = NR >= 4 ? 4 : NR;
+      float x = s[NR >= 4 ? nl * 4 : 0];
+      float m = m_ref[NR >= 4 ? nl * 4 : 0];
+#pragma unroll
+      for (int jj = 1; jj < kSel; ++jj) {
+        if (j == jj) {
+          x = s[(NR >= 4 ? nl * 4 : 0) + jj];
+          m = m_ref[(NR >= 4 ? nl * 4 : 0) + jj];
+        }
+      }
+      float pr = x == kNegInf ? 0.f : exp2_fast(x - m);
+      if (NR < 4 && j >= NR) pr = 0.f;
+      l_part[nl] += pr;
+      if (NR >= 4 || j < NR) p_lds[wave][ts][row_of(nl)] = pr;
+    }
+    // One wave writes and reads its own LDS slice; its LDS operations execute in order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- P.V on this lane's head_dim slice
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float pv[NR];
+#pragma unroll
+      for (int n = 0; n < NR; ++n) pv[n] = p_lds[wave][4 * R + c][n];
+      u32x4 v = tl.v[c];
+      if (masked && tile_p0 + 4 * R + c >= L) v = u32x4{0u, 0u, 0u, 0u};
+      float vf[E];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (BF16) {
+          vf[2 * w] = bf16_lo(v[w]);
+          vf[2 * w + 1] = bf16_hi(v[w]);
+        } else {
+          vf[w] = __uint_as_float(v[w]);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[n][e] = fmaf(pv[n], vf[e], acc[n][e]);
+    }
+  };
+
+  // ---- tile loop, two register buffers so tile i + 1 loads while tile i computes
+  if (my_tiles > 0) {
+    Tile ta, tb;
+    load_tile(0, ta);
+    int i = 0;
+    while (true) {
+      if (i + 1 < my_tiles) load_tile(i + 1, tb);
+      compute_tile(i, ta);
+      if (++i >= my_tiles) break;
+      if (i + 1 < my_tiles) load_tile(i + 1, ta);
+      compute_tile(i, tb);
+      if (++i >= my_tiles) break;
+    }
+  }
+
+  // ---- merge the four V-lane groups, then the waves, then write out or emit the partial
+#pragma unroll
+  for (int n = 0; n < NR; ++n)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float a = acc[n][e];
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      acc[n][e] = a;
+    }
+#pragma unroll
+  for (int nl = 0; nl < NPL; ++nl) {
+    float l = l_part[nl];
+    l += __shfl_xor(l, 4, 64);
+    l += __shfl_xor(l, 8, 64);
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (ts == 0 && (NR >= 4 || j < NR)) red_l[wave][row_of(nl)] = l;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int n = 0; n < NR; ++n) red_m[wave][n] = m_ref[n];
+  }
+  if (R == 0) {
+#pragma unroll
+    for (int n = 0; n < NR; ++n)
+#pragma unroll
+      for (int e = 0; e < E; ++e) red_acc[wave][n][cv * E + e] = acc[n][e];
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < NR * D; idx += NW * 64) {
+    const int n = idx / D, d = idx % D;
+    const int r = rg * NR + n;
+    if (r >= p.rows) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][n]);
+    float lsum = 0.f, a = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = red_m[w][n];
+        if (mw != kNegInf) {
+          const float sc = exp2_fast(mw - M);
+          lsum = fmaf(sc, red_l[w][n], lsum);
+          a = fmaf(sc, red_acc[w][n][d], a);
+        }
+      }
+    }
+    const int t = r / p.G, g = r % p.G;
+    const int64_t orow = (int64_t)(seq * T + t) * p.Hq + kvh * p.G + g;
+    if (p.partial) {
+      const int64_t pi = orow * p.parts + part;
+      p.part_acc[pi * D + d] = a;
+      if (d == 0) {
+        p.part_ml[pi * 2] = M;
+        p.part_ml[pi * 2 + 1] = lsum;
+      }
+    } else {
+      const float o = lsum > 0.f ? a / lsum : 0.f;
+      if (p.out_dtype == PA_F32)
+        static_cast<float*>(p.out)[orow * D + d] = o;
+      else
+        static_cast<uint16_t*>(p.out)[orow * D + d] = f32_to_bf16(o);
+    }
+  }
+}
+
+template <bool BF16, int NR, int BS>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.B * p.parts * p.row_groups * p.Hkv;
+  if (grid == 0) return hipSuccess;
+  decode_valu_kernel<BF16, NR, BS, kWaves><<<dim3((unsigned)grid), dim3(kWaves * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int NR>
+hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
+  switch (p.block_size) {
+    case 4: return launch_t<BF16, NR, 4>(p, stream);
+    case 8: return launch_t<BF16, NR, 8>(p, stream);
+    case 16: return launch_t<BF16, NR, 16>(p, stream);
+    case 32: return launch_t<BF16, NR, 32>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BF16>
+hipError_t launch_nr(const DecodeParams& p, hipStream_t stream) {
+  switch (valu_rows_per_group(p.rows)) {
+    case 1: return launch_bs<BF16, 1>(p, stream);
+    case 2: return launch_bs<BF16, 2>(p, stream);
+    case 4: return launch_bs<BF16, 4>(p, stream);
+    default: return launch_bs<BF16, 8>(p, stream);
+  }
+}
+
+}  // namespace
+
+int valu_rows_per_group(int rows) {
+  if (rows >= 8) return 8;
+  int nr = 1;
+  while (nr < rows) nr *= 2;
+  return nr;
+}
+
+bool valu_supported(const pa_dims& d) {
+  const bool shape = (d.kv_dtype == PA_BF16 && d.head_dim == 128) || (d.kv_dtype == PA_F32 && d.head_dim == 64);
+  const bool block = d.block_size == 4 || d.block_size == 8 || d.block_size == 16 || d.block_size == 32;
+  return shape && block && d.q_dtype == d.kv_dtype;
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
+  return kv_dtype == PA_BF16 ? launch_nr<true>(p, stream) : launch_nr<false>(p, stream);
+}
+
+}  // namespace pa

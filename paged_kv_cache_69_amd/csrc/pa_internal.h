@@ -1,0 +1,47 @@
+// Internal declarations shared by the HIP sources of libpa.so (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;  // log2(e): scores are kept in base-2 units
+
+// Everything a decode launch needs, in one kernel argument.
+struct DecodeParams {
+  const void* q;             // [B, T, Hq, D]
+  const void* k_pool;        // [N, Hkv, b, D]
+  const void* v_pool;        // [N, Hkv, b, D]
+  const int32_t* block_tables;  // [B, MB]
+  const int32_t* seq_lens;   // [B]
+  void* out;                 // [B, T, Hq, D] (single-pass launches)
+  float* part_ml;            // [B*T*Hq, parts, 2]: (m, l) per partition (partitioned launches)
+  float* part_acc;           // [B*T*Hq, parts, D]: unnormalised accumulator per partition
+  float qk_scale_log2;       // scale * log2(e): scores are kept in base-2 exponent units
+  int32_t B, T, Hq, Hkv, G, D, MB, block_size;
+  int32_t rows;              // T * G query rows that share one kv head
+  int32_t row_groups;        // workgroups along the rows, per (sequence, kv head, partition)
+  int32_t parts;             // partitions per sequence in the grid (1 for single pass)
+  int32_t part_tokens;       // positions per partition (single pass: >= every length)
+  int32_t out_dtype;         // pa_dtype of out
+  int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
+};
+
+hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
+                           void* v_pool, const int32_t* block_tables, const int32_t* positions,
+                           hipStream_t stream);
+
+// Rows handled by one VALU workgroup for `rows` query rows per kv head.
+int valu_rows_per_group(int rows);
+bool valu_supported(const pa_dims& d);
+hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t stream);
+
+bool mfma_supported(const pa_dims& d);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace pa

@@ -61,3 +61,33 @@ def oracle_after_write(case):
     """The oracle's pools after the step's KV write, as numpy bit arrays."""
     return oracle.write_kv(bits(case.k_pool), bits(case.v_pool), bits(case.k_new), bits(case.v_new),
                            case.block_tables.numpy(), case.positions.numpy(), case.block_size)
+
+
+def assert_attention_close(got, ref, *, kv_dtype, out_dtype, what=""):
+    """The parity bar for attention outputs.
+
+    * fp32 inputs: for every output row, max_d |got - ref| <= 1e-5 * max_d |ref| (1e-5 relative).
+    * bf16 inputs (fp32 accumulation): |got - ref| <= 2e-3 elementwise, against the oracle run on
+      the same bf16-rounded inputs.
+    * bf16 outputs also get half a bf16 ulp of |ref| on top, the rounding of the stored result.
+    """
+    if isinstance(got, torch.Tensor):
+        got = got.detach().cpu().double().numpy()
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    if out_dtype == torch.bfloat16:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        extra = 0.5 * ulp
+    else:
+        extra = 0.0
+    if kv_dtype == torch.float32:
+        bound = 1e-5 * np.abs(ref).max(axis=-1, keepdims=True) + extra
+    else:
+        bound = 2e-3 + extra
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance; max err {err.max():.3e}; "
+                           f"worst at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+    return float(err.max())

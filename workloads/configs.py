@@ -38,7 +38,7 @@ _FILL_CHUNK = 1 << 25  # elements drawn per randn call when filling big pools
 
 @dataclass
 class Case:
-    """One decode step's inputs, as CPU tensors.
+    """One decode step's inputs, as tensors on the CPU (pools: on the device they were drawn on).
 
     Layouts: ``q [B, T, Hq, D]``; ``k_new``/``v_new [B, T, Hkv, D]``;
     ``k_pool``/``v_pool [N, Hkv, b, D]``; ``block_tables [B, MB]`` int32, where
@@ -82,12 +82,13 @@ def _randn(shape, gen, dtype):
 
 
 def _fill_pool(shape, gen, dtype):
-    """N(0,1) pool, drawn in bounded chunks so big pools never need a full fp32 copy."""
-    out = torch.empty(shape, dtype=dtype)
+    """N(0,1) pool drawn in bounded chunks, so big pools never need a full fp32 copy.
+    ``gen`` is a CPU or CUDA torch.Generator; the pool lives on the generator's device."""
+    out = torch.empty(shape, dtype=dtype, device=gen.device)
     flat = out.view(-1)
     for start in range(0, flat.numel(), _FILL_CHUNK):
         n = min(_FILL_CHUNK, flat.numel() - start)
-        flat[start:start + n] = torch.randn(n, generator=gen, dtype=torch.float32).to(dtype)
+        flat[start:start + n] = torch.randn(n, generator=gen, dtype=torch.float32, device=gen.device).to(dtype)
     return out
 
 
@@ -97,7 +98,8 @@ def _ceil_div(a: int, b: int) -> int:
 
 def build_case(*, name="custom", lengths, num_q_heads, num_kv_heads, head_dim, block_size,
                q_tokens=1, dtype=torch.bfloat16, seed=0, num_blocks=None, shared_prefix_blocks=0,
-               table_pad=INT32_MAX, pool_slack=0.0, explicit_tables=None, poison_unused=True):
+               table_pad=INT32_MAX, pool_slack=0.0, explicit_tables=None, poison_unused=True,
+               pool_device="cpu"):
     """General builder used by every named workload.
 
     Blocks are handed out like a free list over a seeded permutation of the
@@ -107,6 +109,10 @@ def build_case(*, name="custom", lengths, num_q_heads, num_kv_heads, head_dim, b
     equals the number of sequences, as in a forked or prefix-cached prompt
     ([P1] "Sharing blocks"). When ``explicit_tables`` is given, those rows are
     used as they are.
+
+    The pools are drawn on ``pool_device``: CPU by default, or a GPU, where a seeded torch
+    CUDA generator makes multi-GB pools in moments. All other tensors are always drawn on
+    the CPU.
     """
     gen = torch.Generator().manual_seed(int(seed))
     lengths = [int(x) for x in lengths]
@@ -145,12 +151,15 @@ def build_case(*, name="custom", lengths, num_q_heads, num_kv_heads, head_dim, b
     k_new = _randn((n_seq, t, hkv, d), gen, dtype)
     v_new = _randn((n_seq, t, hkv, d), gen, dtype)
     pool_shape = (num_blocks, hkv, block_size, d)
-    k_pool = _fill_pool(pool_shape, gen, dtype)
-    v_pool = _fill_pool(pool_shape, gen, dtype)
+    pool_gen = gen
+    if torch.device(pool_device).type != "cpu":
+        pool_gen = torch.Generator(device=pool_device).manual_seed(int(seed) + 1)
+    k_pool = _fill_pool(pool_shape, pool_gen, dtype)
+    v_pool = _fill_pool(pool_shape, pool_gen, dtype)
     unused = torch.tensor(perm_unused, dtype=torch.int64)
     if poison_unused and unused.numel():
-        k_pool[unused] = float("nan")
-        v_pool[unused] = float("nan")
+        k_pool[unused.to(k_pool.device)] = float("nan")
+        v_pool[unused.to(v_pool.device)] = float("nan")
     seq_lens = torch.tensor(lengths, dtype=torch.int32)
     positions = torch.stack([torch.arange(L - t, L, dtype=torch.int32) for L in lengths]) \
         if n_seq else torch.empty((0, t), dtype=torch.int32)
@@ -184,13 +193,13 @@ def config_lengths(name: str, gen: torch.Generator, num_seqs: int | None = None)
 
 
 def make_case(name: str, *, num_seqs: int | None = None, seed: int | None = None,
-              table_pad: int = INT32_MAX, poison_unused: bool = True) -> Case:
+              table_pad: int = INT32_MAX, poison_unused: bool = True, pool_device="cpu") -> Case:
     """Build a named workload; ``num_seqs`` keeps only its first sequences."""
     seed = _SEEDS[name] if seed is None else seed
     gen = torch.Generator().manual_seed(seed)
     lens = config_lengths(name, gen, num_seqs)
     common = dict(name=name, lengths=lens, seed=seed + 7919, table_pad=table_pad,
-                  poison_unused=poison_unused)
+                  poison_unused=poison_unused, pool_device=pool_device)
     if name == "tiny":
         return build_case(num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
                           dtype=torch.float32, num_blocks=32, **common)
