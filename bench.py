@@ -7,10 +7,11 @@ scatter (pa_write_kv), then decode attention over every sequence
 synthetic, seeded and resident in HBM before the timed region starts.
 R independent replicas of (pools, tables, q, new rows) are rotated step by
 step, so the 256 MB Infinity Cache cannot serve the KV of one step from the
-previous one; R * (bytes one step touches) >= 1 GB. Steps are captured in HIP
-graphs, one step per replica, so host launch cost is not timed. HIP events
-recorded inside the captured graphs, on the same stream, time every decode
-launch in the timed region.
+previous one; R * (bytes one step touches) >= 1 GB. The K timed steps run as
+HIP graph replays (one captured step per replica), so host launch cost is not
+timed; that gives `value`. The same K steps are then launched directly with a
+pair of HIP events on the launch stream around every decode call, which gives
+the dominant kernel's average duration for `roofline`.
 
 Prints one JSON line. `value` is decode tokens per second of the whole step.
 `roofline` relates the dominant kernel's algorithmic bytes to its measured
@@ -86,7 +87,7 @@ def unique_bytes(case) -> int:
 class Replica:
     """One independent copy of a step's device inputs, with ctypes arguments prepacked."""
 
-    def __init__(self, pa, case, src, partition_tokens):
+    def __init__(self, pa, case, src, partition_tokens, variant=0):
         import ctypes
 
         import torch
@@ -94,7 +95,8 @@ class Replica:
         self.t = {k: v.clone() for k, v in src.items()}
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device=src["q"].device)
         self.lib = pa.load_library()
-        self.dims = pa.make_dims(self.t["q"], self.t["k_pool"], self.t["block_tables"], out_dtype=torch.float32)
+        self.dims = pa.make_dims(self.t["q"], self.t["k_pool"], self.t["block_tables"], out_dtype=torch.float32,
+                                 variant=variant)
         kd = case.k_pool.shape
         code = pa.dtype_code(case.k_pool.dtype)
         self.wdims = pa.PaDims(case.q.shape[0], case.q.shape[1], kd[1], kd[1], kd[3], kd[2], kd[0],
@@ -128,7 +130,7 @@ class Replica:
             raise RuntimeError(f"decode: {st}")
 
 
-def measure_gpu(pa, case, partition_tokens, steps, warmup):
+def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0):
     """Returns (seconds per step, per-launch decode-kernel ms list, replicas)."""
     import ctypes
 
@@ -139,7 +141,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup):
                                                    "seq_lens", "positions")}
     touched = algorithmic_bytes(case)
     n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
-    reps = [Replica(pa, case, src, partition_tokens) for _ in range(n_rep)]
+    reps = [Replica(pa, case, src, partition_tokens, variant) for _ in range(n_rep)]
     del src
     torch.cuda.synchronize()
 
@@ -153,10 +155,9 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup):
         r.decode(sh())
     torch.cuda.synchronize()
 
-    # one graph per chunk of consecutive steps; events bracket every decode launch
+    # Timed region A: the K steps as HIP graph replays (one graph per chunk of consecutive steps).
     def capture(first_step, count):
         g = torch.cuda.CUDAGraph()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -164,25 +165,20 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup):
                 for c in range(count):
                     r = reps[(first_step + c) % n_rep]
                     r.write(sh())
-                    evs[c][0].record()
                     r.decode(sh())
-                    evs[c][1].record()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        return g, evs
+        return g
 
     chunk = n_rep
-    full, full_evs = capture(0, chunk)
+    full = capture(0, chunk)
     rem = steps % chunk
-    tail, tail_evs = capture(0, rem) if rem else (None, [])
-    # warm the graphs once (instantiation/upload), outside the timed region
-    full.replay()
+    tail = capture(0, rem) if rem else None
+    full.replay()  # instantiate/upload once, outside the timed region
     if tail is not None:
         tail.replay()
     torch.cuda.synchronize()
 
-    kernel_ms = []
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps // chunk):
         full.replay()
@@ -190,10 +186,21 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup):
         tail.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # the last replay of each graph is inside the timed region; read its per-launch durations
-    if steps // chunk:
-        kernel_ms += [a.elapsed_time(b) for a, b in full_evs]
-    kernel_ms += [a.elapsed_time(b) for a, b in tail_evs]
+
+    # Timed region B: the same K steps launched directly, with HIP events on the launch stream
+    # bracketing every decode call (for a partitioned decode: both of its kernels).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    for s in range(steps):
+        r = reps[s % n_rep]
+        r.write(handle)
+        evs[s][0].record(stream)
+        r.decode(handle)
+        evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in evs]
     return (t1 - t0) / steps, kernel_ms, reps
 
 
@@ -234,19 +241,21 @@ def cpu_baseline(case, budget_s: float):
                       f"({int(case.seq_lens[:n].sum())} positions), one thread, {dt:.1f} s"}
 
 
-def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget):
+def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0):
     import torch
 
     from workloads import make_case
 
     spec = WORKLOADS[name]
     case = make_case(name, pool_device="cuda:0")
-    sec_per_step, kernel_ms, reps = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup)
+    sec_per_step, kernel_ms, reps = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant)
     b, t = case.q.shape[0], case.q.shape[1]
     algo = algorithmic_bytes(case, include_out=spec["partition_tokens"] is None)
     dur_ms = sum(kernel_ms) / max(1, len(kernel_ms))
     achieved = algo / (dur_ms * 1e-3) / 1e9
-    kernel = "decode_valu_kernel" if case.q.shape[2] // case.k_pool.shape[1] * t <= 8 else "decode kernel"
+    rows = case.q.shape[2] // case.k_pool.shape[1] * t
+    mfma_ok = case.k_pool.dtype == torch.bfloat16 and case.q.shape[3] == 128 and rows <= 32
+    kernel = "decode_mfma_kernel" if (variant == 2 or (variant == 0 and mfma_ok)) else "decode_valu_kernel"
     res = {
         "tokens_per_s": b * t / sec_per_step,
         "ms_per_step": sec_per_step * 1e3,
@@ -280,6 +289,7 @@ def main(argv=None):
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 vector-ALU kernel, 2 MFMA kernel")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode step needs no "
@@ -294,7 +304,8 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     pa.load_library()
-    main_res = run_workload(pa, args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_budget)
+    main_res = run_workload(pa, args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_budget,
+                            args.variant)
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 1),
@@ -317,7 +328,7 @@ def main(argv=None):
         line["cpu_baseline"] = main_res["cpu_baseline"]
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = run_workload(pa, name, args.steps, args.warmup, False, 0)
+        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant)
         secondary[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 6),
                            "achieved_gbps": round(r["achieved_gbps"], 1), "roofline": r["roofline"],
                            "config": r["config"], **({"unique_bytes": r["unique_bytes"]} if "unique_bytes" in r else {})}

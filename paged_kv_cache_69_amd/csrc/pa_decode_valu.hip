@@ -46,7 +46,26 @@ namespace {
 constexpr int kTile = 16;             // positions per wave tile
 constexpr int kRowBytes = 256;        // one kv head's K or V row
 constexpr float kRescaleSlack = 8.0f; // lazy-max slack, base-2 exponent units
-constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kTableChunk = 64;       // tiles whose physical block ids one table fetch covers
+
+// Launch shape: waves per workgroup, tiles each wave keeps in flight ahead of
+// the one it computes, q staged in LDS instead of registers, non-temporal K/V loads.
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 4
+#endif
+#ifndef PA_VALU_PREFETCH
+#define PA_VALU_PREFETCH 1
+#endif
+#ifndef PA_VALU_Q_IN_LDS
+#define PA_VALU_Q_IN_LDS 0
+#endif
+#ifndef PA_VALU_NT_LOADS
+#define PA_VALU_NT_LOADS 0
+#endif
+constexpr int kWaves = PA_VALU_WAVES;
+constexpr int kPrefetch = PA_VALU_PREFETCH;
+constexpr bool kQInLds = PA_VALU_Q_IN_LDS != 0;
+constexpr bool kNtLoads = PA_VALU_NT_LOADS != 0;
 
 template <bool BF16>
 struct KvFmt {
@@ -58,13 +77,22 @@ struct Tile {
   u32x4 v[4];
 };
 
-template <bool BF16, int NR, int BS, int NW>
+template <bool NT>
+__device__ __forceinline__ u32x4 load_kv16(const char* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return load16(p);
+}
+
+template <bool BF16, int NR, int BS, int NW, int PF, bool QLDS, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams p) {
   constexpr int E = KvFmt<BF16>::E;
   constexpr int D = 16 * E;
   constexpr int NPL = NR >= 4 ? NR / 4 : 1;  // rows each K lane turns into probabilities
 
   __shared__ float p_lds[NW][kTile][NR];
+  __shared__ u32x4 q_lds[QLDS ? NR : 1][16];
   __shared__ float red_acc[NW][NR][D];
   __shared__ float red_m[NW][NR];
   __shared__ float red_l[NW][NR];
@@ -95,24 +123,37 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   // ---- query rows: row n of this group is global row rg*NR + n = t*G + g
   int row_lim[NR];  // last visible position; -1 for an absent row
   bool rows_all_present = true;
-  u32x4 qv[NR][4];
+  u32x4 qv[QLDS ? 1 : NR][4];
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
     const int r = rg * NR + n;
-    if (r < p.rows) {
-      const int t = r / p.G, g = r % p.G;
-      row_lim[n] = L - T + t;
-      const char* qrow =
-          static_cast<const char*>(p.q) + ((int64_t)(seq * T + t) * p.Hq + kvh * p.G + g) * kRowBytes;
+    row_lim[n] = r < p.rows ? L - T + r / p.G : -1;
+    rows_all_present = rows_all_present && r < p.rows;
+  }
+  auto q_row_ptr = [&](int n) {
+    const int r = rg * NR + n;
+    return static_cast<const char*>(p.q) + ((int64_t)(seq * T + r / p.G) * p.Hq + kvh * p.G + r % p.G) * kRowBytes;
+  };
+  if constexpr (QLDS) {
+    for (int idx = threadIdx.x; idx < NR * 16; idx += NW * 64) {
+      const int n = idx >> 4, c = idx & 15;
+      q_lds[n][c] = rg * NR + n < p.rows ? load16(q_row_ptr(n) + c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qv[n][c] = load16(qrow + (c * 4 + j) * 16);
-    } else {
-      row_lim[n] = -1;
-      rows_all_present = false;
+    for (int n = 0; n < NR; ++n) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qv[n][c] = u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < 4; ++c)
+        qv[QLDS ? 0 : n][c] = rg * NR + n < p.rows ? load16(q_row_ptr(n) + (c * 4 + j) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  auto q_chunk = [&](int n, int c) -> u32x4 {
+    if constexpr (QLDS)
+      return q_lds[n][c * 4 + j];
+    else
+      return qv[QLDS ? 0 : n][c];
+  };
 
   const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
@@ -120,8 +161,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
   const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
 
-  // Physical block of the wave's i-th tile (blocks of >= 16 positions): lane i - tab_base of tab_v.
-  int tab_base = -64;
+  // Physical block of the wave's i-th tile (blocks of >= 16 positions) is lane i - tab_base of
+  // tab_v, fetched once per chunk of kTableChunk tiles so no table load sits inside the pipeline.
+  int tab_base = 0;
   int tab_v = 0;
   auto refill_table = [&](int base) {
     tab_base = base;
@@ -133,27 +175,26 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   auto load_tile = [&](int i, Tile& tl) {
     const int tile_p0 = p_begin + (wave + i * NW) * kTile;
     if constexpr (BS >= kTile) {
-      if (i - tab_base >= 64) refill_table(i);
       const int64_t phys = __builtin_amdgcn_readlane(tab_v, i - tab_base);
       const int64_t off = phys * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
       const char* kb = kbase + off;
       const char* vb = vbase + off;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.k[c] = load16(kb + ts * kRowBytes + (c * 4 + j) * 16);
+      for (int c = 0; c < 4; ++c) tl.k[c] = load_kv16<NT>(kb + ts * kRowBytes + (c * 4 + j) * 16);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.v[c] = load16(vb + (4 * R + c) * kRowBytes + cv * 16);
+      for (int c = 0; c < 4; ++c) tl.v[c] = load_kv16<NT>(vb + (4 * R + c) * kRowBytes + cv * 16);
     } else {
       // Blocks shorter than a tile: each lane finds its own block. Positions past the
       // sequence are clamped to its last position (a valid slot), then masked.
       const int pk = min(tile_p0 + ts, L - 1);
       const char* kb = kbase + (int64_t)trow[pk / BS] * block_bytes + (int64_t)(pk % BS) * kRowBytes;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.k[c] = load16(kb + (c * 4 + j) * 16);
+      for (int c = 0; c < 4; ++c) tl.k[c] = load_kv16<NT>(kb + (c * 4 + j) * 16);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int pv = min(tile_p0 + 4 * R + c, L - 1);
-        tl.v[c] = load16(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * kRowBytes +
-                         cv * 16);
+        tl.v[c] = load_kv16<NT>(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * kRowBytes +
+                                cv * 16);
       }
     }
   };
@@ -183,12 +224,13 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
       float a = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        const u32x4 qc = q_chunk(n, c);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if constexpr (BF16)
-            a = dot2_bf16(qv[n][c][w], tl.k[c][w], a);
+            a = dot2_bf16(qc[w], tl.k[c][w], a);
           else
-            a = fmaf(__uint_as_float(qv[n][c][w]), __uint_as_float(tl.k[c][w]), a);
+            a = fmaf(__uint_as_float(qc[w]), __uint_as_float(tl.k[c][w]), a);
         }
       }
       a += quad_xor1(a);
@@ -270,18 +312,23 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
     }
   };
 
-  // ---- tile loop, two register buffers so tile i + 1 loads while tile i computes
-  if (my_tiles > 0) {
-    Tile ta, tb;
-    load_tile(0, ta);
-    int i = 0;
-    while (true) {
-      if (i + 1 < my_tiles) load_tile(i + 1, tb);
-      compute_tile(i, ta);
-      if (++i >= my_tiles) break;
-      if (i + 1 < my_tiles) load_tile(i + 1, ta);
-      compute_tile(i, tb);
-      if (++i >= my_tiles) break;
+  // ---- tile loop: a ring of PF + 1 register tiles, so tiles i+1 .. i+PF load while tile i computes
+  for (int chunk0 = 0; chunk0 < my_tiles; chunk0 += kTableChunk) {
+    const int n_here = min(kTableChunk, my_tiles - chunk0);
+    if constexpr (BS >= kTile) refill_table(chunk0);
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < n_here) load_tile(chunk0 + u, ring[u]);
+    for (int i0 = 0; i0 < n_here; i0 += PF + 1) {
+#pragma unroll
+      for (int u = 0; u <= PF; ++u) {
+        const int i = i0 + u;
+        if (i < n_here) {
+          if (i + PF < n_here) load_tile(chunk0 + i + PF, ring[(u + PF) % (PF + 1)]);
+          compute_tile(chunk0 + i, ring[u]);
+        }
+      }
     }
   }
 
@@ -358,7 +405,8 @@ template <bool BF16, int NR, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.B * p.parts * p.row_groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_valu_kernel<BF16, NR, BS, kWaves><<<dim3((unsigned)grid), dim3(kWaves * 64), 0, stream>>>(p);
+  decode_valu_kernel<BF16, NR, BS, kWaves, kPrefetch, kQInLds, kNtLoads>
+      <<<dim3((unsigned)grid), dim3(kWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -109,26 +109,30 @@ def test_decode_tiny_fp32(gpu_lib, name, partitioned):
     _check_step(gpu_lib, make_case(name), partitioned=partitioned, partition_tokens=16)
 
 
+@pytest.mark.parametrize("variant", [VALU, MFMA])
 @pytest.mark.parametrize("name,num_seqs", [("batch64", 8), ("long", 2), ("prefix", 4), ("spec", 3)])
 @pytest.mark.parametrize("partitioned", [False, True])
-def test_decode_config_shapes_bf16(gpu_lib, name, num_seqs, partitioned):
-    """Each bf16 workload's shapes and length mix, on its first sequences (the oracle runs in full)."""
-    _check_step(gpu_lib, make_case(name, num_seqs=num_seqs), partitioned=partitioned, partition_tokens=512)
+def test_decode_config_shapes_bf16(gpu_lib, name, num_seqs, partitioned, variant):
+    """Each bf16 workload's shapes and length mix, on its first sequences (the oracle runs in full),
+    through both kernel families."""
+    _check_step(gpu_lib, make_case(name, num_seqs=num_seqs), partitioned=partitioned, partition_tokens=512,
+                variant=variant)
 
 
+@pytest.mark.parametrize("variant", [VALU, MFMA])
 @pytest.mark.parametrize("b", [4, 8, 16, 32])
 @pytest.mark.parametrize("hq,hkv,t", [(4, 4, 1), (8, 4, 1), (8, 2, 1), (16, 2, 1), (8, 2, 2), (12, 4, 3),
-                                      (16, 2, 4), (4, 1, 4)])
-def test_decode_shapes_and_tails_bf16(gpu_lib, b, hq, hkv, t):
+                                      (16, 2, 4), (4, 1, 4), (32, 4, 3), (64, 8, 4)])
+def test_decode_shapes_and_tails_bf16(gpu_lib, b, hq, hkv, t, variant):
     """Block sizes 4-32, GQA groups 1-8, 1-4 causal query tokens (up to 32 rows per kv head),
-    and lengths at block and tile boundaries (b-1, b, b+1, 15, 16, 17, ...) in one launch."""
-    lengths = sorted({max(t, x) for x in (b - 1, b, b + 1, 15, 16, 17, 31, 33, 100, 257)})
-    case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b, q_tokens=t,
-                      dtype=torch.bfloat16, seed=b * 100 + hq * 10 + t, pool_slack=0.2)
-    _check_step(gpu_lib, case)
-    case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b, q_tokens=t,
-                      dtype=torch.bfloat16, seed=b * 100 + hq * 10 + t, pool_slack=0.2)
-    _check_step(gpu_lib, case, partitioned=True, partition_tokens=32 if b <= 32 else b)
+    and lengths at block and tile boundaries (b-1, b, b+1, 15, 16, 17, ...) in one launch,
+    single-pass and with 32- and 48-position partitions (the latter splits tile pairs)."""
+    lengths = sorted({max(t, x) for x in (b - 1, b, b + 1, 15, 16, 17, 31, 33, 47, 100, 257)})
+    for kw in (dict(), dict(partitioned=True, partition_tokens=32),
+               dict(partitioned=True, partition_tokens=48 if 48 % b == 0 else 64)):
+        case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b,
+                          q_tokens=t, dtype=torch.bfloat16, seed=b * 100 + hq * 10 + t, pool_slack=0.2)
+        _check_step(gpu_lib, case, variant=variant, **kw)
 
 
 @pytest.mark.parametrize("t", [1, 3])
@@ -138,27 +142,32 @@ def test_decode_fp32_shapes(gpu_lib, t):
     _check_step(gpu_lib, case)
 
 
+@pytest.mark.parametrize("variant", [VALU, MFMA])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_decode_bf16_output(gpu_lib, out_dtype):
-    _check_step(gpu_lib, make_case("batch64", num_seqs=6), out_dtype=out_dtype)
+def test_decode_bf16_output(gpu_lib, out_dtype, variant):
+    _check_step(gpu_lib, make_case("batch64", num_seqs=6), out_dtype=out_dtype, variant=variant)
     _check_step(gpu_lib, make_case("batch64", num_seqs=6), out_dtype=out_dtype, partitioned=True,
-                partition_tokens=64)
+                partition_tokens=64, variant=variant)
 
 
-def test_single_position_returns_v0_bitwise(gpu_lib):
+@pytest.mark.parametrize("variant", [VALU, MFMA])
+def test_single_position_returns_v0_bitwise(gpu_lib, variant):
     """L = 1: softmax weight exactly 1, so fp32 output == v_0 bit for bit (bf16 and fp32 pools)."""
     for dtype, d in ((torch.float32, 64), (torch.bfloat16, 128)):
+        if dtype == torch.float32 and variant == MFMA:
+            continue
         case = build_case(lengths=[1, 1, 1], num_q_heads=8, num_kv_heads=2, head_dim=d, block_size=16,
                           dtype=dtype, seed=3)
-        g, out = _run_step(gpu_lib, case)
+        g, out = _run_step(gpu_lib, case, variant=variant)
         want = case.v_new[:, 0].to(torch.float32).repeat_interleave(4, dim=1)  # [B, Hq, D]
         assert torch.equal(out[:, 0].cpu(), want)
 
 
-def test_permuted_physical_blocks_bitwise(gpu_lib):
+@pytest.mark.parametrize("variant", [VALU, MFMA])
+def test_permuted_physical_blocks_bitwise(gpu_lib, variant):
     """Relabelling the physical blocks (pool rows + table entries) leaves the GPU output bit-identical."""
     case = make_case("batch64", num_seqs=8)
-    g, out_a = _run_step(gpu_lib, case)
+    g, out_a = _run_step(gpu_lib, case, variant=variant)
     n = case.k_pool.shape[0]
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(9))
     kp2 = torch.empty_like(case.k_pool)
@@ -169,7 +178,7 @@ def test_permuted_physical_blocks_bitwise(gpu_lib):
     valid = tab < n
     tab[valid] = perm[tab[valid].long()].to(torch.int32)
     case.k_pool, case.v_pool, case.block_tables = kp2, vp2, tab
-    _, out_b = _run_step(gpu_lib, case)
+    _, out_b = _run_step(gpu_lib, case, variant=variant)
     assert torch.equal(out_a, out_b)
 
 
@@ -198,11 +207,12 @@ def test_shared_prefix_equals_private_copies_bitwise(gpu_lib):
     assert torch.equal(out_shared, out_private)
 
 
-def test_one_partition_equals_single_pass_bitwise(gpu_lib):
+@pytest.mark.parametrize("variant", [VALU, MFMA])
+def test_one_partition_equals_single_pass_bitwise(gpu_lib, variant):
     case = make_case("batch64", num_seqs=8)
     big = ((case.max_seq_len + 15) // 16) * 16
-    _, a = _run_step(gpu_lib, case)
-    _, b = _run_step(gpu_lib, case, partitioned=True, partition_tokens=big)
+    _, a = _run_step(gpu_lib, case, variant=variant)
+    _, b = _run_step(gpu_lib, case, partitioned=True, partition_tokens=big, variant=variant)
     assert torch.equal(a, b)
 
 
@@ -242,15 +252,16 @@ def _sampled_rows(case, rng, n_random=48):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name,partitioned", [("batch64", False), ("batch64", True), ("long", True),
-                                              ("prefix", True), ("spec", True)])
-def test_full_size_sampled(gpu_lib, name, partitioned):
+@pytest.mark.parametrize("name,partitioned,variant", [("batch64", False, 0), ("batch64", True, 0), ("long", True, 0),
+                                                      ("prefix", True, 0), ("spec", True, 0), ("batch64", False, VALU),
+                                                      ("long", True, VALU)])
+def test_full_size_sampled(gpu_lib, name, partitioned, variant):
     """Full workload sizes in the launch configuration the benchmark times (512-token partitions for the
     long/prefix/speculative cases): the complete KV write is compared bit for bit, and sampled output rows
     against the oracle computed row by row."""
     case = make_case(name, pool_device=DEV)
     print(f"[case] full {name} partitioned={partitioned} pool={tuple(case.k_pool.shape)}", flush=True)
-    g, out = _run_step(gpu_lib, case, partitioned=partitioned, partition_tokens=512)
+    g, out = _run_step(gpu_lib, case, partitioned=partitioned, partition_tokens=512, variant=variant)
     kp, vp = oracle_after_write(case)
     assert np.array_equal(bits(g["k_pool"]), kp)
     assert np.array_equal(bits(g["v_pool"]), vp)
