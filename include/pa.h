@@ -155,7 +155,7 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
  *               entry are irrelevant.
  * Other arguments and the supported shapes are as for pa_decode. Two calls
  * that share one workspace must be ordered by the caller, for example by
- * using the same stream. */
+ * using the same stream: calls that overlap on one workspace race. */
 int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables,
                           const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,

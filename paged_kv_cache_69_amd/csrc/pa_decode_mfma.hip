@@ -1,34 +1,55 @@
 // Paged decode attention on the matrix cores (gfx950 MFMA), bf16 K/V, head_dim 128.
 //
-// It computes exactly what the vector-ALU kernel computes (and what [P1] "25.
-// Paged attention and prefix caching", section "Attention that reads through
-// the table", and [P5] "Chapter 7 Paged KV Cache and Memory Management",
-// sections 4.1-4.2 define): for each query row (token t, head h), softmax over
-// the visible positions p <= L - T + t of scale * q . K[p], applied to V[p],
-// with K/V gathered through the block table. It differs only in how the
-// arithmetic is issued. The query rows of one kv head (T*G of them, padded to
-// 16 or 32) become the N (q.k) and M (P.V) dimension of
-// v_mfma_f32_16x16x32_bf16, so the vector ALU is left with the softmax alone.
+// It computes what the vector-ALU kernel computes (and what [P1] "25. Paged
+// attention and prefix caching", section "Attention that reads through the
+// table", and [P5] "Chapter 7 Paged KV Cache and Memory Management", sections
+// 4.1-4.2 define): for each query row (token t, head h), the softmax over the
+// visible positions p <= L - T + t of scale * q . K[p], applied to V[p], with
+// K/V gathered through the block table. The query rows of one kv head (T*G of
+// them, padded to 16 or 32) form one side of each MFMA, so the vector ALU
+// only runs the softmax.
 //
-// Per wave, positions are consumed in pairs of 16-position tiles (32
-// positions, the K dimension of one P.V MFMA):
-//  * S^T = K Q^T: the K tile is the A operand, loaded straight from the pool
-//    (lane l: position l%16 of the tile, 16 bytes at head_dim 32*kc + 8*(l/16)).
-//    q is the B operand, held in registers for the whole partition. Four
-//    MFMAs per tile cover head_dim 128. The C layout leaves lane l with
-//    positions 4*(l/16) + i of row l%16.
-//  * Softmax: scaled scores in base-2 units, a lazy reference max per row
-//    (raised only when a score exceeds it by more than 2^8), p = 2^(x - m).
-//  * P.V: the C layout above is already the A-operand layout of P (row l%16,
-//    8 positions). P is split into bf16 hi + lo parts, so P.V keeps about 16
-//    mantissa bits of p, and each part gets its own MFMA. V goes through LDS:
-//    the tile is written in its natural [position][head_dim] layout (32-byte
-//    blocks XOR-swizzled by position to spread banks), and two
-//    ds_read_b64_tr_b16 per 16-column block return 8 positions of one column
-//    per lane, which is the B operand.
-// Masked tail tiles (positions >= L, causal limits for T > 1, or a phantom
-// second tile past the partition) select -inf scores and zero V before use,
-// so garbage in unwritten slots can never reach the result.
+// Per wave, positions are consumed in tiles of 16 (4 KiB of K, 4 KiB of V):
+//  * S^T = K Q^T, four v_mfma_f32_16x16x32_bf16 per 16 query rows. The K tile
+//    is the A operand, loaded straight from the pool into registers (lane l:
+//    position l%16, 16 bytes at head_dim 32*kc + 8*(l/16)). q is the B
+//    operand, resident for the whole kernel. The C layout leaves lane l with
+//    positions 4*(l/16) + i of query row l%16.
+//  * That C layout is exactly the A-operand layout of v_mfma_f32_16x16x16_bf16
+//    (row l%16, positions 4*(l/16) .. +3), so P.V needs no cross-lane move.
+//    P is split into bf16 hi + lo parts, which keeps about 16 mantissa bits
+//    of each probability, and each part gets its own MFMA.
+//  * V is loaded into registers with the K tile (16 bytes per lane per KiB,
+//    fully contiguous), then written to a 4 KiB per-wave LDS tile in natural
+//    [position][head_dim] order, its 32-byte blocks XOR-swizzled by position
+//    to spread LDS banks. One ds_read_b64_tr_b16 per 16-column block then
+//    gives each lane 4 positions of one head_dim column, the B operand.
+//  * Tiles inside one block are read through a buffer descriptor built per
+//    tile in SGPRs plus a fixed lane offset: no per-tile vector address math.
+//  * Softmax reference: a wave's first tile sets each row's reference max m.
+//    Later tiles use p = 2^(x - m) with x in base-2 units. If a score ever
+//    exceeds m by more than 2^64, the wave restarts its range with the larger
+//    reference instead of rescaling, so the accumulators are only ever touched
+//    by MFMAs. 2^64 headroom keeps l and acc far inside fp32 range, and
+//    o = acc / l does not depend on the reference ([P5] section 4.2).
+//  * Loads run PF tiles ahead. Every iteration issues the same 8 vector loads
+//    (past the end it re-reads the wave's last tile), so the compiler's wait
+//    before a tile is used leaves the younger tiles' loads in flight.
+// Masked tail tiles (positions >= L, causal limits when T > 1, absent padded
+// rows) select -inf scores and zero the V rows past L before they are stored
+// to LDS, so garbage in unwritten slots never reaches the result.
+//
+// Two ways of sharing the work:
+//  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
+//    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
+//    through LDS at the end.
+//  * Split context (WAVE_ITEMS = true): every wave owns one chunk of
+//    part_tokens positions of one (sequence, kv head) and is independent of
+//    the other waves of its workgroup (no barrier anywhere). It writes its
+//    chunk's (m, l, acc) partial to the workspace straight from registers;
+//    the merge kernel that follows on the stream combines the partials.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -36,76 +57,106 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kTile = 16;
 constexpr int kRowBytes = 256;  // 128 bf16
 constexpr int kD = 128;
-constexpr float kRescaleSlack = 8.0f;
-constexpr int kPairChunk = 32;  // tile pairs whose block ids one table fetch covers
+constexpr int kTileBytes = kTile * kRowBytes;
+constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the reference max by
 
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
+#ifndef PA_MFMA_PREFETCH
+#define PA_MFMA_PREFETCH 1
+#endif
+#ifdef PA_MFMA_WAVES_PER_EU
+#define PA_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
+#else
+#define PA_MFMA_OCCUPANCY
+#endif
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
+constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;
 
-struct PairRegs {
-  u32x4 k[2][4];  // A operands of S^T for the two tiles
-  u32x4 v[2][4];  // V tiles, 16 bytes per lane per 1 KiB
-};
-
-// Byte offset of (position t of the pair, byte b of its 256-byte row) in a wave's V buffer.
-__device__ __forceinline__ int v_lds_offset(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
+// Byte offset of (position t, byte b of its 256-byte row) inside one V tile in LDS.
+__device__ __forceinline__ int v_swz(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Round-to-nearest-even fp32 -> bf16 pair packing, and the residual x - bf16(x).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+// Round-to-nearest-even packing of two fp32 into bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const bf16x2v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int MT, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams p) {
+__device__ __forceinline__ void wave_lds_order() {
+  // one wave reads back LDS it wrote; its LDS operations execute in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, float o) {
+  if (p.out_dtype == PA_F32)
+    static_cast<float*>(p.out)[idx] = o;
+  else
+    static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
+}
+
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS>
+__global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * MT;
-  constexpr int kVBytes = 2 * kTile * kRowBytes;                  // one pair of V tiles per wave
-  constexpr int kRedBytes = (NW * ROWS * kD + 2 * NW * ROWS) * 4;  // end-of-kernel merge buffers
-  constexpr int kLdsBytes = (NW * kVBytes > kRedBytes) ? NW * kVBytes : kRedBytes;
+  constexpr int NBUF = PF + 1;
+  constexpr int kVBytes = NW * kTileBytes;  // one V tile per wave
+  constexpr int kRedBytes = WAVE_ITEMS ? 0 : (NW * ROWS * kD + 2 * NW * ROWS) * 4;
+  constexpr int kLdsBytes = kVBytes > kRedBytes ? kVBytes : kRedBytes;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;    // 16-lane group: k slice of the MFMA operands
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;    // 16-lane group
   const int c16 = lane & 15;  // column inside the group
 
-  int bid = blockIdx.x;  // ((seq * parts + part) * Hkv + kvh)
+  // Single pass: block = seq * Hkv + kvh. Split context: block = (seq * chunk_groups + cg) * Hkv + kvh,
+  // wave w owning chunk cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks are dealt
+  // round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
+  int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
-  const int part = bid % p.parts;
-  const int seq = bid / p.parts;
+  const int groups = WAVE_ITEMS ? (p.parts + NW - 1) / NW : 1;
+  const int cg = bid % groups;
+  const int seq = bid / groups;
+  const int chunk = WAVE_ITEMS ? cg * NW + wave : 0;
 
   const int L = p.seq_lens[seq];
   const int T = p.T;
-  const int p_begin = part * p.part_tokens;
-  if (p.partial && p_begin >= L) return;
-  const int p_end = min(L, p_begin + p.part_tokens);
+  const int p_begin = WAVE_ITEMS ? chunk * p.part_tokens : 0;
+  if (WAVE_ITEMS && (chunk >= p.parts || p_begin >= L)) return;  // empty chunk: the merge never reads it
+  const int p_end = WAVE_ITEMS ? min(L, p_begin + p.part_tokens) : L;
   const int ntiles = p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
-  const int npairs = (ntiles + 1) >> 1;
   const int vis_all = L - T + 1;
   const bool rows_all_present = p.rows == ROWS;
+  const int my_tiles = WAVE_ITEMS ? ntiles : (wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0);
+  auto tile_p0_of = [&](int i) { return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile; };
 
   // ---- q rows as the B operand of S^T: lane (g, c16) holds row c16 + 16*mt, head_dim 32*kc + 8g .. +7
   u32x4 qb[MT][4];
-  int row_lim[MT];  // last visible position of this lane's score row; -1 if absent
+  int row_lim[MT];  // last visible position of this lane's score row; -1 if the row is padding
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + c16;
     const bool present = r < p.rows;
     row_lim[mt] = present ? L - T + r / p.G : -1;
-    const char* qrow = static_cast<const char*>(p.q) +
-                       ((int64_t)(seq * T + (present ? r / p.G : 0)) * p.Hq + kvh * p.G + (present ? r % p.G : 0)) *
-                           kRowBytes;
+    const int rr = present ? r : 0;
+    const char* qrow =
+        static_cast<const char*>(p.q) + ((int64_t)(seq * T + rr / p.G) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qb[mt][kc] = present ? load16(qrow + (kc * 4 + g) * 16) : u32x4{0u, 0u, 0u, 0u};
   }
@@ -114,276 +165,300 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
   const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
-  const int my_pairs = wave < npairs ? (npairs - wave + NW - 1) / NW : 0;
-  char* vbuf = lds + wave * kVBytes;
+  lds_char* vt = (lds_char*)lds + wave * kTileBytes;
 
-  // Block ids: lane 2*i + h of tab_v holds tile h of the wave's (tab_base + i)-th pair.
-  int tab_base = 0;
-  int tab_v = 0;
-  auto refill_table = [&](int base) {
-    tab_base = base;
-    const int pair = wave + (base + (lane >> 1)) * NW;
-    const int tile = 2 * pair + (lane & 1);
-    tab_v = 0;
-    if ((base + (lane >> 1)) < my_pairs && tile < ntiles) tab_v = trow[(p_begin + tile * kTile) / BS];
+  // Physical block ids of the wave's i-th tile, as wave-uniform scalar loads. A tile lies in one
+  // block when BS >= 16, or spans 16 / BS whole blocks otherwise (clamped to the sequence's last
+  // block, so a padding entry is never read).
+  constexpr int kBlocksPerTile = BS >= kTile ? 1 : kTile / BS;
+  struct TileIds {
+    int b[kBlocksPerTile];
+  };
+  auto ids_of = [&](int i) -> TileIds {
+    TileIds ids;
+    const int tile_p0 = tile_p0_of(i);
+    const int last_block = (L - 1) / BS;
+#pragma unroll
+    for (int jj = 0; jj < kBlocksPerTile; ++jj) ids.b[jj] = trow[min(tile_p0 / BS + jj, last_block)];
+    return ids;
   };
 
-  auto load_pair = [&](int i, PairRegs& pr) {
-    const int pair = wave + i * NW;
+  // Byte offset, inside this kv head's view of the pool, of position `pos` of a tile whose blocks are `ids`.
+  auto pos_offset = [&](const TileIds& ids, int tile_p0, int pos) -> int64_t {
+    if constexpr (BS >= kTile) {
+      return (int64_t)ids.b[0] * block_bytes + (int64_t)(pos % BS) * kRowBytes;
+    } else {
+      const int pc = min(pos, L - 1);
+      const int jj = pc / BS - tile_p0 / BS;
+      int phys = ids.b[0];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int tile = 2 * pair + h;
-      if (tile < ntiles) {  // uniform
-        const int tile_p0 = p_begin + tile * kTile;
-        if constexpr (BS >= kTile) {
-          const int64_t phys = __builtin_amdgcn_readlane(tab_v, 2 * (i - tab_base) + h);
-          const int64_t off = phys * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) pr.k[h][kc] = load16(kbase + off + c16 * kRowBytes + (kc * 4 + g) * 16);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) pr.v[h][c] = load16(vbase + off + c * 1024 + lane * 16);
-        } else {
-          const int pk = min(tile_p0 + c16, L - 1);
-          const char* kb = kbase + (int64_t)trow[pk / BS] * block_bytes + (int64_t)(pk % BS) * kRowBytes;
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) pr.k[h][kc] = load16(kb + (kc * 4 + g) * 16);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int pv = min(tile_p0 + c * 4 + (lane >> 4), L - 1);
-            pr.v[h][c] = load16(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * kRowBytes +
-                                (lane & 15) * 16);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pr.k[h][c] = u32x4{0u, 0u, 0u, 0u};
-          pr.v[h][c] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+      for (int k = 1; k < kBlocksPerTile; ++k)
+        if (jj == k) phys = ids.b[k];
+      return (int64_t)phys * block_bytes + (int64_t)(pc % BS) * kRowBytes;
     }
   };
 
-  float m_ref[MT];      // reference max of this lane's score row (row c16 + 16*mt)
-  float l_part[MT];     // sum of p over the positions this lane has seen for that row
-  f32x4 acc[MT][8];     // P.V: rows 4g + i (+16*mt), head_dim 16*j + c16
+  struct TileRegs {
+    u32x4 k[4];  // A operands of S^T
+    u32x4 v[4];  // V: position 4c + lane/16, head_dim chunk lane%16
+  };
+  const uint32_t k_lane_off = c16 * kRowBytes + g * 16;  // + 64 * kc
+  const uint32_t v_lane_off = lane * 16;                 // + 1024 * c: position 4c + lane/16, chunk lane%16
+  auto load_tile = [&](int i, const TileIds& ids, TileRegs& tr) {
+    const int tile_p0 = tile_p0_of(i);
+    if constexpr (BS >= kTile) {
+      const int64_t boff = (int64_t)ids.b[0] * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, kTileBytes);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, kTileBytes);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    m_ref[mt] = kNegInf;
-    l_part[mt] = 0.f;
+      for (int kc = 0; kc < 4; ++kc) tr.k[kc] = buffer_load16(kr, k_lane_off + kc * 64);
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  auto compute_pair = [&](int i, const PairRegs& pr) {
-    const int pair = wave + i * NW;
-    const int pair_p0 = p_begin + pair * 2 * kTile;
-    const bool masked = !rows_all_present || pair_p0 + 2 * kTile > vis_all || 2 * pair + 1 >= ntiles;
-
-    // ---- S^T for both tiles (C layout: lane l has positions 4g + e of score row c16 + 16*mt)
-    f32x4 s[2][MT];
+      for (int c = 0; c < 4; ++c) tr.v[c] = buffer_load16(vr, v_lane_off + c * 1024);
+    } else {
+      const int64_t koff = pos_offset(ids, tile_p0, tile_p0 + c16);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int kc = 0; kc < 4; ++kc) tr.k[kc] = load16(kbase + koff + (kc * 4 + g) * 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pr.k[h][kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
-        s[h][mt] = c * p.qk_scale_log2;
-      }
-    if (masked) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool tile_ok = 2 * pair + h < ntiles;
-        const int pos0 = pair_p0 + h * kTile + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!tile_ok || pos0 + e > row_lim[mt]) s[h][mt][e] = kNegInf;
-      }
+      for (int c = 0; c < 4; ++c)
+        tr.v[c] = load16(vbase + pos_offset(ids, tile_p0, tile_p0 + 4 * c + (lane >> 4)) + (lane & 15) * 16);
     }
+  };
 
-    // ---- lazy reference max per row
-    bool over = false;
+  float m_ref[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) over |= s[h][mt][e] > m_ref[mt] + kRescaleSlack;
-    if (__builtin_expect(__any(over), 0)) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float mx = m_ref[mt];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[h][mt][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // this lane's row changes reference: alpha = 2^(old - new) (0 from -inf, 1 when unchanged)
-        const float alpha = mx == kNegInf ? 1.f : exp2_fast(m_ref[mt] - mx);
-        l_part[mt] *= alpha;
-        m_ref[mt] = mx;
-        // acc rows 4g + e belong to score rows held by lanes c16 = 4g + e
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a_row = __shfl(alpha, 4 * g + e, 64);
-#pragma unroll
-          for (int jb = 0; jb < 8; ++jb) acc[mt][jb][e] *= a_row;
-        }
-      }
-    }
+  for (int mt = 0; mt < MT; ++mt) m_ref[mt] = kNegInf;
+  float l_part[MT];
+  f32x4 acc[MT][8];
+  bool have_ref = false;
 
-    // ---- probabilities, split into bf16 hi + lo A operands of P.V
-    u32x4 p_hi[MT], p_lo[MT];
+  // S^T of one tile (C layout: lane l has positions 4g + e of score row c16 + 16*mt), scaled and masked.
+  auto scores = [&](bool masked, int tile_p0, const u32x4 (&k)[4], f32x4 (&s)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float pv[8];
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int kc = 0; kc < 4; ++kc)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
+      s[mt] = c * p.qk_scale_log2;
+      if (masked) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = s[h][mt][e];
-          const float pe = x == kNegInf ? 0.f : exp2_fast(x - m_ref[mt]);
-          pv[h * 4 + e] = pe;
-          l_part[mt] += pe;
-        }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t hi = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
-        p_hi[mt][w] = hi;
-        p_lo[mt][w] = pack_bf16x2(pv[2 * w] - bf16_lo(hi), pv[2 * w + 1] - bf16_hi(hi));
+        for (int e = 0; e < 4; ++e)
+          if (tile_p0 + 4 * g + e > row_lim[mt]) s[mt][e] = kNegInf;
       }
     }
+  };
 
-    // ---- V pair into this wave's LDS buffer (zero where the position is not readable)
+  // Raise each row's reference to at least the row max of s.
+  auto raise_ref = [&](const f32x4 (&s)[MT]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int mt = 0; mt < MT; ++mt) {
+      float mx = fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_ref[mt] = fmaxf(m_ref[mt], mx);
+    }
+  };
+
+  // P.V of one tile whose scores are s and whose V rows are in vreg. Masked positions have
+  // score -inf (p = 0, selected, never computed from -inf) and V rows past L are zeroed.
+  auto accumulate = [&](bool masked, int tile_p0, const f32x4 (&s)[MT], const u32x4 (&vreg)[4]) {
+    s16x4 a_hi[MT], a_lo[MT];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = h * kTile + c * 4 + (lane >> 4);
-        u32x4 v = pr.v[h][c];
-        if (masked && (2 * pair + h >= ntiles || pair_p0 + t >= L)) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vbuf + v_lds_offset(t, (lane & 15) * 16)) = v;
+    for (int mt = 0; mt < MT; ++mt) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = s[mt][e];
+        pr[e] = x == kNegInf ? 0.f : exp2_fast(x - m_ref[mt]);
+        l_part[mt] += pr[e];
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t h01 = cvt_pk_bf16(pr[0], pr[1]);
+      const uint32_t h23 = cvt_pk_bf16(pr[2], pr[3]);
+      const uint32_t l01 = cvt_pk_bf16(pr[0] - bf16_lo(h01), pr[1] - bf16_hi(h01));
+      const uint32_t l23 = cvt_pk_bf16(pr[2] - bf16_lo(h23), pr[3] - bf16_hi(h23));
+      a_hi[mt] = __builtin_bit_cast(s16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
+      a_lo[mt] = __builtin_bit_cast(s16x4, (uint64_t)l01 | ((uint64_t)l23 << 32));
+    }
 
-    // ---- P.V: B operand = 8 positions of head_dim column 16*jb + c16, via two transpose reads
+    // V tile into this wave's LDS tile (positions >= L zeroed: those slots may hold anything)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = 4 * c + (lane >> 4);
+      u32x4 v = vreg[c];
+      if (masked && tile_p0 + t >= L) v = u32x4{0u, 0u, 0u, 0u};
+      *(lds_u32x4*)(vt + v_swz(t, (lane & 15) * 16)) = v;
+    }
+    wave_lds_order();
+
+    // B operand = positions 4g .. 4g+3 of head_dim column 16*jb + c16 (one transpose read)
     const int rr = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
-      const int col_b = (16 * jb + 4 * qq) * 2;
-      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)((__attribute__((address_space(3))) char*)vbuf + v_lds_offset(4 * g + rr, col_b)));
-      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)((__attribute__((address_space(3))) char*)vbuf + v_lds_offset(kTile + 4 * g + rr, col_b)));
-      const u32x4 bv = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(b0, b0, 0, 1)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(b0, b0, 2, 3)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(b1, b1, 0, 1)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(b1, b1, 2, 3))};
+      const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2)));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p_hi[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
-        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p_lo[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
+        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi[mt], b, acc[mt][jb], 0, 0, 0);
+        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo[mt], b, acc[mt][jb], 0, 0, 0);
       }
     }
+    // the next tile overwrites this LDS tile after these reads, in this wave's order
+    wave_lds_order();
   };
 
-  for (int chunk0 = 0; chunk0 < my_pairs; chunk0 += kPairChunk) {
-    const int n_here = min(kPairChunk, my_pairs - chunk0);
-    if constexpr (BS >= kTile) refill_table(chunk0);
-    PairRegs ring[2];
-    load_pair(chunk0, ring[0]);
-    for (int i0 = 0; i0 < n_here; i0 += 2) {
+  // Process the wave's tiles. Returns false when a score outran the reference: m_ref has then been
+  // raised and the caller runs again from the first tile with cleared accumulators (the tile that
+  // outran was still accumulated, into values that are discarded).
+  auto run = [&]() -> bool {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+    for (int mt = 0; mt < MT; ++mt) {
+      l_part[mt] = 0.f;
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (my_tiles == 0) return true;
+    const int last = my_tiles - 1;
+    TileRegs ring[NBUF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_tile(min(u, last), ids_of(min(u, last)), ring[u]);
+    TileIds ids_next = ids_of(min(PF, last));
+    bool ok = true;
+    for (int i0 = 0; i0 < my_tiles && ok; i0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
         const int i = i0 + u;
-        if (i < n_here) {
-          if (i + 1 < n_here) load_pair(chunk0 + i + 1, ring[u ^ 1]);
-          compute_pair(chunk0 + i, ring[u]);
+        if (i < my_tiles && ok) {
+          const TileIds ids = ids_next;
+          ids_next = ids_of(min(i + PF + 1, last));
+          load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF]);
+          const int tile_p0 = tile_p0_of(i);
+          const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
+          f32x4 s[MT];
+          scores(masked, tile_p0, ring[u].k, s);
+          if (!have_ref) {
+            raise_ref(s);  // the wave's first tile sets the reference
+            have_ref = true;
+          } else {
+            bool over = false;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) over |= s[mt][e] > m_ref[mt] + kRefSlack;
+            if (__builtin_expect(__any(over), 0)) {
+              raise_ref(s);
+              ok = false;
+            }
+          }
+          accumulate(masked, tile_p0, s, ring[u].v);
         }
       }
     }
+    return ok;
+  };
+
+  while (!run()) {
   }
 
-  // ---- merge: per-row (m, l) of each wave, then P.V accumulators across waves
-  __syncthreads();  // every wave is done with its V buffer before the merge reuses the LDS
-  float* red_acc = reinterpret_cast<float*>(lds);  // [NW][ROWS][kD]
-  float* red_m = red_acc + NW * ROWS * kD;         // [NW][ROWS]
-  float* red_l = red_m + NW * ROWS;                // [NW][ROWS]
+  // per-row l of this wave: lanes of column c16 hold row c16 (+16*mt); sum the four 16-lane groups
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    float l = l_part[mt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (g == 0) {
-      red_l[wave * ROWS + mt * 16 + c16] = l;
-      red_m[wave * ROWS + mt * 16 + c16] = m_ref[mt];
-    }
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red_acc[(wave * ROWS + mt * 16 + 4 * g + e) * kD + 16 * jb + c16] = acc[mt][jb][e];
+    l_part[mt] += __shfl_xor(l_part[mt], 16, 64);
+    l_part[mt] += __shfl_xor(l_part[mt], 32, 64);
   }
-  __syncthreads();
+  auto out_row = [&](int n) -> int64_t {  // flat (seq, token, q head) index of query row n
+    return (int64_t)(seq * T + n / p.G) * p.Hq + kvh * p.G + n % p.G;
+  };
 
-  for (int idx = threadIdx.x; idx < ROWS * kD; idx += NW * 64) {
-    const int n = idx / kD, d = idx % kD;
-    if (n >= p.rows) continue;
-    float M = kNegInf;
+  if constexpr (WAVE_ITEMS) {
+    // ---- this chunk's partial, straight from registers
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * ROWS + n]);
-    float lsum = 0.f, a = 0.f;
-    if (M != kNegInf) {
+    for (int mt = 0; mt < MT; ++mt) {
+      const int n = mt * 16 + c16;
+      if (g == 0 && n < p.rows) {
+        const int64_t pi = out_row(n) * p.parts + chunk;
+        *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref[mt], l_part[mt]};
+      }
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = red_m[w * ROWS + n];
-        if (mw != kNegInf) {
-          const float sc = exp2_fast(mw - M);
-          lsum = fmaf(sc, red_l[w * ROWS + n], lsum);
-          a = fmaf(sc, red_acc[(w * ROWS + n) * kD + d], a);
+      for (int e = 0; e < 4; ++e) {
+        const int na = mt * 16 + 4 * g + e;  // accumulator row of this lane
+        if (na < p.rows) {
+          float* dst = p.part_acc + (out_row(na) * p.parts + chunk) * kD + c16;
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[mt][jb][e];
         }
       }
     }
-    const int t = n / p.G, gq = n % p.G;
-    const int64_t orow = (int64_t)(seq * T + t) * p.Hq + kvh * p.G + gq;
-    if (p.partial) {
-      const int64_t pi = orow * p.parts + part;
-      p.part_acc[pi * kD + d] = a;
-      if (d == 0) {
-        p.part_ml[pi * 2] = M;
-        p.part_ml[pi * 2 + 1] = lsum;
+  } else {
+    // ---- merge the waves' (m, l, acc) through LDS ([P5] section 4.2, three-step merge):
+    // M = max_w m_w;  l = sum_w l_w 2^(m_w - M);  acc = sum_w acc_w 2^(m_w - M).
+    // Each wave rescales its own accumulators in registers, so the LDS pass is one float4 sum.
+    __syncthreads();  // every wave is done with its V tile before the merge reuses the LDS
+    float* red_acc = reinterpret_cast<float*>(lds);  // [NW][ROWS][kD]
+    float* red_m = red_acc + NW * ROWS * kD;         // [ROWS][NW]
+    float* red_l = red_m + NW * ROWS;                // [ROWS][NW]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (g == 0) {
+        red_l[(mt * 16 + c16) * NW + wave] = l_part[mt];
+        red_m[(mt * 16 + c16) * NW + wave] = m_ref[mt];
       }
-    } else {
-      const float o = lsum > 0.f ? a / lsum : 0.f;
-      if (p.out_dtype == PA_F32)
-        static_cast<float*>(p.out)[orow * kD + d] = o;
-      else
-        static_cast<uint16_t*>(p.out)[orow * kD + d] = f32_to_bf16(o);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = mt * 16 + 4 * g + e;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[row * NW + w]);
+        const float mw = red_m[row * NW + wave];
+        const float sc = mw == kNegInf ? 0.f : exp2_fast(mw - M);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) red_acc[(wave * ROWS + row) * kD + 16 * jb + c16] = acc[mt][jb][e] * sc;
+      }
+    __syncthreads();
+
+    // Each thread finishes 4 consecutive head_dim values of a row at a time.
+    for (int idx = threadIdx.x; idx < ROWS * (kD / 4); idx += NW * 64) {
+      const int n = idx / (kD / 4), d4 = (idx % (kD / 4)) * 4;
+      if (n >= p.rows) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[n * NW + w]);
+      float lsum = 0.f;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float mw = red_m[n * NW + w];
+          if (mw != kNegInf) lsum = fmaf(exp2_fast(mw - M), red_l[n * NW + w], lsum);
+          a += *reinterpret_cast<const f32x4*>(red_acc + (w * ROWS + n) * kD + d4);
+        }
+      }
+      const int64_t orow = out_row(n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out(p, orow * kD + d4 + e, lsum > 0.f ? a[e] / lsum : 0.f);
     }
   }
 }
 
-template <int MT, int BS>
+template <int MT, int BS, bool WI>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.B * p.parts * p.Hkv;
+  const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
+  const int64_t grid = (int64_t)p.B * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_mfma_kernel<MT, BS, kMfmaWaves><<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  decode_mfma_kernel<MT, BS, kMfmaWaves, kMfmaPrefetch, WI>
+      <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
   switch (p.block_size) {
-    case 4: return launch_t<MT, 4>(p, stream);
-    case 8: return launch_t<MT, 8>(p, stream);
-    case 16: return launch_t<MT, 16>(p, stream);
-    case 32: return launch_t<MT, 32>(p, stream);
+    case 4: return launch_t<MT, 4, WI>(p, stream);
+    case 8: return launch_t<MT, 8, WI>(p, stream);
+    case 16: return launch_t<MT, 16, WI>(p, stream);
+    case 32: return launch_t<MT, 32, WI>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -397,7 +472,8 @@ bool mfma_supported(const pa_dims& d) {
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  return p.rows <= 16 ? launch_bs<1>(p, stream) : launch_bs<2>(p, stream);
+  if (p.partial) return p.rows <= 16 ? launch_bs<1, true>(p, stream) : launch_bs<2, true>(p, stream);
+  return p.rows <= 16 ? launch_bs<1, false>(p, stream) : launch_bs<2, false>(p, stream);
 }
 
 }  // namespace pa

@@ -16,9 +16,9 @@
 // partition's positions are cut into tiles of 16. A kv head's row is 256
 // bytes (128 bf16 or 64 fp32), so one tile of K is 4 KiB. Wave w takes tiles
 // w, w + NW, ... and, while it computes tile i, its loads for tile i + 1 are
-// already in flight. Physical block ids for a wave's tiles are fetched up
-// front, one per lane, and read with v_readlane, so no table lookup sits on
-// the critical path.
+// already in flight. A tile's physical block id is a wave-uniform scalar load
+// issued one tile before the K/V loads that need it, so the table lookup never
+// sits on the critical path and never waits behind vector loads.
 //  * K layout: lane = 4*ts + j holds token ts of the tile, 16-byte chunks
 //    4*r + j (r = 0..3). Four adjacent lanes read 64 contiguous bytes.
 //    q . k is 16 v_dot2_f32_bf16 per row (fp32: 16 FMAs), then a 2-step DPP
@@ -37,6 +37,8 @@
 //    groups with absent rows, take the masked path. There, invisible scores
 //    become -inf, and V chunks of positions >= L are zeroed before use, since
 //    those slots may hold any bits (a 0 * NaN product would otherwise leak).
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -46,7 +48,6 @@ namespace {
 constexpr int kTile = 16;             // positions per wave tile
 constexpr int kRowBytes = 256;        // one kv head's K or V row
 constexpr float kRescaleSlack = 8.0f; // lazy-max slack, base-2 exponent units
-constexpr int kTableChunk = 64;       // tiles whose physical block ids one table fetch covers
 
 // Launch shape: waves per workgroup, tiles each wave keeps in flight ahead of
 // the one it computes, q staged in LDS instead of registers, non-temporal K/V loads.
@@ -54,10 +55,10 @@ constexpr int kTableChunk = 64;       // tiles whose physical block ids one tabl
 #define PA_VALU_WAVES 4
 #endif
 #ifndef PA_VALU_PREFETCH
-#define PA_VALU_PREFETCH 1
+#define PA_VALU_PREFETCH 3
 #endif
 #ifndef PA_VALU_Q_IN_LDS
-#define PA_VALU_Q_IN_LDS 0
+#define PA_VALU_Q_IN_LDS 1
 #endif
 #ifndef PA_VALU_NT_LOADS
 #define PA_VALU_NT_LOADS 0
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   __shared__ float red_l[NW][NR];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Block id = ((seq * parts + part) * row_groups + rg) * Hkv + kvh: workgroups are dealt
   // round-robin to the 8 XCDs, so with Hkv = 8 every workgroup of one kv head shares an L2.
   int bid = blockIdx.x;
@@ -161,28 +162,24 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
   const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
 
-  // Physical block of the wave's i-th tile (blocks of >= 16 positions) is lane i - tab_base of
-  // tab_v, fetched once per chunk of kTableChunk tiles so no table load sits inside the pipeline.
-  int tab_base = 0;
-  int tab_v = 0;
-  auto refill_table = [&](int base) {
-    tab_base = base;
-    const int i = base + lane;
-    tab_v = 0;
-    if (i < my_tiles) tab_v = trow[(p_begin + (wave + i * NW) * kTile) / BS];
-  };
+  // Physical block of the wave's i-th tile when blocks hold >= 16 positions: a wave-uniform
+  // index, so the lookup is a scalar load, fetched one tile ahead of the K/V loads that need it.
+  auto phys_of = [&](int i) -> int { return trow[(p_begin + (wave + i * NW) * kTile) / BS]; };
 
-  auto load_tile = [&](int i, Tile& tl) {
+  // A tile inside one block is read through a buffer descriptor built per tile in SGPRs plus a
+  // lane offset that never changes, so its loads need no per-tile vector address arithmetic.
+  const uint32_t k_lane_off = ts * kRowBytes + j * 16;  // + 64 * c
+  const uint32_t v_lane_off = R * 4 * kRowBytes + cv * 16;  // + 256 * c
+  auto load_tile = [&](int i, int phys32, Tile& tl) {
     const int tile_p0 = p_begin + (wave + i * NW) * kTile;
     if constexpr (BS >= kTile) {
-      const int64_t phys = __builtin_amdgcn_readlane(tab_v, i - tab_base);
-      const int64_t off = phys * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
-      const char* kb = kbase + off;
-      const char* vb = vbase + off;
+      const int64_t off = (int64_t)phys32 * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + off, kTile * kRowBytes);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + off, kTile * kRowBytes);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.k[c] = load_kv16<NT>(kb + ts * kRowBytes + (c * 4 + j) * 16);
+      for (int c = 0; c < 4; ++c) tl.k[c] = buffer_load16(kr, k_lane_off + c * 64);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.v[c] = load_kv16<NT>(vb + (4 * R + c) * kRowBytes + cv * 16);
+      for (int c = 0; c < 4; ++c) tl.v[c] = buffer_load16(vr, v_lane_off + c * kRowBytes);
     } else {
       // Blocks shorter than a tile: each lane finds its own block. Positions past the
       // sequence are clamped to its last position (a valid slot), then masked.
@@ -213,9 +210,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 
   auto row_of = [&](int nl) { return NR >= 4 ? nl * 4 + j : j; };
 
-  auto compute_tile = [&](int i, const Tile& tl) {
+  auto compute_tile = [&](auto masked_tag, int i, const Tile& tl) {
+    constexpr bool masked = decltype(masked_tag)::value;
     const int tile_p0 = p_begin + (wave + i * NW) * kTile;
-    const bool masked = !rows_all_present || (tile_p0 + kTile > vis_all);
 
     // ---- scores of token ts for every row (all four lanes of the quad end up with them)
     float s[NR];
@@ -237,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
       a += quad_xor2(a);
       s[n] = a * p.qk_scale_log2;
     }
-    if (masked) {
+    if constexpr (masked) {
       const int pk = tile_p0 + ts;
 #pragma unroll
       for (int n = 0; n < NR; ++n)
@@ -294,7 +291,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 #pragma unroll
       for (int n = 0; n < NR; ++n) pv[n] = p_lds[wave][4 * R + c][n];
       u32x4 v = tl.v[c];
-      if (masked && tile_p0 + 4 * R + c >= L) v = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (masked) {
+        if (tile_p0 + 4 * R + c >= L) v = u32x4{0u, 0u, 0u, 0u};
+      }
       float vf[E];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -312,21 +311,29 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
     }
   };
 
-  // ---- tile loop: a ring of PF + 1 register tiles, so tiles i+1 .. i+PF load while tile i computes
-  for (int chunk0 = 0; chunk0 < my_tiles; chunk0 += kTableChunk) {
-    const int n_here = min(kTableChunk, my_tiles - chunk0);
-    if constexpr (BS >= kTile) refill_table(chunk0);
+  // ---- tile loop: a ring of PF + 1 register tiles, so tiles i+1 .. i+PF load while tile i computes.
+  // Every iteration issues its prefetch unconditionally (past the end it re-reads the wave's last
+  // tile, a cache hit that is never used), so the number of loads in flight is the same on every
+  // path and the wait before each compute leaves the prefetched tiles outstanding.
+  if (my_tiles > 0) {
+    const int last = my_tiles - 1;
     Tile ring[PF + 1];
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (u < n_here) load_tile(chunk0 + u, ring[u]);
-    for (int i0 = 0; i0 < n_here; i0 += PF + 1) {
+    for (int u = 0; u < PF; ++u) load_tile(min(u, last), BS >= kTile ? phys_of(min(u, last)) : 0, ring[u]);
+    int phys_next = BS >= kTile ? phys_of(min(PF, last)) : 0;
+    for (int i0 = 0; i0 < my_tiles; i0 += PF + 1) {
 #pragma unroll
       for (int u = 0; u <= PF; ++u) {
         const int i = i0 + u;
-        if (i < n_here) {
-          if (i + PF < n_here) load_tile(chunk0 + i + PF, ring[(u + PF) % (PF + 1)]);
-          compute_tile(chunk0 + i, ring[u]);
+        if (i < my_tiles) {
+          const int ph = phys_next;
+          if (BS >= kTile) phys_next = phys_of(min(i + PF + 1, last));
+          load_tile(min(i + PF, last), ph, ring[(u + PF) % (PF + 1)]);
+          const int tile_p0 = p_begin + (wave + i * NW) * kTile;
+          if (!rows_all_present || tile_p0 + kTile > vis_all)
+            compute_tile(std::true_type{}, i, ring[u]);
+          else
+            compute_tile(std::false_type{}, i, ring[u]);
         }
       }
     }

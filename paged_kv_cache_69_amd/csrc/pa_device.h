@@ -56,4 +56,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Raw buffer descriptor for `bytes` bytes at a wave-uniform `base` (gfx9 format word 0x00020000).
+// Loads through it take a 32-bit lane offset, so no 64-bit vector address is formed per load, and
+// any offset at or past `bytes` reads zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
 }  // namespace pa

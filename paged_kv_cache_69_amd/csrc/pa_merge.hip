@@ -6,67 +6,120 @@
 // gives the exact result:
 //   M = max_k m_k,  l = sum_k l_k 2^(m_k - M),  o = sum_k acc_k 2^(m_k - M) / l.
 // A partition whose l_k is 0 (no visible position for this row) contributes
-// nothing and is skipped, so 2^(-inf - -inf) is never formed. One workgroup of
-// four waves handles one query row. Wave w sums partitions w, w + 4, ...
-// (each lane holds D/64 elements), then the waves combine in LDS.
+// nothing and is skipped, so 2^(-inf - -inf) is never formed.
+//
+// The work is pure HBM traffic (each partial is read once), so the layout is
+// chosen for bytes in flight: a workgroup of 256 threads serves RPW query rows;
+// a row's threads form SLOTS groups of D/4, each thread reading a float4 of one
+// partition's accumulator, so a row has SLOTS partitions in flight per step.
+// Few partitions per row -> several rows per workgroup, so short splits do not
+// launch one tiny workgroup per row.
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-constexpr int kMergeWaves = 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(const DecodeParams p) {
-  constexpr int PER_LANE = D / 64;
-  __shared__ float part_sum[kMergeWaves][D];
+constexpr int kMergeThreads = 256;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row = blockIdx.x;  // (seq * T + t) * Hq + h
-  const int seq = (int)(row / ((int64_t)p.T * p.Hq));
-  const int L = p.seq_lens[seq];
-  const int nparts = L > 0 ? min(p.parts, (L + p.part_tokens - 1) / p.part_tokens) : 0;
-  const float* ml = p.part_ml + row * p.parts * 2;
-  const float* acc = p.part_acc + row * p.parts * D;
+template <int D, int RPW>
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const DecodeParams p) {
+  constexpr int LPC = D / 4;                   // threads per partition (one float4 each)
+  constexpr int TPR = kMergeThreads / RPW;     // threads per row
+  constexpr int SLOTS = TPR / LPC;             // partitions of a row in flight per step
+  constexpr int WPR = TPR / 64;                // waves per row
+  static_assert(TPR >= 64 && SLOTS >= 1, "a row needs at least one wave and one slot");
+  __shared__ f32x4 part_sum[RPW][SLOTS][LPC];
+  __shared__ float red_m[kMergeThreads / 64], red_l[kMergeThreads / 64];
 
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = tid / TPR, t = tid % TPR;
+  const int64_t rows = (int64_t)p.B * p.T * p.Hq;
+  const int64_t row = (int64_t)blockIdx.x * RPW + r;  // (seq * T + token) * Hq + head
+  int nparts = 0;
+  if (row < rows) {
+    const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
+    nparts = L > 0 ? min(p.parts, (L + p.part_tokens - 1) / p.part_tokens) : 0;
+  }
+  const f32x2* ml = reinterpret_cast<const f32x2*>(p.part_ml) + row * p.parts;
+
+  // M = max m_k over partitions with l_k > 0, then l = sum l_k 2^(m_k - M)
   float M = kNegInf;
-  for (int k = lane; k < nparts; k += 64)
-    if (ml[2 * k + 1] > 0.f) M = fmaxf(M, ml[2 * k]);
+  for (int k = t; k < nparts; k += TPR) {
+    const f32x2 v = ml[k];
+    if (v[1] > 0.f) M = fmaxf(M, v[0]);
+  }
   M = wave_max(M);
+  if constexpr (WPR > 1) {
+    if (lane == 0) red_m[wave] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) M = fmaxf(M, red_m[r * WPR + w]);
+  }
   float lsum = 0.f;
-  for (int k = lane; k < nparts; k += 64) {
-    const float lk = ml[2 * k + 1];
-    if (lk > 0.f) lsum = fmaf(lk, exp2_fast(ml[2 * k] - M), lsum);
+  for (int k = t; k < nparts; k += TPR) {
+    const f32x2 v = ml[k];
+    if (v[1] > 0.f) lsum = fmaf(v[1], exp2_fast(v[0] - M), lsum);
   }
   lsum = wave_sum(lsum);
+  if constexpr (WPR > 1) {
+    if (lane == 0) red_l[wave] = lsum;
+    __syncthreads();
+    lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) lsum += red_l[r * WPR + w];
+  }
 
-  float o[PER_LANE];
+  // o = sum acc_k 2^(m_k - M): slot s takes partitions s, s + SLOTS, ...
+  const int slot = t / LPC, c = t % LPC;
+  const float* acc = p.part_acc + row * p.parts * D + 4 * c;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int k = slot; k < nparts; k += SLOTS) {
+    const f32x2 v = ml[k];
+    const f32x4 a = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
+    if (v[1] > 0.f) {
+      const float w = exp2_fast(v[0] - M);
 #pragma unroll
-  for (int c = 0; c < PER_LANE; ++c) o[c] = 0.f;
-#pragma unroll 4
-  for (int k = wave; k < nparts; k += kMergeWaves) {
-    const float lk = ml[2 * k + 1];
-    if (lk > 0.f) {
-      const float w = exp2_fast(ml[2 * k] - M);
-#pragma unroll
-      for (int c = 0; c < PER_LANE; ++c) o[c] = fmaf(w, acc[(int64_t)k * D + lane + 64 * c], o[c]);
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(w, a[e], o[e]);
     }
   }
-#pragma unroll
-  for (int c = 0; c < PER_LANE; ++c) part_sum[wave][lane + 64 * c] = o[c];
+  part_sum[r][slot][c] = o;
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += kMergeWaves * 64) {
-    float a = 0.f;
+  if (row < rows && t < LPC) {
+    f32x4 a = part_sum[r][0][t];
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) a += part_sum[w][d];
-    const float out = lsum > 0.f ? a / lsum : 0.f;
-    if (p.out_dtype == PA_F32)
-      static_cast<float*>(p.out)[row * D + d] = out;
-    else
-      static_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16(out);
+    for (int s = 1; s < SLOTS; ++s) a += part_sum[r][s][t];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float out = lsum > 0.f ? a[e] / lsum : 0.f;
+      const int64_t idx = row * D + 4 * t + e;
+      if (p.out_dtype == PA_F32)
+        static_cast<float*>(p.out)[idx] = out;
+      else
+        static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
+    }
   }
+}
+
+template <int D, int RPW>
+hipError_t launch_rpw(const DecodeParams& p, int64_t rows, hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + RPW - 1) / RPW)), block(kMergeThreads);
+  merge_partials_kernel<D, RPW><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, int64_t rows, hipStream_t stream) {
+  // rows per workgroup so that a row's slots roughly match its partition count
+  constexpr int LPC = D / 4;
+  if (p.parts * LPC >= kMergeThreads) return launch_rpw<D, 1>(p, rows, stream);
+  if (2 * p.parts * LPC >= kMergeThreads) return launch_rpw<D, 2>(p, rows, stream);
+  return launch_rpw<D, 4>(p, rows, stream);
 }
 
 }  // namespace
@@ -74,14 +127,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(const 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.T * p.Hq;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(kMergeWaves * 64);
-  if (p.D == 128)
-    merge_partials_kernel<128><<<grid, block, 0, stream>>>(p);
-  else if (p.D == 64)
-    merge_partials_kernel<64><<<grid, block, 0, stream>>>(p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.D == 128) return launch_d<128>(p, rows, stream);
+  if (p.D == 64) return launch_d<64>(p, rows, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -207,13 +207,48 @@ def test_shared_prefix_equals_private_copies_bitwise(gpu_lib):
     assert torch.equal(out_shared, out_private)
 
 
-@pytest.mark.parametrize("variant", [VALU, MFMA])
-def test_one_partition_equals_single_pass_bitwise(gpu_lib, variant):
+def test_one_partition_equals_single_pass_bitwise(gpu_lib):
+    """Vector-ALU kernel: a split run with one partition covering every sequence does the same
+    arithmetic as the single pass (the merge of one partial is exact), so the two agree bit for bit."""
     case = make_case("batch64", num_seqs=8)
     big = ((case.max_seq_len + 15) // 16) * 16
-    _, a = _run_step(gpu_lib, case, variant=variant)
-    _, b = _run_step(gpu_lib, case, partitioned=True, partition_tokens=big, variant=variant)
+    _, a = _run_step(gpu_lib, case, variant=VALU)
+    _, b = _run_step(gpu_lib, case, partitioned=True, partition_tokens=big, variant=VALU)
     assert torch.equal(a, b)
+
+
+def test_one_partition_mfma_matches_oracle(gpu_lib):
+    """Matrix-core kernel: the single pass spreads a sequence's tiles over four waves, while one
+    partition hands them all to one wave, so the two differ only in summation order; both meet the
+    oracle bar."""
+    case = make_case("batch64", num_seqs=8)
+    big = ((case.max_seq_len + 15) // 16) * 16
+    _check_step(gpu_lib, case, variant=MFMA)
+    _check_step(gpu_lib, make_case("batch64", num_seqs=8), partitioned=True, partition_tokens=big, variant=MFMA)
+
+
+@pytest.mark.parametrize("variant", [VALU, MFMA])
+def test_partitioned_workspace_reuse(gpu_lib, variant):
+    """One workspace, sized for the largest call and filled with garbage first, serves a sequence of
+    calls with different batch sizes: each result matches the oracle, and repeating the first call
+    reproduces its output bit for bit (nothing left in the workspace leaks into a result)."""
+    msl, pt = 512, 64
+    big = make_case("batch64", num_seqs=16)
+    small = make_case("batch64", num_seqs=6, seed=4242)
+    need = gpu_lib.workspace_bytes(big.q, big.k_pool, big.block_tables, msl, pt, variant=variant)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)  # every float in it reads as 3.4e38
+    outs = []
+    for case in (big, small, big):
+        print(f"[case] reuse B={case.q.shape[0]} variant={variant}", flush=True)
+        g = _to_gpu(case)
+        out = gpu_lib.decode_partitioned(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"],
+                                         case.scale, msl, pt, workspace=ws, variant=variant)
+        torch.cuda.synchronize()
+        kp, vp = bits(case.k_pool), bits(case.v_pool)
+        assert_attention_close(out.cpu(), _oracle_decode(case, kp, vp), kv_dtype=torch.bfloat16,
+                               out_dtype=torch.float32, what=f"reuse B={case.q.shape[0]}")
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[2])
 
 
 def test_table_padding_never_read(gpu_lib):
