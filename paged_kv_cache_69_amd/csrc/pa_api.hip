@@ -75,6 +75,7 @@ DecodeParams base_params(const pa_dims* d, const void* q, const void* k_pool, co
   p.D = d->head_dim;
   p.MB = d->max_blocks_per_seq;
   p.block_size = d->block_size;
+  p.num_blocks = d->num_blocks;
   p.rows = p.T * p.G;
   p.out_dtype = d->out_dtype;
   return p;

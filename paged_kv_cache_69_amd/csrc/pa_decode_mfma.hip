@@ -43,11 +43,12 @@
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
 //    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
 //    through LDS at the end.
-//  * Split context (WAVE_ITEMS = true): every wave owns one chunk of
+//  * Split context (WAVE_ITEMS = true): every wave owns one partition of
 //    part_tokens positions of one (sequence, kv head) and is independent of
 //    the other waves of its workgroup (no barrier anywhere). It writes its
-//    chunk's (m, l, acc) partial to the workspace straight from registers;
-//    the merge kernel that follows on the stream combines the partials.
+//    partition's (m, l, acc) partial to the workspace straight from
+//    registers; the merge kernel that follows on the stream combines the
+//    partials.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -77,13 +78,17 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 1
 #endif
+#ifndef PA_MFMA_SPLIT_PREFETCH
+#define PA_MFMA_SPLIT_PREFETCH 2
+#endif
 #ifdef PA_MFMA_WAVES_PER_EU
 #define PA_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 #else
 #define PA_MFMA_OCCUPANCY
 #endif
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
-constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;
+constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;            // single pass: few tiles per wave
+constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a whole partition per wave
 
 // Byte offset of (position t, byte b of its 256-byte row) inside one V tile in LDS.
 __device__ __forceinline__ int v_swz(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
@@ -124,8 +129,8 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   const int g = lane >> 4;    // 16-lane group
   const int c16 = lane & 15;  // column inside the group
 
-  // Single pass: block = seq * Hkv + kvh. Split context: block = (seq * chunk_groups + cg) * Hkv + kvh,
-  // wave w owning chunk cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks are dealt
+  // Single pass: block = seq * Hkv + kvh. Split context: block = (seq * groups + cg) * Hkv + kvh, wave w
+  // owning partition cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks are dealt
   // round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
@@ -133,68 +138,79 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   const int groups = WAVE_ITEMS ? (p.parts + NW - 1) / NW : 1;
   const int cg = bid % groups;
   const int seq = bid / groups;
-  const int chunk = WAVE_ITEMS ? cg * NW + wave : 0;
+  const int part = WAVE_ITEMS ? cg * NW + wave : 0;
 
-  const int L = p.seq_lens[seq];
   const int T = p.T;
-  const int p_begin = WAVE_ITEMS ? chunk * p.part_tokens : 0;
-  if (WAVE_ITEMS && (chunk >= p.parts || p_begin >= L)) return;  // empty chunk: the merge never reads it
-  const int p_end = WAVE_ITEMS ? min(L, p_begin + p.part_tokens) : L;
-  const int ntiles = p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
-  const int vis_all = L - T + 1;
-  const bool rows_all_present = p.rows == ROWS;
-  const int my_tiles = WAVE_ITEMS ? ntiles : (wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0);
-  auto tile_p0_of = [&](int i) { return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile; };
+  const int p_begin = WAVE_ITEMS ? part * p.part_tokens : 0;
 
-  // ---- q rows as the B operand of S^T: lane (g, c16) holds row c16 + 16*mt, head_dim 32*kc + 8g .. +7
+  // ---- q rows as the B operand of S^T: lane (g, c16) holds row c16 + 16*mt, head_dim 32*kc + 8g .. +7.
+  // Issued first and unconditionally (an absent row reads row 0, then selects zero): they depend on
+  // nothing else the kernel loads.
   u32x4 qb[MT][4];
-  int row_lim[MT];  // last visible position of this lane's score row; -1 if the row is padding
+  int row_tok[MT];  // query token of this lane's score row
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + c16;
     const bool present = r < p.rows;
-    row_lim[mt] = present ? L - T + r / p.G : -1;
     const int rr = present ? r : 0;
+    row_tok[mt] = rr / p.G;
     const char* qrow =
-        static_cast<const char*>(p.q) + ((int64_t)(seq * T + rr / p.G) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
+        static_cast<const char*>(p.q) + ((int64_t)(seq * T + row_tok[mt]) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qb[mt][kc] = present ? load16(qrow + (kc * 4 + g) * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x4 v = load16(qrow + (kc * 4 + g) * 16);
+      qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   }
-
-  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
-  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
-  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
-  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
-  lds_char* vt = (lds_char*)lds + wave * kTileBytes;
+  auto tile_p0_of = [&](int i) { return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile; };
 
   // Physical block ids of the wave's i-th tile, as wave-uniform scalar loads. A tile lies in one
-  // block when BS >= 16, or spans 16 / BS whole blocks otherwise (clamped to the sequence's last
-  // block, so a padding entry is never read).
+  // block when BS >= 16, or spans 16 / BS whole blocks otherwise. The table index is clamped to the
+  // row and the id to the pool, so a lookup never depends on the length and any entry (padding
+  // included) gives an address inside the pool; positions at or past L are masked out of the
+  // result whatever they hold. That lets the first tile's lookup go out together with the length.
+  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
   constexpr int kBlocksPerTile = BS >= kTile ? 1 : kTile / BS;
   struct TileIds {
     int b[kBlocksPerTile];
   };
   auto ids_of = [&](int i) -> TileIds {
     TileIds ids;
-    const int tile_p0 = tile_p0_of(i);
-    const int last_block = (L - 1) / BS;
+    const int first = tile_p0_of(i) / BS;
 #pragma unroll
-    for (int jj = 0; jj < kBlocksPerTile; ++jj) ids.b[jj] = trow[min(tile_p0 / BS + jj, last_block)];
+    for (int jj = 0; jj < kBlocksPerTile; ++jj)
+      ids.b[jj] = (int)min((uint32_t)trow[min(first + jj, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
     return ids;
   };
+  const TileIds ids0 = ids_of(0);
+  const int L = p.seq_lens[seq];
+  if (WAVE_ITEMS && (part >= p.parts || p_begin >= L)) return;  // empty partition: the merge never reads it
+  const int p_end = WAVE_ITEMS ? min(L, p_begin + p.part_tokens) : L;
+  const int ntiles = p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
+  const int vis_all = L - T + 1;
+  const bool rows_all_present = p.rows == ROWS;
+  const int my_tiles = WAVE_ITEMS ? ntiles : (wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0);
+
+  int row_lim[MT];  // last visible position of this lane's score row; -1 if the row is padding
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) row_lim[mt] = mt * 16 + c16 < p.rows ? L - T + row_tok[mt] : -1;
+
+  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
+  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
+  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
+  lds_char* vt = (lds_char*)lds + wave * kTileBytes;
 
   // Byte offset, inside this kv head's view of the pool, of position `pos` of a tile whose blocks are `ids`.
   auto pos_offset = [&](const TileIds& ids, int tile_p0, int pos) -> int64_t {
     if constexpr (BS >= kTile) {
       return (int64_t)ids.b[0] * block_bytes + (int64_t)(pos % BS) * kRowBytes;
     } else {
-      const int pc = min(pos, L - 1);
-      const int jj = pc / BS - tile_p0 / BS;
+      const int jj = (pos - tile_p0) / BS;  // tile_p0 is a multiple of 16, hence of BS
       int phys = ids.b[0];
 #pragma unroll
       for (int k = 1; k < kBlocksPerTile; ++k)
         if (jj == k) phys = ids.b[k];
-      return (int64_t)phys * block_bytes + (int64_t)(pc % BS) * kRowBytes;
+      return (int64_t)phys * block_bytes + (int64_t)(pos % BS) * kRowBytes;
     }
   };
 
@@ -305,21 +321,51 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     wave_lds_order();
   };
 
-  // Process the wave's tiles. Returns false when a score outran the reference: m_ref has then been
-  // raised and the caller runs again from the first tile with cleared accumulators (the tile that
-  // outran was still accumulated, into values that are discarded).
-  auto run = [&]() -> bool {
+  auto out_row = [&](int n) -> int64_t {  // flat (seq, token, q head) index of query row n
+    return (int64_t)(seq * T + n / p.G) * p.Hq + kvh * p.G + n % p.G;
+  };
+  auto clear = [&]() {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       l_part[mt] = 0.f;
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  // Split context: this partition's (m, l, acc) partial, straight from registers. Lanes of column
+  // c16 hold parts of row c16 (+16*mt)'s l; the four 16-lane groups are summed first.
+  auto flush = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float l = l_part[mt];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const int n = mt * 16 + c16;
+      if (g == 0 && n < p.rows) {
+        const int64_t pi = out_row(n) * p.parts + part;
+        *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref[mt], l};
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int na = mt * 16 + 4 * g + e;  // accumulator row of this lane
+        if (na < p.rows) {
+          float* dst = p.part_acc + (out_row(na) * p.parts + part) * kD + c16;
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[mt][jb][e];
+        }
+      }
+    }
+  };
+  // Process the wave's tiles. Returns false when a score outran the reference: m_ref has then been
+  // raised and the caller runs again from the first tile with cleared accumulators (the tile that
+  // outran was still accumulated, into values that are discarded).
+  auto run = [&]() -> bool {
+    clear();
     if (my_tiles == 0) return true;
     const int last = my_tiles - 1;
     TileRegs ring[NBUF];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load_tile(min(u, last), ids_of(min(u, last)), ring[u]);
+    for (int u = 0; u < PF; ++u) load_tile(min(u, last), u == 0 ? ids0 : ids_of(min(u, last)), ring[u]);
     TileIds ids_next = ids_of(min(PF, last));
     bool ok = true;
     for (int i0 = 0; i0 < my_tiles && ok; i0 += NBUF) {
@@ -358,36 +404,15 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   while (!run()) {
   }
 
-  // per-row l of this wave: lanes of column c16 hold row c16 (+16*mt); sum the four 16-lane groups
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    l_part[mt] += __shfl_xor(l_part[mt], 16, 64);
-    l_part[mt] += __shfl_xor(l_part[mt], 32, 64);
-  }
-  auto out_row = [&](int n) -> int64_t {  // flat (seq, token, q head) index of query row n
-    return (int64_t)(seq * T + n / p.G) * p.Hq + kvh * p.G + n % p.G;
-  };
-
   if constexpr (WAVE_ITEMS) {
-    // ---- this chunk's partial, straight from registers
+    flush();
+  } else {
+    // per-row l of this wave: lanes of column c16 hold row c16 (+16*mt); sum the four 16-lane groups
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int n = mt * 16 + c16;
-      if (g == 0 && n < p.rows) {
-        const int64_t pi = out_row(n) * p.parts + chunk;
-        *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref[mt], l_part[mt]};
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int na = mt * 16 + 4 * g + e;  // accumulator row of this lane
-        if (na < p.rows) {
-          float* dst = p.part_acc + (out_row(na) * p.parts + chunk) * kD + c16;
-#pragma unroll
-          for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[mt][jb][e];
-        }
-      }
+      l_part[mt] += __shfl_xor(l_part[mt], 16, 64);
+      l_part[mt] += __shfl_xor(l_part[mt], 32, 64);
     }
-  } else {
     // ---- merge the waves' (m, l, acc) through LDS ([P5] section 4.2, three-step merge):
     // M = max_w m_w;  l = sum_w l_w 2^(m_w - M);  acc = sum_w acc_w 2^(m_w - M).
     // Each wave rescales its own accumulators in registers, so the LDS pass is one float4 sum.
@@ -447,7 +472,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
   const int64_t grid = (int64_t)p.B * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_mfma_kernel<MT, BS, kMfmaWaves, kMfmaPrefetch, WI>
+  decode_mfma_kernel<MT, BS, kMfmaWaves, WI ? kMfmaSplitPrefetch : kMfmaPrefetch, WI>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }

@@ -22,6 +22,7 @@ struct DecodeParams {
   float* part_acc;           // [B*T*Hq, parts, D]: unnormalised accumulator per partition
   float qk_scale_log2;       // scale * log2(e): scores are kept in base-2 exponent units
   int32_t B, T, Hq, Hkv, G, D, MB, block_size;
+  int32_t num_blocks;        // N: physical blocks in each pool
   int32_t rows;              // T * G query rows that share one kv head
   int32_t row_groups;        // workgroups along the rows, per (sequence, kv head, partition)
   int32_t parts;             // partitions per sequence in the grid (1 for single pass)

@@ -39,12 +39,14 @@ def _oracle_decode(case, kp_bits, vp_bits):
                          case.seq_lens.numpy(), case.scale, case.block_size)
 
 
-def _run_step(pa, case, *, partitioned=False, partition_tokens=512, out_dtype=torch.float32, variant=0):
+def _run_step(pa, case, *, partitioned=False, partition_tokens=512, out_dtype=torch.float32, variant=0,
+              max_seq_len=None):
     g = _to_gpu(case)
     pa.write_kv(g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"], g["positions"])
     if partitioned:
         out = pa.decode_partitioned(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
-                                    case.max_seq_len, partition_tokens, out_dtype=out_dtype, variant=variant)
+                                    max_seq_len or case.max_seq_len, partition_tokens, out_dtype=out_dtype,
+                                    variant=variant)
     else:
         out = pa.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
                         out_dtype=out_dtype, variant=variant)
@@ -133,6 +135,16 @@ def test_decode_shapes_and_tails_bf16(gpu_lib, b, hq, hkv, t, variant):
         case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b,
                           q_tokens=t, dtype=torch.bfloat16, seed=b * 100 + hq * 10 + t, pool_slack=0.2)
         _check_step(gpu_lib, case, variant=variant, **kw)
+
+
+@pytest.mark.parametrize("variant", [VALU, MFMA])
+@pytest.mark.parametrize("partition_tokens,msl_factor", [(16, 1), (48, 1), (16, 2), (32, 3)])
+def test_many_partitions_per_sequence(gpu_lib, partition_tokens, msl_factor, variant):
+    """Dozens of short partitions per sequence, with max_seq_len at 1-3x the longest sequence (partitions
+    past a sequence's end are never written and never read)."""
+    case = make_case("batch64", num_seqs=32)
+    _check_step(gpu_lib, case, partitioned=True, partition_tokens=partition_tokens, variant=variant,
+                max_seq_len=case.max_seq_len * msl_factor)
 
 
 @pytest.mark.parametrize("t", [1, 3])
