@@ -11,20 +11,32 @@ previous one; R * (bytes one step touches) >= 1 GB. The K timed steps run as
 HIP graph replays (one captured step per replica), so host launch cost is not
 timed; that gives `value`. The same K steps are then launched directly with a
 pair of HIP events on the launch stream around every decode call, which gives
-the dominant kernel's average duration for `roofline`.
+the decode call's average duration for `roofline`.
 
 Prints one JSON line. `value` is decode tokens per second of the whole step.
-`roofline` relates the dominant kernel's algorithmic bytes to its measured
-duration and to the 8 TB/s HBM peak. `cpu_baseline` is the float64 oracle on
-this host's cores, over a bounded sample of the same workload.
+`roofline` relates the decode call's algorithmic bytes to its measured
+duration and to the 8 TB/s HBM peak; its `traffic` is the HBM bytes one call
+moved as rocprofv3's FETCH_SIZE + WRITE_SIZE counters read them (scaled by
+what the same counters read for a copy kernel of known size), taken from the
+summary under profiles/ when that summary was made from the current library
+sources, else null. `cpu_baseline` is the float64 oracle on this host's cores,
+over a bounded sample of the same workload.
+
+Two helper modes turn rocprofv3 output into those profiles/ summaries:
+``--summarize-pmc FETCH_DIR WRITE_DIR BENCH_LOG`` and ``--summarize-stats DIR``.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -35,16 +47,19 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
+CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
+PROFILES = os.path.join(ROOT, "profiles")
 
+# Launch configuration per workload: partition_tokens None = single-pass pa_decode.
 WORKLOADS = {
     "batch64": dict(partition_tokens=None, desc="64 seqs, L~U[20,500], 32 q / 8 kv heads, head_dim 128, b=16, "
                                                "bf16 (Llama-3-8B-shaped layer)"),
     "long": dict(partition_tokens=512, desc="16 seqs, L log-uniform [4096,32768], 32 q / 8 kv heads, head_dim 128, "
                                             "b=16, bf16, 512-token partitions + merge"),
-    "prefix": dict(partition_tokens=512, desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] private "
-                                              "suffix, 32 q / 8 kv heads, head_dim 128, b=16, bf16"),
-    "spec": dict(partition_tokens=512, desc="256 seqs, L~U[1024,8192], 4 causal query tokens, 64 q / 8 kv heads, "
-                                            "head_dim 128, b=16, bf16"),
+    "prefix": dict(partition_tokens=None, desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] "
+                                               "private suffix, 32 q / 8 kv heads, head_dim 128, b=16, bf16"),
+    "spec": dict(partition_tokens=None, desc="256 seqs, L~U[1024,8192], 4 causal query tokens, 64 q / 8 kv heads, "
+                                             "head_dim 128, b=16, bf16"),
     "tiny": dict(partition_tokens=None, desc="4 seqs L={1,17,33,64}, 4 q / 2 kv heads, head_dim 64, b=16, fp32"),
 }
 
@@ -55,16 +70,17 @@ def kv_bytes_per_position(num_kv_heads: int, head_dim: int, itemsize: int) -> in
     return 2 * num_kv_heads * head_dim * itemsize
 
 
-def algorithmic_bytes(case, *, include_out: bool = True) -> int:
-    """Bytes the decode step must move: every visible K/V row once, q once, the output once,
-    the used block-table entries and the lengths (4 bytes each)."""
+def algorithmic_bytes(case) -> int:
+    """Bytes one decode call must move: every visible K/V row once, q once, the fp32 output
+    once, the used block-table entries and the lengths (4 bytes each). Partials of a split
+    run are overhead, not part of this figure."""
     b, t, hq, d = case.q.shape
     hkv = case.k_pool.shape[1]
     isz = case.k_pool.element_size()
     lens = [int(x) for x in case.seq_lens]
     kv = sum(lens) * kv_bytes_per_position(hkv, d, isz)
     q = b * t * hq * d * case.q.element_size()
-    out = b * t * hq * d * 4 if include_out else 0
+    out = b * t * hq * d * 4
     tables = 4 * sum(-(-L // case.block_size) for L in lens) + 4 * b
     return kv + q + out + tables
 
@@ -82,6 +98,41 @@ def unique_bytes(case) -> int:
             seen[phys] = max(seen.get(phys, 0), min(bs, L - j * bs))
     kv = sum(seen.values()) * kv_bytes_per_position(hkv, d, isz)
     return kv + b * t * hq * d * (case.q.element_size() + 4) + 4 * sum(len(r) for r in case.table_rows) + 4 * b
+
+
+def library_sources_sha256() -> str:
+    """Hash of everything that decides what the kernels do: the HIP sources, headers and build flags."""
+    files = sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_69_amd", "csrc", "*")))
+    files += [os.path.join(ROOT, "include", "pa.h"), os.path.join(ROOT, "paged_kv_cache_69_amd", "_build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_summary(path: str) -> dict:
+    """``key = value`` lines of a profiles/ summary (other lines ignored)."""
+    out = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^([a-z_0-9]+) = (.*)$", line.strip())
+            if m:
+                out[m.group(1)] = m.group(2)
+    return out
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per decode call from profiles/traffic_<workload>.txt, or None when the summary is
+    missing or was taken from other library sources."""
+    path = os.path.join(PROFILES, f"traffic_decode_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    s = read_summary(path)
+    if s.get("library_sources_sha256") != library_sources_sha256():
+        return None
+    return int(float(s["traffic_bytes_per_call"]))
 
 
 class Replica:
@@ -130,8 +181,10 @@ class Replica:
             raise RuntimeError(f"decode: {st}")
 
 
-def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0):
-    """Returns (seconds per step, per-launch decode-kernel ms list, replicas)."""
+def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=True):
+    """Returns (seconds per step, ms per decode call, replica count). Without ``graphs`` both come
+    from eagerly launched steps (counter-collection runs only; the call time then includes the
+    KV writes)."""
     import ctypes
 
     import torch
@@ -139,7 +192,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0):
     dev = torch.device("cuda:0")
     src = {k: getattr(case, k).to(dev) for k in ("q", "k_new", "v_new", "k_pool", "v_pool", "block_tables",
                                                    "seq_lens", "positions")}
-    touched = algorithmic_bytes(case)
+    touched = unique_bytes(case)  # a block shared by several tables is cached once
     n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
     reps = [Replica(pa, case, src, partition_tokens, variant) for _ in range(n_rep)]
     del src
@@ -156,57 +209,83 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0):
     torch.cuda.synchronize()
 
     # Timed region A: the K steps as HIP graph replays (one graph per chunk of consecutive steps).
-    def capture(first_step, count):
+    def capture(count):
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
                 for c in range(count):
-                    r = reps[(first_step + c) % n_rep]
+                    r = reps[c % n_rep]
                     r.write(sh())
                     r.decode(sh())
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         return g
 
-    chunk = n_rep
-    full = capture(0, chunk)
-    rem = steps % chunk
-    tail = capture(0, rem) if rem else None
-    full.replay()  # instantiate/upload once, outside the timed region
-    if tail is not None:
-        tail.replay()
-    torch.cuda.synchronize()
+    t0 = t1 = 0.0
+    if graphs:
+        chunk = n_rep
+        full = capture(chunk)
+        rem = steps % chunk
+        tail = capture(rem) if rem else None
+        full.replay()  # instantiate/upload once, outside the timed region
+        if tail is not None:
+            tail.replay()
+        torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    for _ in range(steps // chunk):
-        full.replay()
-    if tail is not None:
-        tail.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+        t0 = time.perf_counter()
+        for _ in range(steps // chunk):
+            full.replay()
+        if tail is not None:
+            tail.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
 
-    # Timed region B: the same K steps launched directly, with HIP events on the launch stream
-    # bracketing every decode call (for a partitioned decode: both of its kernels).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+    # Timed region B: the decode calls alone, K of them back to back (replicas rotating), between
+    # one pair of HIP events on the stream they run on. With graphs the calls are one captured
+    # graph, so the figure is the kernels' own time plus the small gaps between graph nodes; a
+    # partitioned call counts both of its kernels.
     stream = torch.cuda.current_stream()
-    handle = ctypes.c_void_p(stream.cuda_stream)
-    for s in range(steps):
-        r = reps[s % n_rep]
-        r.write(handle)
-        evs[s][0].record(stream)
-        r.decode(handle)
-        evs[s][1].record(stream)
-    torch.cuda.synchronize()
-    kernel_ms = [a.elapsed_time(b) for a, b in evs]
-    return (t1 - t0) / steps, kernel_ms, reps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graphs:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for s in range(steps):
+                    reps[s % n_rep].decode(sh())
+        stream.wait_stream(side)
+        g.replay()  # upload, untimed
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        del g
+    else:
+        handle = ctypes.c_void_p(stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        ev0.record(stream)
+        for s in range(steps):
+            r = reps[s % n_rep]
+            r.write(handle)
+            r.decode(handle)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t0, t1 = e0, time.perf_counter()
+    call_ms = ev0.elapsed_time(ev1) / steps
+    del reps
+    torch.cuda.empty_cache()
+    return (t1 - t0) / steps, call_ms, n_rep
 
 
 def cpu_baseline(case, budget_s: float):
-    """The float64 oracle (KV write + decode) on this host, on a bounded sample of the
-    workload's sequences (grown until the sample takes about ``budget_s``)."""
+    """The float64 oracle (KV write + decode) on this host, one thread, on a bounded sample of the
+    workload: the first n sequences, n grown until one pass takes about ``budget_s`` or covers the
+    whole batch; a pass shorter than the budget is repeated until the budget is spent."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -219,64 +298,192 @@ def cpu_baseline(case, budget_s: float):
             t.view(torch.int32).numpy().view(np.uint32)
 
     b = case.q.shape[0]
+    kp_all, vp_all = npbits(case.k_pool), npbits(case.v_pool)
+
+    def one_pass(n):
+        sl = slice(0, n)
+        kp, vp = oracle.write_kv(kp_all, vp_all, npbits(case.k_new[sl]), npbits(case.v_new[sl]),
+                                 case.block_tables[sl].numpy(), case.positions[sl].numpy(), case.block_size)
+        as_f = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).float().numpy()) \
+            if kp.dtype == np.uint16 else (lambda a: a.view(np.float32))
+        oracle.decode(case.q[sl].float().numpy(), as_f(kp), as_f(vp), case.block_tables[sl].numpy(),
+                      case.seq_lens[sl].numpy(), case.scale, case.block_size)
+
     with threadpool_limits(limits=1):
-        kp_all, vp_all = npbits(case.k_pool), npbits(case.v_pool)
         n = 1
         while True:
-            sl = slice(0, n)
             t0 = time.perf_counter()
-            kp, vp = oracle.write_kv(kp_all, vp_all, npbits(case.k_new[sl]), npbits(case.v_new[sl]),
-                                     case.block_tables[sl].numpy(), case.positions[sl].numpy(), case.block_size)
-            as_f = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).float().numpy()) \
-                if kp.dtype == np.uint16 else (lambda a: a.view(np.float32))
-            oracle.decode(case.q[sl].float().numpy(), as_f(kp), as_f(vp), case.block_tables[sl].numpy(),
-                          case.seq_lens[sl].numpy(), case.scale, case.block_size)
+            one_pass(n)
             dt = time.perf_counter() - t0
             if dt >= budget_s or n >= b:
                 break
-            n = min(b, max(n + 1, int(n * min(8.0, 1.5 * budget_s / max(dt, 1e-3)))))
-    tokens = n * case.q.shape[1]
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            n = min(b, max(n + 1, int(n * min(8.0, 1.2 * budget_s / max(dt, 1e-3)))))
+        passes, total = 1, dt
+        while total < budget_s:
+            t0 = time.perf_counter()
+            one_pass(n)
+            total += time.perf_counter() - t0
+            passes += 1
+    tokens = n * case.q.shape[1] * passes
+    return {"value": round(tokens / total, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"KV write + float64 decode of the first {n} of {b} sequences "
-                      f"({int(case.seq_lens[:n].sum())} positions), one thread, {dt:.1f} s"}
+                      f"({int(case.seq_lens[:n].sum())} positions) x {passes} pass(es), one thread, {total:.1f} s"}
 
 
-def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0):
+def calibrate_copy(n_runs: int = 3):
+    """A plain elementwise kernel of known traffic (reads and writes CALIBRATION_BYTES), launched so a
+    rocprofv3 counter run of this process can scale its FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+
+    src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(n_runs):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True):
     import torch
 
     from workloads import make_case
 
     spec = WORKLOADS[name]
     case = make_case(name, pool_device="cuda:0")
-    sec_per_step, kernel_ms, reps = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant)
+    sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs)
     b, t = case.q.shape[0], case.q.shape[1]
-    algo = algorithmic_bytes(case, include_out=spec["partition_tokens"] is None)
-    dur_ms = sum(kernel_ms) / max(1, len(kernel_ms))
+    algo = algorithmic_bytes(case)
     achieved = algo / (dur_ms * 1e-3) / 1e9
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
     mfma_ok = case.k_pool.dtype == torch.bfloat16 and case.q.shape[3] == 128 and rows <= 32
     kernel = "decode_mfma_kernel" if (variant == 2 or (variant == 0 and mfma_ok)) else "decode_valu_kernel"
+    kernel += " + merge_partials_kernel (one pa_decode_partitioned call)" if spec["partition_tokens"] else \
+        " (one pa_decode call)"
+    traffic = traffic_from_profiles(name) if variant == 0 else None
     res = {
         "tokens_per_s": b * t / sec_per_step,
         "ms_per_step": sec_per_step * 1e3,
         "achieved_gbps": algo / sec_per_step / 1e9,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": kernel + (" (partial pass; merge pass excluded)" if spec["partition_tokens"] else ""),
-                     "bytes_per_launch": algo, "avg_launch_us": round(dur_ms * 1e3, 3),
-                     "launches_timed": len(kernel_ms)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": kernel, "bytes_per_launch": algo, "avg_launch_us": round(dur_ms * 1e3, 3),
+                     "launches_timed": steps},
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": b, "q_tokens": t,
                    "kv_positions": case.kv_tokens(), "max_seq_len": case.max_seq_len,
-                   "partition_tokens": spec["partition_tokens"], "replicas": len(reps)},
+                   "partition_tokens": spec["partition_tokens"], "replicas": n_rep},
         "dtype": "bf16" if case.k_pool.dtype == torch.bfloat16 else "f32",
     }
     if name == "prefix":
         res["unique_bytes"] = unique_bytes(case)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(case, cpu_budget)
-    del reps
+    del case
     torch.cuda.empty_cache()
     return res
+
+
+# ----------------------------------------------------------------------------- profiles/ summaries
+
+def _pmc_rows(directory: str):
+    paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no *counter_collection.csv under {directory}")
+    with open(paths[0], newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name: str) -> str:
+    name = re.sub(r"pa::\(anonymous namespace\)::", "", name)
+    return re.sub(r"\(pa::DecodeParams\)", "", name).strip()
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str) -> str:
+    """Text summary of one workload's decode-call traffic from a FETCH_SIZE run and a WRITE_SIZE run
+    (rocprofv3 --pmc ... --output-format csv) of ``bench.py --workload W --calibrate-copy``."""
+    with open(bench_log) as fh:
+        line = [ln for ln in fh if ln.startswith("{")][-1]
+    rec = json.loads(line)
+    algo = int(rec["roofline"]["bytes_per_launch"])
+    per = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _pmc_rows(directory):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault((counter, _short(r["Kernel_Name"])), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+    copy = [k for k in med if "neg" in k[1].lower()]
+    cf = [med[k] for k in copy if k[0] == "FETCH_SIZE"]
+    cw = [med[k] for k in copy if k[0] == "WRITE_SIZE"]
+    if not cf or not cw:
+        raise RuntimeError("calibration copy kernel not found in the counter runs")
+    f_fac = CALIBRATION_BYTES / (cf[0] * 1024.0)
+    w_fac = CALIBRATION_BYTES / (cw[0] * 1024.0)
+    kernels = sorted({k[1] for k in med if k[1].startswith("void decode_") or "merge_partials" in k[1]})
+    lines = [f"# HBM traffic of one decode call, workload {workload}",
+             "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
+             f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
+             "# commands (from the repository root; the summary itself comes from",
+             "#   python bench.py --summarize-pmc gpurun_out/pmc_fetch_W gpurun_out/pmc_write_W <bench log> --workload W):",
+             f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{workload} -o run -- "
+             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
+             f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{workload} -o run -- "
+             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
+             f"workload = {workload}",
+             f"library_sources_sha256 = {library_sources_sha256()}",
+             f"copy_fetch_kib = {cf[0]:.1f}",
+             f"copy_write_kib = {cw[0]:.1f}",
+             f"fetch_factor = {f_fac:.4f}",
+             f"write_factor = {w_fac:.4f}"]
+    total = 0.0
+    for i, k in enumerate(kernels):
+        fk = med.get(("FETCH_SIZE", k), 0.0)
+        wk = med.get(("WRITE_SIZE", k), 0.0)
+        bytes_k = fk * 1024.0 * f_fac + wk * 1024.0 * w_fac
+        total += bytes_k
+        lines += [f"kernel_{i} = {k}", f"kernel_{i}_fetch_kib = {fk:.1f}", f"kernel_{i}_write_kib = {wk:.1f}",
+                  f"kernel_{i}_bytes = {bytes_k:.0f}"]
+    lines += [f"traffic_bytes_per_call = {total:.0f}",
+              f"algorithmic_bytes_per_call = {algo}",
+              f"traffic_over_algorithmic = {total / algo:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_stats(directory: str, command: str, bench_log: str | None = None) -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv, or the kernels
+    of its results database): calls and durations per kernel, plus the bench line's own figure."""
+    stats = []
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if paths:
+        with open(paths[0], newline="") as fh:
+            for r in csv.DictReader(fh):
+                stats.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                              float(r["MaxNs"]), float(r["Percentage"])))
+    else:
+        import sqlite3
+
+        dbs = glob.glob(os.path.join(directory, "**", "*results.db"), recursive=True)
+        if not dbs:
+            raise FileNotFoundError(f"no kernel stats or results database under {directory}")
+        con = sqlite3.connect(dbs[0])
+        per = {}
+        for name, dur in con.execute("select name, duration from kernels"):
+            per.setdefault(_short(name), []).append(float(dur))
+        con.close()
+        total = sum(sum(v) for v in per.values())
+        for name, v in per.items():
+            stats.append((name, len(v), sum(v) / len(v), min(v), max(v), 100.0 * sum(v) / total))
+    stats.sort(key=lambda r: -r[5])
+    out = ["# rocprofv3 --kernel-trace --stats summary", f"# command: {command}",
+           f"{'kernel':80s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for name, calls, avg, mn, mx, pct in stats:
+        out.append(f"{name[:80]:80s} {calls:7d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {pct:6.2f}")
+    if bench_log:
+        with open(bench_log) as fh:
+            rec = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+        out.append(f"# the same run's bench line: decode call avg {rec['roofline']['avg_launch_us']} us over "
+                   f"{rec['roofline']['launches_timed']} calls (HIP events around one graph of the calls)")
+    return "\n".join(out) + "\n"
 
 
 def main(argv=None):
@@ -285,15 +492,27 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="long",
+    ap.add_argument("--secondary", default="long,prefix,spec",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 vector-ALU kernel, 2 MFMA kernel")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a copy kernel of known size (for counter calibration)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eagerly launched steps only (for counter-collection runs; not a headline number)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"))
+    ap.add_argument("--summarize-stats", nargs="+", metavar="DIR COMMAND [BENCH_LOG]")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc, args.workload), end="")
+        return 0
+    if args.summarize_stats:
+        print(summarize_stats(*args.summarize_stats), end="")
+        return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode step needs no "
-              "collectives; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode step runs on one "
+              "GPU and needs no collectives (DESIGN.md says how it would shard).", file=sys.stderr)
         return 2
 
     import torch
@@ -304,8 +523,10 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     pa.load_library()
+    if args.calibrate_copy:
+        calibrate_copy()
     main_res = run_workload(pa, args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_budget,
-                            args.variant)
+                            args.variant, not args.no_graph)
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 1),
@@ -318,7 +539,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": main_res["dtype"],
-        "data": "synthetic",
+        "data": "synthetic" + (" (eager launches, no graphs)" if args.no_graph else ""),
         "config": main_res["config"],
         "achieved_gbps": round(main_res["achieved_gbps"], 1),
         "hbm_frac": round(main_res["achieved_gbps"] / HBM_PEAK_GBPS, 4),
@@ -328,7 +549,7 @@ def main(argv=None):
         line["cpu_baseline"] = main_res["cpu_baseline"]
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant)
+        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant, not args.no_graph)
         secondary[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 6),
                            "achieved_gbps": round(r["achieved_gbps"], 1), "roofline": r["roofline"],
                            "config": r["config"], **({"unique_bytes": r["unique_bytes"]} if "unique_bytes" in r else {})}

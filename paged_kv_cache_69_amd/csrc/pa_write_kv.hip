@@ -23,31 +23,29 @@ struct WriteParams {
   const int32_t* positions;
   int32_t T, Hkv, MB, block_size;
   int32_t chunks_per_row;   // D * sizeof(dtype) / 16
-  int64_t row_bytes;        // D * sizeof(dtype)
+  int32_t row_bytes;        // D * sizeof(dtype)
   int64_t block_bytes;      // Hkv * b * row_bytes
-  int64_t total_chunks;     // B * T * 2 * Hkv * chunks_per_row
+  int32_t total_chunks;     // B * T * 2 * Hkv * chunks_per_row (< 2^31, checked by the launcher)
 };
 
+// Thread idx copies chunk `chunk` of the (token, K or V, kv head) row. The new row's chunk is
+// loaded first: its address does not depend on the slot, so that load overlaps the position and
+// block-table lookups that the store address needs.
 __global__ __launch_bounds__(256) void write_kv_kernel(const WriteParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.total_chunks) return;
-  int64_t rest = idx;
-  const int chunk = (int)(rest % p.chunks_per_row);
-  rest /= p.chunks_per_row;
-  const int kvh = (int)(rest % p.Hkv);
-  rest /= p.Hkv;
-  const int which = (int)(rest & 1);  // 0: K, 1: V
-  const int64_t tok = rest >> 1;      // i * T + t
-  const int seq = (int)(tok / p.T);
+  const int chunk = idx % p.chunks_per_row;
+  const int row = idx / p.chunks_per_row;  // (tok * 2 + which) * Hkv + kvh
+  const int kvh = row % p.Hkv;
+  const int which = (row / p.Hkv) & 1;     // 0: K, 1: V
+  const int tok = row / (2 * p.Hkv);       // i * T + t
+  const int64_t src = ((int64_t)tok * p.Hkv + kvh) * p.row_bytes + chunk * 16;
+  const u32x4 v = load16((which ? p.v_new : p.k_new) + src);
   const int pos = p.positions[tok];
-  const int phys = p.block_tables[(int64_t)seq * p.MB + pos / p.block_size];
-  const int slot = pos % p.block_size;
-  const int64_t src = (tok * p.Hkv + kvh) * p.row_bytes + (int64_t)chunk * 16;
-  const int64_t dst = (int64_t)phys * p.block_bytes + ((int64_t)kvh * p.block_size + slot) * p.row_bytes +
-                      (int64_t)chunk * 16;
-  const char* from = which ? p.v_new : p.k_new;
-  char* to = which ? p.v_pool : p.k_pool;
-  *reinterpret_cast<u32x4*>(to + dst) = load16(from + src);
+  const int phys = p.block_tables[(int64_t)(tok / p.T) * p.MB + pos / p.block_size];
+  const int64_t dst = (int64_t)phys * p.block_bytes +
+                      ((int64_t)kvh * p.block_size + pos % p.block_size) * p.row_bytes + chunk * 16;
+  *reinterpret_cast<u32x4*>((which ? p.v_pool : p.k_pool) + dst) = v;
 }
 
 }  // namespace
@@ -67,12 +65,14 @@ hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_ne
   p.Hkv = d.num_kv_heads;
   p.MB = d.max_blocks_per_seq;
   p.block_size = d.block_size;
-  p.row_bytes = (int64_t)d.head_dim * elt;
-  p.chunks_per_row = (int32_t)(p.row_bytes / 16);
+  p.row_bytes = d.head_dim * elt;
+  p.chunks_per_row = p.row_bytes / 16;
   p.block_bytes = (int64_t)d.num_kv_heads * d.block_size * p.row_bytes;
-  p.total_chunks = (int64_t)d.num_seqs * d.q_tokens * 2 * d.num_kv_heads * p.chunks_per_row;
-  if (p.total_chunks == 0) return hipSuccess;
-  const int64_t blocks = (p.total_chunks + 255) / 256;
+  const int64_t total = (int64_t)d.num_seqs * d.q_tokens * 2 * d.num_kv_heads * p.chunks_per_row;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7fffff00LL) return hipErrorInvalidValue;
+  p.total_chunks = (int32_t)total;
+  const int64_t blocks = (total + 255) / 256;
   write_kv_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
