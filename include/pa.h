@@ -92,8 +92,9 @@ typedef struct {
  *   k_pool[block_tables[i*MB + pos / b]][h][pos % b][:] = k_new[i][t][h][:]
  *   v_pool[...same slot...]                               = v_new[i][t][h][:]
  * for every kv head h. This is the scatter half of `update` in [P1] section
- * "The paged cache"; [P2] `Sequence.append`; and the "write k_t, v_t" step of
- * the decode-step sketch in [P4] section "Block table and allocator".
+ * "The paged cache"; [P2] `Sequence.append`; and the step of the decode-step
+ * sketch in [P4] section "Block table and allocator" that stores the new
+ * token's K and V in the last block.
  *   k_new, v_new : [B, T, Hkv, D], dtype q_dtype (== kv_dtype)
  *   k_pool, v_pool : [N, Hkv, b, D], written in place, bit-exact copies
  *   block_tables : int32 [B, MB];  positions : int32 [B, T], each in

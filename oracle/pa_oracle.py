@@ -88,9 +88,9 @@ def write_kv(k_pool, v_pool, k_new, v_new, block_tables, positions, block_size):
     rows ``k_new[i, t, h, :]`` and ``v_new[i, t, h, :]`` are copied, for every
     kv head h, to ``pool[table[i][pos // b], h, pos % b, :]``. This is the scatter
     half of ``update`` in [P1] "The paged cache", ``Sequence.append`` in [P2]
-    (without its copy-on-write), and the "write k_t, v_t into table[-1] at
-    offset filled" line of the decode-step pseudo-code in [P4] "Block table
-    and allocator".
+    (without its copy-on-write), and the step of the decode-step sketch in [P4]
+    "Block table and allocator" that stores the new token's K and V at the fill
+    offset of the sequence's last block.
 
     The copy is done on unsigned-integer views of the arrays, so every bit is
     kept, NaN payloads included. For bf16, pass the raw uint16 bits.
@@ -131,8 +131,9 @@ def attend_rows(q_rows, keys, values, scale: float):
     """Softmax attention of each query row over the same keys and values, in float64.
 
     ``s[r, p] = scale * q[r] . k[p]``; ``o[r] = sum_p softmax_p(s[r]) v[p]``
-    ([P2] §5 "scores[t] = (q . K[t]) / sqrt(head_dim); out = softmax(scores) . V";
-    [P4] "KV cache in Transformers (reminder)"; [P5] §4.2 "o_i = sum_r alpha_ir v_r").
+    ([P2] §5: scores are q.K scaled by one over root head_dim, the output is their softmax
+    applied to V; [P4] "KV cache in Transformers (reminder)"; [P5] §4.2: the output row is the
+    softmax-weighted sum of the value rows).
 
     Softmax is done in the usual two passes ([P5] §4.2): subtract the row
     maximum, exponentiate, normalise. Shapes: ``q_rows [R, D]``,

@@ -71,14 +71,14 @@ def test_summarize_pmc_scales_by_copy_kernel(tmp_path):
     assert float(s["write_factor"]) == pytest.approx(2.0)
     assert int(s["traffic_bytes_per_call"]) == (1000 + 10) * 1024 * 2   # medians, scaled
     assert float(s["traffic_over_algorithmic"]) == pytest.approx((1010 * 2048) / 4096000, rel=1e-3)
-    assert s["library_sources_sha256"] == bench.library_sources_sha256()
+    assert s["library_sha256"] == bench.library_sha256()
 
 
 def test_traffic_ignored_when_sources_changed(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     (tmp_path / "traffic_decode_batch64.txt").write_text(
-        "library_sources_sha256 = 0000\ntraffic_bytes_per_call = 123\n")
+        "library_sha256 = 0000\ntraffic_bytes_per_call = 123\n")
     assert bench.traffic_from_profiles("batch64") is None
     (tmp_path / "traffic_decode_batch64.txt").write_text(
-        f"library_sources_sha256 = {bench.library_sources_sha256()}\ntraffic_bytes_per_call = 123\n")
+        f"library_sha256 = {bench.library_sha256()}\ntraffic_bytes_per_call = 123\n")
     assert bench.traffic_from_profiles("batch64") == 123
