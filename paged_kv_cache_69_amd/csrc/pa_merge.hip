@@ -38,20 +38,35 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = tid / TPR, t = tid % TPR;
+  const int slot = t / LPC, c = t % LPC;
   const int64_t rows = (int64_t)p.B * p.T * p.Hq;
-  const int64_t row = (int64_t)blockIdx.x * RPW + r;  // (seq * T + token) * Hq + head
-  int nparts = 0;
-  if (row < rows) {
-    const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
-    nparts = L > 0 ? min(p.parts, (L + p.part_tokens - 1) / p.part_tokens) : 0;
-  }
+  const int64_t row_raw = (int64_t)blockIdx.x * RPW + r;  // (seq * T + token) * Hq + head
+  const int64_t row = min(row_raw, rows - 1);             // a padding row re-reads the last one
   const f32x2* ml = reinterpret_cast<const f32x2*>(p.part_ml) + row * p.parts;
+  const float* acc = p.part_acc + row * p.parts * D + 4 * c;
+
+  // Every load below depends only on the row: the (m, l) of partition t (the first TPR of them) and
+  // the accumulators of this slot's first kBatch partitions are in flight together with the length.
+  // Indices are clamped to the workspace's partition count; partitions at or past the sequence's
+  // own count (never written) are masked out once the length is known.
+  constexpr int kBatch = 8;
+  const f32x2 ml_t = ml[min(t, p.parts - 1)];
+  f32x4 a[kBatch];
+  f32x2 v[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int k = min(slot + j * SLOTS, p.parts - 1);
+    v[j] = ml[k];
+    a[j] = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
+  }
+  const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
+  const int nparts = row_raw < rows && L > 0 ? min(p.parts, (L + p.part_tokens - 1) / p.part_tokens) : 0;
 
   // M = max m_k over partitions with l_k > 0, then l = sum l_k 2^(m_k - M)
-  float M = kNegInf;
-  for (int k = t; k < nparts; k += TPR) {
-    const f32x2 v = ml[k];
-    if (v[1] > 0.f) M = fmaxf(M, v[0]);
+  float M = t < nparts && ml_t[1] > 0.f ? ml_t[0] : kNegInf;
+  for (int k = t + TPR; k < nparts; k += TPR) {
+    const f32x2 w = ml[k];
+    if (w[1] > 0.f) M = fmaxf(M, w[0]);
   }
   M = wave_max(M);
   if constexpr (WPR > 1) {
@@ -60,10 +75,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
 #pragma unroll
     for (int w = 0; w < WPR; ++w) M = fmaxf(M, red_m[r * WPR + w]);
   }
-  float lsum = 0.f;
-  for (int k = t; k < nparts; k += TPR) {
-    const f32x2 v = ml[k];
-    if (v[1] > 0.f) lsum = fmaf(v[1], exp2_fast(v[0] - M), lsum);
+  float lsum = t < nparts && ml_t[1] > 0.f ? ml_t[1] * exp2_fast(ml_t[0] - M) : 0.f;
+  for (int k = t + TPR; k < nparts; k += TPR) {
+    const f32x2 w = ml[k];
+    if (w[1] > 0.f) lsum = fmaf(w[1], exp2_fast(w[0] - M), lsum);
   }
   lsum = wave_sum(lsum);
   if constexpr (WPR > 1) {
@@ -74,23 +89,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
     for (int w = 0; w < WPR; ++w) lsum += red_l[r * WPR + w];
   }
 
-  // o = sum acc_k 2^(m_k - M): slot s takes partitions s, s + SLOTS, ...
-  const int slot = t / LPC, c = t % LPC;
-  const float* acc = p.part_acc + row * p.parts * D + 4 * c;
+  // o = sum acc_k 2^(m_k - M): slot s takes partitions s, s + SLOTS, ..., kBatch at a time.
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k = slot; k < nparts; k += SLOTS) {
-    const f32x2 v = ml[k];
-    const f32x4 a = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
-    if (v[1] > 0.f) {
-      const float w = exp2_fast(v[0] - M);
+  for (int k0 = slot;; k0 += kBatch * SLOTS) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = fmaf(w, a[e], o[e]);
+    for (int j = 0; j < kBatch; ++j) {
+      if (k0 + j * SLOTS < nparts && v[j][1] > 0.f) {
+        const float w = exp2_fast(v[j][0] - M);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(w, a[j][e], o[e]);
+      }
+    }
+    if (k0 + kBatch * SLOTS >= nparts) break;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int k = min(k0 + kBatch * SLOTS + j * SLOTS, p.parts - 1);
+      v[j] = ml[k];
+      a[j] = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
     }
   }
   part_sum[r][slot][c] = o;
   __syncthreads();
-  if (row < rows && t < LPC) {
+  if (row_raw < rows && t < LPC) {
     f32x4 a = part_sum[r][0][t];
 #pragma unroll
     for (int s = 1; s < SLOTS; ++s) a += part_sum[r][s][t];
