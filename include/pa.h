@@ -28,6 +28,12 @@
  *      * the slots written by pa_write_kv are distinct, and no other sequence
  *        reads them (copy-on-write is the caller's job: [P1] section
  *        "Sharing blocks: forks and copy-on-write").
+ *    With the environment variable PA_CHECK=1, every entry point first copies
+ *    block_tables, seq_lens and positions to the host (synchronising the
+ *    stream), checks them with pa_check_inputs_host, and returns
+ *    PA_ERR_INVALID_ARG without launching anything when a check fails. This
+ *    is a debugging aid: it is skipped while the stream is being captured
+ *    into a graph.
  *
  * Sources: [P1] "25. Paged attention and prefix caching"
  *          (inference.shantanugoel.com); [P2] "Модуль 09: PagedAttention:
@@ -123,8 +129,8 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
  * sequence. Use pa_decode_partitioned for long contexts.
  * Supported: (kv dtype, D) in {(PA_BF16, 128), (PA_F32, 64)}; b in
  * {4, 8, 16, 32}. The VALU kernel serves any T * G: groups of up to 8 query
- * rows share one workgroup. The MFMA kernel serves PA_BF16 with T * G = 16 or
- * 32. */
+ * rows share one workgroup. The MFMA kernel serves PA_BF16 with D = 128 and
+ * T * G <= 32 (query rows padded to 16 or 32). */
 int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
               pa_stream_t stream);
@@ -162,6 +168,20 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
+
+/* pa_check_inputs_host: the preconditions above, checked on host copies.
+ *   block_tables : int32 [B, MB] (required)
+ *   seq_lens     : int32 [B], or NULL to skip the checks that need lengths
+ *   positions    : int32 [B, T], or NULL to skip the write-slot checks
+ * Checks, for every sequence i (with L = seq_lens[i] when given):
+ *   q_tokens <= L <= MB * b; block_tables[i][j] in [0, num_blocks) for
+ *   j < ceil(L / b); every position in [0, MB * b) with its block's table
+ *   entry in [0, num_blocks); and no two (i, t) writing the same
+ *   (block, offset) slot.
+ * Returns PA_OK, or PA_ERR_INVALID_ARG at the first violation (also for
+ * invalid dims or a NULL block_tables). Host memory only; launches nothing. */
+int pa_check_inputs_host(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* positions);
 
 /* Static text for a status code. Never NULL. */
 const char* pa_status_string(int status);

@@ -28,6 +28,7 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
+    "pa_check_inputs_host",
     "pa_status_string",
     "pa_abi_version",
 )
@@ -76,6 +77,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_check_inputs_host.argtypes = [dims_p, _P, _P, _P]
+    lib.pa_check_inputs_host.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.argtypes = []

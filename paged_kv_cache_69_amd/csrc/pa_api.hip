@@ -124,8 +124,10 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
   if ((int64_t)dims->head_dim * dtype_size(dims->kv_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return PA_ERR_INVALID_ARG;
-  return launch_status(pa::launch_write_kv(*dims, k_new, v_new, k_pool, v_pool, block_tables, positions,
-                                           reinterpret_cast<hipStream_t>(stream)));
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
+  if (chk != PA_OK) return chk;
+  return launch_status(pa::launch_write_kv(*dims, k_new, v_new, k_pool, v_pool, block_tables, positions, s));
 }
 
 int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
@@ -140,11 +142,14 @@ int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void
   int variant = 0;
   st = choose_variant(dims, &variant);
   if (st != PA_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, 0, s);
+  if (st != PA_OK) return st;
   DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
   p.parts = 1;
   p.part_tokens = kSinglePassTokens;
   p.partial = 0;
-  return launch_attention(dims, variant, p, reinterpret_cast<hipStream_t>(stream));
+  return launch_attention(dims, variant, p, s);
 }
 
 size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
@@ -174,6 +179,10 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
   st = choose_variant(dims, &variant);
   if (st != PA_OK) return st;
 
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, max_seq_len, s);
+  if (st != PA_OK) return st;
+
   const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
   size_t ml_bytes = 0, acc_bytes = 0;
   workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
@@ -183,7 +192,6 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
   p.partial = 1;
   p.part_ml = static_cast<float*>(workspace);
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = launch_attention(dims, variant, p, s);
   if (st != PA_OK) return st;
   return launch_status(pa::launch_merge_partials(p, s));

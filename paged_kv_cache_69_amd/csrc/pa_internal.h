@@ -40,6 +40,11 @@ int valu_rows_per_group(int rows);
 bool valu_supported(const pa_dims& d);
 hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t stream);
 
+// PA_CHECK=1: the preconditions of pa.h checked on host copies (PA_OK when unset or capturing).
+// max_seq_len > 0 also bounds every length.
+int debug_check(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                const int32_t* positions, int32_t max_seq_len, hipStream_t stream);
+
 bool mfma_supported(const pa_dims& d);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 

@@ -122,3 +122,58 @@ def test_partitioned_rejects_bad_partitions(lib):
 def test_write_kv_rejects_unaligned_rows(lib):
     d = _dims(head_dim=6, kv_dtype=pa.PA_BF16)  # 12-byte rows cannot be copied in 16-byte chunks
     assert lib.pa_write_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+
+
+# ----------------------------------------------------------------------------- PA_CHECK preconditions
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_case():
+    """b = 4, N = 10 blocks, MB = 3, two sequences of lengths 6 and 9 (2 and 3 blocks), T = 2."""
+    import numpy as np
+
+    d = _dims(num_seqs=2, q_tokens=2, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=4, num_blocks=10,
+              max_blocks_per_seq=3, q_dtype=pa.PA_F32, kv_dtype=pa.PA_F32)
+    tables = np.array([[5, 1, 2**31 - 1], [7, 0, 9]], dtype=np.int32)
+    lens = np.array([6, 9], dtype=np.int32)
+    pos = np.array([[4, 5], [7, 8]], dtype=np.int32)
+    return d, tables, lens, pos
+
+
+def test_check_inputs_accepts_valid(lib):
+    d, tables, lens, pos = _check_case()
+    assert lib.pa_check_inputs_host(ctypes.byref(d), _np_ptr(tables), _np_ptr(lens), _np_ptr(pos)) == 0
+    assert lib.pa_check_inputs_host(ctypes.byref(d), _np_ptr(tables), None, None) == 0
+
+
+@pytest.mark.parametrize("what", ["len_below_T", "len_past_table", "entry_negative", "entry_past_pool",
+                                  "pos_negative", "pos_past_table", "slot_twice", "pos_block_invalid"])
+def test_check_inputs_rejects(lib, what):
+    d, tables, lens, pos = _check_case()
+    if what == "len_below_T":
+        lens[0] = 1
+    elif what == "len_past_table":
+        lens[1] = 13              # MB * b = 12
+    elif what == "entry_negative":
+        tables[1, 2] = -1         # used: ceil(9 / 4) = 3 entries
+    elif what == "entry_past_pool":
+        tables[0, 1] = 10
+    elif what == "pos_negative":
+        pos[0, 0] = -1
+    elif what == "pos_past_table":
+        pos[1, 1] = 12
+    elif what == "slot_twice":
+        tables[1, 1] = 5          # sequence 1 position 7 -> block 5 offset 3; make it collide below
+        pos[0, 1] = 7 - 4         # sequence 0 position 3 -> block 5 offset 3
+        lens[1] = 6
+    elif what == "pos_block_invalid":
+        pos[0, 1] = 9             # block index 2 of sequence 0 is padding
+    assert lib.pa_check_inputs_host(ctypes.byref(d), _np_ptr(tables), _np_ptr(lens), _np_ptr(pos)) == -1
+
+
+def test_check_inputs_padding_past_length_is_ignored(lib):
+    d, tables, lens, pos = _check_case()
+    tables[0, 2] = -5             # sequence 0 uses 2 entries only
+    assert lib.pa_check_inputs_host(ctypes.byref(d), _np_ptr(tables), _np_ptr(lens), None) == 0

@@ -263,6 +263,26 @@ def test_partitioned_workspace_reuse(gpu_lib, variant):
     assert torch.equal(outs[0], outs[2])
 
 
+def test_pa_check_rejects_bad_table_before_launch(gpu_lib, monkeypatch):
+    """PA_CHECK=1: valid inputs give the usual result; a table entry outside the pool is refused on the
+    host with PA_ERR_INVALID_ARG. (The MFMA kernel is forced: it clamps block ids into the pool, so even
+    an unchecked launch could not read outside it.)"""
+    case = make_case("batch64", num_seqs=4)
+    g = _to_gpu(case)
+    ref = gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
+                         variant=MFMA)
+    monkeypatch.setenv("PA_CHECK", "1")
+    out = gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
+                         variant=MFMA)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    bad = g["block_tables"].clone()
+    bad[1, 0] = case.k_pool.shape[0]
+    with pytest.raises(gpu_lib.PaError) as err:
+        gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], bad, g["seq_lens"], case.scale, variant=MFMA)
+    assert err.value.status == -1
+
+
 def test_table_padding_never_read(gpu_lib):
     """Padding INT32_MAX (default) and 0 give identical results: padding is never dereferenced."""
     a = make_case("batch64", num_seqs=5)
