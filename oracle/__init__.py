@@ -15,11 +15,19 @@ blocking, fusion or online recurrence. The pages are:
 * [P5] "Chapter 7 Paged KV Cache and Memory Management" (zero-to-sglang)
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle.py``, which checks it against something other than itself:
+``tests/test_oracle.py`` or ``tests/test_oracle_int8.py``, which checks it
+against something other than itself:
 the pages' worked examples, a library routine, closed forms, invariants or
 brute force. No function is "parity unpinned".
 """
 
+from .pa_oracle_int8 import (  # noqa: F401
+    append_int8,
+    decode_int8,
+    decode_row_int8,
+    dequantize_pool,
+    quantize_block,
+)
 from .pa_oracle import (  # noqa: F401
     attend_rows,
     blocks_needed,
