@@ -61,6 +61,11 @@ WORKLOADS = {
     "spec": dict(partition_tokens=None, desc="256 seqs, L~U[1024,8192], 4 causal query tokens, 64 q / 8 kv heads, "
                                              "head_dim 128, b=16, bf16"),
     "tiny": dict(partition_tokens=None, desc="4 seqs L={1,17,33,64}, 4 q / 2 kv heads, head_dim 64, b=16, fp32"),
+    # int8 KV pools (one fp32 scale per block and kv head) on the same shapes and lengths
+    "batch64_int8": dict(partition_tokens=None, base="batch64", int8=True,
+                         desc="batch64 with int8 K/V pools + per-(block, kv head) scales, bf16 q"),
+    "long_int8": dict(partition_tokens=512, base="long", int8=True,
+                      desc="long with int8 K/V pools + per-(block, kv head) scales, bf16 q, 512-token partitions"),
 }
 
 
@@ -70,18 +75,24 @@ def kv_bytes_per_position(num_kv_heads: int, head_dim: int, itemsize: int) -> in
     return 2 * num_kv_heads * head_dim * itemsize
 
 
+def _scale_bytes_per_block(case) -> int:
+    """int8 pools: the K and V fp32 scales of one block (all kv heads); 0 for float pools."""
+    return 2 * 4 * case.k_pool.shape[1] if hasattr(case, "k_scales") else 0
+
+
 def algorithmic_bytes(case) -> int:
     """Bytes one decode call must move: every visible K/V row once, q once, the fp32 output
-    once, the used block-table entries and the lengths (4 bytes each). Partials of a split
-    run are overhead, not part of this figure."""
+    once, the used block-table entries and the lengths (4 bytes each), and for int8 pools the
+    scales of every used block. Partials of a split run are overhead, not part of this figure."""
     b, t, hq, d = case.q.shape
     hkv = case.k_pool.shape[1]
     isz = case.k_pool.element_size()
     lens = [int(x) for x in case.seq_lens]
-    kv = sum(lens) * kv_bytes_per_position(hkv, d, isz)
+    blocks = sum(-(-L // case.block_size) for L in lens)
+    kv = sum(lens) * kv_bytes_per_position(hkv, d, isz) + blocks * _scale_bytes_per_block(case)
     q = b * t * hq * d * case.q.element_size()
     out = b * t * hq * d * 4
-    tables = 4 * sum(-(-L // case.block_size) for L in lens) + 4 * b
+    tables = 4 * blocks + 4 * b
     return kv + q + out + tables
 
 
@@ -96,7 +107,7 @@ def unique_bytes(case) -> int:
         L = int(case.seq_lens[i])
         for j, phys in enumerate(row):
             seen[phys] = max(seen.get(phys, 0), min(bs, L - j * bs))
-    kv = sum(seen.values()) * kv_bytes_per_position(hkv, d, isz)
+    kv = sum(seen.values()) * kv_bytes_per_position(hkv, d, isz) + len(seen) * _scale_bytes_per_block(case)
     return kv + b * t * hq * d * (case.q.element_size() + 4) + 4 * sum(len(r) for r in case.table_rows) + 4 * b
 
 
@@ -148,9 +159,10 @@ class Replica:
         self.dims = pa.make_dims(self.t["q"], self.t["k_pool"], self.t["block_tables"], out_dtype=torch.float32,
                                  variant=variant)
         kd = case.k_pool.shape
-        code = pa.dtype_code(case.k_pool.dtype)
+        self.int8 = "k_scales" in src
+        code = pa.dtype_code(case.k_new.dtype)
         self.wdims = pa.PaDims(case.q.shape[0], case.q.shape[1], kd[1], kd[1], kd[3], kd[2], kd[0],
-                               case.block_tables.shape[1], code, code, code, 0)
+                               case.block_tables.shape[1], code, pa.dtype_code(case.k_pool.dtype), code, 0)
         self.scale = ctypes.c_float(case.scale)
         self.pt = partition_tokens
         self.max_len = case.max_seq_len
@@ -160,21 +172,26 @@ class Replica:
                                    partition_tokens)
             self.ws = torch.empty(n, dtype=torch.uint8, device=src["q"].device)
         p = {k: v.data_ptr() for k, v in self.t.items()}
-        self.write_args = (ctypes.byref(self.wdims), p["k_new"], p["v_new"], p["k_pool"], p["v_pool"],
+        scales = (p["k_scales"], p["v_scales"]) if self.int8 else ()
+        self.write_args = (ctypes.byref(self.wdims), p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], *scales,
                            p["block_tables"], p["positions"])
-        self.dec_args = (ctypes.byref(self.dims), p["q"], p["k_pool"], p["v_pool"], p["block_tables"],
+        self.dec_args = (ctypes.byref(self.dims), p["q"], p["k_pool"], p["v_pool"], *scales, p["block_tables"],
                          p["seq_lens"], self.scale)
+        sfx = "_int8" if self.int8 else ""
+        self.f_write = getattr(self.lib, "pa_write_kv" + sfx)
+        self.f_decode = getattr(self.lib, "pa_decode" + sfx)
+        self.f_split = getattr(self.lib, "pa_decode_partitioned" + sfx)
 
     def write(self, stream):
-        st = self.lib.pa_write_kv(*self.write_args, stream)
+        st = self.f_write(*self.write_args, stream)
         if st:
             raise RuntimeError(f"pa_write_kv: {st}")
 
     def decode(self, stream):
         if self.ws is None:
-            st = self.lib.pa_decode(*self.dec_args, self.out.data_ptr(), stream)
+            st = self.f_decode(*self.dec_args, self.out.data_ptr(), stream)
         else:
-            st = self.lib.pa_decode_partitioned(*self.dec_args, self.out.data_ptr(), self.max_len, self.pt,
+            st = self.f_split(*self.dec_args, self.out.data_ptr(), self.max_len, self.pt,
                                                 self.ws.data_ptr(), self.ws.numel(), stream)
         if st:
             raise RuntimeError(f"decode: {st}")
@@ -189,8 +206,10 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
     import torch
 
     dev = torch.device("cuda:0")
-    src = {k: getattr(case, k).to(dev) for k in ("q", "k_new", "v_new", "k_pool", "v_pool", "block_tables",
-                                                   "seq_lens", "positions")}
+    keys = ["q", "k_new", "v_new", "k_pool", "v_pool", "block_tables", "seq_lens", "positions"]
+    if hasattr(case, "k_scales"):
+        keys += ["k_scales", "v_scales"]
+    src = {k: getattr(case, k).to(dev) for k in keys}
     touched = unique_bytes(case)  # a block shared by several tables is cached once
     n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
     reps = [Replica(pa, case, src, partition_tokens, variant) for _ in range(n_rep)]
@@ -346,16 +365,18 @@ def calibrate_copy(n_runs: int = 3):
 def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True):
     import torch
 
-    from workloads import make_case
+    from workloads import int8_pools, make_case
 
     spec = WORKLOADS[name]
-    case = make_case(name, pool_device="cuda:0")
+    case = make_case(spec.get("base", name), pool_device="cuda:0")
+    if spec.get("int8"):
+        case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
     sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs)
     b, t = case.q.shape[0], case.q.shape[1]
     algo = algorithmic_bytes(case)
     achieved = algo / (dur_ms * 1e-3) / 1e9
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
-    mfma_ok = case.k_pool.dtype == torch.bfloat16 and case.q.shape[3] == 128 and rows <= 32
+    mfma_ok = case.k_pool.dtype in (torch.bfloat16, torch.int8) and case.q.shape[3] == 128 and rows <= 32
     kernel = "decode_mfma_kernel" if (variant == 2 or (variant == 0 and mfma_ok)) else "decode_valu_kernel"
     kernel += " + merge_partials_kernel (one pa_decode_partitioned call)" if spec["partition_tokens"] else \
         " (one pa_decode call)"
@@ -371,7 +392,7 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": b, "q_tokens": t,
                    "kv_positions": case.kv_tokens(), "max_seq_len": case.max_seq_len,
                    "partition_tokens": spec["partition_tokens"], "replicas": n_rep},
-        "dtype": "bf16" if case.k_pool.dtype == torch.bfloat16 else "f32",
+        "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
     }
     if name == "prefix":
         res["unique_bytes"] = unique_bytes(case)
@@ -491,7 +512,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="long,prefix,spec",
+    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")

@@ -61,7 +61,9 @@ typedef enum {
   PA_ERR_LAUNCH = -3       /* the HIP runtime reported an error for the launch */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_INT8 is a pool dtype only: int8 codes with one fp32 scale per
+ * (block, kv head), used by the *_int8 entry points. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
 
 /* Kernel choice for the attention entry points. PA_VARIANT_AUTO picks the
  * fastest kernel this library has for the shape. The other values force one
@@ -168,6 +170,56 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
+
+/* ---- int8 KV cache ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша",
+ * section 6: block-wise KV quantisation).
+ *
+ * Pools hold int8 codes, [N, Hkv, b, D] like the float pools, plus one fp32
+ * scale per (block, kv head): k_scales, v_scales [N, Hkv]. A stored value is
+ * code * scale. For each (block, head) the scale is the largest magnitude of
+ * that head's values in the block divided by 127, and each code is the value
+ * divided by the scale, rounded half to even and clipped to [-127, 127], the
+ * division done in fp32. The per-element error is then at most the range
+ * over 254. dims->kv_dtype must be PA_INT8; q_dtype (and the dtype of new
+ * rows) is PA_BF16 or PA_F32. Each call halves the K/V bytes a bf16 pool
+ * would move.
+ */
+
+/* pa_write_kv_int8: append the T new tokens of every sequence into int8 pools.
+ * positions[i][0..T) must be consecutive (a decode step's newest positions).
+ * For each block that receives new rows of sequence i and kv head h, with m =
+ * the offset of its first new row:
+ *   - m = 0: the block holds no valid rows; its scale becomes
+ *     max|new rows| / 127 and the new rows are quantised with it;
+ *   - m > 0: the scale becomes max(old scale, max|new rows| / 127). If it
+ *     grew, the m old codes are re-quantised: code' = clip(round(code *
+ *     old_scale / new_scale)), each product and quotient in fp32. The new rows
+ *     are then quantised with the new scale.
+ * A scale of 0 (all-zero values) gives codes 0. A block written here must not
+ * be read or written by another sequence in the same call.
+ *   k_new, v_new : [B, T, Hkv, D], q_dtype;  k_pool, v_pool : int8 [N, Hkv, b, D]
+ *   k_scales, v_scales : fp32 [N, Hkv] (read and written)
+ *   block_tables : int32 [B, MB];  positions : int32 [B, T]
+ * Supported: D a multiple of 16. */
+int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
+                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                     const int32_t* positions, pa_stream_t stream);
+
+/* pa_decode_int8: pa_decode over int8 pools, i.e. exact softmax attention
+ * over the values code * scale. The MFMA kernel keeps the codes exact on the
+ * matrix cores and applies the per-block scales in fp32.
+ * Supported: q_dtype PA_BF16, D = 128, b in {16, 32}, T * G <= 32. */
+int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                   const int32_t* seq_lens, float scale, void* out, pa_stream_t stream);
+
+/* pa_decode_partitioned_int8: pa_decode_partitioned over int8 pools (same
+ * workspace size and rules, same supported shapes as pa_decode_int8). */
+int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                               void* out, int32_t max_seq_len, int32_t partition_tokens,
+                               void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /* pa_check_inputs_host: the preconditions above, checked on host copies.
  *   block_tables : int32 [B, MB] (required)

@@ -21,13 +21,16 @@ import os
 
 from ._build import LIB_PATH
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 EXPORTS = (
     "pa_write_kv",
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
+    "pa_write_kv_int8",
+    "pa_decode_int8",
+    "pa_decode_partitioned_int8",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_abi_version",
@@ -77,6 +80,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_write_kv_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.pa_write_kv_int8.restype = ctypes.c_int
+    lib.pa_decode_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.pa_decode_int8.restype = ctypes.c_int
+    lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
+                                               _P, ctypes.c_size_t, _P]
+    lib.pa_decode_partitioned_int8.restype = ctypes.c_int
     lib.pa_check_inputs_host.argtypes = [dims_p, _P, _P, _P]
     lib.pa_check_inputs_host.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -102,7 +112,9 @@ def dtype_code(dtype) -> int:
         return PA_F32
     if dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16")
+    if dtype == torch.int8:
+        return PA_INT8
+    raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16 (int8 for quantised pools)")
 
 
 def _stream_handle(stream, device):
@@ -213,4 +225,86 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_partitioned", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- int8 pools
+
+def _check_scales(k_pool, k_scales, v_scales):
+    import torch
+
+    _require(k_pool.dtype == torch.int8, "int8 entry points take int8 pools")
+    want = tuple(k_pool.shape[:2])
+    _require(tuple(k_scales.shape) == want and tuple(v_scales.shape) == want, "scales must be [N, Hkv]")
+    _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32, "scales must be float32")
+
+
+def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
+    """``pa_write_kv_int8``: append ``k_new``/``v_new [B, T, Hkv, D]`` (bf16 or fp32) into int8 pools
+    ``[N, Hkv, b, D]`` with per-(block, kv head) scales ``[N, Hkv]`` (updated in place)."""
+    import torch
+
+    lib = load_library()
+    dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales,
+                         v_scales=v_scales, block_tables=block_tables, positions=positions)
+    _check_scales(k_pool, k_scales, v_scales)
+    _require(block_tables.dtype == torch.int32 and positions.dtype == torch.int32, "tables/positions must be int32")
+    _require(k_new.shape == v_new.shape and k_pool.shape == v_pool.shape, "K/V shapes differ")
+    bsz, t, hkv, d = k_new.shape
+    _require(positions.shape == (bsz, t), "positions must be [B, T]")
+    _require(k_pool.shape[1] == hkv and k_pool.shape[3] == d, "pool and new rows disagree")
+    code = dtype_code(k_new.dtype)
+    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, PA_INT8,
+                  code, 0)
+    st = lib.pa_write_kv_int8(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                              v_pool.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
+                              positions.data_ptr(), _stream_handle(stream, dev))
+    _check(lib, "pa_write_kv_int8", st)
+
+
+def decode_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float, out=None, *,
+                out_dtype=None, stream=None):
+    """``pa_decode_int8``: decode over int8 pools; returns ``out [B, T, Hq, D]`` (fp32 by default)."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
+                         block_tables=block_tables, seq_lens=seq_lens, out=out)
+    _check_scales(k_pool, k_scales, v_scales)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
+    st = lib.pa_decode_int8(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                            k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(),
+                            float(scale), out.data_ptr(), _stream_handle(stream, dev))
+    _check(lib, "pa_decode_int8", st)
+    return out
+
+
+def decode_partitioned_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
+                            max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                            stream=None):
+    """``pa_decode_partitioned_int8``: split-context decode + merge over int8 pools."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
+                         block_tables=block_tables, seq_lens=seq_lens, out=out, workspace=workspace)
+    _check_scales(k_pool, k_scales, v_scales)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
+    st = lib.pa_decode_partitioned_int8(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                        k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
+                                        seq_lens.data_ptr(), float(scale), out.data_ptr(), int(max_seq_len),
+                                        int(partition_tokens), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(lib, "pa_decode_partitioned_int8", st)
     return out

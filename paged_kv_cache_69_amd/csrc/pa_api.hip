@@ -15,17 +15,32 @@ bool valid_dtype(int32_t t) { return t == PA_F32 || t == PA_BF16; }
 int dtype_size(int32_t t) { return t == PA_F32 ? 4 : 2; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Checks shared by every entry point. Returns PA_OK when the dims describe a valid problem.
-int check_dims(const pa_dims* d) {
+// Shape checks shared by every entry point. Returns PA_OK when the dims describe a valid problem.
+int check_shape(const pa_dims* d) {
   if (!d) return PA_ERR_INVALID_ARG;
   if (d->num_seqs < 0 || d->q_tokens < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->head_dim < 1 || d->block_size < 1 || d->num_blocks < 1 || d->max_blocks_per_seq < 1)
     return PA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->variant < PA_VARIANT_AUTO || d->variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Float pools: q, kv and out dtypes are PA_F32 / PA_BF16, with q and kv alike.
+int check_dims(const pa_dims* d) {
+  const int st = check_shape(d);
+  if (st != PA_OK) return st;
   if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype) || !valid_dtype(d->out_dtype))
     return PA_ERR_INVALID_ARG;
   if (d->q_dtype != d->kv_dtype) return PA_ERR_UNSUPPORTED;
-  if (d->variant < PA_VARIANT_AUTO || d->variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// int8 pools: kv dtype PA_INT8; q (and new rows) and out PA_F32 / PA_BF16.
+int check_dims_int8(const pa_dims* d) {
+  const int st = check_shape(d);
+  if (st != PA_OK) return st;
+  if (d->kv_dtype != PA_INT8 || !valid_dtype(d->q_dtype) || !valid_dtype(d->out_dtype)) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -99,6 +114,62 @@ void workspace_layout(const pa_dims* d, int32_t parts, size_t* ml_bytes, size_t*
   *acc_bytes = align256(rows * (size_t)parts * d->head_dim * sizeof(float));
 }
 
+// Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
+// run, the merge launch. int8 pools carry their scales and run on the MFMA kernel.
+int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, const void* k_pool, const void* v_pool,
+                 const float* k_scales, const float* v_scales, const int32_t* block_tables, const int32_t* seq_lens,
+                 float scale, void* out, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                 size_t workspace_bytes, pa_stream_t stream) {
+  int st = int8 ? check_dims_int8(dims) : check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (int8 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  int32_t parts = 1;
+  if (split) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+    if (max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
+    if (partition_tokens % 16 != 0 || partition_tokens % dims->block_size != 0) return PA_ERR_INVALID_ARG;
+    if (workspace_bytes < pa_decode_partitioned_workspace_bytes(dims, max_seq_len, partition_tokens))
+      return PA_ERR_INVALID_ARG;
+    parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
+  }
+  int variant = 0;
+  if (int8) {
+    if (dims->variant == PA_VARIANT_VALU || !pa::mfma_int8_supported(*dims)) return PA_ERR_UNSUPPORTED;
+    variant = PA_VARIANT_MFMA;
+  } else {
+    st = choose_variant(dims, &variant);
+    if (st != PA_OK) return st;
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, split ? max_seq_len : 0, s);
+  if (st != PA_OK) return st;
+
+  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  p.kv_int8 = int8 ? 1 : 0;
+  if (!split) {
+    p.parts = 1;
+    p.part_tokens = kSinglePassTokens;
+    p.partial = 0;
+    return launch_attention(dims, variant, p, s);
+  }
+  size_t ml_bytes = 0, acc_bytes = 0;
+  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
+  p.parts = parts;
+  p.part_tokens = partition_tokens;
+  p.partial = 1;
+  p.part_ml = static_cast<float*>(workspace);
+  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
+  st = launch_attention(dims, variant, p, s);
+  if (st != PA_OK) return st;
+  return launch_status(pa::launch_merge_partials(p, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,28 +204,13 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
 int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
               pa_stream_t stream) {
-  int st = check_dims(dims);
-  if (st != PA_OK) return st;
-  if (dims->num_seqs == 0) return PA_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
-  int variant = 0;
-  st = choose_variant(dims, &variant);
-  if (st != PA_OK) return st;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, 0, s);
-  if (st != PA_OK) return st;
-  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
-  p.parts = 1;
-  p.part_tokens = kSinglePassTokens;
-  p.partial = 0;
-  return launch_attention(dims, variant, p, s);
+  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream);
 }
 
 size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
                                              int32_t partition_tokens) {
-  if (check_dims(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return 0;
+  if (check_shape(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return 0;
   const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
   size_t ml = 0, acc = 0;
   workspace_layout(dims, parts, &ml, &acc);
@@ -165,36 +221,41 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
                           int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                           size_t workspace_bytes, pa_stream_t stream) {
-  int st = check_dims(dims);
+  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
+                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
+                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                     const int32_t* positions, pa_stream_t stream) {
+  const int st = check_dims_int8(dims);
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace) return PA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale) || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
-  if (partition_tokens % 16 != 0 || partition_tokens % dims->block_size != 0) return PA_ERR_INVALID_ARG;
-  if (workspace_bytes < pa_decode_partitioned_workspace_bytes(dims, max_seq_len, partition_tokens))
+  if (!k_new || !v_new || !k_pool || !v_pool || !k_scales || !v_scales || !block_tables || !positions)
     return PA_ERR_INVALID_ARG;
-  int variant = 0;
-  st = choose_variant(dims, &variant);
-  if (st != PA_OK) return st;
-
+  if (dims->head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new)) return PA_ERR_INVALID_ARG;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, max_seq_len, s);
-  if (st != PA_OK) return st;
+  const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
+  if (chk != PA_OK) return chk;
+  return launch_status(pa::launch_write_kv_int8(*dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales,
+                                                block_tables, positions, s));
+}
 
-  const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
-  size_t ml_bytes = 0, acc_bytes = 0;
-  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
-  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
-  p.parts = parts;
-  p.part_tokens = partition_tokens;
-  p.partial = 1;
-  p.part_ml = static_cast<float*>(workspace);
-  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
-  st = launch_attention(dims, variant, p, s);
-  if (st != PA_OK) return st;
-  return launch_status(pa::launch_merge_partials(p, s));
+int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                   const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
+  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream);
+}
+
+int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                               void* out, int32_t max_seq_len, int32_t partition_tokens,
+                               void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
+                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// Paged decode attention on the matrix cores (gfx950 MFMA), bf16 K/V, head_dim 128.
+// Paged decode attention on the matrix cores (gfx950 MFMA), bf16 or int8 K/V, head_dim 128.
 //
 // It computes what the vector-ALU kernel computes (and what [P1] "25. Paged
 // attention and prefix caching", section "Attention that reads through the
@@ -39,6 +39,24 @@
 // rows) select -inf scores and zero the V rows past L before they are stored
 // to LDS, so garbage in unwritten slots never reaches the result.
 //
+// int8 pools (Q8): codes with one fp32 scale per (block, kv head) ([P2]
+// "Модуль 09: PagedAttention: пейджинг KV-кэша", section 6). The codes stay
+// exact on the matrix cores and the scales are applied in fp32:
+//  * K: code + 128 as an unsigned byte u, placed under the fp16 exponent byte
+//    0x64, is the fp16 value 1024 + u = 1152 + code (one v_perm_b32 per two
+//    codes). S^T runs as v_mfma_f32_16x16x32_f16 against q converted to fp16,
+//    and the 1152 * sum(q) offset of each row is removed before the tile's
+//    K scale multiplies the scores. Operand kc of lane (g, c16) takes head_dim
+//    32g + 8kc .. +7, so each lane reads 32 contiguous bytes of its K row; q's
+//    B operand is laid out the same way, so the dot products are unchanged.
+//  * V: code + 128 converted to bf16 (exact below 256) goes through the same
+//    LDS tile and transposed reads; P is multiplied by the tile's V scale
+//    before its hi/lo split, and 128 * (sum of those scaled P) is removed from
+//    each accumulator row at the end.
+//  * A tile lies in one block (b >= 16), so one K and one V scale per tile,
+//    loaded with the block id. int8 codes are always finite, so tail V rows
+//    need no zeroing: their P is exactly 0.
+//
 // Two ways of sharing the work:
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
 //    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
@@ -62,6 +80,8 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -94,6 +114,26 @@ constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a 
 __device__ __forceinline__ int v_swz(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Four int8 codes (one dword) -> two dwords of fp16 values 1152 + code: flip the sign bit of each
+// byte (code + 128 as unsigned u), then pair each u with the exponent byte 0x64 (fp16 1024 + u).
+__device__ __forceinline__ u32x2 codes_to_f16(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return u32x2{__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u),   // bytes u0, 0x64, u1, 0x64
+               __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)};  // bytes u2, 0x64, u3, 0x64
+}
+
+// Four int8 codes -> two dwords of bf16 values 128 + code (exact: integers below 256).
+__device__ __forceinline__ u32x2 codes_to_bf16(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const bf16x2v a = {(__bf16)(float)(u & 0xffu), (__bf16)(float)((u >> 8) & 0xffu)};
+  const bf16x2v b = {(__bf16)(float)((u >> 16) & 0xffu), (__bf16)(float)(u >> 24)};
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+constexpr float kKOffset = 1152.f;  // fp16 K code value minus the code
+constexpr float kVOffset = 128.f;   // bf16 V code value minus the code
 
 // Round-to-nearest-even packing of two fp32 into bf16 (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
@@ -115,8 +155,11 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
+  static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
+  constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
+  constexpr int kKvTile = kTile * kKvRow;
   constexpr int ROWS = 16 * MT;
   constexpr int NBUF = PF + 1;
   constexpr int kVBytes = NW * kTileBytes;  // one V tile per wave
@@ -148,6 +191,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   // nothing else the kernel loads.
   u32x4 qb[MT][4];
   int row_tok[MT];  // query token of this lane's score row
+  float qsum[MT];   // int8 pools: sum over head_dim of the row's fp16 q (weight of the K offset)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + c16;
@@ -156,10 +200,34 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     row_tok[mt] = rr / p.G;
     const char* qrow =
         static_cast<const char*>(p.q) + ((int64_t)(seq * T + row_tok[mt]) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
+    if constexpr (Q8) {
+      // lane (g, c16): head_dim 32g .. 32g+31 of the row, as fp16; operand kc = 32g + 8kc .. +7
+      u32x4 raw[4];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const u32x4 v = load16(qrow + (kc * 4 + g) * 16);
-      qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
+      for (int kc = 0; kc < 4; ++kc) raw[kc] = load16(qrow + 64 * g + 16 * kc);
+      float part = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 v = present ? raw[kc] : u32x4{0u, 0u, 0u, 0u};
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (_Float16)bf16_lo(v[e]);
+          h[2 * e + 1] = (_Float16)bf16_hi(v[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)h[e];
+        qb[mt][kc] = __builtin_bit_cast(u32x4, h);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      qsum[mt] = part;
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 v = load16(qrow + (kc * 4 + g) * 16);
+        qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   auto tile_p0_of = [&](int i) { return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile; };
@@ -173,6 +241,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   constexpr int kBlocksPerTile = BS >= kTile ? 1 : kTile / BS;
   struct TileIds {
     int b[kBlocksPerTile];
+    float ks, vs;  // int8 pools: the block's K and V scales
   };
   auto ids_of = [&](int i) -> TileIds {
     TileIds ids;
@@ -180,6 +249,13 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
     for (int jj = 0; jj < kBlocksPerTile; ++jj)
       ids.b[jj] = (int)min((uint32_t)trow[min(first + jj, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+    if constexpr (Q8) {
+      const int64_t si = (int64_t)ids.b[0] * p.Hkv + kvh;
+      ids.ks = p.k_scales[si];
+      ids.vs = p.v_scales[si];
+    } else {
+      ids.ks = ids.vs = 1.f;
+    }
     return ids;
   };
   const TileIds ids0 = ids_of(0);
@@ -195,9 +271,9 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) row_lim[mt] = mt * 16 + c16 < p.rows ? L - T + row_tok[mt] : -1;
 
-  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
-  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
-  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
+  const int64_t block_bytes = (int64_t)p.Hkv * BS * kKvRow;
+  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kKvRow;
+  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kKvRow;
   lds_char* vt = (lds_char*)lds + wave * kTileBytes;
 
   // Byte offset, inside this kv head's view of the pool, of position `pos` of a tile whose blocks are `ids`.
@@ -215,21 +291,28 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   };
 
   struct TileRegs {
-    u32x4 k[4];  // A operands of S^T
-    u32x4 v[4];  // V: position 4c + lane/16, head_dim chunk lane%16
+    u32x4 k[Q8 ? 2 : 4];  // bf16: A operands of S^T; int8: 32 code bytes of row c16 at head_dim 32g
+    u32x4 v[Q8 ? 2 : 4];  // bf16: position 4c + lane/16, chunk lane%16; int8: row lane/4, bytes 32 (lane%4)
   };
-  const uint32_t k_lane_off = c16 * kRowBytes + g * 16;  // + 64 * kc
-  const uint32_t v_lane_off = lane * 16;                 // + 1024 * c: position 4c + lane/16, chunk lane%16
+  const uint32_t k_lane_off = Q8 ? c16 * kD + 32 * g : c16 * kRowBytes + g * 16;
+  const uint32_t v_lane_off = Q8 ? (lane >> 2) * kD + 32 * (lane & 3) : lane * 16;
   auto load_tile = [&](int i, const TileIds& ids, TileRegs& tr) {
     const int tile_p0 = tile_p0_of(i);
     if constexpr (BS >= kTile) {
-      const int64_t boff = (int64_t)ids.b[0] * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
-      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, kTileBytes);
-      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, kTileBytes);
+      const int64_t boff = (int64_t)ids.b[0] * block_bytes + (int64_t)(tile_p0 % BS) * kKvRow;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, kKvTile);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, kKvTile);
+      if constexpr (Q8) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) tr.k[kc] = buffer_load16(kr, k_lane_off + kc * 64);
+        for (int c = 0; c < 2; ++c) tr.k[c] = buffer_load16(kr, k_lane_off + 16 * c);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tr.v[c] = buffer_load16(vr, v_lane_off + c * 1024);
+        for (int c = 0; c < 2; ++c) tr.v[c] = buffer_load16(vr, v_lane_off + 16 * c);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) tr.k[kc] = buffer_load16(kr, k_lane_off + kc * 64);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tr.v[c] = buffer_load16(vr, v_lane_off + c * 1024);
+      }
     } else {
       const int64_t koff = pos_offset(ids, tile_p0, tile_p0 + c16);
 #pragma unroll
@@ -244,18 +327,36 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) m_ref[mt] = kNegInf;
   float l_part[MT];
+  float vcorr[MT];  // int8 pools: this lane's sum of V-scaled P (weight of the V offset)
   f32x4 acc[MT][8];
   bool have_ref = false;
 
   // S^T of one tile (C layout: lane l has positions 4g + e of score row c16 + 16*mt), scaled and masked.
-  auto scores = [&](bool masked, int tile_p0, const u32x4 (&k)[4], f32x4 (&s)[MT]) {
+  auto scores = [&](bool masked, int tile_p0, const TileRegs& tr, float kscale, f32x4 (&s)[MT]) {
+    u32x4 kf[4];  // int8 pools: the K codes as fp16 operands
+    if constexpr (Q8) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int j = 2 * kc;  // dwords j, j + 1 of the lane's 32 code bytes
+        const u32x2 a = codes_to_f16(tr.k[j >> 2][j & 3]);
+        const u32x2 b = codes_to_f16(tr.k[(j + 1) >> 2][(j + 1) & 3]);
+        kf[kc] = u32x4{a[0], a[1], b[0], b[1]};
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
-      s[mt] = c * p.qk_scale_log2;
+        for (int kc = 0; kc < 4; ++kc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(kf[kc]), as_f16x8(qb[mt][kc]), c, 0, 0, 0);
+        s[mt] = (c - kKOffset * qsum[mt]) * (kscale * p.qk_scale_log2);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tr.k[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
+        s[mt] = c * p.qk_scale_log2;
+      }
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -277,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 
   // P.V of one tile whose scores are s and whose V rows are in vreg. Masked positions have
   // score -inf (p = 0, selected, never computed from -inf) and V rows past L are zeroed.
-  auto accumulate = [&](bool masked, int tile_p0, const f32x4 (&s)[MT], const u32x4 (&vreg)[4]) {
+  auto accumulate = [&](bool masked, int tile_p0, const f32x4 (&s)[MT], const TileRegs& tr, float vscale) {
     s16x4 a_hi[MT], a_lo[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -287,6 +388,10 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
         const float x = s[mt][e];
         pr[e] = x == kNegInf ? 0.f : exp2_fast(x - m_ref[mt]);
         l_part[mt] += pr[e];
+        if constexpr (Q8) {
+          pr[e] *= vscale;  // from here on P carries the block's V scale
+          vcorr[mt] += pr[e];
+        }
       }
       const uint32_t h01 = cvt_pk_bf16(pr[0], pr[1]);
       const uint32_t h23 = cvt_pk_bf16(pr[2], pr[3]);
@@ -296,13 +401,25 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
       a_lo[mt] = __builtin_bit_cast(s16x4, (uint64_t)l01 | ((uint64_t)l23 << 32));
     }
 
-    // V tile into this wave's LDS tile (positions >= L zeroed: those slots may hold anything)
+    if constexpr (Q8) {
+      // V codes of row lane/4, head_dim 32 (lane%4) .. +31, as bf16 128 + code, into the LDS tile
+      const int t = lane >> 2;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int t = 4 * c + (lane >> 4);
-      u32x4 v = vreg[c];
-      if (masked && tile_p0 + t >= L) v = u32x4{0u, 0u, 0u, 0u};
-      *(lds_u32x4*)(vt + v_swz(t, (lane & 15) * 16)) = v;
+      for (int c = 0; c < 4; ++c) {
+        const u32x2 a = codes_to_bf16(tr.v[c >> 1][2 * (c & 1)]);
+        const u32x2 b = codes_to_bf16(tr.v[c >> 1][2 * (c & 1) + 1]);
+        const u32x4 w = {a[0], a[1], b[0], b[1]};
+        *(lds_u32x4*)(vt + v_swz(t, 64 * (lane & 3) + 16 * c)) = w;
+      }
+    } else {
+      // V tile into this wave's LDS tile (positions >= L zeroed: those slots may hold anything)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = 4 * c + (lane >> 4);
+        u32x4 v = tr.v[c];
+        if (masked && tile_p0 + t >= L) v = u32x4{0u, 0u, 0u, 0u};
+        *(lds_u32x4*)(vt + v_swz(t, (lane & 15) * 16)) = v;
+      }
     }
     wave_lds_order();
 
@@ -328,6 +445,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       l_part[mt] = 0.f;
+      vcorr[mt] = 0.f;
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -364,8 +482,12 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     if (my_tiles == 0) return true;
     const int last = my_tiles - 1;
     TileRegs ring[NBUF];
+    TileIds cur[NBUF];  // block ids (and scales) of the tile in each ring slot
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load_tile(min(u, last), u == 0 ? ids0 : ids_of(min(u, last)), ring[u]);
+    for (int u = 0; u < PF; ++u) {
+      cur[u] = u == 0 ? ids0 : ids_of(min(u, last));
+      load_tile(min(u, last), cur[u], ring[u]);
+    }
     TileIds ids_next = ids_of(min(PF, last));
     bool ok = true;
     for (int i0 = 0; i0 < my_tiles && ok; i0 += NBUF) {
@@ -376,10 +498,12 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
           const TileIds ids = ids_next;
           ids_next = ids_of(min(i + PF + 1, last));
           load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF]);
+          const TileIds ids_cur = cur[u];  // the scales of tile i
+          cur[(u + PF) % NBUF] = ids;
           const int tile_p0 = tile_p0_of(i);
           const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
           f32x4 s[MT];
-          scores(masked, tile_p0, ring[u].k, s);
+          scores(masked, tile_p0, ring[u], ids_cur.ks, s);
           if (!have_ref) {
             raise_ref(s);  // the wave's first tile sets the reference
             have_ref = true;
@@ -394,7 +518,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
               ok = false;
             }
           }
-          accumulate(masked, tile_p0, s, ring[u].v);
+          accumulate(masked, tile_p0, s, ring[u], ids_cur.vs);
         }
       }
     }
@@ -402,6 +526,22 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   };
 
   while (!run()) {
+  }
+
+  if constexpr (Q8) {
+    // remove the V offset: accumulator row 4g + e (+16 mt) held 128 * sum(scaled P) of that row too
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float tot = vcorr[mt];
+      tot += __shfl_xor(tot, 16, 64);
+      tot += __shfl_xor(tot, 32, 64);  // row c16's total, on every lane of column c16
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ce = kVOffset * __shfl(tot, 4 * g + e, 64);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) acc[mt][jb][e] -= ce;
+      }
+    }
   }
 
   if constexpr (WAVE_ITEMS) {
@@ -467,23 +607,30 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   }
 }
 
-template <int MT, int BS, bool WI>
+template <int MT, int BS, bool WI, bool Q8>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
   const int64_t grid = (int64_t)p.B * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_mfma_kernel<MT, BS, kMfmaWaves, WI ? kMfmaSplitPrefetch : kMfmaPrefetch, WI>
+  decode_mfma_kernel<MT, BS, kMfmaWaves, WI ? kMfmaSplitPrefetch : kMfmaPrefetch, WI, Q8>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
 template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_int8) {
+    switch (p.block_size) {
+      case 16: return launch_t<MT, 16, WI, true>(p, stream);
+      case 32: return launch_t<MT, 32, WI, true>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.block_size) {
-    case 4: return launch_t<MT, 4, WI>(p, stream);
-    case 8: return launch_t<MT, 8, WI>(p, stream);
-    case 16: return launch_t<MT, 16, WI>(p, stream);
-    case 32: return launch_t<MT, 32, WI>(p, stream);
+    case 4: return launch_t<MT, 4, WI, false>(p, stream);
+    case 8: return launch_t<MT, 8, WI, false>(p, stream);
+    case 16: return launch_t<MT, 16, WI, false>(p, stream);
+    case 32: return launch_t<MT, 32, WI, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -494,6 +641,12 @@ bool mfma_supported(const pa_dims& d) {
   const int rows = d.q_tokens * (d.num_q_heads / d.num_kv_heads);
   const bool block = d.block_size == 4 || d.block_size == 8 || d.block_size == 16 || d.block_size == 32;
   return d.kv_dtype == PA_BF16 && d.q_dtype == PA_BF16 && d.head_dim == kD && block && rows <= 32;
+}
+
+bool mfma_int8_supported(const pa_dims& d) {
+  const int rows = d.q_tokens * (d.num_q_heads / d.num_kv_heads);
+  return d.kv_dtype == PA_INT8 && d.q_dtype == PA_BF16 && d.head_dim == kD &&
+         (d.block_size == 16 || d.block_size == 32) && rows <= 32;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {

@@ -20,6 +20,8 @@ struct DecodeParams {
   void* out;                 // [B, T, Hq, D] (single-pass launches)
   float* part_ml;            // [B*T*Hq, parts, 2]: (m, l) per partition (partitioned launches)
   float* part_acc;           // [B*T*Hq, parts, D]: unnormalised accumulator per partition
+  const float* k_scales;     // int8 pools: [N, Hkv] scale of each (block, kv head); else null
+  const float* v_scales;
   float qk_scale_log2;       // scale * log2(e): scores are kept in base-2 exponent units
   int32_t B, T, Hq, Hkv, G, D, MB, block_size;
   int32_t num_blocks;        // N: physical blocks in each pool
@@ -29,11 +31,16 @@ struct DecodeParams {
   int32_t part_tokens;       // positions per partition (single pass: >= every length)
   int32_t out_dtype;         // pa_dtype of out
   int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
+  int32_t kv_int8;           // 1: the pools hold int8 codes scaled by k_scales / v_scales
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* positions,
                            hipStream_t stream);
+
+hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
+                                int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                                const int32_t* positions, hipStream_t stream);
 
 // Rows handled by one VALU workgroup for `rows` query rows per kv head.
 int valu_rows_per_group(int rows);
@@ -45,7 +52,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t s
 int debug_check(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
                 const int32_t* positions, int32_t max_seq_len, hipStream_t stream);
 
-bool mfma_supported(const pa_dims& d);
+bool mfma_supported(const pa_dims& d);       // bf16 pools
+bool mfma_int8_supported(const pa_dims& d);  // int8 pools
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);

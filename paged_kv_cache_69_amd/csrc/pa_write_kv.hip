@@ -48,7 +48,118 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteParams p) {
   *reinterpret_cast<u32x4*>((which ? p.v_pool : p.k_pool) + dst) = v;
 }
 
+// ---- int8 pools ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша", section 6): codes with one
+// scale per (block, kv head). One wave per (sequence, kv head) appends that head's T new rows, block by
+// block: the block's scale grows to cover the new rows (a block first written at offset 0 takes theirs
+// alone), the codes already in it are re-quantised when the scale grew, then the new rows are
+// quantised. Every code is decided with the same fp32 operations the definition states: the scale
+// amax / 127, the quotient x / scale (correctly rounded), round half to even, clip to [-127, 127].
+
+struct WriteInt8Params {
+  const void* k_new;
+  const void* v_new;
+  int8_t* k_pool;
+  int8_t* v_pool;
+  float* k_scales;
+  float* v_scales;
+  const int32_t* block_tables;
+  const int32_t* positions;
+  int32_t T, Hkv, MB, block_size, D;
+  int32_t new_f32;  // new rows are fp32 (else bf16)
+};
+
+__device__ __forceinline__ float new_value(const WriteInt8Params& p, const void* base, int64_t idx) {
+  if (p.new_f32) return static_cast<const float*>(base)[idx];
+  return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[idx] << 16);
+}
+
+__device__ __forceinline__ int quantise(float x, float scale) {
+  if (scale == 0.f) return 0;
+  return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);
+}
+
+__global__ __launch_bounds__(64) void write_kv_int8_kernel(const WriteInt8Params p) {
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.x % p.Hkv;
+  const int seq = blockIdx.x / p.Hkv;
+  const int D = p.D, b = p.block_size;
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which ? p.v_new : p.k_new;
+    int8_t* pool = which ? p.v_pool : p.k_pool;
+    float* scales = which ? p.v_scales : p.k_scales;
+    for (int t = 0; t < p.T;) {
+      const int pos0 = p.positions[(int64_t)seq * p.T + t];
+      const int first = pos0 % b;
+      const int n = min(p.T - t, b - first);  // new rows landing in this block (positions are consecutive)
+      const int blk = p.block_tables[(int64_t)seq * p.MB + pos0 / b];
+      const int64_t row0 = ((int64_t)blk * p.Hkv + kvh) * b;  // row index of offset 0 in the pool
+      // largest magnitude among the new rows of this head
+      float a = 0.f;
+      for (int r = 0; r < n; ++r) {
+        const int64_t base = ((int64_t)(seq * p.T + t + r) * p.Hkv + kvh) * D;
+        for (int d = lane; d < D; d += 64) a = fmaxf(a, fabsf(new_value(p, src, base + d)));
+      }
+      a = wave_max(a);
+      const float cand = a / 127.f;
+      float* sp = scales + (int64_t)blk * p.Hkv + kvh;
+      const float old = first > 0 ? *sp : 0.f;
+      const float scale = first > 0 ? fmaxf(old, cand) : cand;
+      if (first > 0 && scale > old) {
+        // re-quantise the codes already in the block with the larger scale
+        uint32_t* words = reinterpret_cast<uint32_t*>(pool + row0 * D);
+        for (int w = lane; w < first * D / 4; w += 64) {
+          const uint32_t c4 = words[w];
+          uint32_t out = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float c = (float)(int8_t)(c4 >> (8 * k));
+            out |= (uint32_t)(uint8_t)quantise(c * old, scale) << (8 * k);
+          }
+          words[w] = out;
+        }
+      }
+      for (int r = 0; r < n; ++r) {
+        const int64_t base = ((int64_t)(seq * p.T + t + r) * p.Hkv + kvh) * D;
+        uint32_t* words = reinterpret_cast<uint32_t*>(pool + (row0 + first + r) * D);
+        for (int w = lane; w < D / 4; w += 64) {
+          uint32_t out = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            out |= (uint32_t)(uint8_t)quantise(new_value(p, src, base + 4 * w + k), scale) << (8 * k);
+          words[w] = out;
+        }
+      }
+      if (lane == 0) *sp = scale;
+      t += n;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
+                                int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                                const int32_t* positions, hipStream_t stream) {
+  WriteInt8Params p;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  p.block_tables = block_tables;
+  p.positions = positions;
+  p.T = d.q_tokens;
+  p.Hkv = d.num_kv_heads;
+  p.MB = d.max_blocks_per_seq;
+  p.block_size = d.block_size;
+  p.D = d.head_dim;
+  p.new_f32 = d.q_dtype == PA_F32;
+  const int64_t grid = (int64_t)d.num_seqs * d.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  write_kv_int8_kernel<<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* positions,

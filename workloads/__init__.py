@@ -5,4 +5,4 @@ the attention arithmetic. It draws lengths, hands out physical blocks, writes
 block tables, and fills pools and queries with N(0, 1) values.
 """
 
-from .configs import CONFIG_NAMES, Case, build_case, make_case  # noqa: F401
+from .configs import CONFIG_NAMES, Case, build_case, int8_pools, make_case  # noqa: F401

@@ -219,3 +219,30 @@ def make_case(name: str, *, num_seqs: int | None = None, seed: int | None = None
         return build_case(num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
                           q_tokens=4, dtype=torch.bfloat16, **common)
     raise KeyError(name)
+
+
+def int8_pools(case: Case, *, seed: int | None = None, device=None):
+    """Seeded int8 K/V pools of the case's pool shape, for the int8 entry points.
+
+    Codes are round(N(0, 40^2)) clipped to [-127, 127]; each (block, kv head) gets a scale drawn from
+    U[0.02, 0.04] (about what max|x| / 127 gives for a block of N(0, 1) values). No quantiser runs
+    here: codes and scales are drawn directly. Blocks no table references get NaN scales, so a read
+    of one would show in the output. Returns ``(k_codes, k_scales, v_codes, v_scales)`` on ``device``
+    (the case's pool device by default).
+    """
+    device = torch.device(device) if device is not None else case.k_pool.device
+    gen = torch.Generator(device=device).manual_seed(int(seed if seed is not None else 7777))
+    n, hkv, b, d = case.k_pool.shape
+    out = []
+    for _ in range(2):
+        codes = torch.empty((n, hkv, b, d), dtype=torch.int8, device=device)
+        flat = codes.view(-1)
+        for start in range(0, flat.numel(), _FILL_CHUNK):
+            m = min(_FILL_CHUNK, flat.numel() - start)
+            x = torch.randn(m, generator=gen, dtype=torch.float32, device=device) * 40.0
+            flat[start:start + m] = x.round().clamp(-127, 127).to(torch.int8)
+        scales = torch.rand((n, hkv), generator=gen, dtype=torch.float32, device=device) * 0.02 + 0.02
+        if case.unused_blocks is not None and case.unused_blocks.numel():
+            scales[case.unused_blocks.to(device)] = float("nan")
+        out += [codes, scales]
+    return tuple(out)
