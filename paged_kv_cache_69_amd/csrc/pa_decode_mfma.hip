@@ -101,6 +101,12 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 #ifndef PA_MFMA_SPLIT_PREFETCH
 #define PA_MFMA_SPLIT_PREFETCH 2
 #endif
+#ifndef PA_MFMA_Q8_PREFETCH
+#define PA_MFMA_Q8_PREFETCH 1
+#endif
+#ifndef PA_MFMA_Q8_SPLIT_PREFETCH
+#define PA_MFMA_Q8_SPLIT_PREFETCH 3
+#endif
 #ifdef PA_MFMA_WAVES_PER_EU
 #define PA_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 #else
@@ -109,6 +115,9 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
 constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;            // single pass: few tiles per wave
 constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a whole partition per wave
+// int8 tiles are half the bytes and half the registers, so they run further ahead
+constexpr int kMfmaQ8Prefetch = PA_MFMA_Q8_PREFETCH;
+constexpr int kMfmaQ8SplitPrefetch = PA_MFMA_Q8_SPLIT_PREFETCH;
 
 // Byte offset of (position t, byte b of its 256-byte row) inside one V tile in LDS.
 __device__ __forceinline__ int v_swz(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
@@ -612,7 +621,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
   const int64_t grid = (int64_t)p.B * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_mfma_kernel<MT, BS, kMfmaWaves, WI ? kMfmaSplitPrefetch : kMfmaPrefetch, WI, Q8>
+  constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
+  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
