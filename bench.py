@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-KV decode step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the KV-append
-scatter (pa_write_kv), then decode attention over every sequence
-(pa_decode, or pa_decode_partitioned plus its merge pass). Inputs are
-synthetic, seeded and resident in HBM before the timed region starts.
-R independent replicas of (pools, tables, q, new rows) are rotated step by
-step, so the 256 MB Infinity Cache cannot serve the KV of one step from the
-previous one; R * (bytes one step touches) >= 1 GB. The K timed steps run as
-HIP graph replays (one captured step per replica), so host launch cost is not
-timed; that gives `value`. The same K steps are then launched directly with a
-pair of HIP events on the launch stream around every decode call, which gives
-the decode call's average duration for `roofline`.
+A step is one pass of the whole hot path over one batch: the KV append and
+decode attention over every sequence. On the workloads whose launch
+configuration says so (batch64, long) the step is one pa_write_kv_decode call
+(or its split-context form); otherwise it is pa_write_kv then pa_decode /
+pa_decode_partitioned (the _int8 entry points for int8 pools); --no-fused
+always times the separate calls. Inputs are synthetic, seeded and resident in HBM before the timed
+region starts. R independent replicas of (pools, tables, q, new rows) are
+rotated step by step, so the 256 MB Infinity Cache cannot serve the KV of one
+step from the previous one; R * (bytes one step touches) >= 1 GB. The K timed
+steps run as HIP graph replays (one captured step per replica), so host launch
+cost is not timed; that gives `value`. Then K of the step's attention calls
+(the fused call, or the decode call) run back to back as one graph between a
+pair of HIP events on their stream, which gives that call's average duration
+for `roofline`.
 
 Prints one JSON line. `value` is decode tokens per second of the whole step.
 `roofline` relates the decode call's algorithmic bytes to its measured
@@ -50,11 +53,13 @@ COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
 PROFILES = os.path.join(ROOT, "profiles")
 
-# Launch configuration per workload: partition_tokens None = single-pass pa_decode.
+# Launch configuration per workload: partition_tokens None = single-pass decode; fused = the step is
+# one pa_write_kv_decode call (measured faster than the two calls on batch64 and long, slower on the
+# prefix and speculative workloads, where the separate append is a small share of the step).
 WORKLOADS = {
-    "batch64": dict(partition_tokens=None, desc="64 seqs, L~U[20,500], 32 q / 8 kv heads, head_dim 128, b=16, "
+    "batch64": dict(partition_tokens=None, fused=True, desc="64 seqs, L~U[20,500], 32 q / 8 kv heads, head_dim 128, b=16, "
                                                "bf16 (Llama-3-8B-shaped layer)"),
-    "long": dict(partition_tokens=512, desc="16 seqs, L log-uniform [4096,32768], 32 q / 8 kv heads, head_dim 128, "
+    "long": dict(partition_tokens=512, fused=True, desc="16 seqs, L log-uniform [4096,32768], 32 q / 8 kv heads, head_dim 128, "
                                             "b=16, bf16, 512-token partitions + merge"),
     "prefix": dict(partition_tokens=None, desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] "
                                                "private suffix, 32 q / 8 kv heads, head_dim 128, b=16, bf16"),
@@ -148,7 +153,7 @@ def traffic_from_profiles(workload: str):
 class Replica:
     """One independent copy of a step's device inputs, with ctypes arguments prepacked."""
 
-    def __init__(self, pa, case, src, partition_tokens, variant=0):
+    def __init__(self, pa, case, src, partition_tokens, variant=0, fused=False):
         import ctypes
 
         import torch
@@ -181,6 +186,30 @@ class Replica:
         self.f_write = getattr(self.lib, "pa_write_kv" + sfx)
         self.f_decode = getattr(self.lib, "pa_decode" + sfx)
         self.f_split = getattr(self.lib, "pa_decode_partitioned" + sfx)
+        self.fused = fused and not self.int8
+        self.fused_args = (ctypes.byref(self.dims), p["q"], p["k_new"], p["v_new"], p["k_pool"], p["v_pool"],
+                           p["block_tables"], p["seq_lens"], self.scale)
+
+    def step(self, stream):
+        """One whole decode step: the fused append + decode call where there is one, else the two calls."""
+        if self.fused:
+            self.call(stream)
+        else:
+            self.write(stream)
+            self.decode(stream)
+
+    def call(self, stream):
+        """The step's attention call, the one the roofline times: the fused call, or the decode call."""
+        if not self.fused:
+            self.decode(stream)
+            return
+        if self.ws is None:
+            st = self.lib.pa_write_kv_decode(*self.fused_args, self.out.data_ptr(), stream)
+        else:
+            st = self.lib.pa_write_kv_decode_partitioned(*self.fused_args, self.out.data_ptr(), self.max_len, self.pt,
+                                                         self.ws.data_ptr(), self.ws.numel(), stream)
+        if st:
+            raise RuntimeError(f"write_kv_decode: {st}")
 
     def write(self, stream):
         st = self.f_write(*self.write_args, stream)
@@ -197,7 +226,7 @@ class Replica:
             raise RuntimeError(f"decode: {st}")
 
 
-def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=True):
+def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=True, fused=False):
     """Returns (seconds per step, ms per decode call, replica count). Without ``graphs`` both come
     from eagerly launched steps (counter-collection runs only; the call time then includes the
     KV writes)."""
@@ -212,7 +241,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
     src = {k: getattr(case, k).to(dev) for k in keys}
     touched = unique_bytes(case)  # a block shared by several tables is cached once
     n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
-    reps = [Replica(pa, case, src, partition_tokens, variant) for _ in range(n_rep)]
+    reps = [Replica(pa, case, src, partition_tokens, variant, fused) for _ in range(n_rep)]
     del src
     torch.cuda.synchronize()
 
@@ -221,9 +250,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
 
     # untimed warmup, eager
     for s in range(warmup):
-        r = reps[s % n_rep]
-        r.write(sh())
-        r.decode(sh())
+        reps[s % n_rep].step(sh())
     torch.cuda.synchronize()
 
     # Timed region A: the K steps as HIP graph replays (one graph per chunk of consecutive steps).
@@ -234,9 +261,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
                 for c in range(count):
-                    r = reps[c % n_rep]
-                    r.write(sh())
-                    r.decode(sh())
+                    reps[c % n_rep].step(sh())
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         return g
@@ -273,7 +298,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
                 for s in range(steps):
-                    reps[s % n_rep].decode(sh())
+                    reps[s % n_rep].call(sh())
         stream.wait_stream(side)
         g.replay()  # upload, untimed
         torch.cuda.synchronize()
@@ -288,9 +313,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
         e0 = time.perf_counter()
         ev0.record(stream)
         for s in range(steps):
-            r = reps[s % n_rep]
-            r.write(handle)
-            r.decode(handle)
+            reps[s % n_rep].step(handle)
         ev1.record(stream)
         torch.cuda.synchronize()
         t0, t1 = e0, time.perf_counter()
@@ -362,7 +385,7 @@ def calibrate_copy(n_runs: int = 3):
     torch.cuda.empty_cache()
 
 
-def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True):
+def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True, fused=True):
     import torch
 
     from workloads import int8_pools, make_case
@@ -371,15 +394,23 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     case = make_case(spec.get("base", name), pool_device="cuda:0")
     if spec.get("int8"):
         case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
-    sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs)
     b, t = case.q.shape[0], case.q.shape[1]
-    algo = algorithmic_bytes(case)
-    achieved = algo / (dur_ms * 1e-3) / 1e9
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
     mfma_ok = case.k_pool.dtype in (torch.bfloat16, torch.int8) and case.q.shape[3] == 128 and rows <= 32
+    fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok and case.k_pool.dtype == torch.bfloat16
+    sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs,
+                                              fused)
+    algo = algorithmic_bytes(case)
+    if fused:  # the call also reads the new rows and stores them into the pools
+        algo += 2 * case.k_new.numel() * case.k_new.element_size() * 2
+    achieved = algo / (dur_ms * 1e-3) / 1e9
     kernel = "decode_mfma_kernel" if (variant == 2 or (variant == 0 and mfma_ok)) else "decode_valu_kernel"
-    kernel += " + merge_partials_kernel (one pa_decode_partitioned call)" if spec["partition_tokens"] else \
-        " (one pa_decode call)"
+    if fused:
+        kernel += " with the KV append fused in"
+    call = ("pa_write_kv_decode" if fused else "pa_decode") + ("_partitioned" if spec["partition_tokens"] else "")
+    if "int8" in name:
+        call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + "_int8"
+    kernel += (" + merge_partials_kernel" if spec["partition_tokens"] else "") + f" (one {call} call)"
     traffic = traffic_from_profiles(name) if variant == 0 else None
     res = {
         "tokens_per_s": b * t / sec_per_step,
@@ -391,7 +422,8 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
                      "launches_timed": steps},
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": b, "q_tokens": t,
                    "kv_positions": case.kv_tokens(), "max_seq_len": case.max_seq_len,
-                   "partition_tokens": spec["partition_tokens"], "replicas": n_rep},
+                   "partition_tokens": spec["partition_tokens"], "replicas": n_rep,
+                   "step": "one fused append + decode call" if fused else "append call + decode call"},
         "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
     }
     if name == "prefix":
@@ -517,6 +549,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 vector-ALU kernel, 2 MFMA kernel")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="time the step as separate pa_write_kv and decode calls on every workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for counter calibration)")
     ap.add_argument("--no-graph", action="store_true",
@@ -546,7 +580,7 @@ def main(argv=None):
     if args.calibrate_copy:
         calibrate_copy()
     main_res = run_workload(pa, args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_budget,
-                            args.variant, not args.no_graph)
+                            args.variant, not args.no_graph, not args.no_fused)
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 1),
@@ -569,7 +603,8 @@ def main(argv=None):
         line["cpu_baseline"] = main_res["cpu_baseline"]
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant, not args.no_graph)
+        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant, not args.no_graph,
+                         not args.no_fused)
         secondary[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 6),
                            "achieved_gbps": round(r["achieved_gbps"], 1), "roofline": r["roofline"],
                            "config": r["config"], **({"unique_bytes": r["unique_bytes"]} if "unique_bytes" in r else {})}

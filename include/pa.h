@@ -171,6 +171,32 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
 
+/* pa_write_kv_decode: one decode step in one launch: pa_write_kv of the T new
+ * tokens at each sequence's last T positions (positions[i][t] = seq_lens[i] -
+ * T + t, so no positions argument), then pa_decode. The results (pools and
+ * out) are bit for bit those of the two separate calls. The workgroup of each
+ * (sequence, kv head) stores that head's new rows itself and, in the tile that
+ * holds them, reads them from k_new / v_new rather than from the pool, so no
+ * part of the launch waits for its own stores ([P4] section "Block table and
+ * allocator": a decode step appends the new token's K and V, then attends).
+ *   k_new, v_new : [B, T, Hkv, D], q_dtype;  k_pool, v_pool : written in place
+ * Other arguments as pa_decode. Supported: the MFMA shapes of pa_decode
+ * (PA_BF16, D = 128, b in {4, 8, 16, 32}, T * G <= 32); otherwise
+ * PA_ERR_UNSUPPORTED (use pa_write_kv and pa_decode). The new rows' slots
+ * must not be read by another sequence in the same call. */
+int pa_write_kv_decode(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                       void* k_pool, void* v_pool, const int32_t* block_tables,
+                       const int32_t* seq_lens, float scale, void* out, pa_stream_t stream);
+
+/* pa_write_kv_decode_partitioned: the same fused step on the split-context
+ * path (pa_decode_partitioned's workspace, rules and merge pass). */
+int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const void* k_new,
+                                   const void* v_new, void* k_pool, void* v_pool,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   float scale, void* out, int32_t max_seq_len,
+                                   int32_t partition_tokens, void* workspace,
+                                   size_t workspace_bytes, pa_stream_t stream);
+
 /* ---- int8 KV cache ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша",
  * section 6: block-wise KV quantisation).
  *

@@ -28,6 +28,8 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
+    "pa_write_kv_decode",
+    "pa_write_kv_decode_partitioned",
     "pa_write_kv_int8",
     "pa_decode_int8",
     "pa_decode_partitioned_int8",
@@ -80,6 +82,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_write_kv_decode.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.pa_write_kv_decode.restype = ctypes.c_int
+    lib.pa_write_kv_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32,
+                                                   _I32, _P, ctypes.c_size_t, _P]
+    lib.pa_write_kv_decode_partitioned.restype = ctypes.c_int
     lib.pa_write_kv_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.pa_write_kv_int8.restype = ctypes.c_int
     lib.pa_decode_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
@@ -225,6 +232,45 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_partitioned", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- fused append + decode
+
+def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, *,
+                    max_seq_len: int | None = None, partition_tokens: int | None = None, workspace=None,
+                    out_dtype=None, variant: int = VARIANT_AUTO, stream=None):
+    """``pa_write_kv_decode`` (or ``pa_write_kv_decode_partitioned`` when ``partition_tokens`` is
+    given): append ``k_new``/``v_new [B, T, Hkv, D]`` at each sequence's last T positions and decode,
+    in one launch. Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    tensors = dict(q=q, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                   seq_lens=seq_lens, out=out)
+    split = partition_tokens is not None
+    if split:
+        need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        tensors["workspace"] = workspace
+    dev = _check_tensors(**tensors)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape and k_new.shape == v_new.shape, "shape mismatch")
+    _require(k_new.dtype == q.dtype and k_pool.dtype == q.dtype, "q, new rows and pools must share a dtype")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant)
+    args = [ctypes.byref(dims), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+            v_pool.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
+    if split:
+        st = lib.pa_write_kv_decode_partitioned(*args, int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
+                                                workspace.numel() * workspace.element_size(),
+                                                _stream_handle(stream, dev))
+        _check(lib, "pa_write_kv_decode_partitioned", st)
+    else:
+        st = lib.pa_write_kv_decode(*args, _stream_handle(stream, dev))
+        _check(lib, "pa_write_kv_decode", st)
     return out
 
 

@@ -119,12 +119,15 @@ void workspace_layout(const pa_dims* d, int32_t parts, size_t* ml_bytes, size_t*
 int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, const void* k_pool, const void* v_pool,
                  const float* k_scales, const float* v_scales, const int32_t* block_tables, const int32_t* seq_lens,
                  float scale, void* out, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
-                 size_t workspace_bytes, pa_stream_t stream) {
+                 size_t workspace_bytes, pa_stream_t stream, const void* k_new = nullptr,
+                 const void* v_new = nullptr) {
+  const bool append = k_new != nullptr || v_new != nullptr;
   int st = int8 ? check_dims_int8(dims) : check_dims(dims);
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
   if (int8 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+  if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
   int32_t parts = 1;
@@ -140,6 +143,9 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   if (int8) {
     if (dims->variant == PA_VARIANT_VALU || !pa::mfma_int8_supported(*dims)) return PA_ERR_UNSUPPORTED;
     variant = PA_VARIANT_MFMA;
+  } else if (append) {
+    if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
+    variant = PA_VARIANT_MFMA;
   } else {
     st = choose_variant(dims, &variant);
     if (st != PA_OK) return st;
@@ -152,6 +158,9 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   p.k_scales = k_scales;
   p.v_scales = v_scales;
   p.kv_int8 = int8 ? 1 : 0;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.append = append ? 1 : 0;
   if (!split) {
     p.parts = 1;
     p.part_tokens = kSinglePassTokens;
@@ -223,6 +232,21 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           size_t workspace_bytes, pa_stream_t stream) {
   return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_write_kv_decode(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                       void* v_pool, const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                       pa_stream_t stream) {
+  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream, k_new, v_new);
+}
+
+int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                                   void* k_pool, void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                                   float scale, void* out, int32_t max_seq_len, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
+                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,

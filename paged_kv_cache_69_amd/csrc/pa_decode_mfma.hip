@@ -57,6 +57,16 @@
 //    loaded with the block id. int8 codes are always finite, so tail V rows
 //    need no zeroing: their P is exactly 0.
 //
+// Fused append (APPEND, bf16 pools): the call also stores this step's new K/V
+// rows, at positions L - T .. L - 1, into their pool slots ([P4] "Block table
+// and allocator": a decode step writes the new token's K and V, then
+// attends). The workgroup of (sequence, kv head) stores that head's rows
+// itself: wave 0 in a single pass, or the wave whose partition holds them. No
+// wave waits for those stores: in the tile that holds a new position, the
+// lanes of that position take its K/V chunks from k_new / v_new instead of the
+// pool, so the result is bit for bit the one a separate append followed by a
+// decode gives.
+//
 // Two ways of sharing the work:
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
 //    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
@@ -164,9 +174,10 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
+  static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
   constexpr int kKvTile = kTile * kKvRow;
   constexpr int ROWS = 16 * MT;
@@ -285,6 +296,11 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kKvRow;
   lds_char* vt = (lds_char*)lds + wave * kTileBytes;
 
+  // Row t of this sequence's new K or V rows ([B, T, Hkv, D]), for this kv head.
+  auto new_row = [&](const void* base, int t) -> const char* {
+    return static_cast<const char*>(base) + ((int64_t)(seq * T + t) * p.Hkv + kvh) * kRowBytes;
+  };
+
   // Byte offset, inside this kv head's view of the pool, of position `pos` of a tile whose blocks are `ids`.
   auto pos_offset = [&](const TileIds& ids, int tile_p0, int pos) -> int64_t {
     if constexpr (BS >= kTile) {
@@ -329,6 +345,20 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         tr.v[c] = load16(vbase + pos_offset(ids, tile_p0, tile_p0 + 4 * c + (lane >> 4)) + (lane & 15) * 16);
+    }
+    if constexpr (APPEND) {
+      if (tile_p0 + kTile > L - T) {  // the tile holds new positions: their rows come from k_new / v_new
+        const int tk = tile_p0 + c16 - (L - T);
+        if (tk >= 0 && tk < T) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) tr.k[kc] = load16(new_row(p.k_new, tk) + (kc * 4 + g) * 16);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int tv = tile_p0 + 4 * c + (lane >> 4) - (L - T);
+          if (tv >= 0 && tv < T) tr.v[c] = load16(new_row(p.v_new, tv) + (lane & 15) * 16);
+        }
+      }
     }
   };
 
@@ -534,6 +564,24 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     return ok;
   };
 
+  if constexpr (APPEND) {
+    // store the new rows this wave owns (positions L - T .. L - 1 in its range) into the pools
+    // One row per step, so its position and block are wave-uniform (a scalar table load); lanes 0-15
+    // copy the K row's 16-byte chunks and lanes 16-31 the V row's.
+    const int t_lo = WAVE_ITEMS ? max(0, p_begin - (L - T)) : 0;
+    const int t_hi = WAVE_ITEMS ? min(T, p_end - (L - T)) : (wave == 0 ? T : 0);
+    for (int t = max(t_lo, T - L); t < t_hi; ++t) {
+      const int pos = L - T + t;
+      const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+      if (lane < 32) {
+        const int which = lane >> 4, chunk = lane & 15;
+        const int64_t dst = (int64_t)blk * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
+        const u32x4 v = load16(new_row(which ? p.v_new : p.k_new, t) + chunk * 16);
+        *reinterpret_cast<u32x4*>(const_cast<char*>(which ? vbase : kbase) + dst) = v;
+      }
+    }
+  }
+
   while (!run()) {
   }
 
@@ -616,13 +664,13 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   }
 }
 
-template <int MT, int BS, bool WI, bool Q8>
+template <int MT, int BS, bool WI, bool Q8, bool AP>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
   const int64_t grid = (int64_t)p.B * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
   constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
-  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8>
+  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
@@ -631,16 +679,25 @@ template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
   if (p.kv_int8) {
     switch (p.block_size) {
-      case 16: return launch_t<MT, 16, WI, true>(p, stream);
-      case 32: return launch_t<MT, 32, WI, true>(p, stream);
+      case 16: return launch_t<MT, 16, WI, true, false>(p, stream);
+      case 32: return launch_t<MT, 32, WI, true, false>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.append) {
+    switch (p.block_size) {
+      case 4: return launch_t<MT, 4, WI, false, true>(p, stream);
+      case 8: return launch_t<MT, 8, WI, false, true>(p, stream);
+      case 16: return launch_t<MT, 16, WI, false, true>(p, stream);
+      case 32: return launch_t<MT, 32, WI, false, true>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (p.block_size) {
-    case 4: return launch_t<MT, 4, WI, false>(p, stream);
-    case 8: return launch_t<MT, 8, WI, false>(p, stream);
-    case 16: return launch_t<MT, 16, WI, false>(p, stream);
-    case 32: return launch_t<MT, 32, WI, false>(p, stream);
+    case 4: return launch_t<MT, 4, WI, false, false>(p, stream);
+    case 8: return launch_t<MT, 8, WI, false, false>(p, stream);
+    case 16: return launch_t<MT, 16, WI, false, false>(p, stream);
+    case 32: return launch_t<MT, 32, WI, false, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,6 +22,8 @@ struct DecodeParams {
   float* part_acc;           // [B*T*Hq, parts, D]: unnormalised accumulator per partition
   const float* k_scales;     // int8 pools: [N, Hkv] scale of each (block, kv head); else null
   const float* v_scales;
+  const void* k_new;         // fused append: [B, T, Hkv, D] new rows for positions L - T .. L - 1
+  const void* v_new;
   float qk_scale_log2;       // scale * log2(e): scores are kept in base-2 exponent units
   int32_t B, T, Hq, Hkv, G, D, MB, block_size;
   int32_t num_blocks;        // N: physical blocks in each pool
@@ -32,6 +34,7 @@ struct DecodeParams {
   int32_t out_dtype;         // pa_dtype of out
   int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
   int32_t kv_int8;           // 1: the pools hold int8 codes scaled by k_scales / v_scales
+  int32_t append;            // 1: also store k_new / v_new into the pools (MFMA kernel, bf16)
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteParams p) {
 }
 
 // ---- int8 pools ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша", section 6): codes with one
-// scale per (block, kv head). One wave per (sequence, kv head) appends that head's T new rows, block by
-// block: the block's scale grows to cover the new rows (a block first written at offset 0 takes theirs
+// scale per (block, kv head). A workgroup per (sequence, kv head), wave 0 for K and wave 1 for V,
+// appends that head's T new rows, block by block: the block's scale grows to cover the new rows (a block first written at offset 0 takes theirs
 // alone), the codes already in it are re-quantised when the scale grew, then the new rows are
 // quantised. Every code is decided with the same fp32 operations the definition states: the scale
 // amax / 127, the quotient x / scale (correctly rounded), round half to even, clip to [-127, 127].
@@ -78,12 +78,13 @@ __device__ __forceinline__ int quantise(float x, float scale) {
   return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);
 }
 
-__global__ __launch_bounds__(64) void write_kv_int8_kernel(const WriteInt8Params p) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Params p) {
+  const int lane = threadIdx.x & 63;
+  const int which = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, 1: V
   const int kvh = blockIdx.x % p.Hkv;
   const int seq = blockIdx.x / p.Hkv;
   const int D = p.D, b = p.block_size;
-  for (int which = 0; which < 2; ++which) {
+  {
     const void* src = which ? p.v_new : p.k_new;
     int8_t* pool = which ? p.v_pool : p.k_pool;
     float* scales = which ? p.v_scales : p.k_scales;
@@ -157,7 +158,7 @@ hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void*
   p.new_f32 = d.q_dtype == PA_F32;
   const int64_t grid = (int64_t)d.num_seqs * d.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  write_kv_int8_kernel<<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
+  write_kv_int8_kernel<<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
   return hipGetLastError();
 }
 

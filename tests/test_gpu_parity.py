@@ -345,3 +345,65 @@ def test_full_size_sampled(gpu_lib, name, partitioned, variant):
     sel = np.stack([got[i, t, h] for i, t, h in rows])
     err = assert_attention_close(sel, ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what=name)
     print(f"[result] {name}: {len(rows)} sampled rows, max |err| = {err:.2e}", flush=True)
+
+
+# ----------------------------------------------------------------------------- fused append + decode
+
+def _fused_vs_separate(pa, case, *, partition_tokens=None, variant_sep=MFMA):
+    """Run pa_write_kv + decode and pa_write_kv_decode on copies of the same inputs; return both
+    (pools, out) so callers can require bit identity."""
+    a = _to_gpu(case)
+    pa.write_kv(a["k_new"], a["v_new"], a["k_pool"], a["v_pool"], a["block_tables"], a["positions"])
+    if partition_tokens:
+        out_a = pa.decode_partitioned(a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["seq_lens"], case.scale,
+                                      case.max_seq_len, partition_tokens, variant=variant_sep)
+    else:
+        out_a = pa.decode(a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["seq_lens"], case.scale,
+                          variant=variant_sep)
+    b = _to_gpu(case)
+    out_b = pa.write_kv_decode(b["q"], b["k_new"], b["v_new"], b["k_pool"], b["v_pool"], b["block_tables"],
+                               b["seq_lens"], case.scale, max_seq_len=case.max_seq_len if partition_tokens else None,
+                               partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return a, out_a, b, out_b
+
+
+@pytest.mark.parametrize("b", [4, 8, 16, 32])
+@pytest.mark.parametrize("hq,hkv,t", [(4, 4, 1), (32, 8, 1), (8, 2, 4), (16, 2, 4), (12, 4, 3), (64, 8, 4)])
+def test_fused_append_decode_bitwise(gpu_lib, b, hq, hkv, t):
+    """pa_write_kv_decode equals pa_write_kv followed by the MFMA decode, bit for bit (pools and out),
+    single pass and split (new rows inside one partition and straddling two), and meets the oracle."""
+    lengths = sorted({max(t, x) for x in (1, 2, b - 1, b, b + 1, 15, 16, 17, 31, 33, 47, 100, 257)})
+    case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b, q_tokens=t,
+                      dtype=torch.bfloat16, seed=900 + b * 10 + hq + t, pool_slack=0.2)
+    poison_case(case)
+    print(f"[case] fused b={b} hq={hq} hkv={hkv} T={t}", flush=True)
+    for pt in (None, 32, 48 if 48 % b == 0 else 64):
+        a, out_a, g, out_b = _fused_vs_separate(gpu_lib, case, partition_tokens=pt)
+        assert np.array_equal(bits(a["k_pool"]), bits(g["k_pool"])), f"K pool differs (pt={pt})"
+        assert np.array_equal(bits(a["v_pool"]), bits(g["v_pool"])), f"V pool differs (pt={pt})"
+        assert torch.equal(out_a, out_b), f"output differs (pt={pt})"
+    kp, vp = oracle_after_write(case)
+    assert np.array_equal(bits(g["k_pool"]), kp) and np.array_equal(bits(g["v_pool"]), vp)
+    assert_attention_close(out_b.cpu(), _oracle_decode(case, kp, vp), kv_dtype=torch.bfloat16,
+                           out_dtype=torch.float32, what="fused")
+
+
+@pytest.mark.parametrize("name,pt", [("batch64", None), ("long", 512), ("spec", None)])
+def test_fused_append_decode_full_size_bitwise(gpu_lib, name, pt):
+    """Full workload sizes: the fused step equals the two separate calls bit for bit."""
+    case = make_case(name, pool_device=DEV)
+    print(f"[case] fused full {name}", flush=True)
+    a, out_a, g, out_b = _fused_vs_separate(gpu_lib, case, partition_tokens=pt)
+    assert torch.equal(a["k_pool"].view(torch.int16), g["k_pool"].view(torch.int16))
+    assert torch.equal(a["v_pool"].view(torch.int16), g["v_pool"].view(torch.int16))
+    assert torch.equal(out_a, out_b)
+
+
+def test_fused_append_decode_refuses_unsupported(gpu_lib):
+    case = make_case("tiny")  # fp32 pools: no MFMA kernel, so no fused path
+    g = _to_gpu(case)
+    with pytest.raises(gpu_lib.PaError) as err:
+        gpu_lib.write_kv_decode(g["q"], g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"],
+                                g["seq_lens"], case.scale)
+    assert err.value.status == -2
