@@ -61,8 +61,10 @@ WORKLOADS = {
                                                "bf16 (Llama-3-8B-shaped layer)"),
     "long": dict(partition_tokens=512, fused=True, desc="16 seqs, L log-uniform [4096,32768], 32 q / 8 kv heads, head_dim 128, "
                                             "b=16, bf16, 512-token partitions + merge"),
-    "prefix": dict(partition_tokens=None, desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] "
-                                               "private suffix, 32 q / 8 kv heads, head_dim 128, b=16, bf16"),
+    "prefix": dict(partition_tokens=256, cascade=2048,
+                   desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] private suffix, 32 q / 8 kv "
+                        "heads, head_dim 128, b=16, bf16; cascade: the prefix read once for all sequences, "
+                        "256-token suffix partitions + merge"),
     "spec": dict(partition_tokens=None, desc="256 seqs, L~U[1024,8192], 4 causal query tokens, 64 q / 8 kv heads, "
                                              "head_dim 128, b=16, bf16"),
     "tiny": dict(partition_tokens=None, desc="4 seqs L={1,17,33,64}, 4 q / 2 kv heads, head_dim 64, b=16, fp32"),
@@ -153,7 +155,7 @@ def traffic_from_profiles(workload: str):
 class Replica:
     """One independent copy of a step's device inputs, with ctypes arguments prepacked."""
 
-    def __init__(self, pa, case, src, partition_tokens, variant=0, fused=False):
+    def __init__(self, pa, case, src, partition_tokens, variant=0, fused=False, cascade=0):
         import ctypes
 
         import torch
@@ -172,9 +174,14 @@ class Replica:
         self.pt = partition_tokens
         self.max_len = case.max_seq_len
         self.ws = None
+        self.cascade = cascade
         if partition_tokens:
-            n = pa.workspace_bytes(self.t["q"], self.t["k_pool"], self.t["block_tables"], self.max_len,
-                                   partition_tokens)
+            if cascade:
+                n = pa.cascade_workspace_bytes(self.t["q"], self.t["k_pool"], self.t["block_tables"], cascade,
+                                               self.max_len, partition_tokens)
+            else:
+                n = pa.workspace_bytes(self.t["q"], self.t["k_pool"], self.t["block_tables"], self.max_len,
+                                       partition_tokens)
             self.ws = torch.empty(n, dtype=torch.uint8, device=src["q"].device)
         p = {k: v.data_ptr() for k, v in self.t.items()}
         scales = (p["k_scales"], p["v_scales"]) if self.int8 else ()
@@ -217,7 +224,10 @@ class Replica:
             raise RuntimeError(f"pa_write_kv: {st}")
 
     def decode(self, stream):
-        if self.ws is None:
+        if self.cascade:
+            st = self.lib.pa_decode_cascade(*self.dec_args, self.out.data_ptr(), self.cascade, self.max_len, self.pt,
+                                            self.ws.data_ptr(), self.ws.numel(), stream)
+        elif self.ws is None:
             st = self.f_decode(*self.dec_args, self.out.data_ptr(), stream)
         else:
             st = self.f_split(*self.dec_args, self.out.data_ptr(), self.max_len, self.pt,
@@ -226,7 +236,7 @@ class Replica:
             raise RuntimeError(f"decode: {st}")
 
 
-def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=True, fused=False):
+def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=True, fused=False, cascade=0):
     """Returns (seconds per step, ms per decode call, replica count). Without ``graphs`` both come
     from eagerly launched steps (counter-collection runs only; the call time then includes the
     KV writes)."""
@@ -241,7 +251,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
     src = {k: getattr(case, k).to(dev) for k in keys}
     touched = unique_bytes(case)  # a block shared by several tables is cached once
     n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
-    reps = [Replica(pa, case, src, partition_tokens, variant, fused) for _ in range(n_rep)]
+    reps = [Replica(pa, case, src, partition_tokens, variant, fused, cascade) for _ in range(n_rep)]
     del src
     torch.cuda.synchronize()
 
@@ -398,9 +408,11 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
     mfma_ok = case.k_pool.dtype in (torch.bfloat16, torch.int8) and case.q.shape[3] == 128 and rows <= 32
     fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok and case.k_pool.dtype == torch.bfloat16
+    cascade = spec.get("cascade", 0) if variant != 1 else 0
     sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs,
-                                              fused)
-    algo = algorithmic_bytes(case)
+                                              fused, cascade)
+    # a cascade reads each shared block once: count every physical block once
+    algo = unique_bytes(case) if cascade else algorithmic_bytes(case)
     if fused:  # the call also reads the new rows and stores them into the pools
         algo += 2 * case.k_new.numel() * case.k_new.element_size() * 2
     achieved = algo / (dur_ms * 1e-3) / 1e9
@@ -410,6 +422,9 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     call = ("pa_write_kv_decode" if fused else "pa_decode") + ("_partitioned" if spec["partition_tokens"] else "")
     if "int8" in name:
         call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + "_int8"
+    if cascade:
+        call = "pa_decode_cascade"
+        kernel = "decode_mfma_kernel (shared-prefix items + per-sequence items)"
     kernel += (" + merge_partials_kernel" if spec["partition_tokens"] else "") + f" (one {call} call)"
     traffic = traffic_from_profiles(name) if variant == 0 else None
     res = {
@@ -423,6 +438,7 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": b, "q_tokens": t,
                    "kv_positions": case.kv_tokens(), "max_seq_len": case.max_seq_len,
                    "partition_tokens": spec["partition_tokens"], "replicas": n_rep,
+                   **({"shared_prefix_tokens": cascade} if cascade else {}),
                    "step": "one fused append + decode call" if fused else "append call + decode call"},
         "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
     }

@@ -197,6 +197,35 @@ int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const voi
                                    int32_t partition_tokens, void* workspace,
                                    size_t workspace_bytes, pa_stream_t stream);
 
+/* pa_decode_cascade: decode over sequences that all share their first
+ * prefix_tokens positions (the same physical blocks: a forked or
+ * prefix-cached prompt, [P1] section "Sharing blocks: forks and
+ * copy-on-write"; [P2] section 4). The result is pa_decode's.
+ * The shared prefix is attended once per kv head for the query rows of all
+ * sequences together, instead of once per sequence: it is cut into chunks
+ * (the library picks their size from the dims, a multiple of 16 and of b,
+ * so that the prefix work fills the GPU), each processed for all B * T * G
+ * rows of a kv head, 16 rows per wave. Each sequence's own positions (prefix_tokens .. L - 1)
+ * run in partitions of partition_tokens as in pa_decode_partitioned, and one
+ * merge pass combines the prefix's and the sequence's partials exactly
+ * ([P5] section 4.2). Three launches on `stream`.
+ *   prefix_tokens : a multiple of 16 and of b (0: no shared prefix, same as
+ *                   pa_decode_partitioned)
+ *   max_seq_len   : host-known bound of seq_lens, >= prefix_tokens
+ *   partition_tokens : a multiple of 16 and of b
+ *   workspace     : >= pa_decode_cascade_workspace_bytes() bytes, 256-byte
+ *                   aligned; contents on entry irrelevant
+ * Preconditions (checked under PA_CHECK=1): block_tables[i][j] ==
+ * block_tables[0][j] for j < prefix_tokens / b, and seq_lens[i] >=
+ * prefix_tokens + q_tokens (the new tokens lie past the prefix). Supported:
+ * the MFMA shapes of pa_decode (PA_BF16, D = 128, T * G <= 32). */
+size_t pa_decode_cascade_workspace_bytes(const pa_dims* dims, int32_t prefix_tokens,
+                                         int32_t max_seq_len, int32_t partition_tokens);
+int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                      int32_t prefix_tokens, int32_t max_seq_len, int32_t partition_tokens,
+                      void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
 /* ---- int8 KV cache ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша",
  * section 6: block-wise KV quantisation).
  *

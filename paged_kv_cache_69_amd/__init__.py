@@ -28,6 +28,8 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
+    "pa_decode_cascade_workspace_bytes",
+    "pa_decode_cascade",
     "pa_write_kv_decode",
     "pa_write_kv_decode_partitioned",
     "pa_write_kv_int8",
@@ -82,6 +84,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_decode_cascade_workspace_bytes.argtypes = [dims_p, _I32, _I32, _I32]
+    lib.pa_decode_cascade_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_cascade.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32, _P,
+                                      ctypes.c_size_t, _P]
+    lib.pa_decode_cascade.restype = ctypes.c_int
     lib.pa_write_kv_decode.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     lib.pa_write_kv_decode.restype = ctypes.c_int
     lib.pa_write_kv_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32,
@@ -232,6 +239,45 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_partitioned", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- cascade over a shared prefix
+
+def cascade_workspace_bytes(q, k_pool, block_tables, prefix_tokens: int, max_seq_len: int,
+                            partition_tokens: int) -> int:
+    """``pa_decode_cascade_workspace_bytes`` for these tensors."""
+    lib = load_library()
+    dims = make_dims(q, k_pool, block_tables)
+    n = lib.pa_decode_cascade_workspace_bytes(ctypes.byref(dims), int(prefix_tokens), int(max_seq_len),
+                                              int(partition_tokens))
+    if n == 0:
+        raise PaError("pa_decode_cascade_workspace_bytes", -1, "invalid argument")
+    return int(n)
+
+
+def decode_cascade(q, k_pool, v_pool, block_tables, seq_lens, scale: float, prefix_tokens: int, max_seq_len: int,
+                   partition_tokens: int, out=None, workspace=None, *, out_dtype=None, stream=None):
+    """``pa_decode_cascade``: decode where every sequence shares its first ``prefix_tokens`` positions
+    (the same physical blocks); the prefix is attended once per kv head for all sequences."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    need = cascade_workspace_bytes(q, k_pool, block_tables, prefix_tokens, max_seq_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out,
+                         workspace=workspace)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
+    st = lib.pa_decode_cascade(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                               block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                               int(prefix_tokens), int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(lib, "pa_decode_cascade", st)
     return out
 
 

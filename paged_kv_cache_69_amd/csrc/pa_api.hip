@@ -2,6 +2,8 @@
 // The declarations, and their citations of the pages, are in include/pa.h.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace {
@@ -112,6 +114,35 @@ void workspace_layout(const pa_dims* d, int32_t parts, size_t* ml_bytes, size_t*
   const size_t rows = (size_t)d->num_seqs * d->q_tokens * d->num_q_heads;
   *ml_bytes = align256(rows * (size_t)parts * 2 * sizeof(float));
   *acc_bytes = align256(rows * (size_t)parts * d->head_dim * sizeof(float));
+}
+
+// Positions of the shared prefix per prefix item of a cascade call: chunks small enough that the prefix
+// waves (32 query rows x one chunk x one kv head each) number about kCascadePrefixWaves, a multiple of
+// 16 and of b, at most the prefix. A function of the dims alone, so the workspace size is too.
+#ifndef PA_CASCADE_PREFIX_WAVES
+#define PA_CASCADE_PREFIX_WAVES 2048
+#endif
+constexpr int64_t kCascadePrefixWaves = PA_CASCADE_PREFIX_WAVES;
+int32_t cascade_chunk(const pa_dims* d, int32_t prefix_tokens) {
+  int32_t unit = 16;
+  while (unit % d->block_size != 0) unit += 16;
+  if (prefix_tokens <= unit) return unit;
+  const int64_t rows = (int64_t)d->num_seqs * d->q_tokens * (d->num_q_heads / d->num_kv_heads);
+  const int64_t items_per_chunk = (rows + 31) / 32 * d->num_kv_heads;  // 32 query rows per prefix wave
+  const int64_t chunks = std::max<int64_t>(1, kCascadePrefixWaves / std::max<int64_t>(1, items_per_chunk));
+  const int64_t chunk = ((prefix_tokens + chunks - 1) / chunks + unit - 1) / unit * unit;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(chunk, unit), ((prefix_tokens + unit - 1) / unit) * unit);
+}
+
+// Workspace slots of a cascade call: the prefix's (one per workgroup of chunks), then the longest
+// suffix's partitions.
+int32_t cascade_prefix_slots(const pa_dims* d, int32_t prefix_tokens) {
+  const int32_t chunk = cascade_chunk(d, prefix_tokens);
+  const int32_t chunks = (prefix_tokens + chunk - 1) / chunk;
+  return (chunks + pa::mfma_waves() - 1) / pa::mfma_waves();
+}
+int32_t cascade_parts(const pa_dims* d, int32_t prefix_tokens, int32_t max_seq_len, int32_t partition_tokens) {
+  return cascade_prefix_slots(d, prefix_tokens) + (max_seq_len - prefix_tokens + partition_tokens - 1) / partition_tokens;
 }
 
 // Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
@@ -247,6 +278,62 @@ int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const voi
                                    void* workspace, size_t workspace_bytes, pa_stream_t stream) {
   return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+size_t pa_decode_cascade_workspace_bytes(const pa_dims* dims, int32_t prefix_tokens, int32_t max_seq_len,
+                                         int32_t partition_tokens) {
+  if (check_shape(dims) != PA_OK || prefix_tokens < 0 || max_seq_len < 1 || partition_tokens < 1 ||
+      max_seq_len < prefix_tokens)
+    return 0;
+  const int32_t parts = cascade_parts(dims, prefix_tokens, max_seq_len, partition_tokens);
+  size_t ml = 0, acc = 0;
+  workspace_layout(dims, parts, &ml, &acc);
+  return ml + acc;
+}
+
+int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                      int32_t prefix_tokens, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                      size_t workspace_bytes, pa_stream_t stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || prefix_tokens < 0 || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
+  if (max_seq_len < prefix_tokens) return PA_ERR_INVALID_ARG;
+  const int32_t b = dims->block_size;
+  if (partition_tokens % 16 != 0 || partition_tokens % b != 0 || prefix_tokens % 16 != 0 || prefix_tokens % b != 0)
+    return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < pa_decode_cascade_workspace_bytes(dims, prefix_tokens, max_seq_len, partition_tokens))
+    return PA_ERR_INVALID_ARG;
+  if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, max_seq_len, s);
+  if (st == PA_OK) st = pa::debug_check_prefix(dims, block_tables, seq_lens, prefix_tokens, s);
+  if (st != PA_OK) return st;
+
+  const int32_t parts = cascade_parts(dims, prefix_tokens, max_seq_len, partition_tokens);
+  size_t ml_bytes = 0, acc_bytes = 0;
+  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
+  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
+  p.parts = parts;
+  p.part_tokens = partition_tokens;
+  p.partial = 1;
+  p.prefix_tokens = prefix_tokens;
+  p.prefix_part_tokens = cascade_chunk(dims, prefix_tokens);
+  p.prefix_parts = cascade_prefix_slots(dims, prefix_tokens);
+  p.part_ml = static_cast<float*>(workspace);
+  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
+  p.row_groups = 1;
+  if (p.prefix_parts > 0) {
+    st = launch_status(pa::launch_cascade_prefix(p, s));
+    if (st != PA_OK) return st;
+  }
+  st = launch_status(pa::launch_decode_mfma(p, s));
+  if (st != PA_OK) return st;
+  return launch_status(pa::launch_merge_partials(p, s));
 }
 
 int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,

@@ -79,4 +79,24 @@ int debug_check(const pa_dims* dims, const int32_t* block_tables, const int32_t*
                               positions ? pos.data() : nullptr);
 }
 
+int debug_check_prefix(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                       int32_t prefix_tokens, hipStream_t stream) {
+  const char* env = getenv("PA_CHECK");
+  if (!env || strcmp(env, "1") != 0) return PA_OK;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone) return PA_OK;
+  const int64_t B = dims->num_seqs, MB = dims->max_blocks_per_seq;
+  std::vector<int32_t> tables, lens;
+  if (!copy_to_host(tables, block_tables, B * MB, stream) || !copy_to_host(lens, seq_lens, B, stream))
+    return PA_ERR_LAUNCH;
+  const int64_t nb = prefix_tokens / dims->block_size;
+  if (nb > MB) return PA_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < B; ++i) {
+    if (lens[i] < prefix_tokens + dims->q_tokens) return PA_ERR_INVALID_ARG;
+    for (int64_t j = 0; j < nb; ++j)
+      if (tables[i * MB + j] != tables[j]) return PA_ERR_INVALID_ARG;
+  }
+  return PA_OK;
+}
+
 }  // namespace pa

@@ -67,6 +67,19 @@
 // pool, so the result is bit for bit the one a separate append followed by a
 // decode gives.
 //
+// Cascade over a shared prefix (CASCADE, split context): when every sequence's
+// first prefix_tokens positions map to the same physical blocks (a forked or
+// prefix-cached prompt: [P1] "Sharing blocks"), the prefix is attended once
+// per kv head for the query rows of all sequences together: the rows of one
+// wave come from many sequences, so each K/V tile of the prefix is read by
+// B*T*G / 32 waves instead of B workgroups. The prefix is cut into chunks of
+// prefix_part_tokens, small enough for the prefix items to fill the chip; the
+// NW waves of a prefix workgroup take NW consecutive chunks for the same 32
+// rows and merge them through LDS like the single pass, writing one of the
+// first prefix_parts partition slots; the sequences' own positions (from
+// prefix_tokens on) run as ordinary split items in the slots after them, and
+// the merge kernel combines all slots exactly ([P5] section 4.2).
+//
 // Two ways of sharing the work:
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
 //    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
@@ -117,11 +130,15 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 #ifndef PA_MFMA_Q8_SPLIT_PREFETCH
 #define PA_MFMA_Q8_SPLIT_PREFETCH 3
 #endif
-#ifdef PA_MFMA_WAVES_PER_EU
-#define PA_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
-#else
-#define PA_MFMA_OCCUPANCY
+#ifndef PA_MFMA_WAVES_PER_EU
+#define PA_MFMA_WAVES_PER_EU 1
 #endif
+#ifndef PA_CASCADE_WAVES_PER_EU
+#define PA_CASCADE_WAVES_PER_EU 2
+#endif
+// prefix items hold every wave of the grid at once only at two waves per SIMD
+#define PA_MFMA_OCCUPANCY \
+  __attribute__((amdgpu_waves_per_eu(CASCADE && BS >= 16 ? PA_CASCADE_WAVES_PER_EU : PA_MFMA_WAVES_PER_EU)))
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
 constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;            // single pass: few tiles per wave
 constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a whole partition per wave
@@ -174,8 +191,9 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
+  static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
   static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
@@ -183,7 +201,8 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   constexpr int ROWS = 16 * MT;
   constexpr int NBUF = PF + 1;
   constexpr int kVBytes = NW * kTileBytes;  // one V tile per wave
-  constexpr int kRedBytes = WAVE_ITEMS ? 0 : (NW * ROWS * kD + 2 * NW * ROWS) * 4;
+  constexpr bool kLdsMerge = !WAVE_ITEMS || CASCADE;  // the waves' (m, l, acc) meet in LDS at the end
+  constexpr int kRedBytes = kLdsMerge ? (NW * ROWS * kD + 2 * NW * ROWS) * 4 : 0;
   constexpr int kLdsBytes = kVBytes > kRedBytes ? kVBytes : kRedBytes;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
@@ -193,18 +212,32 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   const int c16 = lane & 15;  // column inside the group
 
   // Single pass: block = seq * Hkv + kvh. Split context: block = (seq * groups + cg) * Hkv + kvh, wave w
-  // owning partition cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks are dealt
-  // round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
+  // owning partition cg * NW + w of the sequence's own partitions (the slots after the prefix_parts
+  // prefix slots). Cascade prefix items: `seq` is a group of ROWS query rows over all sequences and
+  // the wave owns prefix partition cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks
+  // are dealt round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
-  const int groups = WAVE_ITEMS ? (p.parts + NW - 1) / NW : 1;
+  // prefix items: NW chunks per workgroup, merged into one workspace slot per workgroup
+  const int item_parts = !WAVE_ITEMS ? 1
+                         : CASCADE ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens
+                                   : p.parts - p.prefix_parts;
+  const int groups = WAVE_ITEMS ? (item_parts + NW - 1) / NW : 1;
   const int cg = bid % groups;
   const int seq = bid / groups;
-  const int part = WAVE_ITEMS ? cg * NW + wave : 0;
+  const int part_local = WAVE_ITEMS ? cg * NW + wave : 0;
+  const int part = !WAVE_ITEMS ? 0 : CASCADE ? cg : p.prefix_parts + part_local;  // workspace slot
 
   const int T = p.T;
-  const int p_begin = WAVE_ITEMS ? part * p.part_tokens : 0;
+  const int p_begin = !WAVE_ITEMS ? 0 : CASCADE ? part_local * p.prefix_part_tokens
+                                                : p.prefix_tokens + part_local * p.part_tokens;
+
+  // Query row n (< ROWS) of this wave: row n of sequence seq, or, for prefix items, row seq*ROWS + n of
+  // all sequences' rows taken together.
+  auto row_seq = [&](int n) { return CASCADE ? (seq * ROWS + n) / p.rows : seq; };
+  auto row_in_seq = [&](int n) { return CASCADE ? (seq * ROWS + n) % p.rows : n; };
+  auto row_present = [&](int n) { return CASCADE ? seq * ROWS + n < p.B * p.rows : n < p.rows; };
 
   // ---- q rows as the B operand of S^T: lane (g, c16) holds row c16 + 16*mt, head_dim 32*kc + 8g .. +7.
   // Issued first and unconditionally (an absent row reads row 0, then selects zero): they depend on
@@ -215,11 +248,12 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + c16;
-    const bool present = r < p.rows;
-    const int rr = present ? r : 0;
+    const bool present = row_present(r);
+    const int rr = present ? row_in_seq(r) : 0;
+    const int rs = present ? row_seq(r) : 0;
     row_tok[mt] = rr / p.G;
     const char* qrow =
-        static_cast<const char*>(p.q) + ((int64_t)(seq * T + row_tok[mt]) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
+        static_cast<const char*>(p.q) + ((int64_t)(rs * T + row_tok[mt]) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
     if constexpr (Q8) {
       // lane (g, c16): head_dim 32g .. 32g+31 of the row, as fp16; operand kc = 32g + 8kc .. +7
       u32x4 raw[4];
@@ -250,14 +284,25 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
       }
     }
   }
-  auto tile_p0_of = [&](int i) { return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile; };
+  // Prefix items: the row groups that share a chunk start at different tiles of it (and wrap round), so
+  // at any moment they read different lines rather than all queueing on the same L2 channel.
+  const int c_tiles =
+      CASCADE ? max(1, (min(p.prefix_tokens, p_begin + p.prefix_part_tokens) - p_begin + kTile - 1) / kTile) : 1;
+  const int rot = CASCADE ? seq % c_tiles : 0;
+  auto tile_p0_of = [&](int i) {
+    if constexpr (CASCADE) {
+      const int j = i + rot;
+      return p_begin + (j >= c_tiles ? j - c_tiles : j) * kTile;
+    }
+    return WAVE_ITEMS ? p_begin + i * kTile : (wave + i * NW) * kTile;
+  };
 
   // Physical block ids of the wave's i-th tile, as wave-uniform scalar loads. A tile lies in one
   // block when BS >= 16, or spans 16 / BS whole blocks otherwise. The table index is clamped to the
   // row and the id to the pool, so a lookup never depends on the length and any entry (padding
   // included) gives an address inside the pool; positions at or past L are masked out of the
   // result whatever they hold. That lets the first tile's lookup go out together with the length.
-  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
+  const int32_t* trow = p.block_tables + (CASCADE ? 0 : (int64_t)seq * p.MB);  // prefix: every row's blocks
   constexpr int kBlocksPerTile = BS >= kTile ? 1 : kTile / BS;
   struct TileIds {
     int b[kBlocksPerTile];
@@ -279,17 +324,21 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     return ids;
   };
   const TileIds ids0 = ids_of(0);
-  const int L = p.seq_lens[seq];
-  if (WAVE_ITEMS && (part >= p.parts || p_begin >= L)) return;  // empty partition: the merge never reads it
-  const int p_end = WAVE_ITEMS ? min(L, p_begin + p.part_tokens) : L;
-  const int ntiles = p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
-  const int vis_all = L - T + 1;
-  const bool rows_all_present = p.rows == ROWS;
+  const int L = CASCADE ? p.prefix_tokens : p.seq_lens[seq];  // prefix items: every prefix position is visible
+  // an empty split partition's wave leaves (the merge never reads its slot); a prefix item's wave with
+  // no chunk stays for the workgroup's merge, with nothing to add
+  if (WAVE_ITEMS && !CASCADE && (part_local >= item_parts || p_begin >= L)) return;
+  const bool idle = CASCADE && (part_local >= item_parts || p_begin >= L);
+  const int p_end = WAVE_ITEMS ? min(L, p_begin + (CASCADE ? p.prefix_part_tokens : p.part_tokens)) : L;
+  const int ntiles = !idle && p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
+  const int vis_all = CASCADE ? L : L - T + 1;
+  const bool rows_all_present = CASCADE ? (seq + 1) * ROWS <= p.B * p.rows : p.rows == ROWS;
   const int my_tiles = WAVE_ITEMS ? ntiles : (wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0);
 
   int row_lim[MT];  // last visible position of this lane's score row; -1 if the row is padding
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) row_lim[mt] = mt * 16 + c16 < p.rows ? L - T + row_tok[mt] : -1;
+  for (int mt = 0; mt < MT; ++mt)
+    row_lim[mt] = !row_present(mt * 16 + c16) ? -1 : CASCADE ? L - 1 : L - T + row_tok[mt];
 
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kKvRow;
   const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kKvRow;
@@ -478,7 +527,8 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   };
 
   auto out_row = [&](int n) -> int64_t {  // flat (seq, token, q head) index of query row n
-    return (int64_t)(seq * T + n / p.G) * p.Hq + kvh * p.G + n % p.G;
+    const int rs = row_seq(n), m = row_in_seq(n);
+    return (int64_t)(rs * T + m / p.G) * p.Hq + kvh * p.G + m % p.G;
   };
   auto clear = [&]() {
 #pragma unroll
@@ -498,14 +548,14 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
       const int n = mt * 16 + c16;
-      if (g == 0 && n < p.rows) {
+      if (g == 0 && row_present(n)) {
         const int64_t pi = out_row(n) * p.parts + part;
         *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref[mt], l};
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int na = mt * 16 + 4 * g + e;  // accumulator row of this lane
-        if (na < p.rows) {
+        if (row_present(na)) {
           float* dst = p.part_acc + (out_row(na) * p.parts + part) * kD + c16;
 #pragma unroll
           for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[mt][jb][e];
@@ -601,7 +651,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     }
   }
 
-  if constexpr (WAVE_ITEMS) {
+  if constexpr (!kLdsMerge) {
     flush();
   } else {
     // per-row l of this wave: lanes of column c16 hold row c16 (+16*mt); sum the four 16-lane groups
@@ -640,10 +690,11 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
       }
     __syncthreads();
 
-    // Each thread finishes 4 consecutive head_dim values of a row at a time.
+    // Each thread finishes 4 consecutive head_dim values of a row at a time: the normalised output, or
+    // (prefix items) the workgroup's partial (M, l, acc) for its slot.
     for (int idx = threadIdx.x; idx < ROWS * (kD / 4); idx += NW * 64) {
       const int n = idx / (kD / 4), d4 = (idx % (kD / 4)) * 4;
-      if (n >= p.rows) continue;
+      if (!row_present(n)) continue;
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[n * NW + w]);
@@ -658,19 +709,28 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
         }
       }
       const int64_t orow = out_row(n);
+      if constexpr (CASCADE) {
+        const int64_t pi = orow * p.parts + part;
+        *reinterpret_cast<f32x4*>(p.part_acc + pi * kD + d4) = a;
+        if (d4 == 0) *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{M, lsum};
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(p, orow * kD + d4 + e, lsum > 0.f ? a[e] / lsum : 0.f);
+        for (int e = 0; e < 4; ++e) store_out(p, orow * kD + d4 + e, lsum > 0.f ? a[e] / lsum : 0.f);
+      }
     }
   }
 }
 
-template <int MT, int BS, bool WI, bool Q8, bool AP>
+template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int64_t groups = WI ? (p.parts + kMfmaWaves - 1) / kMfmaWaves : 1;
-  const int64_t grid = (int64_t)p.B * groups * p.Hkv;
+  const int64_t item_parts =
+      !WI ? 1 : CAS ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens : p.parts - p.prefix_parts;
+  const int64_t groups = WI ? (item_parts + kMfmaWaves - 1) / kMfmaWaves : 1;
+  const int64_t units = CAS ? ((int64_t)p.B * p.rows + 16 * MT - 1) / (16 * MT) : p.B;  // row groups or sequences
+  const int64_t grid = units * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
   constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
-  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP>
+  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
@@ -715,6 +775,19 @@ bool mfma_int8_supported(const pa_dims& d) {
   return d.kv_dtype == PA_INT8 && d.q_dtype == PA_BF16 && d.head_dim == kD &&
          (d.block_size == 16 || d.block_size == 32) && rows <= 32;
 }
+
+hipError_t launch_cascade_prefix(const DecodeParams& p, hipStream_t stream) {
+  // 32 query rows (of many sequences) per wave share each prefix tile
+  switch (p.block_size) {
+    case 4: return launch_t<2, 4, true, false, false, true>(p, stream);
+    case 8: return launch_t<2, 8, true, false, false, true>(p, stream);
+    case 16: return launch_t<2, 16, true, false, false, true>(p, stream);
+    case 32: return launch_t<2, 32, true, false, false, true>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int mfma_waves() { return kMfmaWaves; }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (p.partial) return p.rows <= 16 ? launch_bs<1, true>(p, stream) : launch_bs<2, true>(p, stream);

@@ -35,6 +35,10 @@ struct DecodeParams {
   int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
   int32_t kv_int8;           // 1: the pools hold int8 codes scaled by k_scales / v_scales
   int32_t append;            // 1: also store k_new / v_new into the pools (MFMA kernel, bf16)
+  int32_t prefix_tokens;     // cascade: positions every sequence shares (0: none)
+  int32_t prefix_parts;      // cascade: workspace slots 0 .. prefix_parts-1 hold the prefix's partials
+                             // (one per group of mfma_waves() chunks)
+  int32_t prefix_part_tokens;  // cascade: positions of the prefix per chunk (one wave's share)
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
@@ -55,9 +59,17 @@ hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t s
 int debug_check(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
                 const int32_t* positions, int32_t max_seq_len, hipStream_t stream);
 
+// PA_CHECK=1, cascade: every sequence holds at least prefix_tokens + T positions and its first
+// prefix_tokens / b table entries are sequence 0's.
+int debug_check_prefix(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                       int32_t prefix_tokens, hipStream_t stream);
+
 bool mfma_supported(const pa_dims& d);       // bf16 pools
 bool mfma_int8_supported(const pa_dims& d);  // int8 pools
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+// Cascade: the shared prefix's partitions for all sequences' rows at once (slots 0 .. prefix_parts-1).
+hipError_t launch_cascade_prefix(const DecodeParams& p, hipStream_t stream);
+int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one cascade slot)
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
 

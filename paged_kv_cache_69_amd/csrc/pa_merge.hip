@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
     a[j] = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
   }
   const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
-  const int nparts = row_raw < rows && L > 0 ? min(p.parts, (L + p.part_tokens - 1) / p.part_tokens) : 0;
+  // slots written: the shared prefix's (cascade), then one per partition of the sequence's own positions
+  const int own = max(0, (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens);
+  const int nparts = row_raw < rows && L > 0 ? min(p.parts, p.prefix_parts + own) : 0;
 
   // M = max m_k over partitions with l_k > 0, then l = sum l_k 2^(m_k - M)
   float M = t < nparts && ml_t[1] > 0.f ? ml_t[0] : kNegInf;
@@ -135,10 +137,11 @@ hipError_t launch_rpw(const DecodeParams& p, int64_t rows, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, int64_t rows, hipStream_t stream) {
-  // rows per workgroup so that a row's slots roughly match its partition count
+  // Rows per workgroup: a row's threads load up to 8 partitions per slot in one go, so one wave per row
+  // (2 slots for D = 128) covers 16 partitions; more partitions get more of the workgroup.
   constexpr int LPC = D / 4;
-  if (p.parts * LPC >= kMergeThreads) return launch_rpw<D, 1>(p, rows, stream);
-  if (2 * p.parts * LPC >= kMergeThreads) return launch_rpw<D, 2>(p, rows, stream);
+  if (p.parts * LPC > 8 * kMergeThreads) return launch_rpw<D, 1>(p, rows, stream);
+  if (p.parts * LPC > 4 * kMergeThreads) return launch_rpw<D, 2>(p, rows, stream);
   return launch_rpw<D, 4>(p, rows, stream);
 }
 
