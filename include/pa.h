@@ -205,7 +205,8 @@ int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const voi
  * sequences together, instead of once per sequence: it is cut into chunks
  * (the library picks their size from the dims, a multiple of 16 and of b,
  * so that the prefix work fills the GPU), each processed for all B * T * G
- * rows of a kv head, 16 rows per wave. Each sequence's own positions (prefix_tokens .. L - 1)
+ * rows of a kv head, 32 rows per wave; the four waves of a workgroup merge
+ * their chunks into one partial. Each sequence's own positions (prefix_tokens .. L - 1)
  * run in partitions of partition_tokens as in pa_decode_partitioned, and one
  * merge pass combines the prefix's and the sequence's partials exactly
  * ([P5] section 4.2). Three launches on `stream`.
