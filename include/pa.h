@@ -277,6 +277,51 @@ int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t*
                                void* out, int32_t max_seq_len, int32_t partition_tokens,
                                void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
+/* ---- Paged prefill ([P1] "25. Paged attention and prefix caching", stretch
+ * exercise 4; [P4] "PagedAttention and the KV Cache", section "Prefill vs
+ * decode under paging"; [P5] section 4.1).
+ *
+ * A prefill (or chunked-prefill) step gives sequence i a chunk of
+ * n_i = q_start[i+1] - q_start[i] new tokens, packed one after another:
+ * rows q_start[i] .. q_start[i+1] - 1 of q, k_new and v_new. They are the
+ * sequence's newest positions L_i - n_i .. L_i - 1 (L_i = seq_lens[i] counts
+ * the history and the chunk), so chunk token j sits at position
+ * L_i - n_i + j. In these calls dims->q_tokens is a host-known bound on every
+ * n_i (it sizes the grid); q_start is int32 [B + 1] on the device, with
+ * q_start[0] = 0 and q_start[i] <= q_start[i+1]. A chunk may be empty
+ * (n_i = 0); n_i <= L_i. Under PA_CHECK=1 these and the general preconditions
+ * are checked on host copies (pa_check_prefill_host).
+ */
+
+/* pa_write_kv_varlen: store each chunk's K and V rows at their positions:
+ * row q_start[i] + j of k_new / v_new ([Q, Hkv, D], kv_dtype, Q = q_start[B])
+ * goes, bit for bit, to slot (block_tables[i][p / b], p % b) of the pools,
+ * p = L_i - n_i + j. Same dtypes and rules as pa_write_kv; the slots written
+ * must be distinct. */
+int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool,
+                       void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* q_start, pa_stream_t stream);
+
+/* pa_prefill: causal attention of every chunk token over its sequence's
+ * paged history and the chunk: row q_start[i] + j, query head h attends to
+ * positions 0 .. L_i - n_i + j of kv head h / G, each read through the block
+ * table (the chunk's own K/V must already be in the pools, e.g. from
+ * pa_write_kv_varlen on the same stream).
+ *   q   : [Q, Hq, D], q_dtype        out : [Q, Hq, D], out_dtype (fp32 or bf16)
+ * One launch on `stream`. Supported: bf16 q and KV, head_dim 128,
+ * b in {4, 8, 16, 32}, G <= 128 (PA_ERR_UNSUPPORTED otherwise). */
+int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start,
+               float scale, void* out, pa_stream_t stream);
+
+/* pa_check_prefill_host: the prefill preconditions on host arrays
+ * (block_tables [B, MB], seq_lens [B], q_start [B + 1]): q_start[0] = 0 and
+ * non-decreasing; 0 <= n_i <= min(L_i, q_tokens); L_i <= MB * b; used table
+ * entries in [0, num_blocks); the chunks' (block, offset) slots distinct.
+ * Returns PA_OK or PA_ERR_INVALID_ARG; launches nothing. */
+int pa_check_prefill_host(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* q_start);
+
 /* pa_check_inputs_host: the preconditions above, checked on host copies.
  *   block_tables : int32 [B, MB] (required)
  *   seq_lens     : int32 [B], or NULL to skip the checks that need lengths

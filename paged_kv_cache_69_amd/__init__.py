@@ -12,6 +12,12 @@ Entry points, with the same names as the C ABI:
 * :func:`decode_partitioned`: split-context decode plus its merge pass
   (``pa_decode_partitioned``).
 * :func:`workspace_bytes`: workspace size for :func:`decode_partitioned`.
+* :func:`write_kv_decode`: append + decode in one launch (``pa_write_kv_decode``,
+  ``pa_write_kv_decode_partitioned``).
+* :func:`decode_cascade`: decode with a shared prefix attended once (``pa_decode_cascade``).
+* :func:`write_kv_int8`, :func:`decode_int8`, :func:`decode_partitioned_int8`: the int8 KV cache.
+* :func:`write_kv_varlen`, :func:`prefill`: paged (chunked) prefill over packed chunks
+  (``pa_write_kv_varlen``, ``pa_prefill``).
 """
 
 from __future__ import annotations
@@ -35,6 +41,9 @@ EXPORTS = (
     "pa_write_kv_int8",
     "pa_decode_int8",
     "pa_decode_partitioned_int8",
+    "pa_write_kv_varlen",
+    "pa_prefill",
+    "pa_check_prefill_host",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_abi_version",
@@ -101,6 +110,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
                                                _P, ctypes.c_size_t, _P]
     lib.pa_decode_partitioned_int8.restype = ctypes.c_int
+    lib.pa_write_kv_varlen.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.pa_write_kv_varlen.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_check_prefill_host.argtypes = [dims_p, _P, _P, _P]
+    lib.pa_check_prefill_host.restype = ctypes.c_int
     lib.pa_check_inputs_host.argtypes = [dims_p, _P, _P, _P]
     lib.pa_check_inputs_host.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -399,4 +414,59 @@ def decode_partitioned_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables,
                                         int(partition_tokens), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_partitioned_int8", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- paged prefill
+
+def _prefill_dims(q_rows, k_pool, block_tables, max_chunk: int, num_q_heads: int, code_q, code_out) -> PaDims:
+    n, hkv, bs, d = k_pool.shape
+    return PaDims(block_tables.shape[0], int(max_chunk), num_q_heads, hkv, d, bs, n, block_tables.shape[1], code_q,
+                  dtype_code(k_pool.dtype), code_out, 0)
+
+
+def write_kv_varlen(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, q_start, max_chunk: int, *, stream=None):
+    """``pa_write_kv_varlen``: store packed chunk rows ``k_new``/``v_new [Q, Hkv, D]`` at positions
+    ``L_i - n_i .. L_i - 1`` (``n_i = q_start[i+1] - q_start[i]``, at most ``max_chunk``)."""
+    import torch
+
+    lib = load_library()
+    dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                         seq_lens=seq_lens, q_start=q_start)
+    _require(all(t.dtype == torch.int32 for t in (block_tables, seq_lens, q_start)), "index arrays must be int32")
+    _require(k_new.shape == v_new.shape and k_pool.shape == v_pool.shape, "K/V shapes differ")
+    _require(k_new.dim() == 3 and k_new.shape[1:] == (k_pool.shape[1], k_pool.shape[3]), "new rows must be [Q, Hkv, D]")
+    _require(q_start.shape == (block_tables.shape[0] + 1,) and seq_lens.shape == (block_tables.shape[0],),
+             "q_start must be [B + 1] and seq_lens [B]")
+    code = dtype_code(k_pool.dtype)
+    _require(dtype_code(k_new.dtype) == code, "new rows and pools must share a dtype")
+    dims = _prefill_dims(k_new, k_pool, block_tables, max(1, int(max_chunk)), k_pool.shape[1], code, code)
+    st = lib.pa_write_kv_varlen(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                                v_pool.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), q_start.data_ptr(),
+                                _stream_handle(stream, dev))
+    _check(lib, "pa_write_kv_varlen", st)
+
+
+def prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale: float, max_chunk: int, out=None, *,
+            out_dtype=None, stream=None):
+    """``pa_prefill``: causal attention of packed chunk rows ``q [Q, Hq, D]`` over their sequences'
+    paged history and chunk; returns ``out [Q, Hq, D]`` (fp32 unless ``out``/``out_dtype`` says otherwise)."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens,
+                         q_start=q_start, out=out)
+    _require(all(t.dtype == torch.int32 for t in (block_tables, seq_lens, q_start)), "index arrays must be int32")
+    _require(q.dim() == 3 and out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    _require(q.shape[2] == k_pool.shape[3], "head_dim of q and pools differ")
+    _require(q_start.shape == (block_tables.shape[0] + 1,) and seq_lens.shape == (block_tables.shape[0],),
+             "q_start must be [B + 1] and seq_lens [B]")
+    dims = _prefill_dims(q, k_pool, block_tables, max(1, int(max_chunk)), q.shape[1], dtype_code(q.dtype),
+                         dtype_code(out.dtype))
+    st = lib.pa_prefill(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                        block_tables.data_ptr(), seq_lens.data_ptr(), q_start.data_ptr(), float(scale),
+                        out.data_ptr(), _stream_handle(stream, dev))
+    _check(lib, "pa_prefill", st)
     return out

@@ -369,4 +369,38 @@ int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t*
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
 }
 
+int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start,
+                       pa_stream_t stream) {
+  const int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens || !q_start) return PA_ERR_INVALID_ARG;
+  if ((int64_t)dims->head_dim * dtype_size(dims->kv_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_INVALID_ARG;
+  if (dims->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int chk = pa::debug_check_prefill(dims, block_tables, seq_lens, q_start, s);
+  if (chk != PA_OK) return chk;
+  return launch_status(
+      pa::launch_write_kv_varlen(*dims, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, q_start, s));
+}
+
+int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start, float scale, void* out,
+               pa_stream_t stream) {
+  const int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !q_start || !out) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (dims->variant == PA_VARIANT_VALU || !pa::prefill_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int chk = pa::debug_check_prefill(dims, block_tables, seq_lens, q_start, s);
+  if (chk != PA_OK) return chk;
+  return launch_status(pa::launch_prefill(*dims, q, k_pool, v_pool, block_tables, seq_lens, q_start, scale, out, s));
+}
+
 }  // extern "C"

@@ -59,7 +59,43 @@ extern "C" int pa_check_inputs_host(const pa_dims* dims, const int32_t* block_ta
   return PA_OK;
 }
 
+extern "C" int pa_check_prefill_host(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                                     const int32_t* q_start) {
+  if (!dims_ok(dims) || !block_tables || !seq_lens || !q_start) return PA_ERR_INVALID_ARG;
+  const int64_t B = dims->num_seqs, MB = dims->max_blocks_per_seq;
+  const int64_t b = dims->block_size, N = dims->num_blocks;
+  if (q_start[0] != 0) return PA_ERR_INVALID_ARG;
+  std::vector<int64_t> slots;
+  for (int64_t i = 0; i < B; ++i) {
+    const int64_t n = (int64_t)q_start[i + 1] - q_start[i];
+    const int64_t L = seq_lens[i];
+    if (n < 0 || n > dims->q_tokens || n > L || L > MB * b) return PA_ERR_INVALID_ARG;
+    for (int64_t j = 0; j < (L + b - 1) / b; ++j) {
+      const int32_t e = block_tables[i * MB + j];
+      if (e < 0 || e >= N) return PA_ERR_INVALID_ARG;
+    }
+    for (int64_t pos = L - n; pos < L; ++pos) slots.push_back((int64_t)block_tables[i * MB + pos / b] * b + pos % b);
+  }
+  std::sort(slots.begin(), slots.end());
+  if (std::adjacent_find(slots.begin(), slots.end()) != slots.end()) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 namespace pa {
+
+int debug_check_prefill(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* q_start, hipStream_t stream) {
+  const char* env = getenv("PA_CHECK");
+  if (!env || strcmp(env, "1") != 0) return PA_OK;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone) return PA_OK;
+  const int64_t B = dims->num_seqs;
+  std::vector<int32_t> tables, lens, starts;
+  if (!copy_to_host(tables, block_tables, B * dims->max_blocks_per_seq, stream) ||
+      !copy_to_host(lens, seq_lens, B, stream) || !copy_to_host(starts, q_start, B + 1, stream))
+    return PA_ERR_LAUNCH;
+  return pa_check_prefill_host(dims, tables.data(), lens.data(), starts.data());
+}
 
 int debug_check(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
                 const int32_t* positions, int32_t max_seq_len, hipStream_t stream) {

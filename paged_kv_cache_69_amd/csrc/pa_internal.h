@@ -73,4 +73,18 @@ int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one ca
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
 
+// Paged prefill (packed chunks, q_start offsets): bf16 q/KV, head_dim 128, G <= 128, b in {4, 8, 16, 32}.
+bool prefill_supported(const pa_dims& d);
+hipError_t launch_prefill(const pa_dims& d, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start, float scale,
+                          void* out, hipStream_t stream);
+hipError_t launch_write_kv_varlen(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start,
+                                  hipStream_t stream);
+// PA_CHECK=1, prefill: q_start starts at 0 and never decreases, every chunk fits its sequence and
+// the q_tokens bound, lengths fit the table, used entries lie in the pool, and the chunks' slots
+// are distinct.
+int debug_check_prefill(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* q_start, hipStream_t stream);
+
 }  // namespace pa

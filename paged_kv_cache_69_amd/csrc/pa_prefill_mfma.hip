@@ -1,0 +1,422 @@
+// Paged prefill on the matrix cores (gfx950 MFMA), bf16 K/V, head_dim 128.
+//
+// What it computes ([P1] "25. Paged attention and prefix caching", stretch
+// exercise 4; [P4] "Prefill vs decode under paging"; [P5] "Chapter 7 Paged KV
+// Cache and Memory Management" section 4.1): sequence i brings a chunk of n_i
+// new query tokens, packed as rows q_start[i] .. q_start[i+1]-1 of q, which
+// are its newest positions L_i - n_i .. L_i - 1. Token j, query head h,
+// attends causally to positions 0 .. L_i - n_i + j of kv head h / G: the
+// sequence's paged history and the chunk itself, gathered through the block
+// table (the chunk's K/V rows are already in the pools).
+//
+// Unlike decode, this is a dense contraction: a workgroup takes 128 query rows
+// (floor(128 / G) tokens x the G heads that share one kv head) of one
+// sequence, and every K/V row it reads serves all of them. Design:
+//  * Workgroup = 4 waves x 32 query rows; row r is token r / G, head r % G.
+//    q rows are the resident B operand of S^T = K Q^T, as in the decode
+//    kernel.
+//  * Positions go in tiles of 32. The whole workgroup loads a tile's K and V
+//    (8 KiB each) from the pool into LDS, one tile ahead of the one being
+//    computed (double buffer, one barrier per tile). Each thread loads 16-byte
+//    chunks of two positions and looks up their block itself, so any block
+//    size works.
+//  * K sits in LDS as [position][256 B] with its 16-byte chunks XOR-swizzled
+//    by position, so the A operand reads (16 positions x the same chunk) hit
+//    16 different bank groups.
+//  * P.V: the C layout of the two 16-position halves of S^T gives a lane
+//    positions 4g .. 4g+3 of each half; taken together they are the 8 k-slots
+//    of one v_mfma_f32_16x16x32_bf16 A operand, and the matching B operand is
+//    two transposed LDS reads (ds_read_b64_tr_b16) of V, one per half. P goes
+//    in as bf16 hi + lo parts, as in the decode kernel.
+//  * Online softmax with a lazy reference ([P5] section 4.2): each row keeps a
+//    reference max; a tile whose score exceeds it by more than 2^64 (base-2
+//    units) raises it and rescales that wave's accumulators once. Otherwise
+//    the accumulators are only touched by MFMAs.
+//  * Causal mask by selection (-inf, never computed), only in the tiles that
+//    cross a row's limit; V rows at or past L are zeroed in LDS, so garbage in
+//    unwritten slots never reaches the result.
+//  * Workgroups are launched last query block first (the longest rows first),
+//    and consecutive workgroups are consecutive kv heads, so with 8 kv heads
+//    one kv head's K/V stays in one XCD's L2.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kD = 128;
+constexpr int kRowBytes = 256;          // one bf16 row of head_dim 128
+constexpr int kNW = 4;                  // waves per workgroup
+constexpr int kWaveRows = 32;           // query rows per wave (two 16-row MFMA tiles)
+constexpr int kWgRows = kNW * kWaveRows;
+constexpr int kKT = 32;                 // positions per K/V tile
+constexpr int kKBytes = kKT * kRowBytes;  // 8 KiB of K (or V) per tile
+constexpr int kBufBytes = 2 * kKBytes;    // K then V
+constexpr float kSlack = 64.0f;
+
+struct PrefillParams {
+  const char* q;
+  const char* k_pool;
+  const char* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  void* out;
+  float qk_scale_log2;
+  int32_t B, Hq, Hkv, G, MB, num_blocks, out_dtype;
+  int32_t qb_tokens;  // query tokens per workgroup: floor(128 / G)
+  int32_t n_qblocks;  // query blocks of the longest chunk
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// V tile half (16 positions x 256 B): 32-byte blocks XOR-swizzled by position, as the transposed
+// reads expect.
+__device__ __forceinline__ int v_swz(int t, int byte) { return t * kRowBytes + (byte ^ ((t & 7) << 5)); }
+// K tile (32 positions x 256 B): 16-byte chunk c of position t at chunk c ^ (t % 16).
+__device__ __forceinline__ int k_swz(int t, int chunk) { return t * kRowBytes + ((chunk ^ (t & 15)) << 4); }
+
+template <int BS>
+__global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kBufBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+
+  int bid = blockIdx.x;
+  const int kvh = bid % p.Hkv;
+  bid /= p.Hkv;
+  const int seq = bid % p.B;
+  const int qblk = p.n_qblocks - 1 - bid / p.B;  // longest rows first
+
+  const int q0 = p.q_start[seq];
+  const int n = p.q_start[seq + 1] - q0;
+  const int QB = p.qb_tokens, G = p.G;
+  const int tok0 = qblk * QB;
+  if (tok0 >= n) return;  // the whole workgroup: this sequence's chunk is shorter
+  const int L = p.seq_lens[seq];
+  const int hist = L - n;
+  const int tok_end = min(n, tok0 + QB);
+
+  // ---- this lane's query rows (score layout: row c16 + 16 mt of the wave)
+  int row_lim[2];  // last visible position of the row; -1 for padding rows
+  u32x4 qb[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = wave * kWaveRows + mt * 16 + c16;
+    const int tr = r / G;
+    const bool present = r < QB * G && tok0 + tr < tok_end;
+    row_lim[mt] = present ? hist + tok0 + tr : -1;
+    const int64_t qrow = present ? (int64_t)(q0 + tok0 + tr) * p.Hq + kvh * G + r % G : (int64_t)q0 * p.Hq;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x4 v = load16(p.q + qrow * kRowBytes + (kc * 4 + g) * 16);
+      qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // the wave's rows: tokens tok0 + w*32/G .. ; lowest and highest visible limits
+  const int w_first = wave * kWaveRows;
+  const int w_last_tok = min(min((w_first + kWaveRows - 1) / G, QB - 1), tok_end - 1 - tok0);
+  const bool wave_rows = w_first < QB * G && tok0 + w_first / G < tok_end;
+  const int wave_lo = hist + tok0 + w_first / G;
+  const int wave_hi = wave_rows ? hist + tok0 + w_last_tok : -1;
+
+  const int ntiles = (hist + tok_end + kKT - 1) / kKT;
+
+  // ---- cooperative tile loads: thread (rk, ck) moves chunk ck of positions rk and rk + 16
+  const int rk = tid >> 4, ck = tid & 15;
+  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
+  const int64_t head_off = (int64_t)kvh * BS * kRowBytes + ck * 16;
+  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
+  struct Regs {
+    u32x4 k[2], v[2];
+  };
+  auto load = [&](int tile, Regs& rg) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pos = tile * kKT + 16 * h + rk;
+      const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+      const int64_t off = (int64_t)blk * block_bytes + head_off + (int64_t)(pos % BS) * kRowBytes;
+      rg.k[h] = load16(p.k_pool + off);
+      rg.v[h] = load16(p.v_pool + off);
+      if (pos >= L) rg.v[h] = u32x4{0u, 0u, 0u, 0u};  // unwritten slot: may hold anything
+    }
+  };
+  auto store = [&](int buf, const Regs& rg) {
+    lds_char* base = (lds_char*)lds + buf * kBufBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * h + rk;
+      *(lds_u32x4*)(base + k_swz(t, ck)) = rg.k[h];
+      *(lds_u32x4*)(base + kKBytes + h * (kKBytes / 2) + v_swz(rk, ck * 16)) = rg.v[h];
+    }
+  };
+
+  float m_ref[2] = {kNegInf, kNegInf};
+  float l_part[2] = {0.f, 0.f};
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, int tile) {
+    const int tile_p0 = tile * kKT;
+    if (tile_p0 > wave_hi) return;  // every row of this wave stops before this tile
+    const lds_char* kb = (const lds_char*)lds + buf * kBufBytes;
+    const lds_char* vb = kb + kKBytes;
+    // S^T for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of row c16 + 16 mt
+    f32x4 s[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 ka[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) ka[kc] = *(const lds_u32x4*)(kb + k_swz(16 * h + c16, kc * 4 + g));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
+        s[h][mt] = c * p.qk_scale_log2;
+      }
+    }
+    if (tile_p0 + kKT - 1 > wave_lo) {  // the tile crosses some row's causal limit
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (tile_p0 + 16 * h + 4 * g + e > row_lim[mt]) s[h][mt][e] = kNegInf;
+    }
+    // lazy reference: raise it (and rescale what was accumulated) only when a score outruns it
+    float mx[2];
+    bool over = false;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      float x = fmaxf(fmaxf(fmaxf(s[0][mt][0], s[0][mt][1]), fmaxf(s[0][mt][2], s[0][mt][3])),
+                      fmaxf(fmaxf(s[1][mt][0], s[1][mt][1]), fmaxf(s[1][mt][2], s[1][mt][3])));
+      x = fmaxf(x, __shfl_xor(x, 16, 64));
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      mx[mt] = x;
+      over |= x > m_ref[mt] + kSlack;
+    }
+    if (__any(over)) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const float m_new = fmaxf(m_ref[mt], mx[mt]);
+        const float alpha = m_ref[mt] == kNegInf ? 0.f : exp2_fast(m_ref[mt] - m_new);
+        m_ref[mt] = m_new;
+        l_part[mt] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __shfl(alpha, 4 * g + e, 64);  // accumulator row 4g + e
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) acc[mt][jb][e] *= ae;
+        }
+      }
+    }
+    // P = 2^(s - m) as bf16 hi + lo; k-slots 8g .. 8g+3 = half 0, 8g+4 .. 8g+7 = half 1
+    u32x4 a_hi[2], a_lo[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      float pr[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = s[h][mt][e];
+          pr[4 * h + e] = x == kNegInf ? 0.f : exp2_fast(x - m_ref[mt]);
+          l_part[mt] += pr[4 * h + e];
+        }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t hi = cvt_pk_bf16(pr[2 * w], pr[2 * w + 1]);
+        a_hi[mt][w] = hi;
+        a_lo[mt][w] = cvt_pk_bf16(pr[2 * w] - bf16_lo(hi), pr[2 * w + 1] - bf16_hi(hi));
+      }
+    }
+    // B operand: positions 4g .. 4g+3 of each half, head_dim column 16 jb + c16
+    const int rr = (lane >> 2) & 3, qq = lane & 3;
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2)));
+      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vb + kKBytes / 2 + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2)));
+      const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
+      const u32x4 bv = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
+        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
+      }
+    }
+  };
+
+  {
+    Regs rg;
+    load(0, rg);
+    store(0, rg);
+  }
+  __syncthreads();
+  for (int i = 0; i < ntiles; ++i) {
+    Regs rg;
+    const bool more = i + 1 < ntiles;
+    if (more) load(i + 1, rg);
+    compute(i & 1, i);
+    if (more) store((i + 1) & 1, rg);
+    __syncthreads();
+  }
+
+  // ---- o = acc / l; accumulator row 4g + e of the wave's 16-row tile mt
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    float l = l_part[mt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);  // row c16's sum, on every lane of column c16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float le = __shfl(l, 4 * g + e, 64);
+      const int r = wave * kWaveRows + mt * 16 + 4 * g + e;
+      const int tr = r / G;
+      if (r >= QB * G || tok0 + tr >= tok_end) continue;
+      const int64_t orow = (int64_t)(q0 + tok0 + tr) * p.Hq + kvh * G + r % G;
+      const float inv = le > 0.f ? 1.f / le : 0.f;
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) {
+        const float o = acc[mt][jb][e] * inv;
+        const int64_t idx = orow * kD + 16 * jb + c16;
+        if (p.out_dtype == PA_F32)
+          static_cast<float*>(p.out)[idx] = o;
+        else
+          static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
+      }
+    }
+  }
+}
+
+// ---- the chunk's scatter: row q_start[i] + j of k_new / v_new ([Q, Hkv, D]) to position
+// L_i - n_i + j of sequence i. Grid: (chunks of the longest chunk's rows, sequences).
+struct VarlenWriteParams {
+  const char* k_new;
+  const char* v_new;
+  char* k_pool;
+  char* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int32_t Hkv, MB, block_size, num_blocks;
+  int32_t chunks_per_row;  // D * sizeof(dtype) / 16
+  int32_t row_bytes;
+  int64_t block_bytes;
+};
+
+__global__ __launch_bounds__(256) void write_kv_varlen_kernel(const VarlenWriteParams p) {
+  const int seq = blockIdx.y;
+  const int q0 = p.q_start[seq];
+  const int n = p.q_start[seq + 1] - q0;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int chunk = (int)(idx % p.chunks_per_row);
+  const int64_t row = idx / p.chunks_per_row;  // (j * 2 + which) * Hkv + kvh
+  const int kvh = (int)(row % p.Hkv);
+  const int which = (int)(row / p.Hkv) & 1;
+  const int64_t j = row / (2 * p.Hkv);
+  if (j >= n) return;
+  const int64_t src = ((q0 + j) * p.Hkv + kvh) * p.row_bytes + chunk * 16;
+  const u32x4 v = load16((which ? p.v_new : p.k_new) + src);
+  const int pos = p.seq_lens[seq] - n + (int)j;
+  const int phys = p.block_tables[(int64_t)seq * p.MB + pos / p.block_size];
+  const int64_t dst = (int64_t)phys * p.block_bytes +
+                      ((int64_t)kvh * p.block_size + pos % p.block_size) * p.row_bytes + chunk * 16;
+  *reinterpret_cast<u32x4*>((which ? p.v_pool : p.k_pool) + dst) = v;
+}
+
+template <int BS>
+hipError_t launch_bs(const PrefillParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.n_qblocks * p.B * p.Hkv;
+  if (grid == 0) return hipSuccess;
+  prefill_mfma_kernel<BS><<<dim3((unsigned)grid), dim3(kNW * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(const pa_dims& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return d.q_dtype == PA_BF16 && d.kv_dtype == PA_BF16 && d.head_dim == kD && G <= kWgRows &&
+         (d.block_size == 4 || d.block_size == 8 || d.block_size == 16 || d.block_size == 32) &&
+         (d.out_dtype == PA_F32 || d.out_dtype == PA_BF16);
+}
+
+hipError_t launch_prefill(const pa_dims& d, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start, float scale,
+                          void* out, hipStream_t stream) {
+  PrefillParams p = {};
+  p.q = static_cast<const char*>(q);
+  p.k_pool = static_cast<const char*>(k_pool);
+  p.v_pool = static_cast<const char*>(v_pool);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.q_start = q_start;
+  p.out = out;
+  p.qk_scale_log2 = scale * kLog2eHost;
+  p.B = d.num_seqs;
+  p.Hq = d.num_q_heads;
+  p.Hkv = d.num_kv_heads;
+  p.G = d.num_q_heads / d.num_kv_heads;
+  p.MB = d.max_blocks_per_seq;
+  p.num_blocks = d.num_blocks;
+  p.out_dtype = d.out_dtype;
+  p.qb_tokens = kWgRows / p.G;
+  p.n_qblocks = (d.q_tokens + p.qb_tokens - 1) / p.qb_tokens;
+  switch (d.block_size) {
+    case 4: return launch_bs<4>(p, stream);
+    case 8: return launch_bs<8>(p, stream);
+    case 16: return launch_bs<16>(p, stream);
+    case 32: return launch_bs<32>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_write_kv_varlen(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start,
+                                  hipStream_t stream) {
+  VarlenWriteParams p = {};
+  p.k_new = static_cast<const char*>(k_new);
+  p.v_new = static_cast<const char*>(v_new);
+  p.k_pool = static_cast<char*>(k_pool);
+  p.v_pool = static_cast<char*>(v_pool);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.q_start = q_start;
+  p.Hkv = d.num_kv_heads;
+  p.MB = d.max_blocks_per_seq;
+  p.block_size = d.block_size;
+  p.num_blocks = d.num_blocks;
+  p.row_bytes = d.head_dim * (d.kv_dtype == PA_F32 ? 4 : 2);
+  p.chunks_per_row = p.row_bytes / 16;
+  p.block_bytes = (int64_t)d.num_kv_heads * d.block_size * p.row_bytes;
+  const int64_t per_seq = (int64_t)d.q_tokens * 2 * d.num_kv_heads * p.chunks_per_row;
+  const int64_t blocks_x = (per_seq + 255) / 256;
+  if (blocks_x == 0 || d.num_seqs == 0) return hipSuccess;
+  if (blocks_x > 0x7fffffff || d.num_seqs > 65535) return hipErrorInvalidValue;
+  write_kv_varlen_kernel<<<dim3((unsigned)blocks_x, (unsigned)d.num_seqs), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -5,4 +5,13 @@ the attention arithmetic. It draws lengths, hands out physical blocks, writes
 block tables, and fills pools and queries with N(0, 1) values.
 """
 
-from .configs import CONFIG_NAMES, Case, build_case, int8_pools, make_case  # noqa: F401
+from .configs import (  # noqa: F401
+    CONFIG_NAMES,
+    Case,
+    PrefillCase,
+    build_case,
+    build_prefill_case,
+    int8_pools,
+    make_case,
+    make_prefill_case,
+)

@@ -246,3 +246,85 @@ def int8_pools(case: Case, *, seed: int | None = None, device=None):
             scales[case.unused_blocks.to(device)] = float("nan")
         out += [codes, scales]
     return tuple(out)
+
+
+# ----------------------------------------------------------------------------- paged prefill
+
+@dataclass
+class PrefillCase:
+    """One (chunked) prefill step's inputs, packed: sequence i owns rows ``q_start[i] .. q_start[i+1]-1``
+    of ``q [Q, Hq, D]`` and ``k_new``/``v_new [Q, Hkv, D]``, its newest ``n_i`` positions after a history
+    of ``L_i - n_i``. Pools and tables as in :class:`Case`; the chunk's slots hold stale values until
+    the chunk is written."""
+
+    name: str
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    q_start: torch.Tensor
+    block_size: int
+    scale: float
+    histories: list
+    chunks: list
+
+    @property
+    def max_chunk(self) -> int:
+        return max(self.chunks) if self.chunks else 0
+
+    def attended_pairs(self) -> int:
+        """Sum over chunk tokens of the positions each attends to: sum_i sum_j (h_i + j + 1)."""
+        return sum(n * h + n * (n + 1) // 2 for h, n in zip(self.histories, self.chunks))
+
+
+def build_prefill_case(*, name="custom", histories, chunks, num_q_heads, num_kv_heads, head_dim, block_size,
+                       dtype=torch.bfloat16, seed=0, pool_slack=0.0, pool_device="cpu") -> PrefillCase:
+    """Histories and chunk lengths per sequence; the pools come from :func:`build_case` over the total
+    lengths (blocks from a seeded free-list permutation, unused blocks NaN), then q and the chunk's new
+    K/V rows are drawn N(0, 1) in fp32 and rounded to ``dtype``."""
+    histories = [int(h) for h in histories]
+    chunks = [int(n) for n in chunks]
+    lengths = [h + n for h, n in zip(histories, chunks)]
+    base = build_case(name=name, lengths=lengths, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                      head_dim=head_dim, block_size=block_size, dtype=dtype, seed=seed, pool_slack=pool_slack,
+                      pool_device=pool_device)
+    gen = torch.Generator().manual_seed(int(seed) + 3)
+    total = sum(chunks)
+    q = _randn((total, num_q_heads, head_dim), gen, dtype)
+    k_new = _randn((total, num_kv_heads, head_dim), gen, dtype)
+    v_new = _randn((total, num_kv_heads, head_dim), gen, dtype)
+    q_start = torch.zeros(len(chunks) + 1, dtype=torch.int32)
+    if chunks:
+        q_start[1:] = torch.cumsum(torch.tensor(chunks, dtype=torch.int64), 0).to(torch.int32)
+    return PrefillCase(name=name, q=q, k_new=k_new, v_new=v_new, k_pool=base.k_pool, v_pool=base.v_pool,
+                       block_tables=base.block_tables, seq_lens=base.seq_lens, q_start=q_start,
+                       block_size=block_size, scale=1.0 / math.sqrt(head_dim), histories=histories, chunks=chunks)
+
+
+_PREFILL_SEEDS = {"prefill": 1006, "prefill_small": 1007}
+
+
+def make_prefill_case(name: str, *, num_seqs: int | None = None, pool_device="cpu") -> PrefillCase:
+    """Named prefill workloads:
+
+    * ``prefill``: bf16; 32 q / 8 kv heads; head_dim 128; b 16; 16 sequences, each a chunk of
+      U{512..2048} new tokens after a paged history of U{0..4096} tokens (chunked prefill).
+    * ``prefill_small``: the same shape with 4 sequences, chunks U{1..200}, histories U{0..300}.
+    """
+    gen = torch.Generator().manual_seed(_PREFILL_SEEDS[name])
+    if name == "prefill":
+        n_seq, chunk_rng, hist_rng = 16, (512, 2048), (0, 4096)
+    elif name == "prefill_small":
+        n_seq, chunk_rng, hist_rng = 4, (1, 200), (0, 300)
+    else:
+        raise KeyError(name)
+    chunks = torch.randint(chunk_rng[0], chunk_rng[1] + 1, (n_seq,), generator=gen).tolist()
+    hists = torch.randint(hist_rng[0], hist_rng[1] + 1, (n_seq,), generator=gen).tolist()
+    if num_seqs is not None:
+        chunks, hists = chunks[:num_seqs], hists[:num_seqs]
+    return build_prefill_case(name=name, histories=hists, chunks=chunks, num_q_heads=32, num_kv_heads=8,
+                              head_dim=128, block_size=16, dtype=torch.bfloat16, seed=_PREFILL_SEEDS[name] + 7919,
+                              pool_slack=0.05, pool_device=pool_device)
