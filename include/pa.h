@@ -308,6 +308,7 @@ int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new
  * table (the chunk's own K/V must already be in the pools, e.g. from
  * pa_write_kv_varlen on the same stream).
  *   q   : [Q, Hq, D], q_dtype        out : [Q, Hq, D], out_dtype (fp32 or bf16)
+ *   scale : finite and > 0 (PA_ERR_INVALID_ARG otherwise)
  * One launch on `stream`. Supported: bf16 q and KV, head_dim 128,
  * b in {4, 8, 16, 32}, G <= 128 (PA_ERR_UNSUPPORTED otherwise). */
 int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,

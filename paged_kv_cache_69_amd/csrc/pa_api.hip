@@ -395,7 +395,7 @@ int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const voi
   if (dims->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !q_start || !out) return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
   if (dims->variant == PA_VARIANT_VALU || !pa::prefill_supported(*dims)) return PA_ERR_UNSUPPORTED;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check_prefill(dims, block_tables, seq_lens, q_start, s);

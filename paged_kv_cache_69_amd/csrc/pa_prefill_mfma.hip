@@ -38,6 +38,8 @@
 //  * Workgroups are launched last query block first (the longest rows first),
 //    and consecutive workgroups are consecutive kv heads, so with 8 kv heads
 //    one kv head's K/V stays in one XCD's L2.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -80,6 +82,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Largest of eight scores (IEEE maximum: v_maximum3_f32, no canonicalising moves; a NaN would
+// propagate, and then fails every comparison).
+__device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
+  const float x = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), a[2]);
+  const float y = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], b[0]), b[1]);
+  const float z = __builtin_elementwise_maximum(__builtin_elementwise_maximum(b[2], b[3]), x);
+  return __builtin_elementwise_maximum(y, z);
 }
 
 // V tile half (16 positions x 256 B): 32-byte blocks XOR-swizzled by position, as the transposed
@@ -140,33 +151,59 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
   // ---- cooperative tile loads: thread (rk, ck) moves chunk ck of positions rk and rk + 16
   const int rk = tid >> 4, ck = tid & 15;
   const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
-  const int64_t head_off = (int64_t)kvh * BS * kRowBytes + ck * 16;
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
+  const char* kbase = p.k_pool + (int64_t)kvh * BS * kRowBytes;
+  const char* vbase = p.v_pool + (int64_t)kvh * BS * kRowBytes;
   struct Regs {
     u32x4 k[2], v[2];
   };
   auto load = [&](int tile, Regs& rg) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int pos = tile * kKT + 16 * h + rk;
-      const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-      const int64_t off = (int64_t)blk * block_bytes + head_off + (int64_t)(pos % BS) * kRowBytes;
-      rg.k[h] = load16(p.k_pool + off);
-      rg.v[h] = load16(p.v_pool + off);
-      if (pos >= L) rg.v[h] = u32x4{0u, 0u, 0u, 0u};  // unwritten slot: may hold anything
+      const int p0 = tile * kKT + 16 * h;  // first position of this half
+      if constexpr (BS >= 16) {
+        // the half lies in one block: one scalar table lookup, one buffer descriptor per tensor
+        const int blk = (int)min((uint32_t)trow[min(p0 / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+        const int64_t boff = (int64_t)blk * block_bytes + (int64_t)(p0 % BS) * kRowBytes;
+        const uint32_t lane_off = rk * kRowBytes + ck * 16;
+        rg.k[h] = buffer_load16(buffer_rsrc(kbase + boff, 16 * kRowBytes), lane_off);
+        rg.v[h] = buffer_load16(buffer_rsrc(vbase + boff, 16 * kRowBytes), lane_off);
+      } else {
+        const int pos = p0 + rk;
+        const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+        const int64_t off = (int64_t)blk * block_bytes + (int64_t)(pos % BS) * kRowBytes + ck * 16;
+        rg.k[h] = load16(kbase + off);
+        rg.v[h] = load16(vbase + off);
+      }
     }
-  };
-  auto store = [&](int buf, const Regs& rg) {
-    lds_char* base = (lds_char*)lds + buf * kBufBytes;
+    if (tile * kKT + kKT > L) {  // the last tile: V rows at or past L may hold anything
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = 16 * h + rk;
-      *(lds_u32x4*)(base + k_swz(t, ck)) = rg.k[h];
-      *(lds_u32x4*)(base + kKBytes + h * (kKBytes / 2) + v_swz(rk, ck * 16)) = rg.v[h];
+      for (int h = 0; h < 2; ++h)
+        if (tile * kKT + 16 * h + rk >= L) rg.v[h] = u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // LDS byte offsets inside one buffer, fixed per thread (the buffer is a compile-time offset)
+  const int st_k0 = k_swz(rk, ck), st_k1 = k_swz(16 + rk, ck);
+  const int st_v = kKBytes + v_swz(rk, ck * 16);  // half 1 at + kKBytes / 2
+  auto store = [&](auto bufc, const Regs& rg) {
+    constexpr int base = decltype(bufc)::value * kBufBytes;
+    *(lds_u32x4*)((lds_char*)lds + base + st_k0) = rg.k[0];
+    *(lds_u32x4*)((lds_char*)lds + base + st_k1) = rg.k[1];
+    *(lds_u32x4*)((lds_char*)lds + base + st_v) = rg.v[0];
+    *(lds_u32x4*)((lds_char*)lds + base + st_v + kKBytes / 2) = rg.v[1];
+  };
+  int rd_k[4];  // K A operand: position c16 (+16 for half 1), chunk 4kc + g
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) rd_k[kc] = k_swz(c16, kc * 4 + g);
+  int rd_v[8];  // V B operand (transposed read): positions 4g .. 4g+3, head_dim 16 jb + c16
+  {
+    const int rr = (lane >> 2) & 3, qq = lane & 3;
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) rd_v[jb] = kKBytes + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2);
+  }
 
-  float m_ref[2] = {kNegInf, kNegInf};
+  const float c = p.qk_scale_log2;  // > 0: scores are kept raw and scaled inside the exponent
+  float m_ref[2] = {kNegInf, kNegInf};  // base-2 units
   float l_part[2] = {0.f, 0.f};
   f32x4 acc[2][8];
 #pragma unroll
@@ -174,25 +211,25 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, int tile) {
+  auto compute = [&](auto bufc, int tile) {
+    constexpr int base = decltype(bufc)::value * kBufBytes;
     const int tile_p0 = tile * kKT;
     if (tile_p0 > wave_hi) return;  // every row of this wave stops before this tile
-    const lds_char* kb = (const lds_char*)lds + buf * kBufBytes;
-    const lds_char* vb = kb + kKBytes;
-    // S^T for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of row c16 + 16 mt
+    // raw S^T for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of row c16 + 16 mt
     f32x4 s[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 ka[4];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) ka[kc] = *(const lds_u32x4*)(kb + k_swz(16 * h + c16, kc * 4 + g));
+      for (int kc = 0; kc < 4; ++kc)
+        ka[kc] = *(const lds_u32x4*)((const lds_char*)lds + base + h * (kKBytes / 2) + rd_k[kc]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
-        s[h][mt] = c * p.qk_scale_log2;
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc]), as_bf16x8(qb[mt][kc]), a, 0, 0, 0);
+        s[h][mt] = a;
       }
     }
     if (tile_p0 + kKT - 1 > wave_lo) {  // the tile crosses some row's causal limit
@@ -204,22 +241,22 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
           for (int e = 0; e < 4; ++e)
             if (tile_p0 + 16 * h + 4 * g + e > row_lim[mt]) s[h][mt][e] = kNegInf;
     }
-    // lazy reference: raise it (and rescale what was accumulated) only when a score outruns it
-    float mx[2];
+    // Lazy reference: each lane checks its own 8 scores of a row against the row's reference; only
+    // when one outruns it does the wave reduce the row maxima and rescale what it accumulated.
+    float lmx[2];
     bool over = false;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      float x = fmaxf(fmaxf(fmaxf(s[0][mt][0], s[0][mt][1]), fmaxf(s[0][mt][2], s[0][mt][3])),
-                      fmaxf(fmaxf(s[1][mt][0], s[1][mt][1]), fmaxf(s[1][mt][2], s[1][mt][3])));
-      x = fmaxf(x, __shfl_xor(x, 16, 64));
-      x = fmaxf(x, __shfl_xor(x, 32, 64));
-      mx[mt] = x;
-      over |= x > m_ref[mt] + kSlack;
+      lmx[mt] = max8(s[0][mt], s[1][mt]);
+      over |= lmx[mt] * c > m_ref[mt] + kSlack;
     }
-    if (__any(over)) {
+    if (__builtin_expect(__any(over), 0)) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const float m_new = fmaxf(m_ref[mt], mx[mt]);
+        float x = lmx[mt];
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        const float m_new = fmaxf(m_ref[mt], x * c);
         const float alpha = m_ref[mt] == kNegInf ? 0.f : exp2_fast(m_ref[mt] - m_new);
         m_ref[mt] = m_new;
         l_part[mt] *= alpha;
@@ -231,7 +268,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
         }
       }
     }
-    // P = 2^(s - m) as bf16 hi + lo; k-slots 8g .. 8g+3 = half 0, 8g+4 .. 8g+7 = half 1
+    // P = 2^(c s - m), masked positions exactly 0. Split P = hi + lo: hi is P truncated to bf16 (its
+    // top 16 bits, picked with one byte permute per pair), lo = P - hi exactly, rounded to bf16.
+    // k-slots 8g .. 8g+3 hold half 0 and 8g+4 .. 8g+7 half 1.
     u32x4 a_hi[2], a_lo[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -240,24 +279,22 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x = s[h][mt][e];
-          pr[4 * h + e] = x == kNegInf ? 0.f : exp2_fast(x - m_ref[mt]);
+          pr[4 * h + e] = exp2_fast(fmaf(s[h][mt][e], c, -m_ref[mt]));
           l_part[mt] += pr[4 * h + e];
         }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t hi = cvt_pk_bf16(pr[2 * w], pr[2 * w + 1]);
-        a_hi[mt][w] = hi;
-        a_lo[mt][w] = cvt_pk_bf16(pr[2 * w] - bf16_lo(hi), pr[2 * w + 1] - bf16_hi(hi));
+        const uint32_t u0 = __float_as_uint(pr[2 * w]), u1 = __float_as_uint(pr[2 * w + 1]);
+        a_hi[mt][w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        a_lo[mt][w] = cvt_pk_bf16(pr[2 * w] - __uint_as_float(u0 & 0xffff0000u),
+                                  pr[2 * w + 1] - __uint_as_float(u1 & 0xffff0000u));
       }
     }
-    // B operand: positions 4g .. 4g+3 of each half, head_dim column 16 jb + c16
-    const int rr = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
-      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2)));
-      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vb + kKBytes / 2 + v_swz(4 * g + rr, (16 * jb + 4 * qq) * 2)));
+      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)lds + base + rd_v[jb]));
+      const s16x4 b1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)lds + base + kKBytes / 2 + rd_v[jb]));
       const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
       const u32x4 bv = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
 #pragma unroll
@@ -268,19 +305,33 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
     }
   };
 
+  // One tile per step: load the next tile's K/V into registers, compute this one from LDS, store
+  // the next into the other buffer, barrier. Unrolled by two so the buffer offsets are constants.
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
   {
     Regs rg;
     load(0, rg);
-    store(0, rg);
+    store(Buf0{}, rg);
   }
   __syncthreads();
-  for (int i = 0; i < ntiles; ++i) {
-    Regs rg;
-    const bool more = i + 1 < ntiles;
-    if (more) load(i + 1, rg);
-    compute(i & 1, i);
-    if (more) store((i + 1) & 1, rg);
-    __syncthreads();
+  for (int i = 0; i < ntiles; i += 2) {
+    {
+      Regs rg;
+      const bool more = i + 1 < ntiles;
+      if (more) load(i + 1, rg);
+      compute(Buf0{}, i);
+      if (more) store(Buf1{}, rg);
+      __syncthreads();
+    }
+    if (i + 1 < ntiles) {
+      Regs rg;
+      const bool more = i + 2 < ntiles;
+      if (more) load(i + 2, rg);
+      compute(Buf1{}, i + 1);
+      if (more) store(Buf0{}, rg);
+      __syncthreads();
+    }
   }
 
   // ---- o = acc / l; accumulator row 4g + e of the wave's 16-row tile mt
