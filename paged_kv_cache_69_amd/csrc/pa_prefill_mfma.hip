@@ -93,6 +93,21 @@ __device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
   return __builtin_elementwise_maximum(y, z);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A row of zeros in global memory: the source of tile rows at or past a sequence's length.
+__device__ __attribute__((aligned(16))) const char kZeroRow[kRowBytes] = {};
+
+// Wait until at most N vector-memory operations of this wave are outstanding (vmcnt only).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier with no implied wait for outstanding memory operations; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // V tile half (16 positions x 256 B): 32-byte blocks XOR-swizzled by position, as the transposed
 // reads expect.
 __device__ __forceinline__ int v_swz(int t, int byte) { return t * kRowBytes + (byte ^ ((t & 7) << 5)); }
@@ -101,7 +116,12 @@ __device__ __forceinline__ int k_swz(int t, int chunk) { return t * kRowBytes + 
 
 template <int BS>
 __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBufBytes];
+  // four tile buffers, separate LDS objects: the compiler then tracks the direct-to-LDS loads into
+  // each one apart and does not wait for all of them before reading any buffer
+  __shared__ __attribute__((aligned(16))) char lds0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) char lds1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) char lds2[kBufBytes];
+  __shared__ __attribute__((aligned(16))) char lds3[kBufBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,49 +168,49 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
 
   const int ntiles = (hist + tok_end + kKT - 1) / kKT;
 
-  // ---- cooperative tile loads: thread (rk, ck) moves chunk ck of positions rk and rk + 16
-  const int rk = tid >> 4, ck = tid & 15;
-  const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
+  // ---- tile loads, straight from the pools into LDS (global_load_lds_dwordx4: lane l of one
+  // instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB slot). A tile buffer is 16 slots: K rows 0-31
+  // (4 per slot, K layout), then V halves 0 and 1 (4 rows per slot, V layout). Wave w fills K slots
+  // w and 4 + w and V slots 8 + w and 12 + w: rows 4w .. 4w + 3 of each 16-position half. Each lane
+  // picks the source chunk that its LDS chunk holds under the swizzle; positions at or past L read a
+  // row of zeros instead of the pool (unwritten slots may hold anything).
+  // The table is read through the constant address space: its wave-uniform lookups become scalar
+  // loads (counted by lgkmcnt), so waiting for one never waits for the tile loads in flight.
+  const __attribute__((address_space(4))) int32_t* trow =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)seq * p.MB);
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
   const char* kbase = p.k_pool + (int64_t)kvh * BS * kRowBytes;
   const char* vbase = p.v_pool + (int64_t)kvh * BS * kRowBytes;
-  struct Regs {
-    u32x4 k[2], v[2];
-  };
-  auto load = [&](int tile, Regs& rg) {
+  const int tq = 4 * wave + (lane >> 4);                // row inside a 16-position half
+  const int lc_k = (lane & 15) ^ (tq & 15);              // K chunk this lane's LDS chunk holds
+  const int lc_v = (lane & 15) ^ ((tq & 7) << 1);        // V chunk (32-byte blocks swizzled)
+  constexpr int kHalfBlocks = BS >= 16 ? 1 : 16 / BS;    // blocks one half spans
+  auto issue = [&](lds_char* buf, int tile) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int p0 = tile * kKT + 16 * h;  // first position of this half
+      const int p0 = tile * kKT + 16 * h;
+      // block of this lane's row (scalar table loads; a lane selects among them for b < 16)
+      int64_t row_off;
       if constexpr (BS >= 16) {
-        // the half lies in one block: one scalar table lookup, one buffer descriptor per tensor
         const int blk = (int)min((uint32_t)trow[min(p0 / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-        const int64_t boff = (int64_t)blk * block_bytes + (int64_t)(p0 % BS) * kRowBytes;
-        const uint32_t lane_off = rk * kRowBytes + ck * 16;
-        rg.k[h] = buffer_load16(buffer_rsrc(kbase + boff, 16 * kRowBytes), lane_off);
-        rg.v[h] = buffer_load16(buffer_rsrc(vbase + boff, 16 * kRowBytes), lane_off);
+        row_off = (int64_t)blk * block_bytes + (int64_t)(p0 % BS + tq) * kRowBytes;
       } else {
-        const int pos = p0 + rk;
-        const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-        const int64_t off = (int64_t)blk * block_bytes + (int64_t)(pos % BS) * kRowBytes + ck * 16;
-        rg.k[h] = load16(kbase + off);
-        rg.v[h] = load16(vbase + off);
-      }
-    }
-    if (tile * kKT + kKT > L) {  // the last tile: V rows at or past L may hold anything
+        int ids[kHalfBlocks];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (tile * kKT + 16 * h + rk >= L) rg.v[h] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < kHalfBlocks; ++j)
+          ids[j] = (int)min((uint32_t)trow[min(p0 / BS + j, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+        int blk = ids[0];
+#pragma unroll
+        for (int j = 1; j < kHalfBlocks; ++j)
+          if (tq / BS == j) blk = ids[j];
+        row_off = (int64_t)blk * block_bytes + (int64_t)(tq % BS) * kRowBytes;
+      }
+      const bool live = p0 + tq < L;
+      const char* ksrc = live ? kbase + row_off + lc_k * 16 : kZeroRow + lc_k * 16;
+      const char* vsrc = live ? vbase + row_off + lc_v * 16 : kZeroRow + lc_v * 16;
+      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void*)(buf + (4 * h + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void*)(buf + (8 + 4 * h + wave) * 1024), 16, 0, 0);
     }
-  };
-  // LDS byte offsets inside one buffer, fixed per thread (the buffer is a compile-time offset)
-  const int st_k0 = k_swz(rk, ck), st_k1 = k_swz(16 + rk, ck);
-  const int st_v = kKBytes + v_swz(rk, ck * 16);  // half 1 at + kKBytes / 2
-  auto store = [&](auto bufc, const Regs& rg) {
-    constexpr int base = decltype(bufc)::value * kBufBytes;
-    *(lds_u32x4*)((lds_char*)lds + base + st_k0) = rg.k[0];
-    *(lds_u32x4*)((lds_char*)lds + base + st_k1) = rg.k[1];
-    *(lds_u32x4*)((lds_char*)lds + base + st_v) = rg.v[0];
-    *(lds_u32x4*)((lds_char*)lds + base + st_v + kKBytes / 2) = rg.v[1];
   };
   int rd_k[4];  // K A operand: position c16 (+16 for half 1), chunk 4kc + g
 #pragma unroll
@@ -211,27 +231,29 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](auto bufc, int tile) {
-    constexpr int base = decltype(bufc)::value * kBufBytes;
-    const int tile_p0 = tile * kKT;
-    if (tile_p0 > wave_hi) return;  // every row of this wave stops before this tile
-    // raw S^T for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of row c16 + 16 mt
-    f32x4 s[2][2];
+  // Raw S^T of a tile for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of
+  // row c16 + 16 mt.
+  auto scores = [&](const lds_char* buf, f32x4 (&s)[2][2]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 ka[4];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        ka[kc] = *(const lds_u32x4*)((const lds_char*)lds + base + h * (kKBytes / 2) + rd_k[kc]);
+      for (int mt = 0; mt < 2; ++mt) s[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // four independent accumulation chains, interleaved, so no MFMA waits for the one before it
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x4 ka0 = *(const lds_u32x4*)(buf + rd_k[kc]);
+      const u32x4 ka1 = *(const lds_u32x4*)(buf + kKBytes / 2 + rd_k[kc]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc]), as_bf16x8(qb[mt][kc]), a, 0, 0, 0);
-        s[h][mt] = a;
+        s[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka0), as_bf16x8(qb[mt][kc]), s[0][mt], 0, 0, 0);
+        s[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka1), as_bf16x8(qb[mt][kc]), s[1][mt], 0, 0, 0);
       }
     }
+  };
+  // Softmax and P.V of a tile whose raw scores are s and whose V rows are in buf.
+  // Mask, reference check and (rarely) rescale for a tile whose raw scores are s.
+  auto head = [&](int tile, f32x4 (&s)[2][2]) {
+    const int tile_p0 = tile * kKT;
     if (tile_p0 + kKT - 1 > wave_lo) {  // the tile crosses some row's causal limit
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -268,10 +290,12 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
         }
       }
     }
+  };
+  // P of a tile (hi and lo operands) and its row sums.
+  auto probs = [&](const f32x4 (&s)[2][2], u32x4 (&a_hi)[2], u32x4 (&a_lo)[2]) {
     // P = 2^(c s - m), masked positions exactly 0. Split P = hi + lo: hi is P truncated to bf16 (its
     // top 16 bits, picked with one byte permute per pair), lo = P - hi exactly, rounded to bf16.
     // k-slots 8g .. 8g+3 hold half 0 and 8g+4 .. 8g+7 half 1.
-    u32x4 a_hi[2], a_lo[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       float pr[8];
@@ -290,47 +314,78 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
                                   pr[2 * w + 1] - __uint_as_float(u1 & 0xffff0000u));
       }
     }
+  };
+  // P.V of a tile whose V rows are in buf.
+  auto pv = [&](const lds_char* buf, const u32x4 (&a_hi)[2], const u32x4 (&a_lo)[2]) {
+    // Two head_dim blocks at a time: their hi MFMAs for both row tiles, then their lo MFMAs, so an
+    // accumulator's two updates are four instructions apart.
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) {
-      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)lds + base + rd_v[jb]));
-      const s16x4 b1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)lds + base + kKBytes / 2 + rd_v[jb]));
-      const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
-      const u32x4 bv = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+    for (int jb = 0; jb < 8; jb += 2) {
+      u32x4 bv[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
-        acc[mt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo[mt]), as_bf16x8(bv), acc[mt][jb], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + rd_v[jb + j]));
+        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kKBytes / 2 + rd_v[jb + j]));
+        const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
+        bv[j] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt][jb + j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi[mt]), as_bf16x8(bv[j]), acc[mt][jb + j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt][jb + j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo[mt]), as_bf16x8(bv[j]), acc[mt][jb + j], 0, 0, 0);
     }
   };
 
-  // One tile per step: load the next tile's K/V into registers, compute this one from LDS, store
-  // the next into the other buffer, barrier. Unrolled by two so the buffer offsets are constants.
-  using Buf0 = std::integral_constant<int, 0>;
-  using Buf1 = std::integral_constant<int, 1>;
-  {
-    Regs rg;
-    load(0, rg);
-    store(Buf0{}, rg);
-  }
-  __syncthreads();
-  for (int i = 0; i < ntiles; i += 2) {
-    {
-      Regs rg;
-      const bool more = i + 1 < ntiles;
-      if (more) load(i + 1, rg);
-      compute(Buf0{}, i);
-      if (more) store(Buf1{}, rg);
-      __syncthreads();
-    }
-    if (i + 1 < ntiles) {
-      Regs rg;
-      const bool more = i + 2 < ntiles;
-      if (more) load(i + 2, rg);
-      compute(Buf1{}, i + 1);
-      if (more) store(Buf0{}, rg);
-      __syncthreads();
+  // Software pipeline, step i: wait for this wave's loads of tile i+1 (tile i+2 may stay in flight),
+  // barrier (every wave's part of tile i+1 is in LDS, and every wave is done with tile i-1), issue
+  // tile i+3 into the buffer tile i-1 used, then the scores of tile i+1 on the matrix cores while
+  // the vector ALUs run the softmax of tile i, whose P.V follows. Unrolled by four so that each
+  // buffer is a fixed LDS object.
+  lds_char* const bufs[4] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < ntiles) issue(bufs[t], t);
+  if (ntiles > 2)
+    wait_vmem<8>();
+  else if (ntiles > 1)
+    wait_vmem<4>();
+  else
+    wait_vmem<0>();
+  lds_barrier();
+  f32x4 s_a[2][2], s_b[2][2];
+  scores(bufs[0], s_a);
+  for (int i0 = 0; i0 < ntiles; i0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u;
+      if (i < ntiles) {
+        f32x4(&s_cur)[2][2] = (u & 1) ? s_b : s_a;
+        f32x4(&s_next)[2][2] = (u & 1) ? s_a : s_b;
+        if (i + 1 < ntiles) {
+          if (i + 2 < ntiles)
+            wait_vmem<4>();
+          else
+            wait_vmem<0>();
+          lds_barrier();
+          if (i + 3 < ntiles) issue(bufs[(u + 3) & 3], i + 3);
+        }
+        head(i, s_cur);
+        // One branch-free stretch: the next tile's scores on the matrix cores, this tile's P on the
+        // vector ALUs, then this tile's P.V. Past the last tile the scores read a stale buffer and
+        // are never used; tiles past a wave's rows are fully masked and add nothing.
+        scores(bufs[(u + 1) & 3], s_next);
+        u32x4 a_hi[2], a_lo[2];
+        probs(s_cur, a_hi, a_lo);
+        pv(bufs[u], a_hi, a_lo);
+      }
     }
   }
 
