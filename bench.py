@@ -73,7 +73,12 @@ WORKLOADS = {
                          desc="batch64 with int8 K/V pools + per-(block, kv head) scales, bf16 q"),
     "long_int8": dict(partition_tokens=512, base="long", int8=True,
                       desc="long with int8 K/V pools + per-(block, kv head) scales, bf16 q, 512-token partitions"),
+    # paged (chunked) prefill: a step is one pa_write_kv_varlen + one pa_prefill call
+    "prefill": dict(partition_tokens=None, kind="prefill",
+                    desc="16 seqs, chunks of U[512,2048] new tokens after paged histories of U[0,4096], 32 q / 8 kv "
+                         "heads, head_dim 128, b=16, bf16 (causal attention over history + chunk)"),
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def kv_bytes_per_position(num_kv_heads: int, head_dim: int, itemsize: int) -> int:
@@ -141,9 +146,11 @@ def read_summary(path: str) -> dict:
 
 
 def traffic_from_profiles(workload: str):
-    """HBM bytes per decode call from profiles/traffic_decode_<workload>.txt, or None when the summary
+    """HBM bytes per attention call from profiles/traffic_decode_<workload>.txt (traffic_prefill.txt for
+    the prefill workload), or None when the summary
     is missing or was taken from another build of the library."""
-    path = os.path.join(PROFILES, f"traffic_decode_{workload}.txt")
+    kind = WORKLOADS.get(workload, {}).get("kind", "decode")
+    path = os.path.join(PROFILES, f"traffic_decode_{workload}.txt" if kind == "decode" else f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     s = read_summary(path)
@@ -395,12 +402,147 @@ def calibrate_copy(n_runs: int = 3):
     torch.cuda.empty_cache()
 
 
+def prefill_flops(case) -> int:
+    """Matrix flops of one pa_prefill call: for every chunk token, query head and visible position,
+    a 128-long dot product for the score and a 128-long update of the output, 2 flops per multiply-add:
+    4 * D * Hq * sum_i sum_j (h_i + j + 1)."""
+    return 4 * case.q.shape[2] * case.q.shape[1] * case.attended_pairs()
+
+
+def prefill_algorithmic_bytes(case) -> int:
+    """Bytes a prefill call must move at least: each sequence's K/V rows once (history + chunk, every kv
+    head), q once, the fp32 output once, the used table entries, the lengths and q_start."""
+    hkv, d = case.k_pool.shape[1], case.k_pool.shape[3]
+    lens = [h + n for h, n in zip(case.histories, case.chunks)]
+    blocks = sum(-(-L // case.block_size) for L in lens)
+    total_q, hq, _ = case.q.shape
+    return (sum(lens) * kv_bytes_per_position(hkv, d, case.k_pool.element_size())
+            + total_q * hq * d * (case.q.element_size() + 4) + 4 * blocks + 4 * len(lens) + 4 * (len(lens) + 1))
+
+
+def run_prefill_workload(pa, name, steps, warmup, graphs=True):
+    """The prefill workload: a step is one pa_write_kv_varlen (the chunks' K/V into the pools) and one
+    pa_prefill call, timed like the decode steps (graphs of whole steps; HIP events around a graph of
+    the prefill calls alone)."""
+    import ctypes
+
+    import torch
+
+    from workloads import make_prefill_case
+
+    spec = WORKLOADS[name]
+    case = make_prefill_case(name, pool_device="cuda:0")
+    dev = torch.device("cuda:0")
+    keys = ("q", "k_new", "v_new", "k_pool", "v_pool", "block_tables", "seq_lens", "q_start")
+    touched = sum(getattr(case, k).numel() * getattr(case, k).element_size() for k in keys) + case.q.numel() * 4
+    n_rep = max(1, min(8, math.ceil(COLD_BYTES / touched)))
+    reps = []
+    for _ in range(n_rep):
+        t = {k: getattr(case, k).to(dev, copy=True) for k in keys}
+        t["out"] = torch.empty(case.q.shape, dtype=torch.float32, device=dev)
+        reps.append(t)
+    lib = pa.load_library()
+    hq, hkv, d = case.q.shape[1], case.k_pool.shape[1], case.q.shape[2]
+    dims = pa.PaDims(len(case.chunks), case.max_chunk, hq, hkv, d, case.block_size, case.k_pool.shape[0],
+                     case.block_tables.shape[1], pa.PA_BF16, pa.PA_BF16, pa.PA_F32, 0)
+    wdims = pa.PaDims(len(case.chunks), case.max_chunk, hkv, hkv, d, case.block_size, case.k_pool.shape[0],
+                      case.block_tables.shape[1], pa.PA_BF16, pa.PA_BF16, pa.PA_BF16, 0)
+    scale = ctypes.c_float(case.scale)
+
+    def write(t, h):
+        st = lib.pa_write_kv_varlen(ctypes.byref(wdims), t["k_new"].data_ptr(), t["v_new"].data_ptr(),
+                                    t["k_pool"].data_ptr(), t["v_pool"].data_ptr(), t["block_tables"].data_ptr(),
+                                    t["seq_lens"].data_ptr(), t["q_start"].data_ptr(), h)
+        if st:
+            raise RuntimeError(f"pa_write_kv_varlen: {st}")
+
+    def attend(t, h):
+        st = lib.pa_prefill(ctypes.byref(dims), t["q"].data_ptr(), t["k_pool"].data_ptr(), t["v_pool"].data_ptr(),
+                            t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(), t["q_start"].data_ptr(), scale,
+                            t["out"].data_ptr(), h)
+        if st:
+            raise RuntimeError(f"pa_prefill: {st}")
+
+    def sh():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    for s_ in range(warmup):
+        write(reps[s_ % n_rep], sh())
+        attend(reps[s_ % n_rep], sh())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graphs:
+        def capture(fn_list):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for s_ in range(steps):
+                        for fn in fn_list:
+                            fn(reps[s_ % n_rep], sh())
+            stream.wait_stream(side)
+            g.replay()  # upload, untimed
+            torch.cuda.synchronize()
+            return g
+
+        g_step = capture([write, attend])
+        t0 = time.perf_counter()
+        g_step.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del g_step
+        g_call = capture([attend])
+        ev0.record(stream)
+        g_call.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        del g_call
+    else:
+        h = ctypes.c_void_p(stream.cuda_stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for s_ in range(steps):
+            write(reps[s_ % n_rep], h)
+            attend(reps[s_ % n_rep], h)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    call_ms = ev0.elapsed_time(ev1) / steps
+    sec_per_step = (t1 - t0) / steps
+    flops = prefill_flops(case)
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    tokens = sum(case.chunks)
+    res = {
+        "tokens_per_s": tokens / sec_per_step,
+        "ms_per_step": sec_per_step * 1e3,
+        "achieved_gbps": prefill_algorithmic_bytes(case) / sec_per_step / 1e9,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(name),
+                     "kernel": "prefill_mfma_kernel (one pa_prefill call)", "flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": prefill_algorithmic_bytes(case),
+                     "avg_launch_us": round(call_ms * 1e3, 3), "launches_timed": steps},
+        "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": len(case.chunks), "chunk_tokens": tokens,
+                   "histories": sum(case.histories), "replicas": n_rep,
+                   "step": "pa_write_kv_varlen call + pa_prefill call"},
+        "dtype": "bf16",
+    }
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True, fused=True):
     import torch
 
     from workloads import int8_pools, make_case
 
     spec = WORKLOADS[name]
+    if spec.get("kind") == "prefill":
+        return run_prefill_workload(pa, name, steps, warmup, graphs)
     case = make_case(spec.get("base", name), pool_device="cuda:0")
     if spec.get("int8"):
         case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
@@ -472,7 +614,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
     with open(bench_log) as fh:
         line = [ln for ln in fh if ln.startswith("{")][-1]
     rec = json.loads(line)
-    algo = int(rec["roofline"]["bytes_per_launch"])
+    algo = int(rec["roofline"].get("bytes_per_launch") or rec["roofline"]["algorithmic_bytes_per_launch"])
     per = {}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         for r in _pmc_rows(directory):
@@ -487,7 +629,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
         raise RuntimeError("calibration copy kernel not found in the counter runs")
     f_fac = CALIBRATION_BYTES / (cf[0] * 1024.0)
     w_fac = CALIBRATION_BYTES / (cw[0] * 1024.0)
-    kernels = sorted({k[1] for k in med if k[1].startswith("void decode_") or "merge_partials" in k[1]})
+    kernels = sorted({k[1] for k in med
+                      if k[1].startswith("void decode_") or "merge_partials" in k[1] or "prefill_mfma" in k[1]})
     lines = [f"# HBM traffic of one decode call, workload {workload}",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
              f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
@@ -549,7 +692,7 @@ def summarize_stats(directory: str, command: str, bench_log: str | None = None) 
     if bench_log:
         with open(bench_log) as fh:
             rec = json.loads([ln for ln in fh if ln.startswith("{")][-1])
-        out.append(f"# the same run's bench line: decode call avg {rec['roofline']['avg_launch_us']} us over "
+        out.append(f"# the same run's bench line: attention call avg {rec['roofline']['avg_launch_us']} us over "
                    f"{rec['roofline']['launches_timed']} calls (HIP events around one graph of the calls)")
     return "\n".join(out) + "\n"
 
@@ -560,7 +703,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8",
+    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,prefill",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")

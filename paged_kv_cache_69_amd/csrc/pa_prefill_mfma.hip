@@ -35,9 +35,11 @@
 //  * Causal mask by selection (-inf, never computed), only in the tiles that
 //    cross a row's limit; V rows at or past L are zeroed in LDS, so garbage in
 //    unwritten slots never reaches the result.
-//  * Workgroups are launched last query block first (the longest rows first),
-//    and consecutive workgroups are consecutive kv heads, so with 8 kv heads
-//    one kv head's K/V stays in one XCD's L2.
+//  * Consecutive workgroups are consecutive kv heads, so with 8 kv heads all
+//    workgroups of one kv head run on one XCD; along the grid, one sequence's
+//    query blocks (last block first: the longest rows) come before the next
+//    sequence's, so the workgroups an XCD holds at a time read the K/V of one
+//    or two sequences, which stays in its L2.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
-  const int seq = bid % p.B;
-  const int qblk = p.n_qblocks - 1 - bid / p.B;  // longest rows first
+  const int qblk = p.n_qblocks - 1 - bid % p.n_qblocks;  // a sequence's longest rows first
+  const int seq = bid / p.n_qblocks;
 
   const int q0 = p.q_start[seq];
   const int n = p.q_start[seq + 1] - q0;
