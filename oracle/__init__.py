@@ -15,8 +15,8 @@ blocking, fusion or online recurrence. The pages are:
 * [P5] "Chapter 7 Paged KV Cache and Memory Management" (zero-to-sglang)
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle.py``, ``tests/test_oracle_int8.py`` or
-``tests/test_oracle_prefill.py``, which checks it
+``tests/test_oracle.py``, ``tests/test_oracle_int8.py``,
+``tests/test_oracle_prefill.py`` or ``tests/test_oracle_blocks.py``, which checks it
 against something other than itself:
 the pages' worked examples, a library routine, closed forms, invariants or
 brute force. No function is "parity unpinned".
@@ -29,6 +29,7 @@ from .pa_oracle_int8 import (  # noqa: F401
     dequantize_pool,
     quantize_block,
 )
+from .pa_oracle_blocks import BlockPool, PagedCache, PoolExhausted, PrefixCache  # noqa: F401
 from .pa_oracle_prefill import chunk_positions, prefill, prefill_row, write_kv_varlen  # noqa: F401
 from .pa_oracle import (  # noqa: F401
     attend_rows,
