@@ -77,6 +77,10 @@ WORKLOADS = {
     "prefill": dict(partition_tokens=None, kind="prefill",
                     desc="16 seqs, chunks of U[512,2048] new tokens after paged histories of U[0,4096], 32 q / 8 kv "
                          "heads, head_dim 128, b=16, bf16 (causal attention over history + chunk)"),
+    # copy-on-write block copies: one pa_copy_blocks call over many (source, destination) pairs
+    "cow_copy": dict(partition_tokens=None, kind="copy",
+                     desc="pa_copy_blocks of 4096 block pairs, 8 kv heads x 16 positions x 128 bf16 per block "
+                          "(32 KiB of K and 32 KiB of V each), pools of 8192 blocks"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
@@ -535,6 +539,87 @@ def run_prefill_workload(pa, name, steps, warmup, graphs=True):
     return res
 
 
+def run_copy_workload(pa, name, steps, warmup, graphs=True):
+    """Copy-on-write block copies: one pa_copy_blocks call moves 4096 blocks of K and of V to fresh
+    blocks; algorithmic bytes = 2 (read + write) x 2 (K, V) x 4096 x 32 KiB."""
+    import ctypes
+
+    import torch
+
+    spec = WORKLOADS[name]
+    n_blocks, hkv, b, d, n_pairs = 8192, 8, 16, 128, 4096
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(1008)
+    k_pool = torch.randn((n_blocks, hkv, b, d), generator=gen, device=dev).to(torch.bfloat16)
+    v_pool = torch.randn((n_blocks, hkv, b, d), generator=gen, device=dev).to(torch.bfloat16)
+    perm = torch.randperm(n_blocks, generator=torch.Generator().manual_seed(1009))
+    pairs = torch.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], dim=1).to(torch.int32).to(dev).contiguous()
+    lib = pa.load_library()
+    from paged_kv_cache_69_amd import blocks as _blocks
+
+    _blocks._bind(lib)
+    dims = pa.PaDims(0, 1, hkv, hkv, d, b, n_blocks, 1, pa.PA_BF16, pa.PA_BF16, pa.PA_BF16, 0)
+    block_bytes = hkv * b * d * 2
+    algo = 2 * 2 * n_pairs * block_bytes
+
+    def call(h):
+        st = lib.pa_copy_blocks(ctypes.byref(dims), k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(), n_pairs, h)
+        if st:
+            raise RuntimeError(f"pa_copy_blocks: {st}")
+
+    def sh():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    for _ in range(warmup):
+        call(sh())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graphs:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(steps):
+                    call(sh())
+        stream.wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del g
+    else:
+        h = ctypes.c_void_p(stream.cuda_stream)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            call(h)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    call_ms = ev0.elapsed_time(ev1) / steps
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    res = {
+        "tokens_per_s": n_pairs * b / ((t1 - t0) / steps),  # positions moved per second
+        "ms_per_step": (t1 - t0) / steps * 1e3,
+        "achieved_gbps": algo / ((t1 - t0) / steps) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(name),
+                     "kernel": "copy_blocks_kernel (one pa_copy_blocks call)", "bytes_per_launch": algo,
+                     "avg_launch_us": round(call_ms * 1e3, 3), "launches_timed": steps},
+        "config": {"workload": f"{name}: {spec['desc']}", "block_pairs": n_pairs, "block_bytes": block_bytes},
+        "dtype": "bf16",
+    }
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True, fused=True):
     import torch
 
@@ -543,6 +628,8 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     spec = WORKLOADS[name]
     if spec.get("kind") == "prefill":
         return run_prefill_workload(pa, name, steps, warmup, graphs)
+    if spec.get("kind") == "copy":
+        return run_copy_workload(pa, name, steps, warmup, graphs)
     case = make_case(spec.get("base", name), pool_device="cuda:0")
     if spec.get("int8"):
         case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
@@ -630,7 +717,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
     f_fac = CALIBRATION_BYTES / (cf[0] * 1024.0)
     w_fac = CALIBRATION_BYTES / (cw[0] * 1024.0)
     kernels = sorted({k[1] for k in med
-                      if k[1].startswith("void decode_") or "merge_partials" in k[1] or "prefill_mfma" in k[1]})
+                      if k[1].startswith("void decode_") or "merge_partials" in k[1] or "prefill_mfma" in k[1]
+                      or "copy_blocks" in k[1]})
     lines = [f"# HBM traffic of one decode call, workload {workload}",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
              f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
@@ -703,7 +791,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,prefill",
+    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,prefill,cow_copy",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")

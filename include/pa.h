@@ -58,7 +58,8 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, bad dtype code, workspace too small */
   PA_ERR_UNSUPPORTED = -2, /* valid arguments, but no kernel for this (dtype, head_dim, block, rows) */
-  PA_ERR_LAUNCH = -3       /* the HIP runtime reported an error for the launch */
+  PA_ERR_LAUNCH = -3,      /* the HIP runtime reported an error for the launch */
+  PA_ERR_NO_BLOCKS = -4    /* block manager: the pool has too few free blocks (nothing changed) */
 } pa_status;
 
 /* PA_INT8 is a pool dtype only: int8 codes with one fp32 scale per
@@ -322,6 +323,89 @@ int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const voi
  * Returns PA_OK or PA_ERR_INVALID_ARG; launches nothing. */
 int pa_check_prefill_host(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
                           const int32_t* q_start);
+
+/* ---- Block management ([P1] "25. Paged attention and prefix caching",
+ * sections "The allocator", "The paged cache", "Sharing blocks: forks and
+ * copy-on-write" and "Prefix caching"; [P2] section 4).
+ *
+ * pa_copy_blocks: for each pair i, copy physical block block_pairs[2i] onto
+ * block block_pairs[2i+1] in both pools (all kv heads; the Hkv * b * D
+ * elements of a block are contiguous). This is the data half of
+ * copy-on-write: pa_bm_reserve returns the pairs.
+ *   dims : num_kv_heads, block_size, head_dim, num_blocks and kv_dtype are
+ *          used (any pool dtype, including PA_INT8 codes; an int8 pool's
+ *          scales are copied by the caller)
+ *   block_pairs : int32 [num_pairs, 2] on the device
+ * Preconditions (checked under PA_CHECK=1, pa_check_copies_host): every id in
+ * [0, num_blocks); destinations distinct; no destination is also a source.
+ * One launch on `stream`; num_pairs = 0 launches nothing. */
+int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, const int32_t* block_pairs,
+                   int32_t num_pairs, pa_stream_t stream);
+
+/* pa_check_copies_host: the pa_copy_blocks preconditions on host pairs. */
+int pa_check_copies_host(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs);
+
+/* Host block manager (host memory only; nothing here touches the GPU). One
+ * manager owns the block ids of one pool pair: a first-in first-out free list
+ * over 0 .. num_blocks-1, a reference count per block (tables and prefix-cache
+ * entries that hold it), and a block table and length per sequence (int64
+ * ids chosen by the caller). Not thread-safe: one caller at a time. Calls
+ * return PA_OK (or a count, >= 0) or a negative pa_status; a failed call
+ * changes nothing. */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager over num_blocks blocks of block_size positions; NULL on invalid
+ * sizes or when memory runs out. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* m);
+int32_t pa_bm_num_free(const pa_block_manager* m);
+int32_t pa_bm_refcount(const pa_block_manager* m, int32_t block);
+int32_t pa_bm_num_seqs(const pa_block_manager* m);
+/* A new, empty sequence (error if the id is in use). */
+int pa_bm_add_seq(pa_block_manager* m, int64_t seq);
+/* Make blocks exist for positions [length, length + new_tokens) of seq, before
+ * they are written. A block in that range that other tables or the prefix
+ * cache also hold is replaced by a fresh block first (copy-on-write); the
+ * (old, fresh) pairs go to copies (int32 [copies_capacity, 2], host) in table
+ * order, their count to *num_copies, and the caller must copy those blocks
+ * (pa_copy_blocks) before writing. PA_ERR_NO_BLOCKS when the pool cannot
+ * supply every block the call needs (the caller may evict cached prefixes or
+ * preempt a sequence, then retry). The length is unchanged. */
+int pa_bm_reserve(pa_block_manager* m, int64_t seq, int32_t new_tokens, int32_t* copies,
+                  int32_t copies_capacity, int32_t* num_copies);
+/* Record that seq now holds `length` tokens (after their K/V are written); it
+ * never decreases here, and may not pass the reserved blocks. */
+int pa_bm_commit(pa_block_manager* m, int64_t seq, int32_t length);
+/* child starts as an alias of parent: the same table and length, every block
+ * shared (beam search, parallel sampling). */
+int pa_bm_fork(pa_block_manager* m, int64_t parent, int64_t child);
+/* Drop seq and release its blocks. */
+int pa_bm_free_seq(pa_block_manager* m, int64_t seq);
+/* Roll seq back to `length` (<= its length) tokens, releasing blocks it no
+ * longer needs. */
+int pa_bm_truncate(pa_block_manager* m, int64_t seq, int32_t length);
+int32_t pa_bm_seq_length(const pa_block_manager* m, int64_t seq);
+/* The block count of seq's table; with out != NULL also the table itself
+ * (error if capacity is smaller). */
+int32_t pa_bm_seq_blocks(const pa_block_manager* m, int64_t seq, int32_t* out, int32_t capacity);
+/* Block tables and lengths of a batch, for the attention entry points:
+ * tables int32 [num_seqs, width] (rows padded with `pad`), lengths int32
+ * [num_seqs], both host memory. */
+int pa_bm_build_tables(const pa_block_manager* m, const int64_t* seqs, int32_t num_seqs, int32_t width,
+                       int32_t pad, int32_t* tables, int32_t* lengths);
+/* Prefix cache: full blocks keyed by the whole token prefix that ends with
+ * them, each holding its own reference, in least-recently-used order.
+ * attach: create seq with the longest run of cached full blocks of the
+ * prompt, always leaving at least one prompt token to prefill; returns the
+ * tokens reused (the new length). remember: publish seq's full blocks (its
+ * first num_tokens / b) under the prefixes of `tokens`; returns how many were
+ * new. evict: drop least-recently-used entries that no table holds, until
+ * blocks_wanted blocks are free or no such entry remains; returns the free
+ * count. */
+int32_t pa_bm_prefix_attach(pa_block_manager* m, int64_t seq, const int32_t* tokens, int32_t num_tokens);
+int32_t pa_bm_prefix_remember(pa_block_manager* m, int64_t seq, const int32_t* tokens, int32_t num_tokens);
+int32_t pa_bm_prefix_evict(pa_block_manager* m, int32_t blocks_wanted);
+int32_t pa_bm_prefix_entries(const pa_block_manager* m);
 
 /* pa_check_inputs_host: the preconditions above, checked on host copies.
  *   block_tables : int32 [B, MB] (required)

@@ -18,6 +18,8 @@ Entry points, with the same names as the C ABI:
 * :func:`write_kv_int8`, :func:`decode_int8`, :func:`decode_partitioned_int8`: the int8 KV cache.
 * :func:`write_kv_varlen`, :func:`prefill`: paged (chunked) prefill over packed chunks
   (``pa_write_kv_varlen``, ``pa_prefill``).
+* :mod:`.blocks`: the host block manager (``pa_bm_*``: free list, reference counts, tables with
+  copy-on-write, prefix cache) and :func:`copy_blocks` (``pa_copy_blocks``).
 """
 
 from __future__ import annotations
@@ -44,6 +46,26 @@ EXPORTS = (
     "pa_write_kv_varlen",
     "pa_prefill",
     "pa_check_prefill_host",
+    "pa_copy_blocks",
+    "pa_check_copies_host",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_num_free",
+    "pa_bm_refcount",
+    "pa_bm_num_seqs",
+    "pa_bm_add_seq",
+    "pa_bm_reserve",
+    "pa_bm_commit",
+    "pa_bm_fork",
+    "pa_bm_free_seq",
+    "pa_bm_truncate",
+    "pa_bm_seq_length",
+    "pa_bm_seq_blocks",
+    "pa_bm_build_tables",
+    "pa_bm_prefix_attach",
+    "pa_bm_prefix_remember",
+    "pa_bm_prefix_evict",
+    "pa_bm_prefix_entries",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_abi_version",

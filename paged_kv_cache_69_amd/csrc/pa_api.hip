@@ -222,6 +222,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_INVALID_ARG: return "invalid argument";
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
 }
@@ -367,6 +368,22 @@ int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t*
                                void* workspace, size_t workspace_bytes, pa_stream_t stream) {
   return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, const int32_t* block_pairs, int32_t num_pairs,
+                   pa_stream_t stream) {
+  if (!dims || dims->num_kv_heads < 1 || dims->block_size < 1 || dims->head_dim < 1 || dims->num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_INT8) return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_pairs || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+  const int64_t row = (int64_t)dims->head_dim * (dims->kv_dtype == PA_F32 ? 4 : dims->kv_dtype == PA_BF16 ? 2 : 1);
+  if ((row * dims->block_size * dims->num_kv_heads) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int chk = pa::debug_check_copies(dims, block_pairs, num_pairs, s);
+  if (chk != PA_OK) return chk;
+  return launch_status(pa::launch_copy_blocks(*dims, k_pool, v_pool, block_pairs, num_pairs, s));
 }
 
 int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,

@@ -81,7 +81,33 @@ extern "C" int pa_check_prefill_host(const pa_dims* dims, const int32_t* block_t
   return PA_OK;
 }
 
+extern "C" int pa_check_copies_host(const pa_dims* dims, const int32_t* pairs, int32_t num_pairs) {
+  if (!dims_ok(dims) || num_pairs < 0 || (num_pairs > 0 && !pairs)) return PA_ERR_INVALID_ARG;
+  std::vector<int32_t> dsts, srcs;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= dims->num_blocks || d < 0 || d >= dims->num_blocks) return PA_ERR_INVALID_ARG;
+    srcs.push_back(s);
+    dsts.push_back(d);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end()) return PA_ERR_INVALID_ARG;
+  for (const int32_t s : srcs)
+    if (std::binary_search(dsts.begin(), dsts.end(), s)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 namespace pa {
+
+int debug_check_copies(const pa_dims* dims, const int32_t* pairs, int32_t num_pairs, hipStream_t stream) {
+  const char* env = getenv("PA_CHECK");
+  if (!env || strcmp(env, "1") != 0) return PA_OK;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone) return PA_OK;
+  std::vector<int32_t> host;
+  if (!copy_to_host(host, pairs, 2 * (int64_t)num_pairs, stream)) return PA_ERR_LAUNCH;
+  return pa_check_copies_host(dims, host.data(), num_pairs);
+}
 
 int debug_check_prefill(const pa_dims* dims, const int32_t* block_tables, const int32_t* seq_lens,
                         const int32_t* q_start, hipStream_t stream) {

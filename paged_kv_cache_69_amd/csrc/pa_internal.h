@@ -73,6 +73,12 @@ int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one ca
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
 
+// Copy-on-write block copies: pairs [n, 2] (source, destination) on the device.
+hipError_t launch_copy_blocks(const pa_dims& d, void* k_pool, void* v_pool, const int32_t* pairs, int32_t num_pairs,
+                              hipStream_t stream);
+// PA_CHECK=1: every pair in [0, num_blocks), destinations distinct and never a source.
+int debug_check_copies(const pa_dims* dims, const int32_t* pairs, int32_t num_pairs, hipStream_t stream);
+
 // Paged prefill (packed chunks, q_start offsets): bf16 q/KV, head_dim 128, G <= 128, b in {4, 8, 16, 32}.
 bool prefill_supported(const pa_dims& d);
 hipError_t launch_prefill(const pa_dims& d, const void* q, const void* k_pool, const void* v_pool,
