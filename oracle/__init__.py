@@ -16,7 +16,8 @@ blocking, fusion or online recurrence. The pages are:
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle.py``, ``tests/test_oracle_int8.py``,
-``tests/test_oracle_prefill.py`` or ``tests/test_oracle_blocks.py``, which checks it
+``tests/test_oracle_prefill.py``, ``tests/test_oracle_blocks.py`` or
+``tests/test_oracle_fp8.py``, which checks it
 against something other than itself:
 the pages' worked examples, a library routine, closed forms, invariants or
 brute force. No function is "parity unpinned".
@@ -28,6 +29,15 @@ from .pa_oracle_int8 import (  # noqa: F401
     decode_row_int8,
     dequantize_pool,
     quantize_block,
+)
+from .pa_oracle_fp8 import (  # noqa: F401
+    append_fp8,
+    decode_fp8,
+    decode_row_fp8,
+    dequantize_pool_fp8,
+    e4m3_values,
+    encode_e4m3,
+    quantize_block_fp8,
 )
 from .pa_oracle_blocks import BlockPool, PagedCache, PoolExhausted, PrefixCache  # noqa: F401
 from .pa_oracle_prefill import chunk_positions, prefill, prefill_row, write_kv_varlen  # noqa: F401
