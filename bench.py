@@ -73,6 +73,11 @@ WORKLOADS = {
                          desc="batch64 with int8 K/V pools + per-(block, kv head) scales, bf16 q"),
     "long_int8": dict(partition_tokens=512, base="long", int8=True,
                       desc="long with int8 K/V pools + per-(block, kv head) scales, bf16 q, 512-token partitions"),
+    # FP8 (E4M3) KV pools, same shapes and lengths
+    "batch64_fp8": dict(partition_tokens=None, base="batch64", fp8=True,
+                        desc="batch64 with FP8 E4M3 K/V pools + per-(block, kv head) scales, bf16 q"),
+    "long_fp8": dict(partition_tokens=512, base="long", fp8=True,
+                     desc="long with FP8 E4M3 K/V pools + per-(block, kv head) scales, bf16 q, 512-token partitions"),
     # paged (chunked) prefill: a step is one pa_write_kv_varlen + one pa_prefill call
     "prefill": dict(partition_tokens=None, kind="prefill",
                     desc="16 seqs, chunks of U[512,2048] new tokens after paged histories of U[0,4096], 32 q / 8 kv "
@@ -200,7 +205,7 @@ class Replica:
                            p["block_tables"], p["positions"])
         self.dec_args = (ctypes.byref(self.dims), p["q"], p["k_pool"], p["v_pool"], *scales, p["block_tables"],
                          p["seq_lens"], self.scale)
-        sfx = "_int8" if self.int8 else ""
+        sfx = ("_fp8" if case.k_pool.dtype == torch.float8_e4m3fn else "_int8") if self.int8 else ""
         self.f_write = getattr(self.lib, "pa_write_kv" + sfx)
         self.f_decode = getattr(self.lib, "pa_decode" + sfx)
         self.f_split = getattr(self.lib, "pa_decode_partitioned" + sfx)
@@ -623,7 +628,7 @@ def run_copy_workload(pa, name, steps, warmup, graphs=True):
 def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True, fused=True):
     import torch
 
-    from workloads import int8_pools, make_case
+    from workloads import fp8_pools, int8_pools, make_case
 
     spec = WORKLOADS[name]
     if spec.get("kind") == "prefill":
@@ -633,9 +638,12 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     case = make_case(spec.get("base", name), pool_device="cuda:0")
     if spec.get("int8"):
         case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
+    if spec.get("fp8"):
+        case.k_pool, case.k_scales, case.v_pool, case.v_scales = fp8_pools(case)
     b, t = case.q.shape[0], case.q.shape[1]
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
-    mfma_ok = case.k_pool.dtype in (torch.bfloat16, torch.int8) and case.q.shape[3] == 128 and rows <= 32
+    mfma_ok = (case.k_pool.dtype in (torch.bfloat16, torch.int8, torch.float8_e4m3fn) and case.q.shape[3] == 128
+               and rows <= 32)
     fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok and case.k_pool.dtype == torch.bfloat16
     cascade = spec.get("cascade", 0) if variant != 1 else 0
     sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs,
@@ -649,8 +657,8 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     if fused:
         kernel += " with the KV append fused in"
     call = ("pa_write_kv_decode" if fused else "pa_decode") + ("_partitioned" if spec["partition_tokens"] else "")
-    if "int8" in name:
-        call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + "_int8"
+    if spec.get("int8") or spec.get("fp8"):
+        call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + ("_fp8" if spec.get("fp8") else "_int8")
     if cascade:
         call = "pa_decode_cascade"
         kernel = "decode_mfma_kernel (shared-prefix items + per-sequence items)"
@@ -669,7 +677,8 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
                    "partition_tokens": spec["partition_tokens"], "replicas": n_rep,
                    **({"shared_prefix_tokens": cascade} if cascade else {}),
                    "step": "one fused append + decode call" if fused else "append call + decode call"},
-        "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
+        "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)",
+                  torch.float8_e4m3fn: "fp8 e4m3 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
     }
     if name == "prefix":
         res["unique_bytes"] = unique_bytes(case)
@@ -791,7 +800,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,prefill,cow_copy",
+    ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,batch64_fp8,long_fp8,prefill,"
+                                           "cow_copy",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")

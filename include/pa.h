@@ -62,9 +62,10 @@ typedef enum {
   PA_ERR_NO_BLOCKS = -4    /* block manager: the pool has too few free blocks (nothing changed) */
 } pa_status;
 
-/* PA_INT8 is a pool dtype only: int8 codes with one fp32 scale per
- * (block, kv head), used by the *_int8 entry points. */
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
+/* PA_INT8 and PA_FP8_E4M3 are pool dtypes only: 8-bit codes (int8
+ * integers, or OCP E4M3 floats) with one fp32 scale per (block, kv head),
+ * used by the *_int8 and *_fp8 entry points. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Kernel choice for the attention entry points. PA_VARIANT_AUTO picks the
  * fastest kernel this library has for the shape. The other values force one
@@ -406,6 +407,29 @@ int32_t pa_bm_prefix_attach(pa_block_manager* m, int64_t seq, const int32_t* tok
 int32_t pa_bm_prefix_remember(pa_block_manager* m, int64_t seq, const int32_t* tokens, int32_t num_tokens);
 int32_t pa_bm_prefix_evict(pa_block_manager* m, int32_t blocks_wanted);
 int32_t pa_bm_prefix_entries(const pa_block_manager* m);
+
+/* ---- FP8 KV cache: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite 448, NaN at S.1111.111) with one fp32 scale
+ * per (block, kv head), the format [P2] section 6 names beside int8 (and
+ * [P1] "Attention that reads through the table" among what production paged
+ * kernels add). Same shapes, rules and supported shapes as the int8 entry
+ * points, with kv_dtype PA_FP8_E4M3 and these differences:
+ *   scale = max |x| / 448 (float32); code = E4M3(x / scale), the quotient in
+ *   float32, rounded to the nearest E4M3 value with ties to the even code,
+ *   saturated at +-448 (a value that rounds to zero keeps its sign);
+ *   re-encoding on a scale increase uses (value(code) * old_scale) / new_scale;
+ *   decode attends over value(code) * scale. */
+int pa_write_kv_fp8(const pa_dims* dims, const void* k_new, const void* v_new, uint8_t* k_pool,
+                    uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                    const int32_t* positions, pa_stream_t stream);
+int pa_decode_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                  const int32_t* seq_lens, float scale, void* out, pa_stream_t stream);
+int pa_decode_partitioned_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool,
+                              const uint8_t* v_pool, const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              void* out, int32_t max_seq_len, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /* pa_check_inputs_host: the preconditions above, checked on host copies.
  *   block_tables : int32 [B, MB] (required)

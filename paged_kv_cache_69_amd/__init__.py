@@ -29,7 +29,7 @@ import os
 
 from ._build import LIB_PATH
 
-PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
+PA_F32, PA_BF16, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 EXPORTS = (
     "pa_write_kv",
@@ -43,6 +43,9 @@ EXPORTS = (
     "pa_write_kv_int8",
     "pa_decode_int8",
     "pa_decode_partitioned_int8",
+    "pa_write_kv_fp8",
+    "pa_decode_fp8",
+    "pa_decode_partitioned_fp8",
     "pa_write_kv_varlen",
     "pa_prefill",
     "pa_check_prefill_host",
@@ -132,6 +135,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
                                                _P, ctypes.c_size_t, _P]
     lib.pa_decode_partitioned_int8.restype = ctypes.c_int
+    for suffix in ("write_kv", "decode", "decode_partitioned"):  # the FP8 entry points mirror the int8 ones
+        src, dst = getattr(lib, f"pa_{suffix}_int8"), getattr(lib, f"pa_{suffix}_fp8")
+        dst.argtypes, dst.restype = src.argtypes, src.restype
     lib.pa_write_kv_varlen.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.pa_write_kv_varlen.restype = ctypes.c_int
     lib.pa_prefill.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
@@ -165,6 +171,8 @@ def dtype_code(dtype) -> int:
         return PA_BF16
     if dtype == torch.int8:
         return PA_INT8
+    if dtype == torch.float8_e4m3fn:
+        return PA_FP8_E4M3
     raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16 (int8 for quantised pools)")
 
 
@@ -357,23 +365,31 @@ def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, sca
     return out
 
 
-# ----------------------------------------------------------------------------- int8 pools
+# ----------------------------------------------------------------------------- 8-bit pools (int8, FP8)
+
+def _q8_format(k_pool, fmt: str):
+    import torch
+
+    if fmt == "int8":
+        _require(k_pool.dtype == torch.int8, "int8 entry points take int8 pools")
+        return PA_INT8
+    _require(k_pool.dtype in (torch.float8_e4m3fn, torch.uint8), "fp8 entry points take float8_e4m3fn (or uint8) pools")
+    return PA_FP8_E4M3
+
 
 def _check_scales(k_pool, k_scales, v_scales):
     import torch
 
-    _require(k_pool.dtype == torch.int8, "int8 entry points take int8 pools")
     want = tuple(k_pool.shape[:2])
     _require(tuple(k_scales.shape) == want and tuple(v_scales.shape) == want, "scales must be [N, Hkv]")
     _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32, "scales must be float32")
 
 
-def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
-    """``pa_write_kv_int8``: append ``k_new``/``v_new [B, T, Hkv, D]`` (bf16 or fp32) into int8 pools
-    ``[N, Hkv, b, D]`` with per-(block, kv head) scales ``[N, Hkv]`` (updated in place)."""
+def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream):
     import torch
 
     lib = load_library()
+    kv_code = _q8_format(k_pool, fmt)
     dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales,
                          v_scales=v_scales, block_tables=block_tables, positions=positions)
     _check_scales(k_pool, k_scales, v_scales)
@@ -383,60 +399,89 @@ def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables
     _require(positions.shape == (bsz, t), "positions must be [B, T]")
     _require(k_pool.shape[1] == hkv and k_pool.shape[3] == d, "pool and new rows disagree")
     code = dtype_code(k_new.dtype)
-    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, PA_INT8,
+    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, kv_code,
                   code, 0)
-    st = lib.pa_write_kv_int8(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
-                              v_pool.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
-                              positions.data_ptr(), _stream_handle(stream, dev))
-    _check(lib, "pa_write_kv_int8", st)
+    func = "pa_write_kv_int8" if fmt == "int8" else "pa_write_kv_fp8"
+    st = getattr(lib, func)(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                            v_pool.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
+                            positions.data_ptr(), _stream_handle(stream, dev))
+    _check(lib, func, st)
+
+
+def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype, stream,
+               split=None):
+    import torch
+
+    lib = load_library()
+    kv_code = _q8_format(k_pool, fmt)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
+                   block_tables=block_tables, seq_lens=seq_lens, out=out)
+    if split is not None:
+        max_seq_len, partition_tokens, workspace = split
+        if workspace is None:
+            need = workspace_bytes(q, k_pool.view(torch.int8), block_tables, max_seq_len, partition_tokens)
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        tensors["workspace"] = workspace
+    dev = _check_tensors(**tensors)
+    _check_scales(k_pool, k_scales, v_scales)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool.view(torch.int8), block_tables, out_dtype=out.dtype)
+    dims.kv_dtype = kv_code
+    args = [ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scales.data_ptr(),
+            v_scales.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
+    if split is None:
+        func = "pa_decode_int8" if fmt == "int8" else "pa_decode_fp8"
+        st = getattr(lib, func)(*args, _stream_handle(stream, dev))
+    else:
+        func = "pa_decode_partitioned_int8" if fmt == "int8" else "pa_decode_partitioned_fp8"
+        st = getattr(lib, func)(*args, int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(lib, func, st)
+    return out
+
+
+def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
+    """``pa_write_kv_int8``: append ``k_new``/``v_new [B, T, Hkv, D]`` (bf16 or fp32) into int8 pools
+    ``[N, Hkv, b, D]`` with per-(block, kv head) scales ``[N, Hkv]`` (updated in place)."""
+    _write_kv_q8("int8", k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream)
 
 
 def decode_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float, out=None, *,
                 out_dtype=None, stream=None):
     """``pa_decode_int8``: decode over int8 pools; returns ``out [B, T, Hq, D]`` (fp32 by default)."""
-    import torch
-
-    lib = load_library()
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
-                         block_tables=block_tables, seq_lens=seq_lens, out=out)
-    _check_scales(k_pool, k_scales, v_scales)
-    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
-    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
-    st = lib.pa_decode_int8(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                            k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(),
-                            float(scale), out.data_ptr(), _stream_handle(stream, dev))
-    _check(lib, "pa_decode_int8", st)
-    return out
+    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream)
 
 
 def decode_partitioned_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
                             max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
                             stream=None):
     """``pa_decode_partitioned_int8``: split-context decode + merge over int8 pools."""
-    import torch
+    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream, (max_seq_len, partition_tokens, workspace))
 
-    lib = load_library()
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
-                         block_tables=block_tables, seq_lens=seq_lens, out=out, workspace=workspace)
-    _check_scales(k_pool, k_scales, v_scales)
-    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
-    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
-    st = lib.pa_decode_partitioned_int8(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                                        k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
-                                        seq_lens.data_ptr(), float(scale), out.data_ptr(), int(max_seq_len),
-                                        int(partition_tokens), workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
-    _check(lib, "pa_decode_partitioned_int8", st)
-    return out
+
+def write_kv_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
+    """``pa_write_kv_fp8``: append into E4M3 pools (``torch.float8_e4m3fn`` or their uint8 bits)."""
+    _write_kv_q8("fp8", k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream)
+
+
+def decode_fp8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float, out=None, *,
+               out_dtype=None, stream=None):
+    """``pa_decode_fp8``: decode over E4M3 pools; returns ``out [B, T, Hq, D]`` (fp32 by default)."""
+    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream)
+
+
+def decode_partitioned_fp8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
+                           max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                           stream=None):
+    """``pa_decode_partitioned_fp8``: split-context decode + merge over E4M3 pools."""
+    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream, (max_seq_len, partition_tokens, workspace))
 
 
 # ----------------------------------------------------------------------------- paged prefill

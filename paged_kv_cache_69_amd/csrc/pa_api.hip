@@ -38,11 +38,11 @@ int check_dims(const pa_dims* d) {
   return PA_OK;
 }
 
-// int8 pools: kv dtype PA_INT8; q (and new rows) and out PA_F32 / PA_BF16.
-int check_dims_int8(const pa_dims* d) {
+// 8-bit pools: kv dtype PA_INT8 or PA_FP8_E4M3 (kv8); q (and new rows) and out PA_F32 / PA_BF16.
+int check_dims_int8(const pa_dims* d, int32_t kv8 = PA_INT8) {
   const int st = check_shape(d);
   if (st != PA_OK) return st;
-  if (d->kv_dtype != PA_INT8 || !valid_dtype(d->q_dtype) || !valid_dtype(d->out_dtype)) return PA_ERR_INVALID_ARG;
+  if (d->kv_dtype != kv8 || !valid_dtype(d->q_dtype) || !valid_dtype(d->out_dtype)) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -151,9 +151,9 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
                  const float* k_scales, const float* v_scales, const int32_t* block_tables, const int32_t* seq_lens,
                  float scale, void* out, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                  size_t workspace_bytes, pa_stream_t stream, const void* k_new = nullptr,
-                 const void* v_new = nullptr) {
+                 const void* v_new = nullptr, bool fp8 = false) {
   const bool append = k_new != nullptr || v_new != nullptr;
-  int st = int8 ? check_dims_int8(dims) : check_dims(dims);
+  int st = int8 ? check_dims_int8(dims, fp8 ? PA_FP8_E4M3 : PA_INT8) : check_dims(dims);
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
@@ -189,6 +189,7 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   p.k_scales = k_scales;
   p.v_scales = v_scales;
   p.kv_int8 = int8 ? 1 : 0;
+  p.kv_fp8 = int8 && fp8 ? 1 : 0;
   p.k_new = k_new;
   p.v_new = v_new;
   p.append = append ? 1 : 0;
@@ -337,10 +338,13 @@ int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, co
   return launch_status(pa::launch_merge_partials(p, s));
 }
 
-int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
-                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                     const int32_t* positions, pa_stream_t stream) {
-  const int st = check_dims_int8(dims);
+}  // extern "C"
+
+namespace {
+int write_kv_q8(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                float* k_scales, float* v_scales, const int32_t* block_tables, const int32_t* positions, bool fp8,
+                pa_stream_t stream) {
+  const int st = check_dims_int8(dims, fp8 ? PA_FP8_E4M3 : PA_INT8);
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !k_scales || !v_scales || !block_tables || !positions)
@@ -350,8 +354,40 @@ int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, 
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
   if (chk != PA_OK) return chk;
-  return launch_status(pa::launch_write_kv_int8(*dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales,
-                                                block_tables, positions, s));
+  return launch_status(pa::launch_write_kv_int8(*dims, k_new, v_new, static_cast<int8_t*>(k_pool),
+                                                static_cast<int8_t*>(v_pool), k_scales, v_scales, block_tables,
+                                                positions, fp8, s));
+}
+}  // namespace
+
+extern "C" {
+
+int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
+                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                     const int32_t* positions, pa_stream_t stream) {
+  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, false, stream);
+}
+
+int pa_write_kv_fp8(const pa_dims* dims, const void* k_new, const void* v_new, uint8_t* k_pool,
+                    uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                    const int32_t* positions, pa_stream_t stream) {
+  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, true, stream);
+}
+
+int pa_decode_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                  const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
+  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream, nullptr, nullptr, true);
+}
+
+int pa_decode_partitioned_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool,
+                              const uint8_t* v_pool, const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              void* out, int32_t max_seq_len, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
+                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream, nullptr, nullptr, true);
 }
 
 int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,

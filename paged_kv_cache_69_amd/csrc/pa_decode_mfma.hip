@@ -168,6 +168,13 @@ __device__ __forceinline__ u32x2 codes_to_bf16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
+// Four E4M3 codes (one dword) -> two dwords of bf16, exactly: every E4M3 value is a bf16 value
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1; bytes 0-1, then bytes 2-3).
+__device__ __forceinline__ u32x2 fp8_to_bf16(uint32_t w) {
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
 constexpr float kKOffset = 1152.f;  // fp16 K code value minus the code
 constexpr float kVOffset = 128.f;   // bf16 V code value minus the code
 
@@ -191,11 +198,12 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
   static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
+  static_assert(!F8 || Q8, "FP8 pools are 8-bit pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
   constexpr int kKvTile = kTile * kKvRow;
   constexpr int ROWS = 16 * MT;
@@ -254,7 +262,15 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     row_tok[mt] = rr / p.G;
     const char* qrow =
         static_cast<const char*>(p.q) + ((int64_t)(rs * T + row_tok[mt]) * p.Hq + kvh * p.G + rr % p.G) * kRowBytes;
-    if constexpr (Q8) {
+    if constexpr (F8) {
+      // lane (g, c16): head_dim 32g .. 32g+31 of the row, bf16 as stored; operand kc = 32g + 8kc .. +7
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 v = load16(qrow + 64 * g + 16 * kc);
+        qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      qsum[mt] = 0.f;
+    } else if constexpr (Q8) {
       // lane (g, c16): head_dim 32g .. 32g+31 of the row, as fp16; operand kc = 32g + 8kc .. +7
       u32x4 raw[4];
 #pragma unroll
@@ -421,20 +437,26 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 
   // S^T of one tile (C layout: lane l has positions 4g + e of score row c16 + 16*mt), scaled and masked.
   auto scores = [&](bool masked, int tile_p0, const TileRegs& tr, float kscale, f32x4 (&s)[MT]) {
-    u32x4 kf[4];  // int8 pools: the K codes as fp16 operands
+    u32x4 kf[4];  // 8-bit pools: the K codes as fp16 (int8) or bf16 (FP8) operands
     if constexpr (Q8) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
         const int j = 2 * kc;  // dwords j, j + 1 of the lane's 32 code bytes
-        const u32x2 a = codes_to_f16(tr.k[j >> 2][j & 3]);
-        const u32x2 b = codes_to_f16(tr.k[(j + 1) >> 2][(j + 1) & 3]);
+        const uint32_t w0 = tr.k[j >> 2][j & 3], w1 = tr.k[(j + 1) >> 2][(j + 1) & 3];
+        const u32x2 a = F8 ? fp8_to_bf16(w0) : codes_to_f16(w0);
+        const u32x2 b = F8 ? fp8_to_bf16(w1) : codes_to_f16(w1);
         kf[kc] = u32x4{a[0], a[1], b[0], b[1]};
       }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (Q8) {
+      if constexpr (F8) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
+        s[mt] = c * (kscale * p.qk_scale_log2);
+      } else if constexpr (Q8) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(kf[kc]), as_f16x8(qb[mt][kc]), c, 0, 0, 0);
@@ -478,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
         l_part[mt] += pr[e];
         if constexpr (Q8) {
           pr[e] *= vscale;  // from here on P carries the block's V scale
-          vcorr[mt] += pr[e];
+          if constexpr (!F8) vcorr[mt] += pr[e];
         }
       }
       const uint32_t h01 = cvt_pk_bf16(pr[0], pr[1]);
@@ -490,12 +512,14 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
     }
 
     if constexpr (Q8) {
-      // V codes of row lane/4, head_dim 32 (lane%4) .. +31, as bf16 128 + code, into the LDS tile
+      // V codes of row lane/4, head_dim 32 (lane%4) .. +31, as bf16 (int8: 128 + code; FP8: its value),
+      // into the LDS tile
       const int t = lane >> 2;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x2 a = codes_to_bf16(tr.v[c >> 1][2 * (c & 1)]);
-        const u32x2 b = codes_to_bf16(tr.v[c >> 1][2 * (c & 1) + 1]);
+        const uint32_t w0 = tr.v[c >> 1][2 * (c & 1)], w1 = tr.v[c >> 1][2 * (c & 1) + 1];
+        const u32x2 a = F8 ? fp8_to_bf16(w0) : codes_to_bf16(w0);
+        const u32x2 b = F8 ? fp8_to_bf16(w1) : codes_to_bf16(w1);
         const u32x4 w = {a[0], a[1], b[0], b[1]};
         *(lds_u32x4*)(vt + v_swz(t, 64 * (lane & 3) + 16 * c)) = w;
       }
@@ -635,7 +659,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   while (!run()) {
   }
 
-  if constexpr (Q8) {
+  if constexpr (Q8 && !F8) {
     // remove the V offset: accumulator row 4g + e (+16 mt) held 128 * sum(scaled P) of that row too
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -721,7 +745,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   }
 }
 
-template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false>
+template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false, bool F8 = false>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t item_parts =
       !WI ? 1 : CAS ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens : p.parts - p.prefix_parts;
@@ -730,13 +754,20 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t grid = units * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
   constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
-  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS>
+  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS, F8>
       <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
 template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_int8 && p.kv_fp8) {
+    switch (p.block_size) {
+      case 16: return launch_t<MT, 16, WI, true, false, false, true>(p, stream);
+      case 32: return launch_t<MT, 32, WI, true, false, false, true>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (p.kv_int8) {
     switch (p.block_size) {
       case 16: return launch_t<MT, 16, WI, true, false>(p, stream);
@@ -772,7 +803,7 @@ bool mfma_supported(const pa_dims& d) {
 
 bool mfma_int8_supported(const pa_dims& d) {
   const int rows = d.q_tokens * (d.num_q_heads / d.num_kv_heads);
-  return d.kv_dtype == PA_INT8 && d.q_dtype == PA_BF16 && d.head_dim == kD &&
+  return (d.kv_dtype == PA_INT8 || d.kv_dtype == PA_FP8_E4M3) && d.q_dtype == PA_BF16 && d.head_dim == kD &&
          (d.block_size == 16 || d.block_size == 32) && rows <= 32;
 }
 

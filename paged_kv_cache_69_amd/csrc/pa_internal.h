@@ -33,7 +33,8 @@ struct DecodeParams {
   int32_t part_tokens;       // positions per partition (single pass: >= every length)
   int32_t out_dtype;         // pa_dtype of out
   int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
-  int32_t kv_int8;           // 1: the pools hold int8 codes scaled by k_scales / v_scales
+  int32_t kv_int8;           // 1: the pools hold 8-bit codes scaled by k_scales / v_scales
+  int32_t kv_fp8;            // with kv_int8: the codes are E4M3 values (else int8 integers)
   int32_t append;            // 1: also store k_new / v_new into the pools (MFMA kernel, bf16)
   int32_t prefix_tokens;     // cascade: positions every sequence shares (0: none)
   int32_t prefix_parts;      // cascade: workspace slots 0 .. prefix_parts-1 hold the prefix's partials
@@ -45,9 +46,10 @@ hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_ne
                            void* v_pool, const int32_t* block_tables, const int32_t* positions,
                            hipStream_t stream);
 
+// 8-bit pools (int8 or, with fp8, E4M3 codes): append with per-(block, kv head) scales.
 hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
                                 int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                                const int32_t* positions, hipStream_t stream);
+                                const int32_t* positions, bool fp8, hipStream_t stream);
 
 // Rows handled by one VALU workgroup for `rows` query rows per kv head.
 int valu_rows_per_group(int rows);
@@ -65,7 +67,7 @@ int debug_check_prefix(const pa_dims* dims, const int32_t* block_tables, const i
                        int32_t prefix_tokens, hipStream_t stream);
 
 bool mfma_supported(const pa_dims& d);       // bf16 pools
-bool mfma_int8_supported(const pa_dims& d);  // int8 pools
+bool mfma_int8_supported(const pa_dims& d);  // 8-bit pools (int8 or E4M3)
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 // Cascade: the shared prefix's partitions for all sequences' rows at once (slots 0 .. prefix_parts-1).
 hipError_t launch_cascade_prefix(const DecodeParams& p, hipStream_t stream);

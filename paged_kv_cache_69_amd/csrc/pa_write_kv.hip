@@ -78,7 +78,48 @@ __device__ __forceinline__ int quantise(float x, float scale) {
   return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);
 }
 
+// E4M3 (OCP: 4 exponent bits, bias 7, 3 mantissa bits, largest finite 448) code of a float32 y,
+// rounded to the nearest value with ties to the even code, saturated at +-448; the sign bit is y's.
+// Below 2^-6 the values are the multiples of 2^-9, so y * 512 rounded is the code itself (8 is the
+// smallest normal, 0x08); above, the top 3 mantissa bits are rounded on the other 20, and a carry
+// out of the mantissa steps the exponent, which the code's layout does by itself.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t m = (bits >> 20) & 7u, rest = bits & 0xFFFFFu;
+    code = ((((bits >> 23) - 120u) << 3) | m) + ((rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ? 1u : 0u);
+    code = min(code, 126u);
+  }
+  return code | sign;
+}
+
+// Value of an E4M3 code (exact in float32).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (code & 0x80u) ? -v : v;
+}
+
+// One code of an 8-bit pool: int8 (x / scale rounded to an integer) or E4M3.
+template <bool FP8>
+__device__ __forceinline__ uint32_t encode_code(float x, float scale) {
+  if constexpr (FP8) return scale == 0.f ? 0u : e4m3_encode(x / scale);
+  return (uint32_t)(uint8_t)quantise(x, scale);
+}
+template <bool FP8>
+__device__ __forceinline__ float code_value(uint32_t byte) {
+  if constexpr (FP8) return e4m3_value(byte);
+  return (float)(int8_t)byte;
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Params p) {
+  constexpr float kCodeMax = FP8 ? 448.f : 127.f;  // largest code magnitude: scale = max|x| / kCodeMax
   const int lane = threadIdx.x & 63;
   const int which = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, 1: V
   const int kvh = blockIdx.x % p.Hkv;
@@ -101,7 +142,7 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
         for (int d = lane; d < D; d += 64) a = fmaxf(a, fabsf(new_value(p, src, base + d)));
       }
       a = wave_max(a);
-      const float cand = a / 127.f;
+      const float cand = a / kCodeMax;
       float* sp = scales + (int64_t)blk * p.Hkv + kvh;
       const float old = first > 0 ? *sp : 0.f;
       const float scale = first > 0 ? fmaxf(old, cand) : cand;
@@ -113,8 +154,8 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
           uint32_t out = 0;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const float c = (float)(int8_t)(c4 >> (8 * k));
-            out |= (uint32_t)(uint8_t)quantise(c * old, scale) << (8 * k);
+            const float c = code_value<FP8>((c4 >> (8 * k)) & 0xFFu);
+            out |= encode_code<FP8>(c * old, scale) << (8 * k);
           }
           words[w] = out;
         }
@@ -126,7 +167,7 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
           uint32_t out = 0;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            out |= (uint32_t)(uint8_t)quantise(new_value(p, src, base + 4 * w + k), scale) << (8 * k);
+            out |= encode_code<FP8>(new_value(p, src, base + 4 * w + k), scale) << (8 * k);
           words[w] = out;
         }
       }
@@ -140,7 +181,7 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
 
 hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
                                 int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                                const int32_t* positions, hipStream_t stream) {
+                                const int32_t* positions, bool fp8, hipStream_t stream) {
   WriteInt8Params p;
   p.k_new = k_new;
   p.v_new = v_new;
@@ -158,7 +199,10 @@ hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void*
   p.new_f32 = d.q_dtype == PA_F32;
   const int64_t grid = (int64_t)d.num_seqs * d.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  write_kv_int8_kernel<<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+  if (fp8)
+    write_kv_int8_kernel<true><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+  else
+    write_kv_int8_kernel<false><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
   return hipGetLastError();
 }
 

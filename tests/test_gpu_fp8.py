@@ -1,0 +1,200 @@
+"""Parity of the FP8 (E4M3) KV path (pa_write_kv_fp8, pa_decode_fp8, pa_decode_partitioned_fp8)
+against the FP8 oracle, on the GPU.
+
+Codes and scales written by the append must match the oracle bit for bit (both decide every code in
+float32 with the same operations). Attention over FP8 pools must be within the bf16 bar (2e-3
+absolute) of the oracle's float64 attention over the dequantised values. Inputs come from the seeded
+generators in workloads/; nothing expected comes from the GPU.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import assert_attention_close
+from workloads import build_case, fp8_pools, make_case
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _bits(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy()
+    return t.view(torch.uint8).numpy() if t.dtype == torch.float8_e4m3fn else t.numpy()
+
+
+def _np(pools):
+    """(k codes uint8, k scales, v codes uint8, v scales) as numpy arrays for the oracle."""
+    return [p.cpu().view(torch.uint8).numpy() if p.dtype == torch.float8_e4m3fn else p.cpu().numpy() for p in pools]
+
+
+def _gpu(*ts):
+    return [t.to(DEV, copy=True) for t in ts]
+
+
+def _write(pa, g):
+    """g = [k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_tables, positions] on the GPU."""
+    pa.write_kv_fp8(g[0], g[1], g[2], g[4], g[3], g[5], g[6], g[7])
+
+
+def _append_ref(case, pools, k_new, v_new):
+    kc, ks, vc, vs = _np(pools)
+    return oracle.append_fp8(kc, ks, vc, vs, k_new.float().numpy(), v_new.float().numpy(),
+                              case.block_tables.numpy(), case.positions.numpy(), case.block_size)
+
+
+def _decode_ref(case, pools):
+    kc, ks, vc, vs = _np(pools)
+    return oracle.decode_fp8(case.q.float().numpy(), kc, ks, vc, vs, case.block_tables.numpy(),
+                              case.seq_lens.numpy(), case.scale, case.block_size)
+
+
+# ----------------------------------------------------------------------------- append
+
+@pytest.mark.parametrize("b,t,dtype,hkv", [(16, 1, torch.bfloat16, 8), (16, 4, torch.bfloat16, 2),
+                                           (32, 1, torch.bfloat16, 4), (32, 4, torch.float32, 2),
+                                           (16, 3, torch.float32, 1)])
+def test_write_kv_fp8_bit_exact(gpu_lib, b, t, dtype, hkv):
+    """Lengths put the new rows at offset 0 of a fresh block, in the middle of a block, and (T > 1)
+    across two blocks; every other sequence's new rows are 20x larger, so their block's scale grows
+    and its old codes are re-quantised."""
+    lengths = sorted({max(t, x) for x in (1, b - 1, b, b + 1, 2 * b + 2, 3 * b, 70, 100, 257)})
+    case = build_case(lengths=lengths, num_q_heads=hkv * 2, num_kv_heads=hkv, head_dim=128, block_size=b,
+                      q_tokens=t, dtype=dtype, seed=300 + b + t, pool_slack=0.3)
+    case.k_new[::2] *= 20
+    case.v_new[1::2] *= 20
+    print(f"[case] fp8 append b={b} T={t} {dtype} Hkv={hkv} lengths={lengths}", flush=True)
+    pools = fp8_pools(case, seed=b * 10 + t)
+    g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
+    _write(gpu_lib, g)
+    torch.cuda.synchronize()
+    ref = _append_ref(case, pools, case.k_new, case.v_new)
+    for name, got, want in zip(("k codes", "k scales", "v codes", "v scales"), g[2:6], ref):
+        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want), name
+
+
+# ----------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("b", [16, 32])
+@pytest.mark.parametrize("hq,hkv,t", [(4, 1, 1), (32, 8, 1), (8, 2, 4), (64, 8, 4), (16, 2, 1), (12, 4, 3)])
+def test_decode_fp8_shapes(gpu_lib, b, hq, hkv, t):
+    """GQA groups 1-8, 1-4 causal query tokens (up to 32 rows per kv head), lengths at tile and block
+    boundaries, single pass and with 32/48/64-position partitions."""
+    lengths = sorted({max(t, x) for x in (1, 15, 16, 17, b - 1, b + 1, 47, 100, 257)})
+    case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b,
+                      q_tokens=t, dtype=torch.bfloat16, seed=500 + b + hq + t, pool_slack=0.2)
+    pools = fp8_pools(case, seed=hq * 7 + t)
+    ref = _decode_ref(case, pools)
+    q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
+    kc, ks, vc, vs = _gpu(*pools)
+    print(f"[case] fp8 decode b={b} hq={hq} hkv={hkv} T={t}", flush=True)
+    out = gpu_lib.decode_fp8(q, kc, vc, ks, vs, tables, lens, case.scale)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what="single pass")
+    for pt in (32, 48 if 48 % b == 0 else 64):
+        out = gpu_lib.decode_partitioned_fp8(q, kc, vc, ks, vs, tables, lens, case.scale, case.max_seq_len, pt)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what=f"split {pt}")
+
+
+def test_decode_fp8_bf16_output(gpu_lib):
+    case = make_case("batch64", num_seqs=6)
+    pools = fp8_pools(case, seed=5)
+    ref = _decode_ref(case, pools)
+    q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
+    kc, ks, vc, vs = _gpu(*pools)
+    out = gpu_lib.decode_fp8(q, kc, vc, ks, vs, tables, lens, case.scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.bfloat16, what="bf16 out")
+
+
+def test_append_then_decode_step(gpu_lib):
+    """One whole FP8 decode step (append the new token, then attend) against the oracle's step."""
+    case = make_case("batch64", num_seqs=12)
+    pools = fp8_pools(case, seed=9)
+    g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
+    _write(gpu_lib, g)
+    q, lens = _gpu(case.q, case.seq_lens)
+    out = gpu_lib.decode_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+    torch.cuda.synchronize()
+    kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
+    ref = oracle.decode_fp8(case.q.float().numpy(), kc, ks, vc, vs, case.block_tables.numpy(),
+                             case.seq_lens.numpy(), case.scale, case.block_size)
+    assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what="step")
+
+
+def test_decode_fp8_permuted_blocks_bitwise(gpu_lib):
+    """Relabelling physical blocks (codes, scales and table entries together) leaves the output
+    bit-identical."""
+    case = make_case("batch64", num_seqs=8)
+    kc, ks, vc, vs = fp8_pools(case, seed=11)
+    q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
+    a = gpu_lib.decode_fp8(q, *_gpu(kc, vc, ks, vs), tables, lens, case.scale)
+    n = kc.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(4))
+    moved = []
+    for x in (kc, vc, ks, vs):
+        raw = x.view(torch.uint8) if x.dtype == torch.float8_e4m3fn else x
+        y = torch.empty_like(raw)
+        y[perm] = raw
+        moved.append(y.view(x.dtype))
+    tab = case.block_tables.clone()
+    valid = tab < n
+    tab[valid] = perm[tab[valid].long()].to(torch.int32)
+    b_out = gpu_lib.decode_fp8(q, *_gpu(*moved), tab.to(DEV), lens, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b_out)
+
+
+def test_fp8_unsupported_shapes_are_refused(gpu_lib):
+    """b = 8 (a tile would span two blocks and two scales) and head_dim 64 have no FP8 kernel: the
+    call returns PA_ERR_UNSUPPORTED and launches nothing."""
+    for kw in (dict(block_size=8, head_dim=128), dict(block_size=16, head_dim=64)):
+        case = build_case(lengths=[20, 40], num_q_heads=8, num_kv_heads=2, dtype=torch.bfloat16, seed=1, **kw)
+        pools = _gpu(*fp8_pools(case, seed=2))
+        q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
+        with pytest.raises(gpu_lib.PaError) as err:
+            gpu_lib.decode_fp8(q, pools[0], pools[2], pools[1], pools[3], tables, lens, case.scale)
+        assert err.value.status == -2
+
+
+# ----------------------------------------------------------------------------- full size, sampled
+
+@pytest.mark.parametrize("name,partition_tokens", [("batch64", None), ("long", 512)])
+def test_fp8_full_size_sampled(gpu_lib, name, partition_tokens):
+    """Full workload sizes with FP8 pools, in the launch configuration the benchmark times: the whole
+    append is compared bit for bit, then sampled output rows against the oracle row by row."""
+    case = make_case(name, pool_device=DEV)
+    pools = fp8_pools(case, seed=21)
+    print(f"[case] fp8 full {name} pool={tuple(case.k_pool.shape)}", flush=True)
+    g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
+    _write(gpu_lib, g)
+    q, lens = _gpu(case.q, case.seq_lens)
+    if partition_tokens:
+        out = gpu_lib.decode_partitioned_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale, case.max_seq_len,
+                                              partition_tokens)
+    else:
+        out = gpu_lib.decode_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+    torch.cuda.synchronize()
+    kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
+    for got, want in zip(g[2:6], (kc, ks, vc, vs)):
+        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want)
+    del g, pools
+    got = out.cpu().double().numpy()
+    qf = case.q.float().numpy()
+    tables, lens_np = case.block_tables.numpy(), case.seq_lens.numpy()
+    rng = np.random.default_rng(len(name) + 100)
+    b, t, hq, _ = case.q.shape
+    rows = sorted({(0, 0, h) for h in range(hq)} | {(b - 1, 0, h) for h in range(hq)}
+                  | {(int(rng.integers(b)), int(rng.integers(t)), int(rng.integers(hq))) for _ in range(48)})
+    ref = np.stack([oracle.decode_row_fp8(qf, kc, ks, vc, vs, tables, lens_np, case.scale, case.block_size, i, tt, h)
+                    for i, tt, h in rows])
+    sel = np.stack([got[i, tt, h] for i, tt, h in rows])
+    err = assert_attention_close(sel, ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what=name)
+    print(f"[result] fp8 {name}: {len(rows)} sampled rows, max |err| = {err:.2e}", flush=True)

@@ -11,6 +11,7 @@ from .configs import (  # noqa: F401
     PrefillCase,
     build_case,
     build_prefill_case,
+    fp8_pools,
     int8_pools,
     make_case,
     make_prefill_case,
