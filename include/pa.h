@@ -211,7 +211,9 @@ int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const voi
  * their chunks into one partial. Each sequence's own positions (prefix_tokens .. L - 1)
  * run in partitions of partition_tokens as in pa_decode_partitioned, and one
  * merge pass combines the prefix's and the sequence's partials exactly
- * ([P5] section 4.2). Three launches on `stream`.
+ * ([P5] section 4.2). Two launches on `stream`: the prefix's chunks and the
+ * sequences' own partitions run side by side in the first, the merge is
+ * the second.
  *   prefix_tokens : a multiple of 16 and of b (0: no shared prefix, same as
  *                   pa_decode_partitioned)
  *   max_seq_len   : host-known bound of seq_lens, >= prefix_tokens

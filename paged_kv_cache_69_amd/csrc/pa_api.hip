@@ -329,11 +329,8 @@ int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, co
   p.part_ml = static_cast<float*>(workspace);
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
   p.row_groups = 1;
-  if (p.prefix_parts > 0) {
-    st = launch_status(pa::launch_cascade_prefix(p, s));
-    if (st != PA_OK) return st;
-  }
-  st = launch_status(pa::launch_decode_mfma(p, s));
+  // the prefix's items and the sequences' own partitions in one launch, then the merge
+  st = launch_status(p.prefix_parts > 0 ? pa::launch_cascade(p, s) : pa::launch_decode_mfma(p, s));
   if (st != PA_OK) return st;
   return launch_status(pa::launch_merge_partials(p, s));
 }

@@ -77,8 +77,9 @@
 // NW waves of a prefix workgroup take NW consecutive chunks for the same 32
 // rows and merge them through LDS like the single pass, writing one of the
 // first prefix_parts partition slots; the sequences' own positions (from
-// prefix_tokens on) run as ordinary split items in the slots after them, and
-// the merge kernel combines all slots exactly ([P5] section 4.2).
+// prefix_tokens on) run as ordinary split items in the slots after them, in
+// the same launch (cascade_kernel), and the merge kernel combines all slots
+// exactly ([P5] section 4.2).
 //
 // Two ways of sharing the work:
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
@@ -198,8 +199,18 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
+// LDS of one workgroup: a V tile per wave, or the waves' (m, l, acc) when they merge in LDS.
+template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE>
+constexpr int decode_lds_bytes() {
+  const int v = NW * kTileBytes;
+  const int red = (!WAVE_ITEMS || CASCADE) ? (NW * 16 * MT * kD + 2 * NW * 16 * MT) * 4 : 0;
+  return v > red ? v : red;
+}
+
+// The work of one workgroup, `block` being its index in its kind of work (the launch's block index, or
+// its place among the cascade launch's blocks of the same kind).
 template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8>
-__global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, int block) {
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
   static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
@@ -208,11 +219,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   constexpr int kKvTile = kTile * kKvRow;
   constexpr int ROWS = 16 * MT;
   constexpr int NBUF = PF + 1;
-  constexpr int kVBytes = NW * kTileBytes;  // one V tile per wave
   constexpr bool kLdsMerge = !WAVE_ITEMS || CASCADE;  // the waves' (m, l, acc) meet in LDS at the end
-  constexpr int kRedBytes = kLdsMerge ? (NW * ROWS * kD + 2 * NW * ROWS) * 4 : 0;
-  constexpr int kLdsBytes = kVBytes > kRedBytes ? kVBytes : kRedBytes;
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   // prefix slots). Cascade prefix items: `seq` is a group of ROWS query rows over all sequences and
   // the wave owns prefix partition cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks
   // are dealt round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
-  int bid = blockIdx.x;
+  int bid = block;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
   // prefix items: NW chunks per workgroup, merged into one workspace slot per workgroup
@@ -745,6 +752,32 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
   }
 }
 
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8>
+__global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<MT, NW, WAVE_ITEMS, CASCADE>()];
+  decode_body<MT, BS, NW, PF, WAVE_ITEMS, Q8, APPEND, CASCADE, F8>(p, lds, blockIdx.x);
+}
+
+// Cascade in one launch: the shared prefix's items (32 rows of many sequences per wave, L2-bound) and
+// the sequences' own partitions (HBM-bound) run side by side instead of one launch after the other.
+// Blocks alternate between the two kinds in runs of Hkv (one run is one index of every kv head, so
+// each kind keeps its kv head = XCD placement), and whichever kind has more runs takes the tail.
+template <int MT, int BS>
+__global__ __launch_bounds__(kMfmaWaves * 64) __attribute__((amdgpu_waves_per_eu(PA_CASCADE_WAVES_PER_EU)))
+void cascade_kernel(const DecodeParams p, int pre_runs, int suf_runs) {
+  constexpr int kPre = decode_lds_bytes<2, kMfmaWaves, true, true>();
+  constexpr int kSuf = decode_lds_bytes<MT, kMfmaWaves, true, false>();
+  __shared__ __attribute__((aligned(16))) char lds[kPre > kSuf ? kPre : kSuf];
+  const int run = blockIdx.x / p.Hkv, r = blockIdx.x % p.Hkv;
+  const int both = min(pre_runs, suf_runs);
+  const bool prefix = run < 2 * both ? (run & 1) == 0 : pre_runs > suf_runs;
+  const int idx = (run < 2 * both ? run / 2 : both + (run - 2 * both)) * p.Hkv + r;
+  if (prefix)
+    decode_body<2, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, true, false>(p, lds, idx);
+  else
+    decode_body<MT, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, false, false>(p, lds, idx);
+}
+
 template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false, bool F8 = false>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t item_parts =
@@ -807,15 +840,27 @@ bool mfma_int8_supported(const pa_dims& d) {
          (d.block_size == 16 || d.block_size == 32) && rows <= 32;
 }
 
-hipError_t launch_cascade_prefix(const DecodeParams& p, hipStream_t stream) {
-  // 32 query rows (of many sequences) per wave share each prefix tile
+template <int MT>
+hipError_t launch_cascade_bs(const DecodeParams& p, hipStream_t stream, int pre_runs, int suf_runs) {
+  const dim3 grid((unsigned)((int64_t)(pre_runs + suf_runs) * p.Hkv)), block(kMfmaWaves * 64);
   switch (p.block_size) {
-    case 4: return launch_t<2, 4, true, false, false, true>(p, stream);
-    case 8: return launch_t<2, 8, true, false, false, true>(p, stream);
-    case 16: return launch_t<2, 16, true, false, false, true>(p, stream);
-    case 32: return launch_t<2, 32, true, false, false, true>(p, stream);
+    case 4: cascade_kernel<MT, 4><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 8: cascade_kernel<MT, 8><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 16: cascade_kernel<MT, 16><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 32: cascade_kernel<MT, 32><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade(const DecodeParams& p, hipStream_t stream) {
+  // runs (of Hkv blocks) of each kind, from the same grid arithmetic as the separate launches
+  const int64_t pre_items = (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
+  const int64_t pre_runs = ((int64_t)p.B * p.rows + 31) / 32 * ((pre_items + kMfmaWaves - 1) / kMfmaWaves);
+  const int64_t suf_runs = (int64_t)p.B * ((p.parts - p.prefix_parts + kMfmaWaves - 1) / kMfmaWaves);
+  if (pre_runs + suf_runs == 0) return hipSuccess;
+  return p.rows <= 16 ? launch_cascade_bs<1>(p, stream, (int)pre_runs, (int)suf_runs)
+                      : launch_cascade_bs<2>(p, stream, (int)pre_runs, (int)suf_runs);
 }
 
 int mfma_waves() { return kMfmaWaves; }

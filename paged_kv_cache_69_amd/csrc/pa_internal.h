@@ -69,8 +69,9 @@ int debug_check_prefix(const pa_dims* dims, const int32_t* block_tables, const i
 bool mfma_supported(const pa_dims& d);       // bf16 pools
 bool mfma_int8_supported(const pa_dims& d);  // 8-bit pools (int8 or E4M3)
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
-// Cascade: the shared prefix's partitions for all sequences' rows at once (slots 0 .. prefix_parts-1).
-hipError_t launch_cascade_prefix(const DecodeParams& p, hipStream_t stream);
+// Cascade: in one launch, the shared prefix's partitions for all sequences' rows at once (slots
+// 0 .. prefix_parts-1) and the sequences' own partitions.
+hipError_t launch_cascade(const DecodeParams& p, hipStream_t stream);
 int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one cascade slot)
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
