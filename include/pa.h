@@ -130,7 +130,11 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
  *   k_pool, v_pool : [N, Hkv, b, D], kv_dtype (read only)
  *   block_tables : int32 [B, MB];  seq_lens : int32 [B]
  * One workgroup runs per (sequence, kv head), and loops over the whole
- * sequence. Use pa_decode_partitioned for long contexts.
+ * sequence. On the MFMA kernel, batches of 128 to 512 sequences (more
+ * workgroups than the GPU holds at once) are dealt longest first: the j-th
+ * workgroup of each kv head takes the sequence of length rank j, so the last
+ * workgroups to start are the shortest. Use pa_decode_partitioned for long
+ * contexts.
  * Supported: (kv dtype, D) in {(PA_BF16, 128), (PA_F32, 64)}; b in
  * {4, 8, 16, 32}. The VALU kernel serves any T * G: groups of up to 8 query
  * rows share one workgroup. The MFMA kernel serves PA_BF16 with D = 128 and

@@ -12,6 +12,10 @@ using pa::DecodeParams;
 
 constexpr int kAbiVersion = 1;
 constexpr int32_t kSinglePassTokens = 0x7ffffff0;  // one partition that covers any length
+#ifndef PA_LPT_MIN_SEQS
+#define PA_LPT_MIN_SEQS 128
+#endif
+constexpr int32_t kLptMinSeqs = PA_LPT_MIN_SEQS;  // smaller batches fit the GPU in one round
 
 bool valid_dtype(int32_t t) { return t == PA_F32 || t == PA_BF16; }
 int dtype_size(int32_t t) { return t == PA_F32 ? 4 : 2; }
@@ -197,6 +201,8 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
     p.parts = 1;
     p.part_tokens = kSinglePassTokens;
     p.partial = 0;
+    // batches of many sequences run as several rounds of workgroups: deal the longest first
+    p.lpt = variant == PA_VARIANT_MFMA && dims->num_seqs >= kLptMinSeqs && dims->num_seqs <= pa::mfma_lpt_max_seqs();
     return launch_attention(dims, variant, p, s);
   }
   size_t ml_bytes = 0, acc_bytes = 0;

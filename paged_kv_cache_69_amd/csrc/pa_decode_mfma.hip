@@ -84,7 +84,8 @@
 // Two ways of sharing the work:
 //  * Single pass (WAVE_ITEMS = false): one workgroup per (sequence, kv head).
 //    Wave w takes tiles w, w + NW, ..., and the waves' (m, l, acc) are merged
-//    through LDS at the end.
+//    through LDS at the end. Batches large enough to need several rounds of
+//    workgroups are dealt longest sequence first (p.lpt).
 //  * Split context (WAVE_ITEMS = true): every wave owns one partition of
 //    part_tokens positions of one (sequence, kv head) and is independent of
 //    the other waves of its workgroup (no barrier anywhere). It writes its
@@ -141,6 +142,7 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 #define PA_MFMA_OCCUPANCY \
   __attribute__((amdgpu_waves_per_eu(CASCADE && BS >= 16 ? PA_CASCADE_WAVES_PER_EU : PA_MFMA_WAVES_PER_EU)))
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
+constexpr int kLptMaxSeqs = 512;  // largest batch the single pass orders longest first
 constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;            // single pass: few tiles per wave
 constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a whole partition per wave
 // int8 tiles are half the bytes and half the registers, so they run further ahead
@@ -240,7 +242,33 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
                                    : p.parts - p.prefix_parts;
   const int groups = WAVE_ITEMS ? (item_parts + NW - 1) / NW : 1;
   const int cg = bid % groups;
-  const int seq = bid / groups;
+  // Longest first (p.lpt, single pass): when the grid takes several rounds of workgroups, the j-th
+  // workgroup of each kv head takes the sequence of length rank j (ties by index), so the rounds end
+  // with the short sequences and the last workgroups to start are the quickest to finish. The ranking
+  // reads every length once through LDS, past the V tiles' part of it.
+  int seq = bid / groups;
+  if constexpr (!WAVE_ITEMS && !CASCADE) {
+    if (p.lpt) {
+      int* lens = reinterpret_cast<int*>(lds + NW * kTileBytes);  // [kLptMaxSeqs], then the winner
+      const int b4 = (p.B + 3) / 4;
+      for (int t = threadIdx.x; t < 4 * b4; t += NW * 64) lens[t] = t < p.B ? p.seq_lens[t] : INT32_MIN;
+      __syncthreads();
+      const int j = seq;
+      for (int t = threadIdx.x; t < p.B; t += NW * 64) {
+        const int lt = lens[t];
+        int rank = 0;  // sequences ahead of t: longer, or as long with a lower index
+#pragma unroll 4
+        for (int i = 0; i < b4; ++i) {
+          const int4 v = reinterpret_cast<const int4*>(lens)[i];
+          rank += (v.x > lt || (v.x == lt && 4 * i < t)) + (v.y > lt || (v.y == lt && 4 * i + 1 < t)) +
+                  (v.z > lt || (v.z == lt && 4 * i + 2 < t)) + (v.w > lt || (v.w == lt && 4 * i + 3 < t));
+        }
+        if (rank == j) lens[kLptMaxSeqs] = t;
+      }
+      __syncthreads();
+      seq = __builtin_amdgcn_readfirstlane(lens[kLptMaxSeqs]);
+    }
+  }
   const int part_local = WAVE_ITEMS ? cg * NW + wave : 0;
   const int part = !WAVE_ITEMS ? 0 : CASCADE ? cg : p.prefix_parts + part_local;  // workspace slot
 
@@ -864,6 +892,7 @@ hipError_t launch_cascade(const DecodeParams& p, hipStream_t stream) {
 }
 
 int mfma_waves() { return kMfmaWaves; }
+int mfma_lpt_max_seqs() { return kLptMaxSeqs; }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (p.partial) return p.rows <= 16 ? launch_bs<1, true>(p, stream) : launch_bs<2, true>(p, stream);

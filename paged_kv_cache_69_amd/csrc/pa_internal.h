@@ -40,6 +40,7 @@ struct DecodeParams {
   int32_t prefix_parts;      // cascade: workspace slots 0 .. prefix_parts-1 hold the prefix's partials
                              // (one per group of mfma_waves() chunks)
   int32_t prefix_part_tokens;  // cascade: positions of the prefix per chunk (one wave's share)
+  int32_t lpt;               // single pass on the MFMA kernel: sequences dealt longest first
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
@@ -73,6 +74,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 // 0 .. prefix_parts-1) and the sequences' own partitions.
 hipError_t launch_cascade(const DecodeParams& p, hipStream_t stream);
 int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one cascade slot)
+int mfma_lpt_max_seqs();  // largest batch the single pass can order longest first
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
 

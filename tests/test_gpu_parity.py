@@ -292,6 +292,22 @@ def test_table_padding_never_read(gpu_lib):
     assert torch.equal(oa, ob)
 
 
+@pytest.mark.parametrize("b,hq,hkv,t", [(16, 32, 8, 1), (8, 16, 2, 4), (32, 64, 8, 4)])
+def test_longest_first_batches(gpu_lib, b, hq, hkv, t):
+    """Single passes over 128 to 512 sequences deal the sequences longest first (the j-th workgroup of a
+    kv head takes length rank j, ties by index): lengths drawn from a few values, so most are tied, and
+    every row still meets the oracle, separate and fused."""
+    gen = torch.Generator().manual_seed(4100 + b + t)
+    pool_of_lengths = torch.tensor([t, 5, 17, 64, 100, 150, 151, 300])
+    lengths = pool_of_lengths[torch.randint(0, len(pool_of_lengths), (200,), generator=gen)].tolist()
+    case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b, q_tokens=t,
+                      dtype=torch.bfloat16, seed=4200 + b + t, pool_slack=0.1)
+    _check_step(gpu_lib, case, variant=MFMA)
+    a, out_a, g, out_b = _fused_vs_separate(gpu_lib, case)
+    assert torch.equal(out_a, out_b)
+    assert np.array_equal(bits(a["k_pool"]), bits(g["k_pool"]))
+
+
 def test_zero_query_averages_values(gpu_lib):
     case = build_case(lengths=[5, 40, 200], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                       q_tokens=2, dtype=torch.bfloat16, seed=12)
@@ -320,6 +336,7 @@ def _sampled_rows(case, rng, n_random=48):
 
 
 @pytest.mark.parametrize("name,partitioned,variant", [("batch64", False, 0), ("batch64", True, 0), ("long", True, 0),
+                                                      ("spec", False, 0),
                                                       ("prefix", True, 0), ("spec", True, 0), ("batch64", False, VALU),
                                                       ("long", True, VALU)])
 def test_full_size_sampled(gpu_lib, name, partitioned, variant):
