@@ -107,6 +107,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -m paged_kv_cache_69_amd._build, "
                            "or __graft_entry__.build())")
+    # torch first: its HIP runtime (libamdhip64.so.7, the same soname as ROCm's) is then the one
+    # libpa.so binds to. Loaded the other way round, the process would hold two HIP runtimes and the
+    # streams and device pointers torch hands over would belong to the other one.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     dims_p = ctypes.POINTER(PaDims)
     lib.pa_write_kv.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P]

@@ -177,3 +177,19 @@ def test_check_inputs_padding_past_length_is_ignored(lib):
     d, tables, lens, pos = _check_case()
     tables[0, 2] = -5             # sequence 0 uses 2 entries only
     assert lib.pa_check_inputs_host(ctypes.byref(d), _np_ptr(tables), _np_ptr(lens), None) == 0
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loading libpa.so in a fresh process before anything imported torch still leaves one HIP runtime
+    in the process: the binding imports torch first, so libpa.so binds to torch's copy."""
+    import subprocess
+    import sys
+
+    code = ("import paged_kv_cache_69_amd as pa; pa.load_library(); "
+            "maps = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in maps if l.split()[-1].endswith('libamdhip64.so.7') "
+            "or 'libamdhip64.so' in l.split()[-1].rsplit('/', 1)[-1]}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
