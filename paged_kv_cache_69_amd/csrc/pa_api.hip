@@ -52,6 +52,11 @@ int check_dims_int8(const pa_dims* d, int32_t kv8 = PA_INT8) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// A launch's status is read with hipGetLastError, which also reports an earlier failed runtime call
+// of this thread that nobody read (the caller's, say). That error is not the launch's: drop it just
+// before launching.
+void discard_stale_error() { (void)hipGetLastError(); }
+
 // Which kernel family serves these dims, or PA_ERR_UNSUPPORTED.
 int choose_variant(const pa_dims* d, int* variant) {
   const bool mfma = pa::mfma_supported(*d);
@@ -103,6 +108,7 @@ DecodeParams base_params(const pa_dims* d, const void* q, const void* k_pool, co
 }
 
 int launch_attention(const pa_dims* d, int variant, DecodeParams& p, hipStream_t stream) {
+  discard_stale_error();
   if (variant == PA_VARIANT_MFMA) {
     p.row_groups = 1;
     return launch_status(pa::launch_decode_mfma(p, stream));
@@ -246,6 +252,7 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
   if (chk != PA_OK) return chk;
+  discard_stale_error();
   return launch_status(pa::launch_write_kv(*dims, k_new, v_new, k_pool, v_pool, block_tables, positions, s));
 }
 
@@ -336,6 +343,7 @@ int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, co
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
   p.row_groups = 1;
   // the prefix's items and the sequences' own partitions in one launch, then the merge
+  discard_stale_error();
   st = launch_status(p.prefix_parts > 0 ? pa::launch_cascade(p, s) : pa::launch_decode_mfma(p, s));
   if (st != PA_OK) return st;
   return launch_status(pa::launch_merge_partials(p, s));
@@ -357,6 +365,7 @@ int write_kv_q8(const pa_dims* dims, const void* k_new, const void* v_new, void*
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
   if (chk != PA_OK) return chk;
+  discard_stale_error();
   return launch_status(pa::launch_write_kv_int8(*dims, k_new, v_new, static_cast<int8_t*>(k_pool),
                                                 static_cast<int8_t*>(v_pool), k_scales, v_scales, block_tables,
                                                 positions, fp8, s));
@@ -422,6 +431,7 @@ int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, const int32_
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check_copies(dims, block_pairs, num_pairs, s);
   if (chk != PA_OK) return chk;
+  discard_stale_error();
   return launch_status(pa::launch_copy_blocks(*dims, k_pool, v_pool, block_pairs, num_pairs, s));
 }
 
@@ -439,6 +449,7 @@ int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check_prefill(dims, block_tables, seq_lens, q_start, s);
   if (chk != PA_OK) return chk;
+  discard_stale_error();
   return launch_status(
       pa::launch_write_kv_varlen(*dims, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, q_start, s));
 }
@@ -456,6 +467,7 @@ int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const voi
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check_prefill(dims, block_tables, seq_lens, q_start, s);
   if (chk != PA_OK) return chk;
+  discard_stale_error();
   return launch_status(pa::launch_prefill(*dims, q, k_pool, v_pool, block_tables, seq_lens, q_start, scale, out, s));
 }
 
