@@ -61,7 +61,9 @@
 // rows, at positions L - T .. L - 1, into their pool slots ([P4] "Block table
 // and allocator": a decode step writes the new token's K and V, then
 // attends). The workgroup of (sequence, kv head) stores that head's rows
-// itself: wave 0 in a single pass, or the wave whose partition holds them. No
+// itself: in a single pass the last wave, after its tiles, from rows and slots
+// it fetched at the start (wave 0 before its tiles when T > 2); split, the
+// wave whose partition holds them. No
 // wave waits for those stores: in the tile that holds a new position, the
 // lanes of that position take its K/V chunks from k_new / v_new instead of the
 // pool, so the result is bit for bit the one a separate append followed by a
@@ -673,12 +675,31 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     return ok;
   };
 
+  // Single pass with T <= 2: the last wave (the fewest tiles) stores the new rows after its tiles. Their
+  // data and slots are fetched now, ahead of the tiles, so those stores wait on nothing by then.
+  const bool late = APPEND && !WAVE_ITEMS && T <= 2;
+  u32x4 late_row = {0u, 0u, 0u, 0u};
+  int64_t late_dst = -1;
+  if constexpr (APPEND && !WAVE_ITEMS) {
+    if (late && wave == NW - 1) {
+      // lane: row t = lane / 32; K (lanes 0-15 of the half) or V (16-31); 16-byte chunk lane % 16
+      const int t = lane >> 5, which = (lane >> 4) & 1, chunk = lane & 15;
+      const int pos0 = L - T, pos1 = L - 1;  // the rows' positions (one row when T = 1)
+      const int blk0 = (int)min((uint32_t)trow[min(max(pos0, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+      const int blk1 = (int)min((uint32_t)trow[min(max(pos1, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+      const int pos = L - T + t;
+      if (t < T && pos >= 0) {
+        late_row = load16(new_row(which ? p.v_new : p.k_new, t) + chunk * 16);
+        late_dst = (int64_t)(t ? blk1 : blk0) * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
+      }
+    }
+  }
   if constexpr (APPEND) {
     // store the new rows this wave owns (positions L - T .. L - 1 in its range) into the pools
     // One row per step, so its position and block are wave-uniform (a scalar table load); lanes 0-15
     // copy the K row's 16-byte chunks and lanes 16-31 the V row's.
     const int t_lo = WAVE_ITEMS ? max(0, p_begin - (L - T)) : 0;
-    const int t_hi = WAVE_ITEMS ? min(T, p_end - (L - T)) : (wave == 0 ? T : 0);
+    const int t_hi = WAVE_ITEMS ? min(T, p_end - (L - T)) : (wave == 0 && !late ? T : 0);
     for (int t = max(t_lo, T - L); t < t_hi; ++t) {
       const int pos = L - T + t;
       const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
@@ -692,6 +713,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   }
 
   while (!run()) {
+  }
+  if constexpr (APPEND && !WAVE_ITEMS) {
+    if (late_dst >= 0) {
+      const bool v_half = (lane >> 4) & 1;
+      *reinterpret_cast<u32x4*>(const_cast<char*>(v_half ? vbase : kbase) + late_dst) = late_row;
+    }
   }
 
   if constexpr (Q8 && !F8) {

@@ -386,7 +386,7 @@ def _fused_vs_separate(pa, case, *, partition_tokens=None, variant_sep=MFMA):
 
 
 @pytest.mark.parametrize("b", [4, 8, 16, 32])
-@pytest.mark.parametrize("hq,hkv,t", [(4, 4, 1), (32, 8, 1), (8, 2, 4), (16, 2, 4), (12, 4, 3), (64, 8, 4)])
+@pytest.mark.parametrize("hq,hkv,t", [(4, 4, 1), (32, 8, 1), (8, 2, 2), (32, 8, 2), (8, 2, 4), (16, 2, 4), (12, 4, 3), (64, 8, 4)])
 def test_fused_append_decode_bitwise(gpu_lib, b, hq, hkv, t):
     """pa_write_kv_decode equals pa_write_kv followed by the MFMA decode, bit for bit (pools and out),
     single pass and split (new rows inside one partition and straddling two), and meets the oracle."""
