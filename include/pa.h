@@ -170,12 +170,28 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
  *               entry are irrelevant.
  * Other arguments and the supported shapes are as for pa_decode. Two calls
  * that share one workspace must be ordered by the caller, for example by
- * using the same stream: calls that overlap on one workspace race. */
+ * using the same stream: calls that overlap on one workspace race. On the
+ * matrix-core kernel one wave may walk several consecutive partitions (see
+ * pa_decode_partitioned_wave_parts); it still writes one partial per
+ * partition, each with its own reference maximum, so the result is the same
+ * bits either way. */
 int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables,
                           const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
+
+/* pa_decode_partitioned_wave_parts: the number of consecutive partitions (1
+ * or 2) that one wave of the matrix-core kernel walks in a split call with
+ * these arguments (pa_decode_partitioned, pa_write_kv_decode_partitioned).
+ * It is 2 for bf16 pools when T * G <= 16 and B * Hkv * ceil(max_seq_len /
+ * partition_tokens) exceeds the 2048 split waves the GPU holds at once, so
+ * that long-context batches run in one round of waves; 8-bit pools keep one
+ * partition per wave. The environment variable PA_SPLIT_WAVE_PARTS=1 or 2
+ * overrides that choice for bf16 pools with T * G <= 16 (read on every
+ * call). Host-only; returns
+ * PA_ERR_INVALID_ARG for invalid dims or sizes. */
+int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);
 
 /* pa_write_kv_decode: one decode step in one launch: pa_write_kv of the T new
  * tokens at each sequence's last T positions (positions[i][t] = seq_lens[i] -

@@ -36,6 +36,7 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
+    "pa_decode_partitioned_wave_parts",
     "pa_decode_cascade_workspace_bytes",
     "pa_decode_cascade",
     "pa_write_kv_decode",
@@ -120,6 +121,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode_partitioned_workspace_bytes.argtypes = [dims_p, _I32, _I32]
     lib.pa_decode_partitioned_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_partitioned_wave_parts.argtypes = [dims_p, _I32, _I32]
+    lib.pa_decode_partitioned_wave_parts.restype = ctypes.c_int
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
@@ -263,6 +266,16 @@ def workspace_bytes(q, k_pool, block_tables, max_seq_len: int, partition_tokens:
     n = lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
     if n == 0:
         raise PaError("pa_decode_partitioned_workspace_bytes", -1, "invalid argument")
+    return int(n)
+
+
+def wave_parts(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int) -> int:
+    """``pa_decode_partitioned_wave_parts``: consecutive partitions per wave of the matrix-core split kernel."""
+    lib = load_library()
+    dims = make_dims(q, k_pool, block_tables)
+    n = lib.pa_decode_partitioned_wave_parts(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
+    if n < 0:
+        raise PaError("pa_decode_partitioned_wave_parts", n, "invalid argument")
     return int(n)
 
 

@@ -1,6 +1,7 @@
 // extern "C" entry points of libpa.so: argument checks, kernel choice, launches.
 // The declarations, and their citations of the pages, are in include/pa.h.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -16,6 +17,11 @@ constexpr int32_t kSinglePassTokens = 0x7ffffff0;  // one partition that covers 
 #define PA_LPT_MIN_SEQS 128
 #endif
 constexpr int32_t kLptMinSeqs = PA_LPT_MIN_SEQS;  // smaller batches fit the GPU in one round
+// Split waves the GPU holds at once: 256 CUs x 4 SIMDs x 2 waves (the split kernels' register use).
+#ifndef PA_RESIDENT_SPLIT_WAVES
+#define PA_RESIDENT_SPLIT_WAVES 2048
+#endif
+constexpr int64_t kResidentSplitWaves = PA_RESIDENT_SPLIT_WAVES;
 
 bool valid_dtype(int32_t t) { return t == PA_F32 || t == PA_BF16; }
 int dtype_size(int32_t t) { return t == PA_F32 ? 4 : 2; }
@@ -155,6 +161,19 @@ int32_t cascade_parts(const pa_dims* d, int32_t prefix_tokens, int32_t max_seq_l
   return cascade_prefix_slots(d, prefix_tokens) + (max_seq_len - prefix_tokens + partition_tokens - 1) / partition_tokens;
 }
 
+// Consecutive partitions per wave of the matrix-core split kernel: two once one partition per wave
+// would need more waves than the GPU holds at once (B * Hkv * parts bounds the waves from above), for
+// bf16 pools and 16 query rows per kv head (T * G <= 16). 8-bit tiles are half the bytes, so those
+// kernels need every wave they can get in flight and keep one partition per wave.
+// PA_SPLIT_WAVE_PARTS=1 or 2 overrides the choice (the results are the same bits either way).
+int32_t split_wave_parts(const pa_dims* d, int32_t parts) {
+  const bool rows16 = d->q_tokens * (d->num_q_heads / d->num_kv_heads) <= 16;
+  if (!rows16 || d->kv_dtype != PA_BF16) return 1;
+  const char* env = getenv("PA_SPLIT_WAVE_PARTS");
+  if (env && (env[0] == '1' || env[0] == '2') && env[1] == '\0') return env[0] - '0';
+  return (int64_t)d->num_seqs * d->num_kv_heads * parts > kResidentSplitWaves ? 2 : 1;
+}
+
 // Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
 // run, the merge launch. int8 pools carry their scales and run on the MFMA kernel.
 int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, const void* k_pool, const void* v_pool,
@@ -216,6 +235,7 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   p.parts = parts;
   p.part_tokens = partition_tokens;
   p.partial = 1;
+  p.wave_parts = variant == PA_VARIANT_MFMA ? split_wave_parts(dims, parts) : 1;
   p.part_ml = static_cast<float*>(workspace);
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
   st = launch_attention(dims, variant, p, s);
@@ -270,6 +290,11 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
   size_t ml = 0, acc = 0;
   workspace_layout(dims, parts, &ml, &acc);
   return ml + acc;
+}
+
+int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens) {
+  if (check_shape(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
+  return split_wave_parts(dims, (max_seq_len + partition_tokens - 1) / partition_tokens);
 }
 
 int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,

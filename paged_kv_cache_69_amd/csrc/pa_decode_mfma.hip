@@ -151,6 +151,14 @@ constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a 
 constexpr int kMfmaQ8Prefetch = PA_MFMA_Q8_PREFETCH;
 constexpr int kMfmaQ8SplitPrefetch = PA_MFMA_Q8_SPLIT_PREFETCH;
 
+// A view of memory no part of the launch writes (tables, lengths, scales), in the constant address
+// space: uniform loads through it stay scalar loads even after the launch's own stores (partials, the
+// fused append's rows), which would otherwise make the compiler fall back to vector loads and waits.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* read_only(const T* ptr) {
+  return (const __attribute__((address_space(4))) T*)ptr;
+}
+
 // Byte offset of (position t, byte b of its 256-byte row) inside one V tile in LDS.
 __device__ __forceinline__ int v_swz(int t, int b) { return t * kRowBytes + (b ^ ((t & 7) << 5)); }
 
@@ -203,18 +211,27 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int64_t idx, fl
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
 }
 
-// LDS of one workgroup: a V tile per wave, or the waves' (m, l, acc) when they merge in LDS.
-template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE>
+// A wave's registers of one partition's partial (acc, then each lane's (m, l)), parked in LDS.
+template <int MT>
+constexpr int stash_bytes() {
+  return MT * (8 * 64 * 16 + 64 * 8);
+}
+
+// LDS of one workgroup: a V tile per wave, or the waves' (m, l, acc) when they merge in LDS; waves that
+// walk two partitions (MULTI) also park the first one's partial after the V tiles.
+template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE, bool MULTI = false>
 constexpr int decode_lds_bytes() {
-  const int v = NW * kTileBytes;
+  const int v = NW * kTileBytes + (MULTI ? NW * stash_bytes<MT>() : 0);
   const int red = (!WAVE_ITEMS || CASCADE) ? (NW * 16 * MT * kD + 2 * NW * 16 * MT) * 4 : 0;
   return v > red ? v : red;
 }
 
 // The work of one workgroup, `block` being its index in its kind of work (the launch's block index, or
 // its place among the cascade launch's blocks of the same kind).
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8,
+          bool MULTI = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, int block) {
+  static_assert(!MULTI || (WAVE_ITEMS && !CASCADE && !Q8), "two partitions per wave are for bf16 split items");
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
   static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
@@ -238,10 +255,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   int bid = block;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
-  // prefix items: NW chunks per workgroup, merged into one workspace slot per workgroup
+  // prefix items: NW chunks per workgroup, merged into one workspace slot per workgroup. Split items: KP
+  // consecutive partitions per wave (one partial each), so that a long-context batch needs fewer waves
+  // than the GPU holds at once.
+  const int KP = MULTI && p.wave_parts > 1 ? 2 : 1;
   const int item_parts = !WAVE_ITEMS ? 1
                          : CASCADE ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens
-                                   : p.parts - p.prefix_parts;
+                                   : (p.parts - p.prefix_parts + KP - 1) / KP;
   const int groups = WAVE_ITEMS ? (item_parts + NW - 1) / NW : 1;
   const int cg = bid % groups;
   // Longest first (p.lpt, single pass): when the grid takes several rounds of workgroups, the j-th
@@ -272,11 +292,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
   }
   const int part_local = WAVE_ITEMS ? cg * NW + wave : 0;
-  const int part = !WAVE_ITEMS ? 0 : CASCADE ? cg : p.prefix_parts + part_local;  // workspace slot
+  // workspace slot (of the item's first partition)
+  const int part = !WAVE_ITEMS ? 0 : CASCADE ? cg : p.prefix_parts + part_local * KP;
+  const int part_tiles = p.part_tokens / kTile;  // split items: tiles per partition
 
   const int T = p.T;
   const int p_begin = !WAVE_ITEMS ? 0 : CASCADE ? part_local * p.prefix_part_tokens
-                                                : p.prefix_tokens + part_local * p.part_tokens;
+                                                : p.prefix_tokens + part_local * KP * p.part_tokens;
 
   // Query row n (< ROWS) of this wave: row n of sequence seq, or, for prefix items, row seq*ROWS + n of
   // all sequences' rows taken together.
@@ -355,7 +377,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   // row and the id to the pool, so a lookup never depends on the length and any entry (padding
   // included) gives an address inside the pool; positions at or past L are masked out of the
   // result whatever they hold. That lets the first tile's lookup go out together with the length.
-  const int32_t* trow = p.block_tables + (CASCADE ? 0 : (int64_t)seq * p.MB);  // prefix: every row's blocks
+  const auto* trow = read_only(p.block_tables + (CASCADE ? 0 : (int64_t)seq * p.MB));  // prefix: every row's blocks
   constexpr int kBlocksPerTile = BS >= kTile ? 1 : kTile / BS;
   struct TileIds {
     int b[kBlocksPerTile];
@@ -369,20 +391,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
       ids.b[jj] = (int)min((uint32_t)trow[min(first + jj, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
     if constexpr (Q8) {
       const int64_t si = (int64_t)ids.b[0] * p.Hkv + kvh;
-      ids.ks = p.k_scales[si];
-      ids.vs = p.v_scales[si];
+      ids.ks = read_only(p.k_scales)[si];
+      ids.vs = read_only(p.v_scales)[si];
     } else {
       ids.ks = ids.vs = 1.f;
     }
     return ids;
   };
   const TileIds ids0 = ids_of(0);
-  const int L = CASCADE ? p.prefix_tokens : p.seq_lens[seq];  // prefix items: every prefix position is visible
+  const int L = CASCADE ? p.prefix_tokens : read_only(p.seq_lens)[seq];  // prefix items: every prefix position is visible
   // an empty split partition's wave leaves (the merge never reads its slot); a prefix item's wave with
   // no chunk stays for the workgroup's merge, with nothing to add
   if (WAVE_ITEMS && !CASCADE && (part_local >= item_parts || p_begin >= L)) return;
   const bool idle = CASCADE && (part_local >= item_parts || p_begin >= L);
-  const int p_end = WAVE_ITEMS ? min(L, p_begin + (CASCADE ? p.prefix_part_tokens : p.part_tokens)) : L;
+  const int p_end = WAVE_ITEMS ? min(L, p_begin + (CASCADE ? p.prefix_part_tokens : KP * p.part_tokens)) : L;
   const int ntiles = !idle && p_end > p_begin ? (p_end - p_begin + kTile - 1) / kTile : 0;
   const int vis_all = CASCADE ? L : L - T + 1;
   const bool rows_all_present = CASCADE ? (seq + 1) * ROWS <= p.B * p.rows : p.rows == ROWS;
@@ -397,6 +419,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kKvRow;
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kKvRow;
   lds_char* vt = (lds_char*)lds + wave * kTileBytes;
+  lds_char* stash = (lds_char*)lds + NW * kTileBytes + wave * stash_bytes<MT>();  // MULTI only
+  bool stashed = false;  // the wave's first partition's partial waits in its stash
 
   // Row t of this sequence's new K or V rows ([B, T, Hkv, D]), for this kv head.
   auto new_row = [&](const void* base, int t) -> const char* {
@@ -602,7 +626,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   };
   // Split context: this partition's (m, l, acc) partial, straight from registers. Lanes of column
   // c16 hold parts of row c16 (+16*mt)'s l; the four 16-lane groups are summed first.
-  auto flush = [&]() {
+  auto flush = [&](int slot) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float l = l_part[mt];
@@ -610,41 +634,63 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
       l += __shfl_xor(l, 32, 64);
       const int n = mt * 16 + c16;
       if (g == 0 && row_present(n)) {
-        const int64_t pi = out_row(n) * p.parts + part;
+        const int64_t pi = out_row(n) * p.parts + slot;
         *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref[mt], l};
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int na = mt * 16 + 4 * g + e;  // accumulator row of this lane
         if (row_present(na)) {
-          float* dst = p.part_acc + (out_row(na) * p.parts + part) * kD + c16;
+          float* dst = p.part_acc + (out_row(na) * p.parts + slot) * kD + c16;
 #pragma unroll
           for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[mt][jb][e];
         }
       }
     }
   };
-  // Process the wave's tiles. Returns false when a score outran the reference: m_ref has then been
-  // raised and the caller runs again from the first tile with cleared accumulators (the tile that
-  // outran was still accumulated, into values that are discarded).
-  auto run = [&]() -> bool {
+  // int8 pools: remove the V offset (accumulator row 4g + e (+16 mt) held 128 * sum(scaled P) of that row too)
+  auto remove_v_offset = [&]() {
+    if constexpr (Q8 && !F8) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float tot = vcorr[mt];
+        tot += __shfl_xor(tot, 16, 64);
+        tot += __shfl_xor(tot, 32, 64);  // row c16's total, on every lane of column c16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ce = kVOffset * __shfl(tot, 4 * g + e, 64);
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) acc[mt][jb][e] -= ce;
+        }
+      }
+    }
+  };
+  // Process the wave's tiles from tile ib on. Returns -1 when done, or the tile to run again from when a
+  // score outran the reference: m_ref has then been raised and the caller runs again from the start of
+  // that tile's partition (its first tile, or ib) with cleared accumulators (the tile that outran was
+  // still accumulated, into values that are discarded). With KP > 1 the loads run on across the end of
+  // a partition: its partial is written there and the next partition starts with cleared accumulators
+  // and a reference of its own.
+  auto run = [&](int ib) -> int {
+    ib = __builtin_amdgcn_readfirstlane(ib);  // uniform, so the table lookups below stay scalar loads
     clear();
-    if (my_tiles == 0) return true;
+    if (ib >= my_tiles) return -1;
     const int last = my_tiles - 1;
     TileRegs ring[NBUF];
     TileIds cur[NBUF];  // block ids (and scales) of the tile in each ring slot
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      cur[u] = u == 0 ? ids0 : ids_of(min(u, last));
-      load_tile(min(u, last), cur[u], ring[u]);
+      cur[u] = ib + u == 0 ? ids0 : ids_of(min(ib + u, last));
+      load_tile(min(ib + u, last), cur[u], ring[u]);
     }
-    TileIds ids_next = ids_of(min(PF, last));
-    bool ok = true;
-    for (int i0 = 0; i0 < my_tiles && ok; i0 += NBUF) {
+    TileIds ids_next = ids_of(min(ib + PF, last));
+    int again = -1;
+    int part_end = KP > 1 ? (ib / part_tiles + 1) * part_tiles : my_tiles;  // tile after this partition
+    for (int i0 = ib; i0 < my_tiles && again < 0; i0 += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int i = i0 + u;
-        if (i < my_tiles && ok) {
+        if (i < my_tiles && again < 0) {
           const TileIds ids = ids_next;
           ids_next = ids_of(min(i + PF + 1, last));
           load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF]);
@@ -665,14 +711,35 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
               for (int e = 0; e < 4; ++e) over |= s[mt][e] > m_ref[mt] + kRefSlack;
             if (__builtin_expect(__any(over), 0)) {
               raise_ref(s);
-              ok = false;
+              again = KP > 1 ? part_end - part_tiles : ib;
             }
           }
           accumulate(masked, tile_p0, s, ring[u], ids_cur.vs);
+          if (KP > 1 && i + 1 == part_end && i + 1 < my_tiles && again < 0) {
+            // the first partition ends here: its partial waits in LDS until the wave's end. Written to
+            // memory now, its stores would be younger than the tile loads in flight, and the waits for
+            // those tiles would then wait for the stores too.
+            if constexpr (MULTI) {
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int jb = 0; jb < 8; ++jb)
+                  *(__attribute__((address_space(3))) f32x4*)(stash + ((mt * 8 + jb) * 64 + lane) * 16) = acc[mt][jb];
+                *(__attribute__((address_space(3))) f32x2*)(stash + MT * 8192 + (mt * 64 + lane) * 8) =
+                    f32x2{m_ref[mt], l_part[mt]};
+              }
+              stashed = true;
+            }
+            clear();
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) m_ref[mt] = kNegInf;
+            have_ref = false;
+            part_end += part_tiles;
+          }
         }
       }
     }
-    return ok;
+    return again;
   };
 
   // Single pass with T <= 2: the last wave (the fewest tiles) stores the new rows after its tiles. Their
@@ -712,7 +779,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
   }
 
-  while (!run()) {
+  for (int from = 0; (from = run(from)) >= 0;) {
   }
   if constexpr (APPEND && !WAVE_ITEMS) {
     if (late_dst >= 0) {
@@ -721,24 +788,24 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
   }
 
-  if constexpr (Q8 && !F8) {
-    // remove the V offset: accumulator row 4g + e (+16 mt) held 128 * sum(scaled P) of that row too
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float tot = vcorr[mt];
-      tot += __shfl_xor(tot, 16, 64);
-      tot += __shfl_xor(tot, 32, 64);  // row c16's total, on every lane of column c16
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ce = kVOffset * __shfl(tot, 4 * g + e, 64);
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb) acc[mt][jb][e] -= ce;
-      }
-    }
-  }
+  remove_v_offset();
 
   if constexpr (!kLdsMerge) {
-    flush();
+    flush(part + (KP > 1 ? (my_tiles - 1) / part_tiles : 0));
+    if constexpr (MULTI) {
+      if (stashed) {  // the first partition's partial, back from LDS
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb)
+            acc[mt][jb] = *(__attribute__((address_space(3))) f32x4*)(stash + ((mt * 8 + jb) * 64 + lane) * 16);
+          const f32x2 ml = *(__attribute__((address_space(3))) f32x2*)(stash + MT * 8192 + (mt * 64 + lane) * 8);
+          m_ref[mt] = ml[0];
+          l_part[mt] = ml[1];
+        }
+        flush(part);
+      }
+    }
   } else {
     // per-row l of this wave: lanes of column c16 hold row c16 (+16*mt); sum the four 16-lane groups
 #pragma unroll
@@ -807,10 +874,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   }
 }
 
-template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8>
+template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8, bool MULTI>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<MT, NW, WAVE_ITEMS, CASCADE>()];
-  decode_body<MT, BS, NW, PF, WAVE_ITEMS, Q8, APPEND, CASCADE, F8>(p, lds, blockIdx.x);
+  __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<MT, NW, WAVE_ITEMS, CASCADE, MULTI>()];
+  decode_body<MT, BS, NW, PF, WAVE_ITEMS, Q8, APPEND, CASCADE, F8, MULTI>(p, lds, blockIdx.x);
 }
 
 // Cascade in one launch: the shared prefix's items (32 rows of many sequences per wave, L2-bound) and
@@ -835,15 +902,23 @@ void cascade_kernel(const DecodeParams p, int pre_runs, int suf_runs) {
 
 template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false, bool F8 = false>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int64_t item_parts =
-      !WI ? 1 : CAS ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens : p.parts - p.prefix_parts;
+  // two partitions per wave: a kernel of its own (the extra flush costs registers), bf16 16-row tiles only
+  constexpr bool kMultiOk = WI && !CAS && MT == 1 && !Q8;
+  const int64_t kp = kMultiOk && p.wave_parts > 1 ? p.wave_parts : 1;
+  const int64_t item_parts = !WI ? 1
+                             : CAS ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens
+                                   : (p.parts - p.prefix_parts + kp - 1) / kp;
   const int64_t groups = WI ? (item_parts + kMfmaWaves - 1) / kMfmaWaves : 1;
   const int64_t units = CAS ? ((int64_t)p.B * p.rows + 16 * MT - 1) / (16 * MT) : p.B;  // row groups or sequences
   const int64_t grid = units * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
   constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
-  decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS, F8>
-      <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  if (kp > 1)
+    decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS, F8, kMultiOk>
+        <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  else
+    decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS, F8, false>
+        <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 

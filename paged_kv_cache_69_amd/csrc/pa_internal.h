@@ -41,6 +41,7 @@ struct DecodeParams {
                              // (one per group of mfma_waves() chunks)
   int32_t prefix_part_tokens;  // cascade: positions of the prefix per chunk (one wave's share)
   int32_t lpt;               // single pass on the MFMA kernel: sequences dealt longest first
+  int32_t wave_parts;        // split launches on the MFMA kernel: consecutive partitions per wave (<= 1: one)
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,

@@ -107,6 +107,37 @@ def test_partitioned_workspace_arithmetic(lib):
     assert lib.pa_decode_partitioned_workspace_bytes(None, 10, 512) == 0
 
 
+def test_partitioned_wave_parts_arithmetic(lib):
+    """Two partitions per split wave once B * Hkv * ceil(max_seq_len / partition_tokens) > 2048."""
+    d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
+    assert d.num_kv_heads == 8
+    f = lambda msl, pt: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), msl, pt)  # noqa: E731
+    assert f(32768, 512) == 2            # 16 * 8 * 64 = 8192 partitions
+    assert f(16 * 512, 512) == 1         # 16 * 8 * 16 = 2048: one round already
+    assert f(16 * 512 + 1, 512) == 2     # 17 partitions per sequence
+    assert f(0, 512) == -1 and f(100, 0) == -1
+    assert lib.pa_decode_partitioned_wave_parts(None, 100, 512) == -1
+    d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128)  # 32 rows per kv head: one partition
+    assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d32), 32768, 512) == 1
+    for code in (pa.PA_INT8, pa.PA_FP8_E4M3):  # 8-bit pools: one partition per wave
+        d8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code)
+        assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d8), 32768, 512) == 1
+
+
+def test_partitioned_wave_parts_override(lib, monkeypatch):
+    d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
+    f = lambda: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), 32768, 512)  # noqa: E731
+    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "1")
+    assert f() == 1
+    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "2")
+    assert f() == 2
+    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "7")  # not 1 or 2: the usual choice
+    assert f() == 2
+    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "2")
+    d8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=pa.PA_INT8)
+    assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d8), 32768, 512) == 1
+
+
 def test_partitioned_rejects_bad_partitions(lib):
     d = _dims()
     ws = ctypes.c_void_p(0x100000)
