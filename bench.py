@@ -661,7 +661,7 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + ("_fp8" if spec.get("fp8") else "_int8")
     if cascade:
         call = "pa_decode_cascade"
-        kernel = "decode_mfma_kernel (shared-prefix items + per-sequence items)"
+        kernel = "cascade_kernel (shared-prefix items and per-sequence items in one launch)"
     kernel += (" + merge_partials_kernel" if spec["partition_tokens"] else "") + f" (one {call} call)"
     traffic = traffic_from_profiles(name) if variant == 0 else None
     res = {
@@ -727,7 +727,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
     w_fac = CALIBRATION_BYTES / (cw[0] * 1024.0)
     kernels = sorted({k[1] for k in med
                       if k[1].startswith("void decode_") or "merge_partials" in k[1] or "prefill_mfma" in k[1]
-                      or "copy_blocks" in k[1]})
+                      or "copy_blocks" in k[1] or "cascade_kernel" in k[1]})
     lines = [f"# HBM traffic of one decode call, workload {workload}",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
              f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
