@@ -93,7 +93,11 @@
 //    the other waves of its workgroup (no barrier anywhere). It writes its
 //    partition's (m, l, acc) partial to the workspace straight from
 //    registers; the merge kernel that follows on the stream combines the
-//    partials.
+//    partials. When one partition per wave would need more waves than the
+//    GPU holds at once (MULTI, bf16), a wave walks two consecutive
+//    partitions with one unbroken load pipeline and parks the first
+//    partition's partial in LDS until its end; each partition keeps its own
+//    reference, so every partial is the one a wave of its own would write.
 #include <type_traits>
 
 #include "pa_device.h"
