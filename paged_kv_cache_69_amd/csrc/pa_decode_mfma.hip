@@ -144,9 +144,18 @@ constexpr float kRefSlack = 64.0f;  // base-2 units a score may exceed the refer
 #ifndef PA_CASCADE_WAVES_PER_EU
 #define PA_CASCADE_WAVES_PER_EU 2
 #endif
-// prefix items hold every wave of the grid at once only at two waves per SIMD
-#define PA_MFMA_OCCUPANCY \
-  __attribute__((amdgpu_waves_per_eu(CASCADE && BS >= 16 ? PA_CASCADE_WAVES_PER_EU : PA_MFMA_WAVES_PER_EU)))
+#ifndef PA_MFMA_F8_SPLIT_PREFETCH
+#define PA_MFMA_F8_SPLIT_PREFETCH 1
+#endif
+#ifndef PA_MFMA_F8_SPLIT_WAVES_PER_EU
+#define PA_MFMA_F8_SPLIT_WAVES_PER_EU 4
+#endif
+// prefix items hold every wave of the grid at once only at two waves per SIMD; FP8 split waves of 16 rows
+// fit four per SIMD with one tile ahead (a long-context batch's waves then run in one round, not two)
+#define PA_MFMA_OCCUPANCY                                                                             \
+  __attribute__((amdgpu_waves_per_eu(CASCADE && BS >= 16 ? PA_CASCADE_WAVES_PER_EU                  \
+                                     : F8 && WAVE_ITEMS && MT == 1 ? PA_MFMA_F8_SPLIT_WAVES_PER_EU   \
+                                                         : PA_MFMA_WAVES_PER_EU)))
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
 constexpr int kLptMaxSeqs = 512;  // largest batch the single pass orders longest first
 constexpr int kMfmaPrefetch = PA_MFMA_PREFETCH;            // single pass: few tiles per wave
@@ -154,6 +163,7 @@ constexpr int kMfmaSplitPrefetch = PA_MFMA_SPLIT_PREFETCH;  // split context: a 
 // int8 tiles are half the bytes and half the registers, so they run further ahead
 constexpr int kMfmaQ8Prefetch = PA_MFMA_Q8_PREFETCH;
 constexpr int kMfmaQ8SplitPrefetch = PA_MFMA_Q8_SPLIT_PREFETCH;
+constexpr int kMfmaF8SplitPrefetch = PA_MFMA_F8_SPLIT_PREFETCH;
 
 // A view of memory no part of the launch writes (tables, lengths, scales), in the constant address
 // space: uniform loads through it stay scalar loads even after the launch's own stores (partials, the
@@ -916,7 +926,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t units = CAS ? ((int64_t)p.B * p.rows + 16 * MT - 1) / (16 * MT) : p.B;  // row groups or sequences
   const int64_t grid = units * groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  constexpr int PF = Q8 ? (WI ? kMfmaQ8SplitPrefetch : kMfmaQ8Prefetch) : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
+  constexpr int PF = Q8 ? (WI ? (F8 && MT == 1 ? kMfmaF8SplitPrefetch : kMfmaQ8SplitPrefetch) : kMfmaQ8Prefetch)
+                        : (WI ? kMfmaSplitPrefetch : kMfmaPrefetch);
   if (kp > 1)
     decode_mfma_kernel<MT, BS, kMfmaWaves, PF, WI, Q8, AP, CAS, F8, kMultiOk>
         <<<dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream>>>(p);
