@@ -231,12 +231,21 @@ constexpr int stash_bytes() {
   return MT * (8 * 64 * 16 + 64 * 8);
 }
 
-// LDS of one workgroup: a V tile per wave, or the waves' (m, l, acc) when they merge in LDS; waves that
-// walk two partitions (MULTI) also park the first one's partial after the V tiles.
+// The single pass of 16-row tiles merges its waves with one barrier: each wave writes its (m, l, acc) to
+// LDS of its own as soon as its tiles are done, beside the V tiles rather than over them.
+template <int MT, bool WAVE_ITEMS, bool CASCADE>
+constexpr bool one_barrier_merge() {
+  return !WAVE_ITEMS && !CASCADE && MT == 1;
+}
+
+// LDS of one workgroup: a V tile per wave, or the waves' (m, l, acc) when they merge in LDS (after the V
+// tiles and the longest-first ranking's lengths for a one-barrier merge, over the V tiles otherwise);
+// waves that walk two partitions (MULTI) also park the first one's partial after the V tiles.
 template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE, bool MULTI = false>
 constexpr int decode_lds_bytes() {
   const int v = NW * kTileBytes + (MULTI ? NW * stash_bytes<MT>() : 0);
   const int red = (!WAVE_ITEMS || CASCADE) ? (NW * 16 * MT * kD + 2 * NW * 16 * MT) * 4 : 0;
+  if (one_barrier_merge<MT, WAVE_ITEMS, CASCADE>()) return v + (kLptMaxSeqs + 4) * 4 + red;
   return v > red ? v : red;
 }
 
@@ -286,6 +295,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   if constexpr (!WAVE_ITEMS && !CASCADE) {
     if (p.lpt) {
       int* lens = reinterpret_cast<int*>(lds + NW * kTileBytes);  // [kLptMaxSeqs], then the winner
+      // (with a one-barrier merge the waves' partials go after these lengths, so no wave overwrites them
+      // while another still reads its winner)
       const int b4 = (p.B + 3) / 4;
       for (int t = threadIdx.x; t < 4 * b4; t += NW * 64) lens[t] = t < p.B ? p.seq_lens[t] : INT32_MIN;
       __syncthreads();
@@ -829,11 +840,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
     // ---- merge the waves' (m, l, acc) through LDS ([P5] section 4.2, three-step merge):
     // M = max_w m_w;  l = sum_w l_w 2^(m_w - M);  acc = sum_w acc_w 2^(m_w - M).
-    // Each wave rescales its own accumulators in registers, so the LDS pass is one float4 sum.
-    __syncthreads();  // every wave is done with its V tile before the merge reuses the LDS
-    float* red_acc = reinterpret_cast<float*>(lds);  // [NW][ROWS][kD]
-    float* red_m = red_acc + NW * ROWS * kD;         // [ROWS][NW]
-    float* red_l = red_m + NW * ROWS;                // [ROWS][NW]
+    constexpr bool kOneBarrier = one_barrier_merge<MT, WAVE_ITEMS, CASCADE>();
+    float* red_acc = reinterpret_cast<float*>(lds + (kOneBarrier ? NW * kTileBytes + (kLptMaxSeqs + 4) * 4 : 0));
+    float* red_m = red_acc + NW * ROWS * kD;  // [ROWS][NW]
+    float* red_l = red_m + NW * ROWS;         // [ROWS][NW]
+    // [NW][ROWS][kD]: one barrier, each wave's accumulators as they are (the final pass scales them); else
+    // each wave rescales its own in registers once every m is known, and the final pass only sums
+    if constexpr (!kOneBarrier) __syncthreads();  // every wave is done with its V tile before the merge reuses the LDS
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (g == 0) {
@@ -841,20 +854,29 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
         red_m[(mt * 16 + c16) * NW + wave] = m_ref[mt];
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    if constexpr (kOneBarrier) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = mt * 16 + 4 * g + e;
-        float M = kNegInf;
+        const int row = 4 * g + e;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[row * NW + w]);
-        const float mw = red_m[row * NW + wave];
-        const float sc = mw == kNegInf ? 0.f : exp2_fast(mw - M);
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb) red_acc[(wave * ROWS + row) * kD + 16 * jb + c16] = acc[mt][jb][e] * sc;
+        for (int jb = 0; jb < 8; ++jb) red_acc[(wave * ROWS + row) * kD + 16 * jb + c16] = acc[0][jb][e];
       }
+    } else {
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = mt * 16 + 4 * g + e;
+          float M = kNegInf;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[row * NW + w]);
+          const float mw = red_m[row * NW + wave];
+          const float sc = mw == kNegInf ? 0.f : exp2_fast(mw - M);
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) red_acc[(wave * ROWS + row) * kD + 16 * jb + c16] = acc[mt][jb][e] * sc;
+        }
+    }
     __syncthreads();
 
     // Each thread finishes 4 consecutive head_dim values of a row at a time: the normalised output, or
@@ -871,8 +893,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float mw = red_m[n * NW + w];
-          if (mw != kNegInf) lsum = fmaf(exp2_fast(mw - M), red_l[n * NW + w], lsum);
-          a += *reinterpret_cast<const f32x4*>(red_acc + (w * ROWS + n) * kD + d4);
+          const float sc = mw == kNegInf ? 0.f : exp2_fast(mw - M);
+          lsum = fmaf(sc, red_l[n * NW + w], lsum);
+          const f32x4 aw = *reinterpret_cast<const f32x4*>(red_acc + (w * ROWS + n) * kD + d4);
+          if constexpr (kOneBarrier)
+            a += sc * aw;
+          else
+            a += aw;
         }
       }
       const int64_t orow = out_row(n);
