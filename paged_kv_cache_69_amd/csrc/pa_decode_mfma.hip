@@ -908,8 +908,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
         *reinterpret_cast<f32x4*>(p.part_acc + pi * kD + d4) = a;
         if (d4 == 0) *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{M, lsum};
       } else {
+        f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_out(p, orow * kD + d4 + e, lsum > 0.f ? a[e] / lsum : 0.f);
+        for (int e = 0; e < 4; ++e) o[e] = lsum > 0.f ? a[e] / lsum : 0.f;
+        if (p.out_dtype == PA_F32) {  // one 16-byte store (out is 16-byte aligned, d4 a multiple of 4)
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * kD + d4) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_out(p, orow * kD + d4 + e, o[e]);
+        }
       }
     }
   }
