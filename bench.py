@@ -54,14 +54,14 @@ CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic cou
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Launch configuration per workload: partition_tokens None = single-pass decode; fused = the step is
-# one pa_write_kv_decode call (measured faster than the two calls on batch64 and long, slower on the
-# prefix and speculative workloads, where the separate append is a small share of the step).
+# one fused append + decode call (pa_write_kv_decode[_partitioned|_cascade]), measured faster than the
+# two calls on batch64, long and prefix; the speculative workload keeps the two calls.
 WORKLOADS = {
     "batch64": dict(partition_tokens=None, fused=True, desc="64 seqs, L~U[20,500], 32 q / 8 kv heads, head_dim 128, b=16, "
                                                "bf16 (Llama-3-8B-shaped layer)"),
     "long": dict(partition_tokens=512, fused=True, desc="16 seqs, L log-uniform [4096,32768], 32 q / 8 kv heads, head_dim 128, "
                                             "b=16, bf16, 512-token partitions + merge"),
-    "prefix": dict(partition_tokens=256, cascade=2048,
+    "prefix": dict(partition_tokens=256, cascade=2048, fused=True,
                    desc="128 seqs sharing a 2048-token (128-block) prefix + U[64,1024] private suffix, 32 q / 8 kv "
                         "heads, head_dim 128, b=16, bf16; cascade: the prefix read once for all sequences, "
                         "256-token suffix partitions + merge"),
@@ -226,7 +226,10 @@ class Replica:
         if not self.fused:
             self.decode(stream)
             return
-        if self.ws is None:
+        if self.cascade:
+            st = self.lib.pa_write_kv_decode_cascade(*self.fused_args, self.out.data_ptr(), self.cascade, self.max_len,
+                                                     self.pt, self.ws.data_ptr(), self.ws.numel(), stream)
+        elif self.ws is None:
             st = self.lib.pa_write_kv_decode(*self.fused_args, self.out.data_ptr(), stream)
         else:
             st = self.lib.pa_write_kv_decode_partitioned(*self.fused_args, self.out.data_ptr(), self.max_len, self.pt,

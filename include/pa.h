@@ -251,6 +251,24 @@ int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, co
                       int32_t prefix_tokens, int32_t max_seq_len, int32_t partition_tokens,
                       void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
+/* pa_write_kv_decode_cascade: pa_write_kv of the T new tokens at each
+ * sequence's last T positions (seq_lens[i] - T .. seq_lens[i] - 1), then
+ * pa_decode_cascade, in the same two launches as pa_decode_cascade: the
+ * suffix items that hold the new positions store them and read them from
+ * k_new / v_new rather than from the pool ([P4] section "Block table and
+ * allocator"), so the results (pools and out) are bit for bit those of
+ * pa_write_kv followed by pa_decode_cascade.
+ *   k_new, v_new : [B, T, Hkv, D], q_dtype, 16-byte aligned
+ * Other arguments, shapes and preconditions as pa_decode_cascade; the new
+ * positions must lie past the shared prefix (seq_lens[i] - T >=
+ * prefix_tokens, checked under PA_CHECK=1), in each sequence's private
+ * blocks. Null k_new or v_new: PA_ERR_INVALID_ARG. */
+int pa_write_kv_decode_cascade(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                               void* k_pool, void* v_pool, const int32_t* block_tables,
+                               const int32_t* seq_lens, float scale, void* out, int32_t prefix_tokens,
+                               int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, pa_stream_t stream);
+
 /* ---- int8 KV cache ([P2] "Модуль 09: PagedAttention: пейджинг KV-кэша",
  * section 6: block-wise KV quantisation).
  *

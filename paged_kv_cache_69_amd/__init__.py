@@ -39,6 +39,7 @@ EXPORTS = (
     "pa_decode_partitioned_wave_parts",
     "pa_decode_cascade_workspace_bytes",
     "pa_decode_cascade",
+    "pa_write_kv_decode_cascade",
     "pa_write_kv_decode",
     "pa_write_kv_decode_partitioned",
     "pa_write_kv_int8",
@@ -131,6 +132,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_cascade.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32, _P,
                                       ctypes.c_size_t, _P]
     lib.pa_decode_cascade.restype = ctypes.c_int
+    lib.pa_write_kv_decode_cascade.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
+                                               _I32, _P, ctypes.c_size_t, _P]
+    lib.pa_write_kv_decode_cascade.restype = ctypes.c_int
     lib.pa_write_kv_decode.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     lib.pa_write_kv_decode.restype = ctypes.c_int
     lib.pa_write_kv_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32,
@@ -341,6 +345,32 @@ def decode_cascade(q, k_pool, v_pool, block_tables, seq_lens, scale: float, pref
                                int(prefix_tokens), int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_cascade", st)
+    return out
+
+
+def write_kv_decode_cascade(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, scale: float, prefix_tokens: int,
+                            max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                            stream=None):
+    """``pa_write_kv_decode_cascade``: the step's KV append and the cascade decode in the same launches."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    need = cascade_workspace_bytes(q, k_pool, block_tables, prefix_tokens, max_seq_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dev = _check_tensors(q=q, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                         seq_lens=seq_lens, out=out, workspace=workspace)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape and k_new.shape == v_new.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype)
+    st = lib.pa_write_kv_decode_cascade(ctypes.byref(dims), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                        k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+                                        seq_lens.data_ptr(), float(scale), out.data_ptr(), int(prefix_tokens),
+                                        int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(lib, "pa_write_kv_decode_cascade", st)
     return out
 
 

@@ -245,6 +245,57 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
 
 }  // namespace
 
+// Both cascade entry points: argument checks, then the prefix and suffix items in one launch and the
+// merge. With k_new / v_new the suffix items also append the new rows (they follow the shared prefix).
+static int cascade_entry(const pa_dims* dims, bool append, const void* q, const void* k_new, const void* v_new,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         const int32_t* seq_lens, float scale, void* out, int32_t prefix_tokens,
+                         int32_t max_seq_len, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         pa_stream_t stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || prefix_tokens < 0 || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
+  if (max_seq_len < prefix_tokens) return PA_ERR_INVALID_ARG;
+  const int32_t b = dims->block_size;
+  if (partition_tokens % 16 != 0 || partition_tokens % b != 0 || prefix_tokens % 16 != 0 || prefix_tokens % b != 0)
+    return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < pa_decode_cascade_workspace_bytes(dims, prefix_tokens, max_seq_len, partition_tokens))
+    return PA_ERR_INVALID_ARG;
+  if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, max_seq_len, s);
+  if (st == PA_OK) st = pa::debug_check_prefix(dims, block_tables, seq_lens, prefix_tokens, s);
+  if (st != PA_OK) return st;
+
+  const int32_t parts = cascade_parts(dims, prefix_tokens, max_seq_len, partition_tokens);
+  size_t ml_bytes = 0, acc_bytes = 0;
+  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
+  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
+  p.parts = parts;
+  p.part_tokens = partition_tokens;
+  p.partial = 1;
+  p.prefix_tokens = prefix_tokens;
+  p.prefix_part_tokens = cascade_chunk(dims, prefix_tokens);
+  p.prefix_parts = cascade_prefix_slots(dims, prefix_tokens);
+  p.part_ml = static_cast<float*>(workspace);
+  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
+  p.row_groups = 1;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.append = append ? 1 : 0;
+  // the prefix's items and the sequences' own partitions in one launch, then the merge
+  discard_stale_error();
+  st = launch_status(p.prefix_parts > 0 ? pa::launch_cascade(p, s) : pa::launch_decode_mfma(p, s));
+  if (st != PA_OK) return st;
+  return launch_status(pa::launch_merge_partials(p, s));
+}
+
+
 extern "C" {
 
 int pa_abi_version(void) { return kAbiVersion; }
@@ -335,43 +386,17 @@ int pa_decode_cascade(const pa_dims* dims, const void* q, const void* k_pool, co
                       const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
                       int32_t prefix_tokens, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                       size_t workspace_bytes, pa_stream_t stream) {
-  int st = check_dims(dims);
-  if (st != PA_OK) return st;
-  if (dims->num_seqs == 0) return PA_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace) return PA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale) || prefix_tokens < 0 || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
-  if (max_seq_len < prefix_tokens) return PA_ERR_INVALID_ARG;
-  const int32_t b = dims->block_size;
-  if (partition_tokens % 16 != 0 || partition_tokens % b != 0 || prefix_tokens % 16 != 0 || prefix_tokens % b != 0)
-    return PA_ERR_INVALID_ARG;
-  if (workspace_bytes < pa_decode_cascade_workspace_bytes(dims, prefix_tokens, max_seq_len, partition_tokens))
-    return PA_ERR_INVALID_ARG;
-  if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = pa::debug_check(dims, block_tables, seq_lens, nullptr, max_seq_len, s);
-  if (st == PA_OK) st = pa::debug_check_prefix(dims, block_tables, seq_lens, prefix_tokens, s);
-  if (st != PA_OK) return st;
+  return cascade_entry(dims, false, q, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                       prefix_tokens, max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+}
 
-  const int32_t parts = cascade_parts(dims, prefix_tokens, max_seq_len, partition_tokens);
-  size_t ml_bytes = 0, acc_bytes = 0;
-  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
-  DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
-  p.parts = parts;
-  p.part_tokens = partition_tokens;
-  p.partial = 1;
-  p.prefix_tokens = prefix_tokens;
-  p.prefix_part_tokens = cascade_chunk(dims, prefix_tokens);
-  p.prefix_parts = cascade_prefix_slots(dims, prefix_tokens);
-  p.part_ml = static_cast<float*>(workspace);
-  p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
-  p.row_groups = 1;
-  // the prefix's items and the sequences' own partitions in one launch, then the merge
-  discard_stale_error();
-  st = launch_status(p.prefix_parts > 0 ? pa::launch_cascade(p, s) : pa::launch_decode_mfma(p, s));
-  if (st != PA_OK) return st;
-  return launch_status(pa::launch_merge_partials(p, s));
+int pa_write_kv_decode_cascade(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                               void* k_pool, void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                               float scale, void* out, int32_t prefix_tokens, int32_t max_seq_len,
+                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                               pa_stream_t stream) {
+  return cascade_entry(dims, true, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                       prefix_tokens, max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -769,18 +769,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 
   // Single pass with T <= 2: the last wave (the fewest tiles) stores the new rows after its tiles. Their
   // data and slots are fetched now, ahead of the tiles, so those stores wait on nothing by then.
-  const bool late = APPEND && !WAVE_ITEMS && T <= 2;
+  // Split items: the wave whose range holds a new row stores it the same way, after its own tiles.
+  const bool late = APPEND && !CASCADE && T <= 2;
   u32x4 late_row = {0u, 0u, 0u, 0u};
   int64_t late_dst = -1;
-  if constexpr (APPEND && !WAVE_ITEMS) {
-    if (late && wave == NW - 1) {
+  if constexpr (APPEND && !CASCADE) {
+    if (late && (WAVE_ITEMS || wave == NW - 1)) {
       // lane: row t = lane / 32; K (lanes 0-15 of the half) or V (16-31); 16-byte chunk lane % 16
       const int t = lane >> 5, which = (lane >> 4) & 1, chunk = lane & 15;
       const int pos0 = L - T, pos1 = L - 1;  // the rows' positions (one row when T = 1)
       const int blk0 = (int)min((uint32_t)trow[min(max(pos0, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
       const int blk1 = (int)min((uint32_t)trow[min(max(pos1, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
       const int pos = L - T + t;
-      if (t < T && pos >= 0) {
+      const bool mine = !WAVE_ITEMS || (pos >= p_begin && pos < p_end);
+      if (t < T && pos >= 0 && mine) {
         late_row = load16(new_row(which ? p.v_new : p.k_new, t) + chunk * 16);
         late_dst = (int64_t)(t ? blk1 : blk0) * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
       }
@@ -791,7 +793,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     // One row per step, so its position and block are wave-uniform (a scalar table load); lanes 0-15
     // copy the K row's 16-byte chunks and lanes 16-31 the V row's.
     const int t_lo = WAVE_ITEMS ? max(0, p_begin - (L - T)) : 0;
-    const int t_hi = WAVE_ITEMS ? min(T, p_end - (L - T)) : (wave == 0 && !late ? T : 0);
+    const int t_hi = late ? 0 : WAVE_ITEMS ? min(T, p_end - (L - T)) : (wave == 0 ? T : 0);
     for (int t = max(t_lo, T - L); t < t_hi; ++t) {
       const int pos = L - T + t;
       const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
@@ -806,7 +808,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 
   for (int from = 0; (from = run(from)) >= 0;) {
   }
-  if constexpr (APPEND && !WAVE_ITEMS) {
+  if constexpr (APPEND && !CASCADE) {
     if (late_dst >= 0) {
       const bool v_half = (lane >> 4) & 1;
       *reinterpret_cast<u32x4*>(const_cast<char*>(v_half ? vbase : kbase) + late_dst) = late_row;
@@ -932,7 +934,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(
 // the sequences' own partitions (HBM-bound) run side by side instead of one launch after the other.
 // Blocks alternate between the two kinds in runs of Hkv (one run is one index of every kv head, so
 // each kind keeps its kv head = XCD placement), and whichever kind has more runs takes the tail.
-template <int MT, int BS>
+template <int MT, int BS, bool AP>
 __global__ __launch_bounds__(kMfmaWaves * 64) __attribute__((amdgpu_waves_per_eu(PA_CASCADE_WAVES_PER_EU)))
 void cascade_kernel(const DecodeParams p, int pre_runs, int suf_runs) {
   constexpr int kPre = decode_lds_bytes<2, kMfmaWaves, true, true>();
@@ -945,7 +947,7 @@ void cascade_kernel(const DecodeParams p, int pre_runs, int suf_runs) {
   if (prefix)
     decode_body<2, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, true, false>(p, lds, idx);
   else
-    decode_body<MT, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, false, false>(p, lds, idx);
+    decode_body<MT, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, AP, false, false>(p, lds, idx);
 }
 
 template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false, bool F8 = false>
@@ -1019,14 +1021,14 @@ bool mfma_int8_supported(const pa_dims& d) {
          (d.block_size == 16 || d.block_size == 32) && rows <= 32;
 }
 
-template <int MT>
+template <int MT, bool AP>
 hipError_t launch_cascade_bs(const DecodeParams& p, hipStream_t stream, int pre_runs, int suf_runs) {
   const dim3 grid((unsigned)((int64_t)(pre_runs + suf_runs) * p.Hkv)), block(kMfmaWaves * 64);
   switch (p.block_size) {
-    case 4: cascade_kernel<MT, 4><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
-    case 8: cascade_kernel<MT, 8><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
-    case 16: cascade_kernel<MT, 16><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
-    case 32: cascade_kernel<MT, 32><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 4: cascade_kernel<MT, 4, AP><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 8: cascade_kernel<MT, 8, AP><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 16: cascade_kernel<MT, 16, AP><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
+    case 32: cascade_kernel<MT, 32, AP><<<grid, block, 0, stream>>>(p, pre_runs, suf_runs); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1038,8 +1040,12 @@ hipError_t launch_cascade(const DecodeParams& p, hipStream_t stream) {
   const int64_t pre_runs = ((int64_t)p.B * p.rows + 31) / 32 * ((pre_items + kMfmaWaves - 1) / kMfmaWaves);
   const int64_t suf_runs = (int64_t)p.B * ((p.parts - p.prefix_parts + kMfmaWaves - 1) / kMfmaWaves);
   if (pre_runs + suf_runs == 0) return hipSuccess;
-  return p.rows <= 16 ? launch_cascade_bs<1>(p, stream, (int)pre_runs, (int)suf_runs)
-                      : launch_cascade_bs<2>(p, stream, (int)pre_runs, (int)suf_runs);
+  // fused append: the suffix items hold every new row (they follow the shared prefix)
+  if (p.append)
+    return p.rows <= 16 ? launch_cascade_bs<1, true>(p, stream, (int)pre_runs, (int)suf_runs)
+                        : launch_cascade_bs<2, true>(p, stream, (int)pre_runs, (int)suf_runs);
+  return p.rows <= 16 ? launch_cascade_bs<1, false>(p, stream, (int)pre_runs, (int)suf_runs)
+                      : launch_cascade_bs<2, false>(p, stream, (int)pre_runs, (int)suf_runs);
 }
 
 int mfma_waves() { return kMfmaWaves; }

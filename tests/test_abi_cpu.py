@@ -138,6 +138,18 @@ def test_partitioned_wave_parts_override(lib, monkeypatch):
     assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d8), 32768, 512) == 1
 
 
+def test_fused_cascade_refuses_missing_rows(lib):
+    d = _dims()
+    ws = ctypes.c_void_p(0x100000)
+    call = lambda kn, vn, n=10**9: lib.pa_write_kv_decode_cascade(  # noqa: E731
+        ctypes.byref(d), FAKE, kn, vn, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 32, 1000, 512, ws, n, None)
+    assert call(None, FAKE) == -1 and call(FAKE, None) == -1
+    assert call(ctypes.c_void_p(0x1008), FAKE) == -1  # k_new not 16-byte aligned
+    d0 = _dims(num_seqs=0)  # an empty batch is a no-op
+    assert lib.pa_write_kv_decode_cascade(ctypes.byref(d0), None, None, None, None, None, None, None, 0.1, None, 0, 1,
+                                          16, None, 0, None) == 0
+
+
 def test_partitioned_rejects_bad_partitions(lib):
     d = _dims()
     ws = ctypes.c_void_p(0x100000)

@@ -37,6 +37,21 @@ def _step(pa, case, prefix_tokens, pt):
     return g, out
 
 
+def _fused_step(pa, case, prefix_tokens, pt):
+    """pa_write_kv_decode_cascade on fresh copies of the inputs."""
+    f = _gpu(case)
+    out = pa.write_kv_decode_cascade(f["q"], f["k_new"], f["v_new"], f["k_pool"], f["v_pool"], f["block_tables"],
+                                     f["seq_lens"], case.scale, prefix_tokens, case.max_seq_len, pt)
+    torch.cuda.synchronize()
+    return f, out
+
+
+def _same_step(g, out, f, fout):
+    assert torch.equal(g["k_pool"].view(torch.int16), f["k_pool"].view(torch.int16)), "fused append: K pool differs"
+    assert torch.equal(g["v_pool"].view(torch.int16), f["v_pool"].view(torch.int16)), "fused append: V pool differs"
+    assert torch.equal(out, fout), "fused append: output differs"
+
+
 @pytest.mark.parametrize("b", [4, 8, 16, 32])
 @pytest.mark.parametrize("hq,hkv,t", [(4, 4, 1), (32, 8, 1), (8, 2, 4), (64, 8, 4), (12, 4, 3)])
 def test_cascade_shapes(gpu_lib, b, hq, hkv, t):
@@ -58,6 +73,7 @@ def test_cascade_shapes(gpu_lib, b, hq, hkv, t):
             assert np.array_equal(bits(g["k_pool"]), kp) and np.array_equal(bits(g["v_pool"]), vp)
             assert_attention_close(out.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32,
                                    what=f"cascade prefix={prefix} pt={pt}")
+            _same_step(g, out, *_fused_step(gpu_lib, case, prefix, pt))
 
 
 def test_cascade_without_prefix_is_the_split_path_bitwise(gpu_lib):
@@ -81,6 +97,16 @@ def test_cascade_prefix_workload_subset(gpu_lib, pt):
     g, out = _step(gpu_lib, case, 2048, pt)
     assert_attention_close(out.cpu(), _oracle(case, kp, vp), kv_dtype=torch.bfloat16, out_dtype=torch.float32,
                            what=f"prefix pt={pt}")
+
+
+def test_cascade_fused_append_full_size_bitwise(gpu_lib):
+    """All 128 sequences of the prefix workload: the fused append + cascade equals pa_write_kv followed by
+    pa_decode_cascade bit for bit (pools and out), in the launch configuration the benchmark times."""
+    case = make_case("prefix", pool_device=DEV)
+    print("[case] cascade fused full", flush=True)
+    g, out = _step(gpu_lib, case, 2048, 256)
+    f, fout = _fused_step(gpu_lib, case, 2048, 256)
+    _same_step(g, out, f, fout)
 
 
 def test_cascade_full_size_sampled(gpu_lib):
