@@ -767,24 +767,26 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     return again;
   };
 
-  // Single pass with T <= 2: the last wave (the fewest tiles) stores the new rows after its tiles. Their
-  // data and slots are fetched now, ahead of the tiles, so those stores wait on nothing by then.
-  // Split items: the wave whose range holds a new row stores it the same way, after its own tiles.
-  const bool late = APPEND && !CASCADE && T <= 2;
+  // Single pass: the last waves (the fewest tiles) store the new rows after their tiles, two rows each
+  // (wave NW - 1 rows 0-1, wave NW - 2 rows 2-3, ...). Their data and slots are fetched now, ahead of the
+  // tiles, so those stores wait on nothing by then. Split items with T <= 2: the wave whose range holds a
+  // new row stores it the same way, after its own tiles.
+  const bool late = APPEND && !CASCADE && (WAVE_ITEMS ? T <= 2 : T <= 2 * NW);
   u32x4 late_row = {0u, 0u, 0u, 0u};
   int64_t late_dst = -1;
   if constexpr (APPEND && !CASCADE) {
-    if (late && (WAVE_ITEMS || wave == NW - 1)) {
-      // lane: row t = lane / 32; K (lanes 0-15 of the half) or V (16-31); 16-byte chunk lane % 16
-      const int t = lane >> 5, which = (lane >> 4) & 1, chunk = lane & 15;
-      const int pos0 = L - T, pos1 = L - 1;  // the rows' positions (one row when T = 1)
+    const int t_base = WAVE_ITEMS ? 0 : 2 * (NW - 1 - wave);  // this wave's first row
+    if (late && t_base < T) {
+      // lane: row t_base + lane / 32; K (lanes 0-15 of the half) or V (16-31); 16-byte chunk lane % 16
+      const int t = t_base + (lane >> 5), which = (lane >> 4) & 1, chunk = lane & 15;
+      const int pos0 = L - T + t_base, pos1 = min(pos0 + 1, L - 1);  // the two rows' positions
       const int blk0 = (int)min((uint32_t)trow[min(max(pos0, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
       const int blk1 = (int)min((uint32_t)trow[min(max(pos1, 0) / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
       const int pos = L - T + t;
       const bool mine = !WAVE_ITEMS || (pos >= p_begin && pos < p_end);
       if (t < T && pos >= 0 && mine) {
         late_row = load16(new_row(which ? p.v_new : p.k_new, t) + chunk * 16);
-        late_dst = (int64_t)(t ? blk1 : blk0) * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
+        late_dst = (int64_t)(t > t_base ? blk1 : blk0) * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
       }
     }
   }
