@@ -50,6 +50,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
+REPLICAS = 0  # --replicas N: that many input copies instead of enough for a cold cache (a warm-cache run)
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -269,7 +270,7 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
         keys += ["k_scales", "v_scales"]
     src = {k: getattr(case, k).to(dev) for k in keys}
     touched = unique_bytes(case)  # a block shared by several tables is cached once
-    n_rep = max(1, min(64, math.ceil(COLD_BYTES / touched)))
+    n_rep = REPLICAS or max(1, min(64, math.ceil(COLD_BYTES / touched)))
     reps = [Replica(pa, case, src, partition_tokens, variant, fused, cascade) for _ in range(n_rep)]
     del src
     torch.cuda.synchronize()
@@ -760,6 +761,28 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
     return "\n".join(lines) + "\n"
 
 
+def summarize_l2(directory: str, workload: str, command: str) -> str:
+    """L2 (TCC) hits and misses per kernel, median over dispatches, from a
+    ``rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum`` run of ``bench.py --workload W``."""
+    per = {}
+    for r in _pmc_rows(directory):
+        if r["Counter_Name"] in ("TCC_HIT_sum", "TCC_MISS_sum"):
+            per.setdefault((r["Counter_Name"], _short(r["Kernel_Name"])), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+    kernels = sorted({k[1] for k in med
+                      if k[1].startswith("void decode_") or "merge_partials" in k[1] or "cascade_kernel" in k[1]
+                      or "prefill_mfma" in k[1]})
+    lines = [f"# L2 (TCC) hits and misses of one decode call, workload {workload} (median over dispatches)",
+             f"# command (from the repository root): {command}",
+             f"workload = {workload}", f"library_sha256 = {library_sha256()}"]
+    for i, k in enumerate(kernels):
+        hit, miss = med.get(("TCC_HIT_sum", k), 0.0), med.get(("TCC_MISS_sum", k), 0.0)
+        rate = hit / (hit + miss) if hit + miss else 0.0
+        lines += [f"kernel_{i} = {k}", f"kernel_{i}_tcc_hit = {hit:.0f}", f"kernel_{i}_tcc_miss = {miss:.0f}",
+                  f"kernel_{i}_l2_hit_rate = {rate:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
 def summarize_stats(directory: str, command: str, bench_log: str | None = None) -> str:
     """Text summary of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv, or the kernels
     of its results database): calls and durations per kernel, plus the bench line's own figure."""
@@ -816,10 +839,16 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true",
                     help="time eagerly launched steps only (for counter-collection runs; not a headline number)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"))
+    ap.add_argument("--summarize-l2", nargs=2, metavar=("L2_DIR", "COMMAND"))
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="input copies to rotate over (default: enough to miss every cache; 1: warm)")
     ap.add_argument("--summarize-stats", nargs="+", metavar="DIR COMMAND [BENCH_LOG]")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.workload), end="")
+        return 0
+    if args.summarize_l2:
+        print(summarize_l2(args.summarize_l2[0], args.workload, args.summarize_l2[1]), end="")
         return 0
     if args.summarize_stats:
         print(summarize_stats(*args.summarize_stats), end="")
@@ -828,6 +857,8 @@ def main(argv=None):
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode step runs on one "
               "GPU and needs no collectives (DESIGN.md says how it would shard).", file=sys.stderr)
         return 2
+    global REPLICAS
+    REPLICAS = max(0, args.replicas)
 
     import torch
 
