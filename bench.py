@@ -664,8 +664,9 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     if spec.get("int8") or spec.get("fp8"):
         call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + ("_fp8" if spec.get("fp8") else "_int8")
     if cascade:
-        call = "pa_decode_cascade"
-        kernel = "cascade_kernel (shared-prefix items and per-sequence items in one launch)"
+        call = "pa_write_kv_decode_cascade" if fused else "pa_decode_cascade"
+        kernel = "cascade_kernel (shared-prefix items and per-sequence items in one launch" + (
+            ", the KV append fused in)" if fused else ")")
     kernel += (" + merge_partials_kernel" if spec["partition_tokens"] else "") + f" (one {call} call)"
     traffic = traffic_from_profiles(name) if variant == 0 else None
     res = {
@@ -684,8 +685,13 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         "dtype": {torch.bfloat16: "bf16", torch.int8: "int8 KV (bf16 q, fp32 scales)",
                   torch.float8_e4m3fn: "fp8 e4m3 KV (bf16 q, fp32 scales)"}.get(case.k_pool.dtype, "f32"),
     }
-    if name == "prefix":
+    if cascade:
+        # the roofline counts every shared block once; every sequence reading its whole context is the
+        # logical figure (what a decode without the cascade would ask of memory)
+        logical = algorithmic_bytes(case)
         res["unique_bytes"] = unique_bytes(case)
+        res["logical_bytes"] = logical
+        res["achieved_gbps_logical"] = round(logical / (dur_ms * 1e-3) / 1e9, 1)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(case, cpu_budget)
     del case
