@@ -904,7 +904,7 @@ def main(argv=None):
                          not args.no_fused)
         secondary[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 6),
                            "achieved_gbps": round(r["achieved_gbps"], 1), "roofline": r["roofline"],
-                           "config": r["config"], **({"unique_bytes": r["unique_bytes"]} if "unique_bytes" in r else {})}
+                           "config": r["config"], **{k: r[k] for k in ("unique_bytes", "logical_bytes", "achieved_gbps_logical") if k in r}}
     if secondary:
         line["secondary"] = secondary
     print(json.dumps(line), flush=True)
