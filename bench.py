@@ -210,9 +210,11 @@ class Replica:
         self.f_write = getattr(self.lib, "pa_write_kv" + sfx)
         self.f_decode = getattr(self.lib, "pa_decode" + sfx)
         self.f_split = getattr(self.lib, "pa_decode_partitioned" + sfx)
-        self.fused = fused and not self.int8
+        # 8-bit pools: the fused call serves the single pass over 16-position blocks
+        self.fused = fused and (not self.int8 or (not partition_tokens and case.block_size == 16))
         self.fused_args = (ctypes.byref(self.dims), p["q"], p["k_new"], p["v_new"], p["k_pool"], p["v_pool"],
-                           p["block_tables"], p["seq_lens"], self.scale)
+                           *scales, p["block_tables"], p["seq_lens"], self.scale)
+        self.f_fused8 = getattr(self.lib, "pa_write_kv_decode" + sfx) if self.int8 else None
 
     def step(self, stream):
         """One whole decode step: the fused append + decode call where there is one, else the two calls."""
@@ -227,7 +229,9 @@ class Replica:
         if not self.fused:
             self.decode(stream)
             return
-        if self.cascade:
+        if self.int8:
+            st = self.f_fused8(*self.fused_args, self.out.data_ptr(), stream)
+        elif self.cascade:
             st = self.lib.pa_write_kv_decode_cascade(*self.fused_args, self.out.data_ptr(), self.cascade, self.max_len,
                                                      self.pt, self.ws.data_ptr(), self.ws.numel(), stream)
         elif self.ws is None:
@@ -648,21 +652,22 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
     mfma_ok = (case.k_pool.dtype in (torch.bfloat16, torch.int8, torch.float8_e4m3fn) and case.q.shape[3] == 128
                and rows <= 32)
-    fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok and case.k_pool.dtype == torch.bfloat16
+    fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok
     cascade = spec.get("cascade", 0) if variant != 1 else 0
     sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs,
                                               fused, cascade)
     # a cascade reads each shared block once: count every physical block once
     algo = unique_bytes(case) if cascade else algorithmic_bytes(case)
     if fused:  # the call also reads the new rows and stores them into the pools
-        algo += 2 * case.k_new.numel() * case.k_new.element_size() * 2
+        algo += 2 * case.k_new.numel() * (case.k_new.element_size() + case.k_pool.element_size())
     achieved = algo / (dur_ms * 1e-3) / 1e9
     kernel = "decode_mfma_kernel" if (variant == 2 or (variant == 0 and mfma_ok)) else "decode_valu_kernel"
     if fused:
         kernel += " with the KV append fused in"
     call = ("pa_write_kv_decode" if fused else "pa_decode") + ("_partitioned" if spec["partition_tokens"] else "")
     if spec.get("int8") or spec.get("fp8"):
-        call = "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "") + ("_fp8" if spec.get("fp8") else "_int8")
+        call = ("pa_write_kv_decode" if fused else "pa_decode" + ("_partitioned" if spec["partition_tokens"] else "")) + (
+            "_fp8" if spec.get("fp8") else "_int8")
     if cascade:
         call = "pa_write_kv_decode_cascade" if fused else "pa_decode_cascade"
         kernel = "cascade_kernel (shared-prefix items and per-sequence items in one launch" + (

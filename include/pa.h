@@ -319,6 +319,31 @@ int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t*
                                void* out, int32_t max_seq_len, int32_t partition_tokens,
                                void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
+/* pa_write_kv_decode_int8 / pa_write_kv_decode_fp8: one decode step over
+ * 8-bit pools in one launch: pa_write_kv_int8 (or _fp8) of the T new tokens
+ * at each sequence's last T positions (seq_lens[i] - T .. seq_lens[i] - 1),
+ * then pa_decode_int8 (or _fp8). The workgroup of each (sequence, kv head)
+ * appends that head's rows itself, in the tile that holds them: the block's
+ * scale grows to cover the new rows, the codes already in the block are
+ * re-quantised when it grew, the new rows are quantised, and the changed
+ * codes and the scale are stored; that tile then takes part in the
+ * attention with its new codes. Every code and scale is decided with the
+ * operations of the separate append, so the results (pools, scales and
+ * out) are bit for bit those of the two calls.
+ *   k_new, v_new : [B, T, Hkv, D] bf16;  k_pool, v_pool, k_scales, v_scales :
+ *                  written in place
+ * Supported: the shapes of pa_decode_int8 with b = 16; otherwise
+ * PA_ERR_UNSUPPORTED. Null k_new or v_new (B > 0): PA_ERR_INVALID_ARG. The
+ * new rows' blocks must not be read by another sequence in the same call. */
+int pa_write_kv_decode_int8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                            int8_t* k_pool, int8_t* v_pool, float* k_scales, float* v_scales,
+                            const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                            pa_stream_t stream);
+int pa_write_kv_decode_fp8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                           uint8_t* k_pool, uint8_t* v_pool, float* k_scales, float* v_scales,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                           pa_stream_t stream);
+
 /* ---- Paged prefill ([P1] "25. Paged attention and prefix caching", stretch
  * exercise 4; [P4] "PagedAttention and the KV Cache", section "Prefill vs
  * decode under paging"; [P5] section 4.1).

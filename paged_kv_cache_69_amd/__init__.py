@@ -45,9 +45,11 @@ EXPORTS = (
     "pa_write_kv_int8",
     "pa_decode_int8",
     "pa_decode_partitioned_int8",
+    "pa_write_kv_decode_int8",
     "pa_write_kv_fp8",
     "pa_decode_fp8",
     "pa_decode_partitioned_fp8",
+    "pa_write_kv_decode_fp8",
     "pa_write_kv_varlen",
     "pa_prefill",
     "pa_check_prefill_host",
@@ -142,6 +144,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_write_kv_decode_partitioned.restype = ctypes.c_int
     lib.pa_write_kv_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.pa_write_kv_int8.restype = ctypes.c_int
+    for name in ("pa_write_kv_decode_int8", "pa_write_kv_decode_fp8"):
+        getattr(lib, name).argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+        getattr(lib, name).restype = ctypes.c_int
     lib.pa_decode_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     lib.pa_decode_int8.restype = ctypes.c_int
     lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
@@ -457,7 +462,7 @@ def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_ta
 
 
 def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype, stream,
-               split=None):
+               split=None, new_rows=None):
     import torch
 
     lib = load_library()
@@ -466,6 +471,8 @@ def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_len
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
     tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
                    block_tables=block_tables, seq_lens=seq_lens, out=out)
+    if new_rows is not None:
+        tensors.update(k_new=new_rows[0], v_new=new_rows[1])
     if split is not None:
         max_seq_len, partition_tokens, workspace = split
         if workspace is None:
@@ -480,7 +487,13 @@ def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_len
     dims.kv_dtype = kv_code
     args = [ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scales.data_ptr(),
             v_scales.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
-    if split is None:
+    if new_rows is not None:
+        _require(new_rows[0].dtype == torch.bfloat16 and new_rows[0].shape == new_rows[1].shape,
+                 "k_new/v_new must be bf16 of one shape")
+        func = "pa_write_kv_decode_int8" if fmt == "int8" else "pa_write_kv_decode_fp8"
+        st = getattr(lib, func)(args[0], args[1], new_rows[0].data_ptr(), new_rows[1].data_ptr(), *args[2:],
+                                _stream_handle(stream, dev))
+    elif split is None:
         func = "pa_decode_int8" if fmt == "int8" else "pa_decode_fp8"
         st = getattr(lib, func)(*args, _stream_handle(stream, dev))
     else:
@@ -489,6 +502,20 @@ def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_len
                                 workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, func, st)
     return out
+
+
+def write_kv_decode_int8(q, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
+                         out=None, *, out_dtype=None, stream=None):
+    """``pa_write_kv_decode_int8``: append the step's rows into int8 pools and decode, in one launch."""
+    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream, new_rows=(k_new, v_new))
+
+
+def write_kv_decode_fp8(q, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
+                        out=None, *, out_dtype=None, stream=None):
+    """``pa_write_kv_decode_fp8``: append the step's rows into E4M3 pools and decode, in one launch."""
+    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
+                      stream, new_rows=(k_new, v_new))
 
 
 def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):

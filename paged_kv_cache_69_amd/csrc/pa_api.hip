@@ -202,6 +202,8 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   int variant = 0;
   if (int8) {
     if (dims->variant == PA_VARIANT_VALU || !pa::mfma_int8_supported(*dims)) return PA_ERR_UNSUPPORTED;
+    // the fused append into 8-bit pools: single pass, one 16-position block per tile
+    if (append && (split || dims->block_size != 16)) return PA_ERR_UNSUPPORTED;
     variant = PA_VARIANT_MFMA;
   } else if (append) {
     if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
@@ -450,6 +452,22 @@ int pa_decode_partitioned_fp8(const pa_dims* dims, const void* q, const uint8_t*
                               void* workspace, size_t workspace_bytes, pa_stream_t stream) {
   return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+int pa_write_kv_decode_int8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, int8_t* k_pool,
+                            int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                            const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
+  if (dims && dims->num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream, k_new, v_new);
+}
+
+int pa_write_kv_decode_fp8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, uint8_t* k_pool,
+                           uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
+  if (dims && dims->num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
+                      nullptr, 0, stream, k_new, v_new, true);
 }
 
 int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,

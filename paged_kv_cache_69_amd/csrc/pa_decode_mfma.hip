@@ -245,7 +245,7 @@ template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE, bool MULTI = false>
 constexpr int decode_lds_bytes() {
   const int v = NW * kTileBytes + (MULTI ? NW * stash_bytes<MT>() : 0);
   const int red = (!WAVE_ITEMS || CASCADE) ? (NW * 16 * MT * kD + 2 * NW * 16 * MT) * 4 : 0;
-  if (one_barrier_merge<MT, WAVE_ITEMS, CASCADE>()) return v + (kLptMaxSeqs + 4) * 4 + red;
+  if (one_barrier_merge<MT, WAVE_ITEMS, CASCADE>()) return v + (kLptMaxSeqs + 4) * 4 + red + 64;
   return v > red ? v : red;
 }
 
@@ -257,7 +257,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   static_assert(!MULTI || (WAVE_ITEMS && !CASCADE && !Q8), "two partitions per wave are for bf16 split items");
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
-  static_assert(!(Q8 && APPEND), "the fused append serves bf16 pools");
+  static_assert(!(Q8 && APPEND) || (!WAVE_ITEMS && BS == kTile && NW >= 2),
+                "8-bit pools take the fused append in a single pass of one-tile blocks");
   static_assert(!F8 || Q8, "FP8 pools are 8-bit pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
   constexpr int kKvTile = kTile * kKvRow;
@@ -497,7 +498,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
       for (int c = 0; c < 4; ++c)
         tr.v[c] = load16(vbase + pos_offset(ids, tile_p0, tile_p0 + 4 * c + (lane >> 4)) + (lane & 15) * 16);
     }
-    if constexpr (APPEND) {
+    if constexpr (APPEND && !Q8) {
       if (tile_p0 + kTile > L - T) {  // the tile holds new positions: their rows come from k_new / v_new
         const int tk = tile_p0 + c16 - (L - T);
         if (tk >= 0 && tk < T) {
@@ -520,6 +521,71 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   float vcorr[MT];  // int8 pools: this lane's sum of V-scaled P (weight of the V offset)
   f32x4 acc[MT][8];
   bool have_ref = false;
+
+  // Fused append into 8-bit pools (single pass, one block per tile). Before the tile loop, while the
+  // first tiles are on their way, the workgroup does what the separate append does for the (one or two)
+  // blocks of this kv head that take new rows: waves 0 and 1 the K and V of the first such block, waves
+  // 2 and 3 those of the second. The block's scale grows to cover the new rows (a block whose first row
+  // is new takes theirs alone), the codes already in it are re-quantised when it grew, the new rows are
+  // quantised, and the changed codes and the scale are stored; a barrier then makes the codes visible to
+  // the wave whose tile holds them. That wave takes the new scales from LDS (the scale array itself is
+  // read through the scalar cache, which may hold the old ones).
+  // fetch_new: this lane's 64 bytes of the new row `row` of the block at tile_p0, head_dim col0 .. +31.
+  // append_side: one side (K or V) of a block; w = this lane's 32 codes of block row `row` at col0 .. +31.
+  auto fetch_new = [&](u32x4 (&nv)[4], int tile_p0, int row, int col0, const void* src) {
+    const int pos = tile_p0 + row;
+    if (pos >= L - T && pos < L) {
+      const char* srow = static_cast<const char*>(src) +
+                         ((int64_t)(seq * T + (pos - (L - T))) * p.Hkv + kvh) * kRowBytes + col0 * 2;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) nv[c] = load16(srow + 16 * c);
+    }
+  };
+  float* q8_scales = reinterpret_cast<float*>(lds + decode_lds_bytes<MT, NW, false, false>() - 64);
+  auto append_side = [&](u32x4* w, int tile_p0, int row, int col0, const u32x4 (&nv)[4], float old_scale,
+                         char* block_base) -> float {
+    constexpr float kCodeMax = F8 ? 448.f : 127.f;  // scale = amax / kCodeMax
+    const int first_new = L - T;
+    const int first = max(0, first_new - tile_p0);  // rows of this block written before this step
+    const int pos = tile_p0 + row;
+    const bool is_new = pos >= first_new && pos < L;
+    float x[32];
+    float a = 0.f;
+    if (is_new) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = nv[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * c + 2 * e] = bf16_lo(v[e]);
+          x[8 * c + 2 * e + 1] = bf16_hi(v[e]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(x[j]));
+    }
+    a = wave_max(a);  // the largest magnitude among the new rows of this block and kv head
+    const float cand = a / kCodeMax;
+    const float old = first > 0 ? old_scale : 0.f;
+    const float scale = first > 0 ? fmaxf(old, cand) : cand;
+    if ((row < first && scale > old) || is_new) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {  // dword c: codes of head_dim col0 + 4c .. +3
+        const uint32_t word = w[c >> 2][c & 3];
+        uint32_t out = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float val = is_new ? x[4 * c + k] : code_value<F8>((word >> (8 * k)) & 0xFFu) * old;
+          out |= encode_code<F8>(val, scale) << (8 * k);
+        }
+        w[c >> 2][c & 3] = out;
+      }
+      char* dst = block_base + (int64_t)row * kD + col0;
+      *reinterpret_cast<u32x4*>(dst) = w[0];
+      *reinterpret_cast<u32x4*>(dst + 16) = w[1];
+    }
+    return scale;
+  };
 
   // S^T of one tile (C layout: lane l has positions 4g + e of score row c16 + 16*mt), scaled and masked.
   auto scores = [&](bool masked, int tile_p0, const TileRegs& tr, float kscale, f32x4 (&s)[MT]) {
@@ -723,8 +789,16 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
           cur[(u + PF) % NBUF] = ids;
           const int tile_p0 = tile_p0_of(i);
           const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
+          float kscale = ids_cur.ks, vscale = ids_cur.vs;
+          if constexpr (Q8 && APPEND) {
+            if (tile_p0 + kTile > L - T) {  // this tile (one block) took new rows: its new scales
+              const int sel = tile_p0 / kTile == (L - T) / kTile ? 0 : 2;
+              kscale = q8_scales[sel];
+              vscale = q8_scales[sel + 1];
+            }
+          }
           f32x4 s[MT];
-          scores(masked, tile_p0, ring[u], ids_cur.ks, s);
+          scores(masked, tile_p0, ring[u], kscale, s);
           if (!have_ref) {
             raise_ref(s);  // the wave's first tile sets the reference
             have_ref = true;
@@ -739,7 +813,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
               again = KP > 1 ? part_end - part_tiles : ib;
             }
           }
-          accumulate(masked, tile_p0, s, ring[u], ids_cur.vs);
+          accumulate(masked, tile_p0, s, ring[u], vscale);
           if (KP > 1 && i + 1 == part_end && i + 1 < my_tiles && again < 0) {
             // the first partition ends here: its partial waits in LDS until the wave's end. Written to
             // memory now, its stores would be younger than the tile loads in flight, and the waits for
@@ -771,10 +845,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   // (wave NW - 1 rows 0-1, wave NW - 2 rows 2-3, ...). Their data and slots are fetched now, ahead of the
   // tiles, so those stores wait on nothing by then. Split items with T <= 2: the wave whose range holds a
   // new row stores it the same way, after its own tiles.
-  const bool late = APPEND && !CASCADE && (WAVE_ITEMS ? T <= 2 : T <= 2 * NW);
+  const bool late = APPEND && !Q8 && !CASCADE && (WAVE_ITEMS ? T <= 2 : T <= 2 * NW);
   u32x4 late_row = {0u, 0u, 0u, 0u};
   int64_t late_dst = -1;
-  if constexpr (APPEND && !CASCADE) {
+  if constexpr (APPEND && !Q8 && !CASCADE) {
     const int t_base = WAVE_ITEMS ? 0 : 2 * (NW - 1 - wave);  // this wave's first row
     if (late && t_base < T) {
       // lane: row t_base + lane / 32; K (lanes 0-15 of the half) or V (16-31); 16-byte chunk lane % 16
@@ -790,7 +864,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
       }
     }
   }
-  if constexpr (APPEND) {
+  if constexpr (APPEND && !Q8) {
     // store the new rows this wave owns (positions L - T .. L - 1 in its range) into the pools
     // One row per step, so its position and block are wave-uniform (a scalar table load); lanes 0-15
     // copy the K row's 16-byte chunks and lanes 16-31 the V row's.
@@ -808,9 +882,31 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
   }
 
+  if constexpr (Q8 && APPEND) {
+    const int t0 = (L - T) / kTile, t1 = (L - 1) / kTile;  // the blocks taking new rows (b = 16)
+    const int which = wave & 1, tsel = wave >> 1;            // K or V; first or second block
+    if (L >= T && L > 0 && tsel < 2 && (tsel == 0 || t1 != t0)) {
+      const int tt = tsel ? t1 : t0;
+      const int blk = (int)min((uint32_t)trow[min(tt, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+      const int64_t si = (int64_t)blk * p.Hkv + kvh;
+      float* scales = const_cast<float*>(which ? p.v_scales : p.k_scales);
+      char* block_base = const_cast<char*>(which ? vbase : kbase) + (int64_t)blk * block_bytes;
+      // lane: row lane / 4 of the block, codes 32 (lane % 4) .. +31
+      const int row = lane >> 2, col0 = 32 * (lane & 3);
+      u32x4 w[2] = {load16(block_base + row * kD + col0), load16(block_base + row * kD + col0 + 16)};
+      u32x4 nv[4];
+      fetch_new(nv, tt * kTile, row, col0, which ? p.v_new : p.k_new);
+      const float sc = append_side(w, tt * kTile, row, col0, nv, scales[si], block_base);
+      if (lane == 0) {
+        scales[si] = sc;
+        q8_scales[tsel * 2 + which] = sc;
+      }
+    }
+    __syncthreads();  // the new codes are in the pools (and the scales in LDS) before any tile loads them
+  }
   for (int from = 0; (from = run(from)) >= 0;) {
   }
-  if constexpr (APPEND && !CASCADE) {
+  if constexpr (APPEND && !Q8 && !CASCADE) {
     if (late_dst >= 0) {
       const bool v_half = (lane >> 4) & 1;
       *reinterpret_cast<u32x4*>(const_cast<char*>(v_half ? vbase : kbase) + late_dst) = late_row;
@@ -977,6 +1073,11 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 
 template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_int8 && p.append) {  // fused append into 8-bit pools: single pass, 16-position blocks
+    if (WI || p.block_size != 16) return hipErrorInvalidValue;
+    return p.kv_fp8 ? launch_t<MT, 16, false, true, true, false, true>(p, stream)
+                    : launch_t<MT, 16, false, true, true, false, false>(p, stream);
+  }
   if (p.kv_int8 && p.kv_fp8) {
     switch (p.block_size) {
       case 16: return launch_t<MT, 16, WI, true, false, false, true>(p, stream);

@@ -66,4 +66,52 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
 }
 
+// ---- codes of 8-bit pools, shared by the append and the decode that appends in the same launch, so
+// both decide every code with the same fp32 operations: the scale amax / 127 (int8) or amax / 448
+// (E4M3), the quotient x / scale (correctly rounded), then round half to even and clip (int8) or the
+// E4M3 rounding below.
+__device__ __forceinline__ int quantise(float x, float scale) {
+  if (scale == 0.f) return 0;
+  return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);
+}
+
+// E4M3 (OCP: 4 exponent bits, bias 7, 3 mantissa bits, largest finite 448) code of a float32 y,
+// rounded to the nearest value with ties to the even code, saturated at +-448; the sign bit is y's.
+// Below 2^-6 the values are the multiples of 2^-9, so y * 512 rounded is the code itself (8 is the
+// smallest normal, 0x08); above, the top 3 mantissa bits are rounded on the other 20, and a carry
+// out of the mantissa steps the exponent, which the code's layout does by itself.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t m = (bits >> 20) & 7u, rest = bits & 0xFFFFFu;
+    code = ((((bits >> 23) - 120u) << 3) | m) + ((rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ? 1u : 0u);
+    code = min(code, 126u);
+  }
+  return code | sign;
+}
+
+// Value of an E4M3 code (exact in float32).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (code & 0x80u) ? -v : v;
+}
+
+// One code of an 8-bit pool: int8 (x / scale rounded to an integer) or E4M3.
+template <bool FP8>
+__device__ __forceinline__ uint32_t encode_code(float x, float scale) {
+  if constexpr (FP8) return scale == 0.f ? 0u : e4m3_encode(x / scale);
+  return (uint32_t)(uint8_t)quantise(x, scale);
+}
+template <bool FP8>
+__device__ __forceinline__ float code_value(uint32_t byte) {
+  if constexpr (FP8) return e4m3_value(byte);
+  return (float)(int8_t)byte;
+}
+
 }  // namespace pa

@@ -73,49 +73,6 @@ __device__ __forceinline__ float new_value(const WriteInt8Params& p, const void*
   return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[idx] << 16);
 }
 
-__device__ __forceinline__ int quantise(float x, float scale) {
-  if (scale == 0.f) return 0;
-  return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);
-}
-
-// E4M3 (OCP: 4 exponent bits, bias 7, 3 mantissa bits, largest finite 448) code of a float32 y,
-// rounded to the nearest value with ties to the even code, saturated at +-448; the sign bit is y's.
-// Below 2^-6 the values are the multiples of 2^-9, so y * 512 rounded is the code itself (8 is the
-// smallest normal, 0x08); above, the top 3 mantissa bits are rounded on the other 20, and a carry
-// out of the mantissa steps the exponent, which the code's layout does by itself.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(a * 512.f);
-  } else {
-    const uint32_t bits = __float_as_uint(a);
-    const uint32_t m = (bits >> 20) & 7u, rest = bits & 0xFFFFFu;
-    code = ((((bits >> 23) - 120u) << 3) | m) + ((rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ? 1u : 0u);
-    code = min(code, 126u);
-  }
-  return code | sign;
-}
-
-// Value of an E4M3 code (exact in float32).
-__device__ __forceinline__ float e4m3_value(uint32_t code) {
-  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
-  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return (code & 0x80u) ? -v : v;
-}
-
-// One code of an 8-bit pool: int8 (x / scale rounded to an integer) or E4M3.
-template <bool FP8>
-__device__ __forceinline__ uint32_t encode_code(float x, float scale) {
-  if constexpr (FP8) return scale == 0.f ? 0u : e4m3_encode(x / scale);
-  return (uint32_t)(uint8_t)quantise(x, scale);
-}
-template <bool FP8>
-__device__ __forceinline__ float code_value(uint32_t byte) {
-  if constexpr (FP8) return e4m3_value(byte);
-  return (float)(int8_t)byte;
-}
 
 template <bool FP8>
 __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Params p) {
