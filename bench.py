@@ -747,10 +747,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
              f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
              "# commands (from the repository root; the summary itself comes from",
-             "#   python bench.py --summarize-pmc gpurun_out/pmc_fetch_W gpurun_out/pmc_write_W <bench log> --workload W):",
-             f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{workload} -o run -- "
+             "#   python bench.py --summarize-pmc /tmp/pa_prof/pmc_fetch_W /tmp/pa_prof/pmc_write_W <bench log> --workload W):",
+             f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/pa_prof/pmc_fetch_{workload} -o run -- "
              f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
-             f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{workload} -o run -- "
+             f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/pa_prof/pmc_write_{workload} -o run -- "
              f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
              f"workload = {workload}",
              f"library_sha256 = {library_sha256()}",
@@ -866,7 +866,8 @@ def main(argv=None):
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode step runs on one "
-              "GPU and needs no collectives (DESIGN.md says how it would shard).", file=sys.stderr)
+              "GPU and needs no collectives: its (sequence, kv head) units split across GPUs with no exchange.",
+              file=sys.stderr)
         return 2
     global REPLICAS
     REPLICAS = max(0, args.replicas)
