@@ -74,6 +74,26 @@ def test_summarize_pmc_scales_by_copy_kernel(tmp_path):
     assert s["library_sha256"] == bench.library_sha256()
 
 
+def test_summarize_l2_hit_rate(tmp_path):
+    """TCC_HIT_sum / TCC_MISS_sum medians per kernel give hits / (hits + misses); other kernels are left out."""
+    cas = "void pa::(anonymous namespace)::cascade_kernel<1, 16, true>(pa::DecodeParams, int, int)"
+    other = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>"
+    d = tmp_path / "l2"
+    os.makedirs(d)
+    with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        rows = [(cas, "TCC_HIT_sum", v) for v in (300, 100, 300)] + [(cas, "TCC_MISS_sum", v) for v in (100, 900, 100)]
+        rows += [(other, "TCC_HIT_sum", 5), (other, "TCC_MISS_sum", 5)]
+        for i, (name, counter, value) in enumerate(rows):
+            w.writerow([i, name, counter, value])
+    text = bench.summarize_l2(str(d), "prefix", "rocprofv3 ...")
+    s = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line and not line.startswith("#"))
+    assert s["kernel_0_tcc_hit"] == "300" and s["kernel_0_tcc_miss"] == "100"
+    assert float(s["kernel_0_l2_hit_rate"]) == pytest.approx(0.75)
+    assert "kernel_1" not in s and "neg_kernel" not in text
+
+
 def test_traffic_ignored_when_sources_changed(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     (tmp_path / "traffic_decode_batch64.txt").write_text(
