@@ -137,6 +137,26 @@ def test_decode_shapes_and_tails_bf16(gpu_lib, b, hq, hkv, t, variant):
         _check_step(gpu_lib, case, variant=variant, **kw)
 
 
+@pytest.mark.parametrize("variant", [0, VALU])
+@pytest.mark.parametrize("b", [4, 16])
+@pytest.mark.parametrize("hq,hkv,t", [(8, 2, 5), (16, 4, 6), (8, 2, 8), (16, 2, 8), (32, 4, 8)])
+def test_decode_five_to_eight_query_tokens(gpu_lib, b, hq, hkv, t, variant):
+    """5-8 causal query tokens per sequence (10-64 query rows per kv head): the default choice (matrix
+    cores up to 32 rows, the vector-ALU kernel's 8-row groups above) and the vector-ALU kernel forced,
+    single pass and split, against the oracle. Forcing the matrix cores on more than 32 rows is refused."""
+    lengths = sorted({max(t, x) for x in (t, b - 1, b, b + 1, 15, 16, 17, 31, 33, 47, 100, 257)})
+    for kw in (dict(), dict(partitioned=True, partition_tokens=32), dict(partitioned=True, partition_tokens=48)):
+        case = build_case(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b,
+                          q_tokens=t, dtype=torch.bfloat16, seed=9100 + b * 100 + hq * 10 + t, pool_slack=0.2)
+        _check_step(gpu_lib, case, variant=variant, **kw)
+    if t * (hq // hkv) > 32:
+        g = _to_gpu(case)
+        with pytest.raises(gpu_lib.PaError) as err:
+            gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
+                           variant=MFMA)
+        assert err.value.status == -2
+
+
 @pytest.mark.parametrize("variant", [VALU, MFMA])
 @pytest.mark.parametrize("partition_tokens,msl_factor", [(16, 1), (48, 1), (16, 2), (32, 3)])
 def test_many_partitions_per_sequence(gpu_lib, partition_tokens, msl_factor, variant):
