@@ -39,7 +39,7 @@ from .pa_oracle_fp8 import (  # noqa: F401
     encode_e4m3,
     quantize_block_fp8,
 )
-from .pa_oracle_blocks import BlockPool, PagedCache, PoolExhausted, PrefixCache  # noqa: F401
+from .pa_oracle_blocks import BlockLedger, PoolExhausted  # noqa: F401
 from .pa_oracle_prefill import chunk_positions, prefill, prefill_row, write_kv_varlen  # noqa: F401
 from .pa_oracle import (  # noqa: F401
     attend_rows,

@@ -137,15 +137,18 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, seq_lens, 
 
 def decode_row_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, seq_lens, scale, block_size, i, t, h):
     """One output row of :func:`decode_fp8` (dequantises only the blocks that row reads)."""
+    return decode_row(q, _LazyDequantFp8(k_codes, k_scales), _LazyDequantFp8(v_codes, v_scales), block_tables,
+                      seq_lens, scale, block_size, i, t, h)
 
-    class _Lazy:
-        def __init__(self, codes, scales):
-            self.codes, self.scales, self.shape = codes, scales, codes.shape
 
-        def __getitem__(self, idx):
-            blocks, head, offsets, sl = idx
-            return _VALUES[np.asarray(self.codes[blocks, head, offsets, sl], dtype=np.uint8)] * \
-                np.asarray(self.scales[blocks, head], dtype=np.float64)[..., None]
+class _LazyDequantFp8:
+    """Pool view that dequantises only the rows an index expression (blocks, head, offsets, slice)
+    asks for: value(code) times the scale of that row's own (block, kv head)."""
 
-    return decode_row(q, _Lazy(k_codes, k_scales), _Lazy(v_codes, v_scales), block_tables, seq_lens, scale,
-                      block_size, i, t, h)
+    def __init__(self, codes, scales):
+        self.codes, self.scales, self.shape = codes, scales, codes.shape
+
+    def __getitem__(self, idx):
+        blocks, head, offsets, sl = idx
+        values = _VALUES[np.asarray(self.codes[blocks, head, offsets, sl], dtype=np.uint8)]
+        return values * np.asarray(self.scales[blocks, head], dtype=np.float64)[..., None]

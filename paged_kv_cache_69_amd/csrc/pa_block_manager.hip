@@ -130,6 +130,8 @@ int pa_bm_reserve(pa_block_manager* m, int64_t seq, int32_t new_tokens, int32_t*
   if (!m || new_tokens < 0 || !num_copies) return PA_ERR_INVALID_ARG;
   Seq* s = find_seq(m, seq);
   if (!s) return PA_ERR_INVALID_ARG;
+  *num_copies = 0;
+  if (new_tokens == 0) return PA_OK;  // nothing is written, so nothing needs a private copy
   const int64_t end = (int64_t)s->length + new_tokens;
   const int32_t want = m->blocks_for(end);
   const int32_t have = (int32_t)s->table.size();

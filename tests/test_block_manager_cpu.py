@@ -96,11 +96,11 @@ def test_errors_change_nothing(blocks):
             bad()
     assert (m.table(1), m.refcounts(), m.num_free) == state
 
-def _state(m_cpp, oc, opc):
+def _state(m_cpp, o):
     cpp = (m_cpp.num_free, m_cpp.refcounts(), m_cpp.num_seqs, m_cpp.num_entries,
-           {s: (m_cpp.table(s), m_cpp.length(s)) for s in oc.tables})
-    ref = (oc.pool.num_free, list(oc.pool.refs), len(oc.tables), len(opc.entries),
-           {s: (list(t), oc.lengths[s]) for s, t in oc.tables.items()})
+           {s: (m_cpp.table(s), m_cpp.length(s)) for s in o.seqs})
+    ref = (o.num_free, list(o.refcount), len(o.seqs), o.num_entries,
+           {s: (o.table(s), o.length(s)) for s in o.seqs})
     return cpp, ref
 
 @pytest.mark.parametrize("seed", range(8))
@@ -108,62 +108,80 @@ def test_random_workloads_match_the_oracle(blocks, seed):
     rng = random.Random(1000 + seed)
     n_blocks, b = rng.choice([(24, 2), (40, 4), (64, 3)])
     m = blocks.BlockManager(n_blocks, b)
-    oc = O.PagedCache(n_blocks, b)
-    opc = O.PrefixCache(oc)
+    o = O.BlockLedger(n_blocks, b)
     next_id = 0
     for step in range(400):
-        seqs = sorted(oc.tables)
+        seqs = sorted(o.seqs)
         op = rng.random()
         if op < 0.25 or not seqs:
             prompt = [rng.randrange(3) for _ in range(rng.randrange(1, 4 * b))]
             s = next_id
             next_id += 1
-            assert m.attach(s, prompt) == opc.attach(s, prompt)
-            n = len(prompt) - oc.lengths[s]
+            assert m.attach(s, prompt) == o.attach(s, prompt)
+            n = len(prompt) - o.length(s)
             try:
-                want = oc.reserve(s, n)
+                want = o.reserve(s, n)
             except O.PoolExhausted:
                 with pytest.raises(blocks.PoolExhausted):
                     m.reserve(s, n)
                 m.free(s)
-                oc.free(s)
+                o.free(s)
             else:
                 assert m.reserve(s, n) == want
                 m.commit(s, len(prompt))
-                oc.commit(s, len(prompt))
-                assert m.remember(s, prompt) == opc.remember(s, prompt)
+                o.commit(s, len(prompt))
+                assert m.remember(s, prompt) == o.remember(s, prompt)
         elif op < 0.5:
             s = rng.choice(seqs)
             n = rng.randrange(0, 2 * b + 1)
             try:
-                want = oc.reserve(s, n)
+                want = o.reserve(s, n)
             except O.PoolExhausted:
                 with pytest.raises(blocks.PoolExhausted):
                     m.reserve(s, n)
             else:
                 assert m.reserve(s, n) == want
-                new_len = oc.lengths[s] + rng.randrange(0, n + 1)
+                new_len = o.length(s) + rng.randrange(0, n + 1)
                 m.commit(s, new_len)
-                oc.commit(s, new_len)
+                o.commit(s, new_len)
         elif op < 0.65:
             s = rng.choice(seqs)
             m.fork(s, next_id)
-            oc.fork(s, next_id)
+            o.fork(s, next_id)
             next_id += 1
         elif op < 0.8:
             s = rng.choice(seqs)
             m.free(s)
-            oc.free(s)
+            o.free(s)
         elif op < 0.9:
             s = rng.choice(seqs)
-            n = rng.randrange(0, oc.lengths[s] + 1)
+            n = rng.randrange(0, o.length(s) + 1)
             m.truncate(s, n)
-            oc.truncate(s, n)
+            o.truncate(s, n)
         else:
             want = rng.randrange(n_blocks + 1)
-            assert m.evict(want) == opc.evict(want)
-        cpp, ref = _state(m, oc, opc)
+            assert m.evict(want) == o.evict(want)
+        cpp, ref = _state(m, o)
         assert cpp == ref, f"step {step}"
-    width = max([len(t) for t in oc.tables.values()] + [1])
-    seqs = sorted(oc.tables)
-    assert m.build_tables(seqs, width, pad=-7) == tuple(map(list, oc.build_tables(seqs, width, -7)))
+    width = max([len(o.table(s)) for s in o.seqs] + [1])
+    seqs = sorted(o.seqs)
+    assert m.build_tables(seqs, width, pad=-7) == tuple(map(list, o.build_tables(seqs, width, -7)))
+
+
+def test_zero_token_reserve_and_multi_block_copies(blocks):
+    """The two copy-on-write edge cases the oracle pins: a reserve of no tokens copies nothing, and a
+    write that spans two shared blocks copies both."""
+    m = blocks.BlockManager(8, 4)
+    m.add_seq(0)
+    m.reserve(0, 6)
+    m.commit(0, 6)
+    m.fork(0, 1)
+    assert m.reserve(1, 0) == [] and m.num_free == 6
+    assert m.reserve(1, 1) == [(1, 2)] and m.num_free == 5
+    m = blocks.BlockManager(8, 4)
+    m.add_seq(0)
+    m.reserve(0, 8)
+    m.commit(0, 1)
+    m.fork(0, 1)
+    assert m.reserve(1, 7) == [(0, 2), (1, 3)]
+    assert (m.table(0), m.table(1), m.num_free) == ([0, 1], [2, 3], 4)

@@ -137,10 +137,35 @@ def test_decode_fp8_is_decode_of_the_torch_dequantised_pool():
     assert np.array_equal(got, oracle.decode(q, kf, vf, tables, lens, 0.3, b))
 
 
+def test_decode_row_fp8_equals_decode_fp8_row_by_row():
+    """Every output row of the one-row oracle equals the same row of the whole-batch oracle (itself
+    pinned above to the float decode of torch's dequantisation). Scales differ per (block, kv head),
+    and two query tokens per sequence read two kv heads across several blocks, so a row that took
+    another head's or another block's scale would differ."""
+    rng = np.random.default_rng(21)
+    n, hkv, b, d, T = 7, 2, 4, 8, 2
+    kc = rng.integers(0, 256, (n, hkv, b, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (n, hkv, b, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x30
+    vc[(vc & 0x7F) == 0x7F] = 0x30
+    ks = rng.uniform(0.01, 0.05, (n, hkv)).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, (n, hkv)).astype(np.float32)
+    q = rng.standard_normal((2, T, 4, d))
+    tables = np.array([[6, 0, 3, 5], [1, 2, 4, 0]])
+    lens = np.array([14, 9])
+    whole = F.decode_fp8(q, kc, ks, vc, vs, tables, lens, 0.4, b)
+    for i in range(2):
+        for t in range(T):
+            for h in range(4):
+                row = F.decode_row_fp8(q, kc, ks, vc, vs, tables, lens, 0.4, b, i, t, h)
+                np.testing.assert_allclose(row, whole[i, t, h], rtol=0, atol=1e-13)
+
+
 def _pins_fail(mod) -> bool:
     tests = [test_format_closed_forms, test_encoder_matches_torch_cast, test_quantiser_error_bounds,
              test_append_rescale_and_untouched, test_append_in_max_first_order_equals_whole_block,
-             test_decode_fp8_is_decode_of_the_torch_dequantised_pool, test_code_values_match_torch]
+             test_decode_fp8_is_decode_of_the_torch_dequantised_pool, test_code_values_match_torch,
+             test_decode_row_fp8_equals_decode_fp8_row_by_row]
     global F
     saved = F
     F = mod
@@ -196,6 +221,26 @@ def test_planted_mistakes_are_caught():
     orig_enc = m.encode_e4m3
     m.encode_e4m3 = lambda y: orig_enc(np.abs(np.asarray(y, dtype=np.float32)))
     mutants["no-sign"] = m
+
+    m = fresh()  # the one-row oracle reads the scale of the neighbouring kv head
+    class OtherHead(m._LazyDequantFp8):
+        def __getitem__(self, idx):
+            blocks, head, offsets, sl = idx
+            values = m._VALUES[np.asarray(self.codes[blocks, head, offsets, sl], dtype=np.uint8)]
+            other = (head + 1) % self.scales.shape[1]
+            return values * np.asarray(self.scales[blocks, other], dtype=np.float64)[..., None]
+    m._LazyDequantFp8 = OtherHead
+    mutants["row-scale-other-head"] = m
+
+    m = fresh()  # the one-row oracle reads every position's scale from the row's first block
+    class FirstBlock(m._LazyDequantFp8):
+        def __getitem__(self, idx):
+            blocks, head, offsets, sl = idx
+            values = m._VALUES[np.asarray(self.codes[blocks, head, offsets, sl], dtype=np.uint8)]
+            first = np.full_like(np.asarray(blocks), np.asarray(blocks).reshape(-1)[0])
+            return values * np.asarray(self.scales[first, head], dtype=np.float64)[..., None]
+    m._LazyDequantFp8 = FirstBlock
+    mutants["row-scale-first-block"] = m
 
     for name, mod in mutants.items():
         assert _pins_fail(mod), f"planted mistake '{name}' was not caught by the pins"
