@@ -98,8 +98,8 @@ def kv_bytes_per_position(num_kv_heads: int, head_dim: int, itemsize: int) -> in
 
 
 def _scale_bytes_per_block(case) -> int:
-    """int8 pools: the K and V fp32 scales of one block (all kv heads); 0 for float pools."""
-    return 2 * 4 * case.k_pool.shape[1] if hasattr(case, "k_scales") else 0
+    """8-bit pools: the K and V fp32 scales of one block (all kv heads); 0 for float pools."""
+    return 2 * 4 * case.k_pool.shape[1] if hasattr(case, "scales") else 0
 
 
 def algorithmic_bytes(case) -> int:
@@ -183,7 +183,7 @@ class Replica:
         self.dims = pa.make_dims(self.t["q"], self.t["k_pool"], self.t["block_tables"], out_dtype=torch.float32,
                                  variant=variant)
         kd = case.k_pool.shape
-        self.int8 = "k_scales" in src
+        self.int8 = "scales" in src
         code = pa.dtype_code(case.k_new.dtype)
         self.wdims = pa.PaDims(case.q.shape[0], case.q.shape[1], kd[1], kd[1], kd[3], kd[2], kd[0],
                                case.block_tables.shape[1], code, pa.dtype_code(case.k_pool.dtype), code, 0)
@@ -201,7 +201,7 @@ class Replica:
                                        partition_tokens)
             self.ws = torch.empty(n, dtype=torch.uint8, device=src["q"].device)
         p = {k: v.data_ptr() for k, v in self.t.items()}
-        scales = (p["k_scales"], p["v_scales"]) if self.int8 else ()
+        scales = (p["scales"],) if self.int8 else ()
         self.write_args = (ctypes.byref(self.wdims), p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], *scales,
                            p["block_tables"], p["positions"])
         self.dec_args = (ctypes.byref(self.dims), p["q"], p["k_pool"], p["v_pool"], *scales, p["block_tables"],
@@ -210,11 +210,10 @@ class Replica:
         self.f_write = getattr(self.lib, "pa_write_kv" + sfx)
         self.f_decode = getattr(self.lib, "pa_decode" + sfx)
         self.f_split = getattr(self.lib, "pa_decode_partitioned" + sfx)
-        # 8-bit pools: the fused call serves the single pass over 16-position blocks
-        self.fused = fused and (not self.int8 or (not partition_tokens and case.block_size == 16))
+        # 8-bit pools append with their own append call
+        self.fused = fused and not self.int8
         self.fused_args = (ctypes.byref(self.dims), p["q"], p["k_new"], p["v_new"], p["k_pool"], p["v_pool"],
-                           *scales, p["block_tables"], p["seq_lens"], self.scale)
-        self.f_fused8 = getattr(self.lib, "pa_write_kv_decode" + sfx) if self.int8 else None
+                           p["block_tables"], p["seq_lens"], self.scale)
 
     def step(self, stream):
         """One whole decode step: the fused append + decode call where there is one, else the two calls."""
@@ -229,9 +228,7 @@ class Replica:
         if not self.fused:
             self.decode(stream)
             return
-        if self.int8:
-            st = self.f_fused8(*self.fused_args, self.out.data_ptr(), stream)
-        elif self.cascade:
+        if self.cascade:
             st = self.lib.pa_write_kv_decode_cascade(*self.fused_args, self.out.data_ptr(), self.cascade, self.max_len,
                                                      self.pt, self.ws.data_ptr(), self.ws.numel(), stream)
         elif self.ws is None:
@@ -270,8 +267,8 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
 
     dev = torch.device("cuda:0")
     keys = ["q", "k_new", "v_new", "k_pool", "v_pool", "block_tables", "seq_lens", "positions"]
-    if hasattr(case, "k_scales"):
-        keys += ["k_scales", "v_scales"]
+    if hasattr(case, "scales"):
+        keys += ["scales"]
     src = {k: getattr(case, k).to(dev) for k in keys}
     touched = unique_bytes(case)  # a block shared by several tables is cached once
     n_rep = REPLICAS or max(1, min(64, math.ceil(COLD_BYTES / touched)))
@@ -576,7 +573,8 @@ def run_copy_workload(pa, name, steps, warmup, graphs=True):
     algo = 2 * 2 * n_pairs * block_bytes
 
     def call(h):
-        st = lib.pa_copy_blocks(ctypes.byref(dims), k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(), n_pairs, h)
+        st = lib.pa_copy_blocks(ctypes.byref(dims), k_pool.data_ptr(), v_pool.data_ptr(), None, pairs.data_ptr(), n_pairs,
+                                h)
         if st:
             raise RuntimeError(f"pa_copy_blocks: {st}")
 
@@ -645,9 +643,9 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         return run_copy_workload(pa, name, steps, warmup, graphs)
     case = make_case(spec.get("base", name), pool_device="cuda:0")
     if spec.get("int8"):
-        case.k_pool, case.k_scales, case.v_pool, case.v_scales = int8_pools(case)
+        case.k_pool, case.v_pool, case.scales = int8_pools(case)
     if spec.get("fp8"):
-        case.k_pool, case.k_scales, case.v_pool, case.v_scales = fp8_pools(case)
+        case.k_pool, case.v_pool, case.scales = fp8_pools(case)
     b, t = case.q.shape[0], case.q.shape[1]
     rows = case.q.shape[2] // case.k_pool.shape[1] * t
     mfma_ok = (case.k_pool.dtype in (torch.bfloat16, torch.int8, torch.float8_e4m3fn) and case.q.shape[3] == 128

@@ -95,6 +95,11 @@ typedef struct {
   int32_t kv_dtype;  /* pa_dtype of the pools; must equal q_dtype */
   int32_t out_dtype; /* pa_dtype of out */
   int32_t variant;   /* pa_variant */
+  int32_t wave_parts; /* split calls on the matrix-core kernel: consecutive partitions per wave.
+                         0 lets the library choose (pa_decode_partitioned_wave_parts); 1 or 2 forces
+                         that count where two are possible (bf16 pools, T * G <= 16) and is ignored
+                         elsewhere. Any other value: PA_ERR_INVALID_ARG. The results are the same
+                         bits for every value. */
 } pa_dims;
 
 /* pa_write_kv: the KV-append scatter.
@@ -135,10 +140,11 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
  * workgroup of each kv head takes the sequence of length rank j, so the last
  * workgroups to start are the shortest. Use pa_decode_partitioned for long
  * contexts.
- * Supported: (kv dtype, D) in {(PA_BF16, 128), (PA_F32, 64)}; b in
- * {4, 8, 16, 32}. The VALU kernel serves any T * G: groups of up to 8 query
- * rows share one workgroup. The MFMA kernel serves PA_BF16 with D = 128 and
- * T * G <= 32 (query rows padded to 16 or 32). */
+ * Supported: kv dtype (= q dtype) PA_BF16 or PA_F32, D in {64, 128}, b in
+ * {4, 8, 16, 32}, fp32 or bf16 out. The VALU kernel serves all of these and
+ * any T * G: groups of up to 8 query rows share one workgroup. The MFMA
+ * kernel serves PA_BF16 with D = 128 and T * G <= 32 (query rows padded to
+ * 16 or 32), and PA_VARIANT_AUTO picks it there. */
 int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
               pa_stream_t stream);
@@ -187,10 +193,9 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
  * It is 2 for bf16 pools when T * G <= 16 and B * Hkv * ceil(max_seq_len /
  * partition_tokens) exceeds the 2048 split waves the GPU holds at once, so
  * that long-context batches run in one round of waves; 8-bit pools keep one
- * partition per wave. The environment variable PA_SPLIT_WAVE_PARTS=1 or 2
- * overrides that choice for bf16 pools with T * G <= 16 (read on every
- * call). Host-only; returns
- * PA_ERR_INVALID_ARG for invalid dims or sizes. */
+ * partition per wave. dims->wave_parts = 1 or 2 overrides that choice for
+ * bf16 pools with T * G <= 16, and this query then returns it. Host-only;
+ * returns PA_ERR_INVALID_ARG for invalid dims or sizes. */
 int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);
 
 /* pa_write_kv_decode: one decode step in one launch: pa_write_kv of the T new
@@ -273,8 +278,9 @@ int pa_write_kv_decode_cascade(const pa_dims* dims, const void* q, const void* k
  * section 6: block-wise KV quantisation).
  *
  * Pools hold int8 codes, [N, Hkv, b, D] like the float pools, plus one fp32
- * scale per (block, kv head): k_scales, v_scales [N, Hkv]. A stored value is
- * code * scale. For each (block, head) the scale is the largest magnitude of
+ * scale per (block, kv head) for K and one for V, interleaved:
+ * scales [N, Hkv, 2] holds (K scale, V scale) of each (block, kv head), so
+ * a tile's two scales share one 8-byte word. A stored value is code * scale. For each (block, head) the scale is the largest magnitude of
  * that head's values in the block divided by 127, and each code is the value
  * divided by the scale, rounded half to even and clipped to [-127, 127], the
  * division done in fp32. The per-element error is then at most the range
@@ -296,53 +302,34 @@ int pa_write_kv_decode_cascade(const pa_dims* dims, const void* q, const void* k
  * A scale of 0 (all-zero values) gives codes 0. A block written here must not
  * be read or written by another sequence in the same call.
  *   k_new, v_new : [B, T, Hkv, D], q_dtype;  k_pool, v_pool : int8 [N, Hkv, b, D]
- *   k_scales, v_scales : fp32 [N, Hkv] (read and written)
+ *   scales : fp32 [N, Hkv, 2] (read and written)
  *   block_tables : int32 [B, MB];  positions : int32 [B, T]
  * Supported: D a multiple of 16. */
 int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
-                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                     int8_t* v_pool, float* scales, const int32_t* block_tables,
                      const int32_t* positions, pa_stream_t stream);
 
 /* pa_decode_int8: pa_decode over int8 pools, i.e. exact softmax attention
  * over the values code * scale. The MFMA kernel keeps the codes exact on the
  * matrix cores and applies the per-block scales in fp32.
+ * For the K products q is converted to fp16, which holds every bf16 value
+ * of magnitude 2^-14 .. 2^15 exactly. A query row whose largest |q| reaches
+ * 2^15 is first multiplied by a power of two that brings it below 2^15 (exact),
+ * and its scores by the inverse, so any finite q works; elements far below
+ * the row's largest then round to fp16 subnormals (absolute error under
+ * 2^-25 of the row's scale). The FP8 path keeps q in bf16.
  * Supported: q_dtype PA_BF16, D = 128, b in {16, 32}, T * G <= 32. */
 int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,
-                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                   const float* scales, const int32_t* block_tables,
                    const int32_t* seq_lens, float scale, void* out, pa_stream_t stream);
 
 /* pa_decode_partitioned_int8: pa_decode_partitioned over int8 pools (same
  * workspace size and rules, same supported shapes as pa_decode_int8). */
 int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t* k_pool,
-                               const int8_t* v_pool, const float* k_scales, const float* v_scales,
+                               const int8_t* v_pool, const float* scales,
                                const int32_t* block_tables, const int32_t* seq_lens, float scale,
                                void* out, int32_t max_seq_len, int32_t partition_tokens,
                                void* workspace, size_t workspace_bytes, pa_stream_t stream);
-
-/* pa_write_kv_decode_int8 / pa_write_kv_decode_fp8: one decode step over
- * 8-bit pools in one launch: pa_write_kv_int8 (or _fp8) of the T new tokens
- * at each sequence's last T positions (seq_lens[i] - T .. seq_lens[i] - 1),
- * then pa_decode_int8 (or _fp8). The workgroup of each (sequence, kv head)
- * appends that head's rows itself, in the tile that holds them: the block's
- * scale grows to cover the new rows, the codes already in the block are
- * re-quantised when it grew, the new rows are quantised, and the changed
- * codes and the scale are stored; that tile then takes part in the
- * attention with its new codes. Every code and scale is decided with the
- * operations of the separate append, so the results (pools, scales and
- * out) are bit for bit those of the two calls.
- *   k_new, v_new : [B, T, Hkv, D] bf16;  k_pool, v_pool, k_scales, v_scales :
- *                  written in place
- * Supported: the shapes of pa_decode_int8 with b = 16; otherwise
- * PA_ERR_UNSUPPORTED. Null k_new or v_new (B > 0): PA_ERR_INVALID_ARG. The
- * new rows' blocks must not be read by another sequence in the same call. */
-int pa_write_kv_decode_int8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
-                            int8_t* k_pool, int8_t* v_pool, float* k_scales, float* v_scales,
-                            const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
-                            pa_stream_t stream);
-int pa_write_kv_decode_fp8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
-                           uint8_t* k_pool, uint8_t* v_pool, float* k_scales, float* v_scales,
-                           const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
-                           pa_stream_t stream);
 
 /* ---- Paged prefill ([P1] "25. Paged attention and prefix caching", stretch
  * exercise 4; [P4] "PagedAttention and the KV Cache", section "Prefill vs
@@ -396,17 +383,20 @@ int pa_check_prefill_host(const pa_dims* dims, const int32_t* block_tables, cons
  *
  * pa_copy_blocks: for each pair i, copy physical block block_pairs[2i] onto
  * block block_pairs[2i+1] in both pools (all kv heads; the Hkv * b * D
- * elements of a block are contiguous). This is the data half of
+ * elements of a block are contiguous) and, for 8-bit pools, the block's
+ * 2 * Hkv scales with it: a block's scales are part of the block ([P2]
+ * section 6), and the copy is the whole block. This is the data half of
  * copy-on-write: pa_bm_reserve returns the pairs.
  *   dims : num_kv_heads, block_size, head_dim, num_blocks and kv_dtype are
- *          used (any pool dtype, including PA_INT8 codes; an int8 pool's
- *          scales are copied by the caller)
+ *          used (PA_F32, PA_BF16, PA_INT8 or PA_FP8_E4M3)
+ *   scales : 8-bit pools: the pools' fp32 [N, Hkv, 2] scales (required);
+ *            float pools: must be NULL
  *   block_pairs : int32 [num_pairs, 2] on the device
  * Preconditions (checked under PA_CHECK=1, pa_check_copies_host): every id in
  * [0, num_blocks); destinations distinct; no destination is also a source.
  * One launch on `stream`; num_pairs = 0 launches nothing. */
-int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, const int32_t* block_pairs,
-                   int32_t num_pairs, pa_stream_t stream);
+int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, float* scales,
+                   const int32_t* block_pairs, int32_t num_pairs, pa_stream_t stream);
 
 /* pa_check_copies_host: the pa_copy_blocks preconditions on host pairs. */
 int pa_check_copies_host(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs);
@@ -485,13 +475,13 @@ int32_t pa_bm_prefix_entries(const pa_block_manager* m);
  *   re-encoding on a scale increase uses (value(code) * old_scale) / new_scale;
  *   decode attends over value(code) * scale. */
 int pa_write_kv_fp8(const pa_dims* dims, const void* k_new, const void* v_new, uint8_t* k_pool,
-                    uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                    uint8_t* v_pool, float* scales, const int32_t* block_tables,
                     const int32_t* positions, pa_stream_t stream);
 int pa_decode_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
-                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                  const float* scales, const int32_t* block_tables,
                   const int32_t* seq_lens, float scale, void* out, pa_stream_t stream);
 int pa_decode_partitioned_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool,
-                              const uint8_t* v_pool, const float* k_scales, const float* v_scales,
+                              const uint8_t* v_pool, const float* scales,
                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
                               void* out, int32_t max_seq_len, int32_t partition_tokens,
                               void* workspace, size_t workspace_bytes, pa_stream_t stream);

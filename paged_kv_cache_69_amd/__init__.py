@@ -15,7 +15,9 @@ Entry points, with the same names as the C ABI:
 * :func:`write_kv_decode`: append + decode in one launch (``pa_write_kv_decode``,
   ``pa_write_kv_decode_partitioned``).
 * :func:`decode_cascade`: decode with a shared prefix attended once (``pa_decode_cascade``).
-* :func:`write_kv_int8`, :func:`decode_int8`, :func:`decode_partitioned_int8`: the int8 KV cache.
+* :func:`write_kv_int8`, :func:`decode_int8`, :func:`decode_partitioned_int8`: the int8 KV cache, and
+  the same three for FP8 (E4M3) pools. 8-bit pools carry one ``scales [N, Hkv, 2]`` float32 tensor,
+  the (K, V) scale pair of every (block, kv head).
 * :func:`write_kv_varlen`, :func:`prefill`: paged (chunked) prefill over packed chunks
   (``pa_write_kv_varlen``, ``pa_prefill``).
 * :mod:`.blocks`: the host block manager (``pa_bm_*``: free list, reference counts, tables with
@@ -45,11 +47,9 @@ EXPORTS = (
     "pa_write_kv_int8",
     "pa_decode_int8",
     "pa_decode_partitioned_int8",
-    "pa_write_kv_decode_int8",
     "pa_write_kv_fp8",
     "pa_decode_fp8",
     "pa_decode_partitioned_fp8",
-    "pa_write_kv_decode_fp8",
     "pa_write_kv_varlen",
     "pa_prefill",
     "pa_check_prefill_host",
@@ -77,10 +77,10 @@ EXPORTS = (
     "pa_status_string",
     "pa_abi_version",
 )
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _DIM_FIELDS = ("num_seqs", "q_tokens", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
-               "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "variant")
+               "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "variant", "wave_parts")
 
 
 class PaDims(ctypes.Structure):
@@ -142,14 +142,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_write_kv_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32,
                                                    _I32, _P, ctypes.c_size_t, _P]
     lib.pa_write_kv_decode_partitioned.restype = ctypes.c_int
-    lib.pa_write_kv_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.pa_write_kv_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.pa_write_kv_int8.restype = ctypes.c_int
-    for name in ("pa_write_kv_decode_int8", "pa_write_kv_decode_fp8"):
-        getattr(lib, name).argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
-        getattr(lib, name).restype = ctypes.c_int
-    lib.pa_decode_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.pa_decode_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     lib.pa_decode_int8.restype = ctypes.c_int
-    lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
+    lib.pa_decode_partitioned_int8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
                                                _P, ctypes.c_size_t, _P]
     lib.pa_decode_partitioned_int8.restype = ctypes.c_int
     for suffix in ("write_kv", "decode", "decode_partitioned"):  # the FP8 entry points mirror the int8 ones
@@ -216,7 +213,7 @@ def _check_tensors(**tensors):
     return dev
 
 
-def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT_AUTO) -> PaDims:
+def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT_AUTO, wave_parts: int = 0) -> PaDims:
     """Dims for q ``[B, T, Hq, D]``, pools ``[N, Hkv, b, D]`` and tables ``[B, MB]``."""
     _require(q.dim() == 4 and k_pool.dim() == 4 and block_tables.dim() == 2, "bad tensor ranks")
     b, t, hq, d = q.shape
@@ -224,7 +221,7 @@ def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT
     _require(d == d2, "head_dim of q and pools differ")
     _require(block_tables.shape[0] == b, "block_tables rows != num_seqs")
     return PaDims(b, t, hq, hkv, d, bs, n, block_tables.shape[1], dtype_code(q.dtype), dtype_code(k_pool.dtype),
-                  dtype_code(out_dtype if out_dtype is not None else q.dtype), int(variant))
+                  dtype_code(out_dtype if out_dtype is not None else q.dtype), int(variant), int(wave_parts))
 
 
 def write_kv(k_new, v_new, k_pool, v_pool, block_tables, positions, *, stream=None):
@@ -241,7 +238,7 @@ def write_kv(k_new, v_new, k_pool, v_pool, block_tables, positions, *, stream=No
     _require(k_pool.shape[1] == hkv and k_pool.shape[3] == d, "pool and new rows disagree")
     code = dtype_code(k_pool.dtype)
     _require(dtype_code(k_new.dtype) == code, "new rows and pools must share a dtype")
-    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, code, code, 0)
+    dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, code, code, 0, 0)
     st = lib.pa_write_kv(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                          v_pool.data_ptr(), block_tables.data_ptr(), positions.data_ptr(),
                          _stream_handle(stream, dev))
@@ -278,10 +275,11 @@ def workspace_bytes(q, k_pool, block_tables, max_seq_len: int, partition_tokens:
     return int(n)
 
 
-def wave_parts(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int) -> int:
-    """``pa_decode_partitioned_wave_parts``: consecutive partitions per wave of the matrix-core split kernel."""
+def wave_parts(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int, *, force: int = 0) -> int:
+    """``pa_decode_partitioned_wave_parts``: consecutive partitions per wave of the matrix-core split kernel
+    (``force`` = 1 or 2 is ``pa_dims.wave_parts``)."""
     lib = load_library()
-    dims = make_dims(q, k_pool, block_tables)
+    dims = make_dims(q, k_pool, block_tables, wave_parts=force)
     n = lib.pa_decode_partitioned_wave_parts(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
     if n < 0:
         raise PaError("pa_decode_partitioned_wave_parts", n, "invalid argument")
@@ -290,9 +288,10 @@ def wave_parts(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int)
 
 def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
                        partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
-                       variant: int = VARIANT_AUTO, stream=None):
+                       variant: int = VARIANT_AUTO, wave_parts: int = 0, stream=None):
     """``pa_decode_partitioned``: split-context decode + merge. ``workspace`` is a uint8 device tensor
-    of at least :func:`workspace_bytes` bytes (allocated here if omitted)."""
+    of at least :func:`workspace_bytes` bytes (allocated here if omitted); ``wave_parts`` is
+    ``pa_dims.wave_parts`` (0: the library's choice)."""
     import torch
 
     lib = load_library()
@@ -305,7 +304,7 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
                          workspace=workspace)
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant)
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
     st = lib.pa_decode_partitioned(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                    block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
@@ -383,7 +382,7 @@ def write_kv_decode_cascade(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
 
 def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, *,
                     max_seq_len: int | None = None, partition_tokens: int | None = None, workspace=None,
-                    out_dtype=None, variant: int = VARIANT_AUTO, stream=None):
+                    out_dtype=None, variant: int = VARIANT_AUTO, wave_parts: int = 0, stream=None):
     """``pa_write_kv_decode`` (or ``pa_write_kv_decode_partitioned`` when ``partition_tokens`` is
     given): append ``k_new``/``v_new [B, T, Hkv, D]`` at each sequence's last T positions and decode,
     in one launch. Returns ``out``."""
@@ -404,7 +403,7 @@ def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, sca
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape and k_new.shape == v_new.shape, "shape mismatch")
     _require(k_new.dtype == q.dtype and k_pool.dtype == q.dtype, "q, new rows and pools must share a dtype")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant)
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
     args = [ctypes.byref(dims), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
             v_pool.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
     if split:
@@ -430,22 +429,22 @@ def _q8_format(k_pool, fmt: str):
     return PA_FP8_E4M3
 
 
-def _check_scales(k_pool, k_scales, v_scales):
+def _check_scales(k_pool, scales):
     import torch
 
-    want = tuple(k_pool.shape[:2])
-    _require(tuple(k_scales.shape) == want and tuple(v_scales.shape) == want, "scales must be [N, Hkv]")
-    _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32, "scales must be float32")
+    want = tuple(k_pool.shape[:2]) + (2,)
+    _require(tuple(scales.shape) == want, "scales must be [N, Hkv, 2] (K scale, V scale)")
+    _require(scales.dtype == torch.float32, "scales must be float32")
 
 
-def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream):
+def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, scales, block_tables, positions, stream):
     import torch
 
     lib = load_library()
     kv_code = _q8_format(k_pool, fmt)
-    dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales,
-                         v_scales=v_scales, block_tables=block_tables, positions=positions)
-    _check_scales(k_pool, k_scales, v_scales)
+    dev = _check_tensors(k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, scales=scales,
+                         block_tables=block_tables, positions=positions)
+    _check_scales(k_pool, scales)
     _require(block_tables.dtype == torch.int32 and positions.dtype == torch.int32, "tables/positions must be int32")
     _require(k_new.shape == v_new.shape and k_pool.shape == v_pool.shape, "K/V shapes differ")
     bsz, t, hkv, d = k_new.shape
@@ -453,26 +452,23 @@ def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_ta
     _require(k_pool.shape[1] == hkv and k_pool.shape[3] == d, "pool and new rows disagree")
     code = dtype_code(k_new.dtype)
     dims = PaDims(bsz, t, hkv, hkv, d, k_pool.shape[2], k_pool.shape[0], block_tables.shape[1], code, kv_code,
-                  code, 0)
+                  code, 0, 0)
     func = "pa_write_kv_int8" if fmt == "int8" else "pa_write_kv_fp8"
     st = getattr(lib, func)(ctypes.byref(dims), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
-                            v_pool.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
-                            positions.data_ptr(), _stream_handle(stream, dev))
+                            v_pool.data_ptr(), scales.data_ptr(), block_tables.data_ptr(), positions.data_ptr(),
+                            _stream_handle(stream, dev))
     _check(lib, func, st)
 
 
-def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype, stream,
-               split=None, new_rows=None):
+def _decode_q8(fmt, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream, split=None):
     import torch
 
     lib = load_library()
     kv_code = _q8_format(k_pool, fmt)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, k_scales=k_scales, v_scales=v_scales,
-                   block_tables=block_tables, seq_lens=seq_lens, out=out)
-    if new_rows is not None:
-        tensors.update(k_new=new_rows[0], v_new=new_rows[1])
+    tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, scales=scales, block_tables=block_tables, seq_lens=seq_lens,
+                   out=out)
     if split is not None:
         max_seq_len, partition_tokens, workspace = split
         if workspace is None:
@@ -480,20 +476,14 @@ def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_len
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         tensors["workspace"] = workspace
     dev = _check_tensors(**tensors)
-    _check_scales(k_pool, k_scales, v_scales)
+    _check_scales(k_pool, scales)
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
     dims = make_dims(q, k_pool.view(torch.int8), block_tables, out_dtype=out.dtype)
     dims.kv_dtype = kv_code
-    args = [ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scales.data_ptr(),
-            v_scales.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
-    if new_rows is not None:
-        _require(new_rows[0].dtype == torch.bfloat16 and new_rows[0].shape == new_rows[1].shape,
-                 "k_new/v_new must be bf16 of one shape")
-        func = "pa_write_kv_decode_int8" if fmt == "int8" else "pa_write_kv_decode_fp8"
-        st = getattr(lib, func)(args[0], args[1], new_rows[0].data_ptr(), new_rows[1].data_ptr(), *args[2:],
-                                _stream_handle(stream, dev))
-    elif split is None:
+    args = [ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), scales.data_ptr(),
+            block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
+    if split is None:
         func = "pa_decode_int8" if fmt == "int8" else "pa_decode_fp8"
         st = getattr(lib, func)(*args, _stream_handle(stream, dev))
     else:
@@ -504,59 +494,41 @@ def _decode_q8(fmt, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_len
     return out
 
 
-def write_kv_decode_int8(q, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
-                         out=None, *, out_dtype=None, stream=None):
-    """``pa_write_kv_decode_int8``: append the step's rows into int8 pools and decode, in one launch."""
-    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream, new_rows=(k_new, v_new))
-
-
-def write_kv_decode_fp8(q, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
-                        out=None, *, out_dtype=None, stream=None):
-    """``pa_write_kv_decode_fp8``: append the step's rows into E4M3 pools and decode, in one launch."""
-    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream, new_rows=(k_new, v_new))
-
-
-def write_kv_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
+def write_kv_int8(k_new, v_new, k_pool, v_pool, scales, block_tables, positions, *, stream=None):
     """``pa_write_kv_int8``: append ``k_new``/``v_new [B, T, Hkv, D]`` (bf16 or fp32) into int8 pools
-    ``[N, Hkv, b, D]`` with per-(block, kv head) scales ``[N, Hkv]`` (updated in place)."""
-    _write_kv_q8("int8", k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream)
+    ``[N, Hkv, b, D]`` with per-(block, kv head) scale pairs ``scales [N, Hkv, 2]`` (updated in place)."""
+    _write_kv_q8("int8", k_new, v_new, k_pool, v_pool, scales, block_tables, positions, stream)
 
 
-def decode_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float, out=None, *,
-                out_dtype=None, stream=None):
+def decode_int8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, out=None, *, out_dtype=None,
+                stream=None):
     """``pa_decode_int8``: decode over int8 pools; returns ``out [B, T, Hq, D]`` (fp32 by default)."""
-    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream)
+    return _decode_q8("int8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream)
 
 
-def decode_partitioned_int8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
-                            max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
-                            stream=None):
+def decode_partitioned_int8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, max_seq_len: int,
+                            partition_tokens: int, out=None, workspace=None, *, out_dtype=None, stream=None):
     """``pa_decode_partitioned_int8``: split-context decode + merge over int8 pools."""
-    return _decode_q8("int8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream, (max_seq_len, partition_tokens, workspace))
+    return _decode_q8("int8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream,
+                      (max_seq_len, partition_tokens, workspace))
 
 
-def write_kv_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, *, stream=None):
+def write_kv_fp8(k_new, v_new, k_pool, v_pool, scales, block_tables, positions, *, stream=None):
     """``pa_write_kv_fp8``: append into E4M3 pools (``torch.float8_e4m3fn`` or their uint8 bits)."""
-    _write_kv_q8("fp8", k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, stream)
+    _write_kv_q8("fp8", k_new, v_new, k_pool, v_pool, scales, block_tables, positions, stream)
 
 
-def decode_fp8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float, out=None, *,
-               out_dtype=None, stream=None):
+def decode_fp8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, out=None, *, out_dtype=None,
+               stream=None):
     """``pa_decode_fp8``: decode over E4M3 pools; returns ``out [B, T, Hq, D]`` (fp32 by default)."""
-    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream)
+    return _decode_q8("fp8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream)
 
 
-def decode_partitioned_fp8(q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale: float,
-                           max_seq_len: int, partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
-                           stream=None):
+def decode_partitioned_fp8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, max_seq_len: int,
+                           partition_tokens: int, out=None, workspace=None, *, out_dtype=None, stream=None):
     """``pa_decode_partitioned_fp8``: split-context decode + merge over E4M3 pools."""
-    return _decode_q8("fp8", q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, out_dtype,
-                      stream, (max_seq_len, partition_tokens, workspace))
+    return _decode_q8("fp8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream,
+                      (max_seq_len, partition_tokens, workspace))
 
 
 # ----------------------------------------------------------------------------- paged prefill
@@ -564,7 +536,7 @@ def decode_partitioned_fp8(q, k_pool, v_pool, k_scales, v_scales, block_tables, 
 def _prefill_dims(q_rows, k_pool, block_tables, max_chunk: int, num_q_heads: int, code_q, code_out) -> PaDims:
     n, hkv, bs, d = k_pool.shape
     return PaDims(block_tables.shape[0], int(max_chunk), num_q_heads, hkv, d, bs, n, block_tables.shape[1], code_q,
-                  dtype_code(k_pool.dtype), code_out, 0)
+                  dtype_code(k_pool.dtype), code_out, 0, 0)
 
 
 def write_kv_varlen(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, q_start, max_chunk: int, *, stream=None):

@@ -44,7 +44,7 @@ def _bind(lib):
         "pa_bm_prefix_remember": ([_P, _I64, _P, _I32], _I32),
         "pa_bm_prefix_evict": ([_P, _I32], _I32),
         "pa_bm_prefix_entries": ([_P], _I32),
-        "pa_copy_blocks": ([_P, _P, _P, _P, _I32, _P], ctypes.c_int),
+        "pa_copy_blocks": ([_P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
         "pa_check_copies_host": ([_P, _P, _I32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -162,23 +162,31 @@ class BlockManager:
         return self._ok("pa_bm_prefix_evict", self._lib.pa_bm_prefix_evict(self._h, int(blocks_wanted)))
 
 
-def copy_blocks(k_pool, v_pool, pairs, *, stream=None):
-    """``pa_copy_blocks``: copy block ``pairs[i, 0]`` onto block ``pairs[i, 1]`` in both pools.
-    ``pairs`` is an int32 ``[n, 2]`` tensor on the pools' device (or a list of pairs, copied there)."""
+def copy_blocks(k_pool, v_pool, pairs, *, scales=None, stream=None):
+    """``pa_copy_blocks``: copy block ``pairs[i, 0]`` onto block ``pairs[i, 1]`` in both pools, and for
+    8-bit pools (int8 or float8_e4m3fn) the blocks' ``scales [N, Hkv, 2]`` with them (required there,
+    absent for float pools). ``pairs`` is an int32 ``[n, 2]`` tensor on the pools' device (or a list of
+    pairs, copied there)."""
     import torch
 
     lib = _bind(load_library())
     if not isinstance(pairs, torch.Tensor):
         pairs = torch.tensor([list(p) for p in pairs], dtype=torch.int32).reshape(-1, 2).to(k_pool.device)
-    dev = _check_tensors(k_pool=k_pool, v_pool=v_pool, pairs=pairs)
+    tensors = dict(k_pool=k_pool, v_pool=v_pool, pairs=pairs)
+    if scales is not None:
+        tensors["scales"] = scales
+    dev = _check_tensors(**tensors)
     _require(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2, "pairs must be int32 [n, 2]")
     _require(k_pool.shape == v_pool.shape and k_pool.dim() == 4, "pools must be [N, Hkv, b, D] alike")
     from . import PaDims
 
     n, hkv, bs, d = k_pool.shape
     code = dtype_code(k_pool.dtype)
-    dims = PaDims(0, 1, hkv, hkv, d, bs, n, 1, code, code, code, 0)
-    st = lib.pa_copy_blocks(ctypes.byref(dims), k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
+    if scales is not None:
+        _require(scales.dtype == torch.float32 and tuple(scales.shape) == (n, hkv, 2), "scales must be float32 [N, Hkv, 2]")
+    dims = PaDims(0, 1, hkv, hkv, d, bs, n, 1, code, code, code, 0, 0)
+    st = lib.pa_copy_blocks(ctypes.byref(dims), k_pool.data_ptr(), v_pool.data_ptr(),
+                            scales.data_ptr() if scales is not None else None, pairs.data_ptr(),
                             int(pairs.shape[0]), _stream_handle(stream, dev))
     if st:
         raise PaError("pa_copy_blocks", st, lib.pa_status_string(st).decode())

@@ -11,7 +11,7 @@ namespace {
 
 using pa::DecodeParams;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int32_t kSinglePassTokens = 0x7ffffff0;  // one partition that covers any length
 #ifndef PA_LPT_MIN_SEQS
 #define PA_LPT_MIN_SEQS 128
@@ -35,6 +35,7 @@ int check_shape(const pa_dims* d) {
     return PA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (d->variant < PA_VARIANT_AUTO || d->variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  if (d->wave_parts < 0 || d->wave_parts > 2) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -164,20 +165,19 @@ int32_t cascade_parts(const pa_dims* d, int32_t prefix_tokens, int32_t max_seq_l
 // Consecutive partitions per wave of the matrix-core split kernel: two once one partition per wave
 // would need more waves than the GPU holds at once (B * Hkv * parts bounds the waves from above), for
 // bf16 pools and 16 query rows per kv head (T * G <= 16). 8-bit tiles are half the bytes, so those
-// kernels need every wave they can get in flight and keep one partition per wave.
-// PA_SPLIT_WAVE_PARTS=1 or 2 overrides the choice (the results are the same bits either way).
+// kernels need every wave they can get in flight and keep one partition per wave. dims->wave_parts
+// = 1 or 2 forces the count (the results are the same bits either way).
 int32_t split_wave_parts(const pa_dims* d, int32_t parts) {
   const bool rows16 = d->q_tokens * (d->num_q_heads / d->num_kv_heads) <= 16;
   if (!rows16 || d->kv_dtype != PA_BF16) return 1;
-  const char* env = getenv("PA_SPLIT_WAVE_PARTS");
-  if (env && (env[0] == '1' || env[0] == '2') && env[1] == '\0') return env[0] - '0';
+  if (d->wave_parts == 1 || d->wave_parts == 2) return d->wave_parts;
   return (int64_t)d->num_seqs * d->num_kv_heads * parts > kResidentSplitWaves ? 2 : 1;
 }
 
 // Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
 // run, the merge launch. int8 pools carry their scales and run on the MFMA kernel.
 int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, const void* k_pool, const void* v_pool,
-                 const float* k_scales, const float* v_scales, const int32_t* block_tables, const int32_t* seq_lens,
+                 const float* scales, const int32_t* block_tables, const int32_t* seq_lens,
                  float scale, void* out, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                  size_t workspace_bytes, pa_stream_t stream, const void* k_new = nullptr,
                  const void* v_new = nullptr, bool fp8 = false) {
@@ -186,7 +186,8 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
-  if (int8 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+  if (int8 && (!scales || (reinterpret_cast<uintptr_t>(scales) & 7u) != 0)) return PA_ERR_INVALID_ARG;
+  if (int8 && append) return PA_ERR_UNSUPPORTED;  // 8-bit pools append with pa_write_kv_int8 / _fp8
   if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
@@ -202,8 +203,6 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   int variant = 0;
   if (int8) {
     if (dims->variant == PA_VARIANT_VALU || !pa::mfma_int8_supported(*dims)) return PA_ERR_UNSUPPORTED;
-    // the fused append into 8-bit pools: single pass, one 16-position block per tile
-    if (append && (split || dims->block_size != 16)) return PA_ERR_UNSUPPORTED;
     variant = PA_VARIANT_MFMA;
   } else if (append) {
     if (dims->variant == PA_VARIANT_VALU || !pa::mfma_supported(*dims)) return PA_ERR_UNSUPPORTED;
@@ -217,8 +216,7 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   if (st != PA_OK) return st;
 
   DecodeParams p = base_params(dims, q, k_pool, v_pool, block_tables, seq_lens, scale, out);
-  p.k_scales = k_scales;
-  p.v_scales = v_scales;
+  p.scales = scales;
   p.kv_int8 = int8 ? 1 : 0;
   p.kv_fp8 = int8 && fp8 ? 1 : 0;
   p.k_new = k_new;
@@ -332,7 +330,7 @@ int pa_write_kv(const pa_dims* dims, const void* k_new, const void* v_new, void*
 int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
               pa_stream_t stream) {
-  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out, 0, 0,
+  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out, 0, 0,
                       nullptr, 0, stream);
 }
 
@@ -354,14 +352,14 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
                           int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                           size_t workspace_bytes, pa_stream_t stream) {
-  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
+  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int pa_write_kv_decode(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, void* k_pool,
                        void* v_pool, const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
                        pa_stream_t stream) {
-  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out, 0, 0,
+  return decode_entry(dims, false, false, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out, 0, 0,
                       nullptr, 0, stream, k_new, v_new);
 }
 
@@ -369,7 +367,7 @@ int pa_write_kv_decode_partitioned(const pa_dims* dims, const void* q, const voi
                                    void* k_pool, void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                                    float scale, void* out, int32_t max_seq_len, int32_t partition_tokens,
                                    void* workspace, size_t workspace_bytes, pa_stream_t stream) {
-  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, scale, out,
+  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
@@ -404,103 +402,90 @@ int pa_write_kv_decode_cascade(const pa_dims* dims, const void* q, const void* k
 }  // extern "C"
 
 namespace {
-int write_kv_q8(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                float* k_scales, float* v_scales, const int32_t* block_tables, const int32_t* positions, bool fp8,
-                pa_stream_t stream) {
+int write_kv_q8(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* scales,
+                const int32_t* block_tables, const int32_t* positions, bool fp8, pa_stream_t stream) {
   const int st = check_dims_int8(dims, fp8 ? PA_FP8_E4M3 : PA_INT8);
   if (st != PA_OK) return st;
   if (dims->num_seqs == 0) return PA_OK;
-  if (!k_new || !v_new || !k_pool || !v_pool || !k_scales || !v_scales || !block_tables || !positions)
-    return PA_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !k_pool || !v_pool || !scales || !block_tables || !positions) return PA_ERR_INVALID_ARG;
   if (dims->head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new)) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(scales) & 7u) != 0) return PA_ERR_INVALID_ARG;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check(dims, block_tables, nullptr, positions, 0, s);
   if (chk != PA_OK) return chk;
   discard_stale_error();
   return launch_status(pa::launch_write_kv_int8(*dims, k_new, v_new, static_cast<int8_t*>(k_pool),
-                                                static_cast<int8_t*>(v_pool), k_scales, v_scales, block_tables,
-                                                positions, fp8, s));
+                                                static_cast<int8_t*>(v_pool), scales, block_tables, positions, fp8,
+                                                s));
 }
 }  // namespace
 
 extern "C" {
 
 int pa_write_kv_int8(const pa_dims* dims, const void* k_new, const void* v_new, int8_t* k_pool,
-                     int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                     const int32_t* positions, pa_stream_t stream) {
-  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, false, stream);
+                     int8_t* v_pool, float* scales, const int32_t* block_tables, const int32_t* positions,
+                     pa_stream_t stream) {
+  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, scales, block_tables, positions, false, stream);
 }
 
 int pa_write_kv_fp8(const pa_dims* dims, const void* k_new, const void* v_new, uint8_t* k_pool,
-                    uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                    const int32_t* positions, pa_stream_t stream) {
-  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, positions, true, stream);
+                    uint8_t* v_pool, float* scales, const int32_t* block_tables, const int32_t* positions,
+                    pa_stream_t stream) {
+  return write_kv_q8(dims, k_new, v_new, k_pool, v_pool, scales, block_tables, positions, true, stream);
 }
 
 int pa_decode_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
-                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
-                  const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
-  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
-                      nullptr, 0, stream, nullptr, nullptr, true);
+                  const float* scales, const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                  pa_stream_t stream) {
+  return decode_entry(dims, true, false, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, 0, 0, nullptr,
+                      0, stream, nullptr, nullptr, true);
 }
 
 int pa_decode_partitioned_fp8(const pa_dims* dims, const void* q, const uint8_t* k_pool,
-                              const uint8_t* v_pool, const float* k_scales, const float* v_scales,
-                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                              void* out, int32_t max_seq_len, int32_t partition_tokens,
-                              void* workspace, size_t workspace_bytes, pa_stream_t stream) {
-  return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
-                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream, nullptr, nullptr, true);
-}
-
-int pa_write_kv_decode_int8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, int8_t* k_pool,
-                            int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                            const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
-  if (dims && dims->num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
-  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
-                      nullptr, 0, stream, k_new, v_new);
-}
-
-int pa_write_kv_decode_fp8(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, uint8_t* k_pool,
-                           uint8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
-                           const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
-  if (dims && dims->num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
-  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
-                      nullptr, 0, stream, k_new, v_new, true);
+                              const uint8_t* v_pool, const float* scales, const int32_t* block_tables,
+                              const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
+                              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                              pa_stream_t stream) {
+  return decode_entry(dims, true, true, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, workspace, workspace_bytes, stream, nullptr, nullptr, true);
 }
 
 int pa_decode_int8(const pa_dims* dims, const void* q, const int8_t* k_pool, const int8_t* v_pool,
-                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
-                   const int32_t* seq_lens, float scale, void* out, pa_stream_t stream) {
-  return decode_entry(dims, true, false, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out, 0, 0,
-                      nullptr, 0, stream);
+                   const float* scales, const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                   pa_stream_t stream) {
+  return decode_entry(dims, true, false, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, 0, 0, nullptr,
+                      0, stream);
 }
 
 int pa_decode_partitioned_int8(const pa_dims* dims, const void* q, const int8_t* k_pool,
-                               const int8_t* v_pool, const float* k_scales, const float* v_scales,
-                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                               void* out, int32_t max_seq_len, int32_t partition_tokens,
-                               void* workspace, size_t workspace_bytes, pa_stream_t stream) {
-  return decode_entry(dims, true, true, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale, out,
-                      max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+                               const int8_t* v_pool, const float* scales, const int32_t* block_tables,
+                               const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
+                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                               pa_stream_t stream) {
+  return decode_entry(dims, true, true, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, workspace, workspace_bytes, stream);
 }
 
-int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, const int32_t* block_pairs, int32_t num_pairs,
-                   pa_stream_t stream) {
+int pa_copy_blocks(const pa_dims* dims, void* k_pool, void* v_pool, float* scales, const int32_t* block_pairs,
+                   int32_t num_pairs, pa_stream_t stream) {
   if (!dims || dims->num_kv_heads < 1 || dims->block_size < 1 || dims->head_dim < 1 || dims->num_blocks < 1)
     return PA_ERR_INVALID_ARG;
-  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_INT8) return PA_ERR_INVALID_ARG;
+  const int32_t t = dims->kv_dtype;
+  if (t != PA_F32 && t != PA_BF16 && t != PA_INT8 && t != PA_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  const bool q8 = t == PA_INT8 || t == PA_FP8_E4M3;
+  if (q8 != (scales != nullptr)) return PA_ERR_INVALID_ARG;  // 8-bit pools bring their scales; float pools none
   if (num_pairs < 0) return PA_ERR_INVALID_ARG;
   if (num_pairs == 0) return PA_OK;
   if (!k_pool || !v_pool || !block_pairs || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
-  const int64_t row = (int64_t)dims->head_dim * (dims->kv_dtype == PA_F32 ? 4 : dims->kv_dtype == PA_BF16 ? 2 : 1);
+  if (q8 && (reinterpret_cast<uintptr_t>(scales) & 7u) != 0) return PA_ERR_INVALID_ARG;
+  const int64_t row = (int64_t)dims->head_dim * (t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1);
   if ((row * dims->block_size * dims->num_kv_heads) % 16 != 0) return PA_ERR_UNSUPPORTED;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chk = pa::debug_check_copies(dims, block_pairs, num_pairs, s);
   if (chk != PA_OK) return chk;
   discard_stale_error();
-  return launch_status(pa::launch_copy_blocks(*dims, k_pool, v_pool, block_pairs, num_pairs, s));
+  return launch_status(pa::launch_copy_blocks(*dims, k_pool, v_pool, scales, block_pairs, num_pairs, s));
 }
 
 int pa_write_kv_varlen(const pa_dims* dims, const void* k_new, const void* v_new, void* k_pool, void* v_pool,

@@ -46,7 +46,10 @@
 //    0x64, is the fp16 value 1024 + u = 1152 + code (one v_perm_b32 per two
 //    codes). S^T runs as v_mfma_f32_16x16x32_f16 against q converted to fp16,
 //    and the 1152 * sum(q) offset of each row is removed before the tile's
-//    K scale multiplies the scores. Operand kc of lane (g, c16) takes head_dim
+//    K scale multiplies the scores. fp16 holds every bf16 value of magnitude
+//    2^-14 .. 2^15 exactly; a query row whose largest |q| reaches 2^15 is
+//    first multiplied by a power of two 2^-k that brings it below, and its
+//    scores by 2^k, so any finite q converts without overflow. Operand kc of lane (g, c16) takes head_dim
 //    32g + 8kc .. +7, so each lane reads 32 contiguous bytes of its K row; q's
 //    B operand is laid out the same way, so the dot products are unchanged.
 //  * V: code + 128 converted to bf16 (exact below 256) goes through the same
@@ -54,10 +57,11 @@
 //    before its hi/lo split, and 128 * (sum of those scaled P) is removed from
 //    each accumulator row at the end.
 //  * A tile lies in one block (b >= 16), so one K and one V scale per tile,
-//    loaded with the block id. int8 codes are always finite, so tail V rows
-//    need no zeroing: their P is exactly 0.
+//    one 8-byte scalar load (the scales are [N, Hkv, 2]) issued with the
+//    block id. int8 codes are always finite, so tail V rows need no zeroing:
+//    their P is exactly 0.
 //
-// Fused append (APPEND, bf16 pools): the call also stores this step's new K/V
+// Fused append (APPEND, bf16 pools only): the call also stores this step's new K/V
 // rows, at positions L - T .. L - 1, into their pool slots ([P4] "Block table
 // and allocator": a decode step writes the new token's K and V, then
 // attends). The workgroup of (sequence, kv head) stores that head's rows
@@ -245,7 +249,7 @@ template <int MT, int NW, bool WAVE_ITEMS, bool CASCADE, bool MULTI = false>
 constexpr int decode_lds_bytes() {
   const int v = NW * kTileBytes + (MULTI ? NW * stash_bytes<MT>() : 0);
   const int red = (!WAVE_ITEMS || CASCADE) ? (NW * 16 * MT * kD + 2 * NW * 16 * MT) * 4 : 0;
-  if (one_barrier_merge<MT, WAVE_ITEMS, CASCADE>()) return v + (kLptMaxSeqs + 4) * 4 + red + 64;
+  if (one_barrier_merge<MT, WAVE_ITEMS, CASCADE>()) return v + (kLptMaxSeqs + 4) * 4 + red;
   return v > red ? v : red;
 }
 
@@ -257,8 +261,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   static_assert(!MULTI || (WAVE_ITEMS && !CASCADE && !Q8), "two partitions per wave are for bf16 split items");
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
-  static_assert(!(Q8 && APPEND) || (!WAVE_ITEMS && BS == kTile && NW >= 2),
-                "8-bit pools take the fused append in a single pass of one-tile blocks");
+  static_assert(!(Q8 && APPEND), "8-bit pools append with the separate append kernel");
   static_assert(!F8 || Q8, "FP8 pools are 8-bit pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
   constexpr int kKvTile = kTile * kKvRow;
@@ -338,6 +341,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   u32x4 qb[MT][4];
   int row_tok[MT];  // query token of this lane's score row
   float qsum[MT];   // int8 pools: sum over head_dim of the row's fp16 q (weight of the K offset)
+  float qk_mul[MT];  // base-2 score scale of this lane's score row (int8: times the row's 2^k)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + c16;
@@ -355,11 +359,24 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
         qb[mt][kc] = present ? v : u32x4{0u, 0u, 0u, 0u};
       }
       qsum[mt] = 0.f;
+      qk_mul[mt] = p.qk_scale_log2;
     } else if constexpr (Q8) {
       // lane (g, c16): head_dim 32g .. 32g+31 of the row, as fp16; operand kc = 32g + 8kc .. +7
       u32x4 raw[4];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) raw[kc] = load16(qrow + 64 * g + 16 * kc);
+      // the row's largest |q| (the four 16-lane groups hold a quarter each); a row at or above 2^15
+      // is scaled by 2^-k (k = its exponent - 14) so that its fp16 values stay finite and exact
+      float amax = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[kc][e])), fabsf(bf16_hi(raw[kc][e]))));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int k = present && amax >= 32768.f ? (int)((__float_as_uint(amax) >> 23) & 0xffu) - 141 : 0;
+      const float down = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, k <= 114
+      qk_mul[mt] = p.qk_scale_log2 * __uint_as_float((uint32_t)(127 + k) << 23);
       float part = 0.f;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
@@ -367,8 +384,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
         f16x8 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          h[2 * e] = (_Float16)bf16_lo(v[e]);
-          h[2 * e + 1] = (_Float16)bf16_hi(v[e]);
+          h[2 * e] = (_Float16)(bf16_lo(v[e]) * down);
+          h[2 * e + 1] = (_Float16)(bf16_hi(v[e]) * down);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) part += (float)h[e];
@@ -378,6 +395,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
       part += __shfl_xor(part, 32, 64);
       qsum[mt] = part;
     } else {
+      qk_mul[mt] = p.qk_scale_log2;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
         const u32x4 v = load16(qrow + (kc * 4 + g) * 16);
@@ -416,9 +434,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     for (int jj = 0; jj < kBlocksPerTile; ++jj)
       ids.b[jj] = (int)min((uint32_t)trow[min(first + jj, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
     if constexpr (Q8) {
-      const int64_t si = (int64_t)ids.b[0] * p.Hkv + kvh;
-      ids.ks = read_only(p.k_scales)[si];
-      ids.vs = read_only(p.v_scales)[si];
+      const f32x2 sc = read_only(reinterpret_cast<const f32x2*>(p.scales))[(int64_t)ids.b[0] * p.Hkv + kvh];
+      ids.ks = sc[0];
+      ids.vs = sc[1];
     } else {
       ids.ks = ids.vs = 1.f;
     }
@@ -522,71 +540,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   f32x4 acc[MT][8];
   bool have_ref = false;
 
-  // Fused append into 8-bit pools (single pass, one block per tile). Before the tile loop, while the
-  // first tiles are on their way, the workgroup does what the separate append does for the (one or two)
-  // blocks of this kv head that take new rows: waves 0 and 1 the K and V of the first such block, waves
-  // 2 and 3 those of the second. The block's scale grows to cover the new rows (a block whose first row
-  // is new takes theirs alone), the codes already in it are re-quantised when it grew, the new rows are
-  // quantised, and the changed codes and the scale are stored; a barrier then makes the codes visible to
-  // the wave whose tile holds them. That wave takes the new scales from LDS (the scale array itself is
-  // read through the scalar cache, which may hold the old ones).
-  // fetch_new: this lane's 64 bytes of the new row `row` of the block at tile_p0, head_dim col0 .. +31.
-  // append_side: one side (K or V) of a block; w = this lane's 32 codes of block row `row` at col0 .. +31.
-  auto fetch_new = [&](u32x4 (&nv)[4], int tile_p0, int row, int col0, const void* src) {
-    const int pos = tile_p0 + row;
-    if (pos >= L - T && pos < L) {
-      const char* srow = static_cast<const char*>(src) +
-                         ((int64_t)(seq * T + (pos - (L - T))) * p.Hkv + kvh) * kRowBytes + col0 * 2;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) nv[c] = load16(srow + 16 * c);
-    }
-  };
-  float* q8_scales = reinterpret_cast<float*>(lds + decode_lds_bytes<MT, NW, false, false>() - 64);
-  auto append_side = [&](u32x4* w, int tile_p0, int row, int col0, const u32x4 (&nv)[4], float old_scale,
-                         char* block_base) -> float {
-    constexpr float kCodeMax = F8 ? 448.f : 127.f;  // scale = amax / kCodeMax
-    const int first_new = L - T;
-    const int first = max(0, first_new - tile_p0);  // rows of this block written before this step
-    const int pos = tile_p0 + row;
-    const bool is_new = pos >= first_new && pos < L;
-    float x[32];
-    float a = 0.f;
-    if (is_new) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = nv[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[8 * c + 2 * e] = bf16_lo(v[e]);
-          x[8 * c + 2 * e + 1] = bf16_hi(v[e]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(x[j]));
-    }
-    a = wave_max(a);  // the largest magnitude among the new rows of this block and kv head
-    const float cand = a / kCodeMax;
-    const float old = first > 0 ? old_scale : 0.f;
-    const float scale = first > 0 ? fmaxf(old, cand) : cand;
-    if ((row < first && scale > old) || is_new) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {  // dword c: codes of head_dim col0 + 4c .. +3
-        const uint32_t word = w[c >> 2][c & 3];
-        uint32_t out = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float val = is_new ? x[4 * c + k] : code_value<F8>((word >> (8 * k)) & 0xFFu) * old;
-          out |= encode_code<F8>(val, scale) << (8 * k);
-        }
-        w[c >> 2][c & 3] = out;
-      }
-      char* dst = block_base + (int64_t)row * kD + col0;
-      *reinterpret_cast<u32x4*>(dst) = w[0];
-      *reinterpret_cast<u32x4*>(dst + 16) = w[1];
-    }
-    return scale;
-  };
-
   // S^T of one tile (C layout: lane l has positions 4g + e of score row c16 + 16*mt), scaled and masked.
   auto scores = [&](bool masked, int tile_p0, const TileRegs& tr, float kscale, f32x4 (&s)[MT]) {
     u32x4 kf[4];  // 8-bit pools: the K codes as fp16 (int8) or bf16 (FP8) operands
@@ -607,17 +560,17 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
-        s[mt] = c * (kscale * p.qk_scale_log2);
+        s[mt] = c * (kscale * qk_mul[mt]);
       } else if constexpr (Q8) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(kf[kc]), as_f16x8(qb[mt][kc]), c, 0, 0, 0);
-        s[mt] = (c - kKOffset * qsum[mt]) * (kscale * p.qk_scale_log2);
+        s[mt] = (c - kKOffset * qsum[mt]) * (kscale * qk_mul[mt]);
       } else {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tr.k[kc]), as_bf16x8(qb[mt][kc]), c, 0, 0, 0);
-        s[mt] = c * p.qk_scale_log2;
+        s[mt] = c * qk_mul[mt];
       }
       if (masked) {
 #pragma unroll
@@ -789,14 +742,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
           cur[(u + PF) % NBUF] = ids;
           const int tile_p0 = tile_p0_of(i);
           const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
-          float kscale = ids_cur.ks, vscale = ids_cur.vs;
-          if constexpr (Q8 && APPEND) {
-            if (tile_p0 + kTile > L - T) {  // this tile (one block) took new rows: its new scales
-              const int sel = tile_p0 / kTile == (L - T) / kTile ? 0 : 2;
-              kscale = q8_scales[sel];
-              vscale = q8_scales[sel + 1];
-            }
-          }
+          const float kscale = ids_cur.ks, vscale = ids_cur.vs;
           f32x4 s[MT];
           scores(masked, tile_p0, ring[u], kscale, s);
           if (!have_ref) {
@@ -882,28 +828,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     }
   }
 
-  if constexpr (Q8 && APPEND) {
-    const int t0 = (L - T) / kTile, t1 = (L - 1) / kTile;  // the blocks taking new rows (b = 16)
-    const int which = wave & 1, tsel = wave >> 1;            // K or V; first or second block
-    if (L >= T && L > 0 && tsel < 2 && (tsel == 0 || t1 != t0)) {
-      const int tt = tsel ? t1 : t0;
-      const int blk = (int)min((uint32_t)trow[min(tt, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-      const int64_t si = (int64_t)blk * p.Hkv + kvh;
-      float* scales = const_cast<float*>(which ? p.v_scales : p.k_scales);
-      char* block_base = const_cast<char*>(which ? vbase : kbase) + (int64_t)blk * block_bytes;
-      // lane: row lane / 4 of the block, codes 32 (lane % 4) .. +31
-      const int row = lane >> 2, col0 = 32 * (lane & 3);
-      u32x4 w[2] = {load16(block_base + row * kD + col0), load16(block_base + row * kD + col0 + 16)};
-      u32x4 nv[4];
-      fetch_new(nv, tt * kTile, row, col0, which ? p.v_new : p.k_new);
-      const float sc = append_side(w, tt * kTile, row, col0, nv, scales[si], block_base);
-      if (lane == 0) {
-        scales[si] = sc;
-        q8_scales[tsel * 2 + which] = sc;
-      }
-    }
-    __syncthreads();  // the new codes are in the pools (and the scales in LDS) before any tile loads them
-  }
   for (int from = 0; (from = run(from)) >= 0;) {
   }
   if constexpr (APPEND && !Q8 && !CASCADE) {
@@ -1073,11 +997,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 
 template <int MT, bool WI>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
-  if (p.kv_int8 && p.append) {  // fused append into 8-bit pools: single pass, 16-position blocks
-    if (WI || p.block_size != 16) return hipErrorInvalidValue;
-    return p.kv_fp8 ? launch_t<MT, 16, false, true, true, false, true>(p, stream)
-                    : launch_t<MT, 16, false, true, true, false, false>(p, stream);
-  }
+  if (p.kv_int8 && p.append) return hipErrorInvalidValue;  // 8-bit pools append with the append kernel
   if (p.kv_int8 && p.kv_fp8) {
     switch (p.block_size) {
       case 16: return launch_t<MT, 16, WI, true, false, false, true>(p, stream);

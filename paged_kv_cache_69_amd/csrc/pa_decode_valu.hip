@@ -13,21 +13,22 @@
 // Mapping onto the hardware. One workgroup of NW waves handles one
 // (sequence, kv head, context partition, group of up to 8 query rows). All
 // query rows of the GQA group share every K/V byte the workgroup loads. The
-// partition's positions are cut into tiles of 16. A kv head's row is 256
-// bytes (128 bf16 or 64 fp32), so one tile of K is 4 KiB. Wave w takes tiles
-// w, w + NW, ... and, while it computes tile i, its loads for tile i + 1 are
-// already in flight. A tile's physical block id is a wave-uniform scalar load
-// issued one tile before the K/V loads that need it, so the table lookup never
-// sits on the critical path and never waits behind vector loads.
+// partition's positions are cut into tiles of 16. A kv head's row is C
+// 16-byte chunks: C = 8 (64 bf16), 16 (128 bf16 or 64 fp32) or 32 (128 fp32),
+// so one tile of K is C KiB. Wave w takes tiles w, w + NW, ... and, while it
+// computes tile i, its loads for the next tiles are already in flight. A
+// tile's physical block id is a wave-uniform scalar load issued one tile
+// before the K/V loads that need it, so the table lookup never sits on the
+// critical path and never waits behind vector loads.
 //  * K layout: lane = 4*ts + j holds token ts of the tile, 16-byte chunks
-//    4*r + j (r = 0..3). Four adjacent lanes read 64 contiguous bytes.
-//    q . k is 16 v_dot2_f32_bf16 per row (fp32: 16 FMAs), then a 2-step DPP
+//    4*r + j (r = 0 .. C/4 - 1). Four adjacent lanes read 64 contiguous bytes.
+//    q . k is C v_dot2_f32_bf16 per row (fp32: C FMAs), then a 2-step DPP
 //    quad reduction.
-//  * V layout: lane = 16*R + cv holds chunk cv of tokens 4R + r. Each lane
-//    accumulates a contiguous 8-element (bf16) or 4-element (fp32) slice of
-//    head_dim for every row, so P.V needs no cross-lane reduction. The
-//    probabilities move from the K lanes to the V lanes through 16 * NR
-//    floats of LDS per wave.
+//  * V layout: lane = C*R + cv holds chunk cv of tokens (C/4)*R + r. Each
+//    lane accumulates a contiguous 8-element (bf16) or 4-element (fp32) slice
+//    of head_dim for every row, so P.V needs no cross-lane reduction until
+//    the end, where the 64/C lanes of a chunk add up. The probabilities move
+//    from the K lanes to the V lanes through 16 * NR floats of LDS per wave.
 //  * Lazy max: the reference max of a row is only raised when a score
 //    exceeds it by more than 2^8 (base-2 units). That happens once per row in
 //    practice, so the common path rescales nothing. acc and l stay within
@@ -46,7 +47,6 @@ namespace pa {
 namespace {
 
 constexpr int kTile = 16;             // positions per wave tile
-constexpr int kRowBytes = 256;        // one kv head's K or V row
 constexpr float kRescaleSlack = 8.0f; // lazy-max slack, base-2 exponent units
 
 // Launch shape: waves per workgroup, tiles each wave keeps in flight ahead of
@@ -73,9 +73,11 @@ struct KvFmt {
   static constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
 };
 
+// One tile held by a wave: C/4 K chunks (the lane's token) and C/4 V chunks (its chunk of C/4 tokens).
+template <int KC>
 struct Tile {
-  u32x4 k[4];
-  u32x4 v[4];
+  u32x4 k[KC];
+  u32x4 v[KC];
 };
 
 template <bool NT>
@@ -86,14 +88,18 @@ __device__ __forceinline__ u32x4 load_kv16(const char* p) {
     return load16(p);
 }
 
-template <bool BF16, int NR, int BS, int NW, int PF, bool QLDS, bool NT>
+template <bool BF16, int C, int NR, int BS, int NW, int PF, bool QLDS, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams p) {
+  static_assert(C == 8 || C == 16 || C == 32, "a row is 8, 16 or 32 chunks of 16 bytes");
   constexpr int E = KvFmt<BF16>::E;
-  constexpr int D = 16 * E;
+  constexpr int D = C * E;
+  constexpr int RB = C * 16;                 // bytes of one kv head's K or V row (and of a q row)
+  constexpr int KC = C / 4;                  // chunks per lane per tile, for K and for V
   constexpr int NPL = NR >= 4 ? NR / 4 : 1;  // rows each K lane turns into probabilities
+  using TileT = Tile<KC>;
 
   __shared__ float p_lds[NW][kTile][NR];
-  __shared__ u32x4 q_lds[QLDS ? NR : 1][16];
+  __shared__ u32x4 q_lds[QLDS ? NR : 1][C];
   __shared__ float red_acc[NW][NR][D];
   __shared__ float red_m[NW][NR];
   __shared__ float red_l[NW][NR];
@@ -119,12 +125,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   const int vis_all = L - T + 1;  // positions below this are visible to every query row
 
   const int ts = lane >> 2, j = lane & 3;  // K lanes
-  const int R = lane >> 4, cv = lane & 15; // V lanes
+  const int R = lane / C, cv = lane % C;   // V lanes: chunk cv of tokens KC*R .. KC*R + KC - 1
 
   // ---- query rows: row n of this group is global row rg*NR + n = t*G + g
   int row_lim[NR];  // last visible position; -1 for an absent row
   bool rows_all_present = true;
-  u32x4 qv[QLDS ? 1 : NR][4];
+  u32x4 qv[QLDS ? 1 : NR][KC];
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
     const int r = rg * NR + n;
@@ -133,11 +139,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   }
   auto q_row_ptr = [&](int n) {
     const int r = rg * NR + n;
-    return static_cast<const char*>(p.q) + ((int64_t)(seq * T + r / p.G) * p.Hq + kvh * p.G + r % p.G) * kRowBytes;
+    return static_cast<const char*>(p.q) + ((int64_t)(seq * T + r / p.G) * p.Hq + kvh * p.G + r % p.G) * RB;
   };
   if constexpr (QLDS) {
-    for (int idx = threadIdx.x; idx < NR * 16; idx += NW * 64) {
-      const int n = idx >> 4, c = idx & 15;
+    for (int idx = threadIdx.x; idx < NR * C; idx += NW * 64) {
+      const int n = idx / C, c = idx % C;
       q_lds[n][c] = rg * NR + n < p.rows ? load16(q_row_ptr(n) + c * 16) : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < KC; ++c)
         qv[QLDS ? 0 : n][c] = rg * NR + n < p.rows ? load16(q_row_ptr(n) + (c * 4 + j) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -157,9 +163,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   };
 
   const int32_t* trow = p.block_tables + (int64_t)seq * p.MB;
-  const int64_t block_bytes = (int64_t)p.Hkv * BS * kRowBytes;
-  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kRowBytes;
-  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kRowBytes;
+  const int64_t block_bytes = (int64_t)p.Hkv * BS * RB;
+  const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * RB;
+  const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * RB;
   const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
 
   // Physical block of the wave's i-th tile when blocks hold >= 16 positions: a wave-uniform
@@ -168,30 +174,29 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 
   // A tile inside one block is read through a buffer descriptor built per tile in SGPRs plus a
   // lane offset that never changes, so its loads need no per-tile vector address arithmetic.
-  const uint32_t k_lane_off = ts * kRowBytes + j * 16;  // + 64 * c
-  const uint32_t v_lane_off = R * 4 * kRowBytes + cv * 16;  // + 256 * c
-  auto load_tile = [&](int i, int phys32, Tile& tl) {
+  const uint32_t k_lane_off = ts * RB + j * 16;        // + 64 * c
+  const uint32_t v_lane_off = R * KC * RB + cv * 16;    // + RB * c
+  auto load_tile = [&](int i, int phys32, TileT& tl) {
     const int tile_p0 = p_begin + (wave + i * NW) * kTile;
     if constexpr (BS >= kTile) {
-      const int64_t off = (int64_t)phys32 * block_bytes + (int64_t)(tile_p0 % BS) * kRowBytes;
-      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + off, kTile * kRowBytes);
-      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + off, kTile * kRowBytes);
+      const int64_t off = (int64_t)phys32 * block_bytes + (int64_t)(tile_p0 % BS) * RB;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + off, kTile * RB);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + off, kTile * RB);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.k[c] = buffer_load16(kr, k_lane_off + c * 64);
+      for (int c = 0; c < KC; ++c) tl.k[c] = buffer_load16(kr, k_lane_off + c * 64);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.v[c] = buffer_load16(vr, v_lane_off + c * kRowBytes);
+      for (int c = 0; c < KC; ++c) tl.v[c] = buffer_load16(vr, v_lane_off + c * RB);
     } else {
       // Blocks shorter than a tile: each lane finds its own block. Positions past the
       // sequence are clamped to its last position (a valid slot), then masked.
       const int pk = min(tile_p0 + ts, L - 1);
-      const char* kb = kbase + (int64_t)trow[pk / BS] * block_bytes + (int64_t)(pk % BS) * kRowBytes;
+      const char* kb = kbase + (int64_t)trow[pk / BS] * block_bytes + (int64_t)(pk % BS) * RB;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tl.k[c] = load_kv16<NT>(kb + (c * 4 + j) * 16);
+      for (int c = 0; c < KC; ++c) tl.k[c] = load_kv16<NT>(kb + (c * 4 + j) * 16);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int pv = min(tile_p0 + 4 * R + c, L - 1);
-        tl.v[c] = load_kv16<NT>(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * kRowBytes +
-                                cv * 16);
+      for (int c = 0; c < KC; ++c) {
+        const int pv = min(tile_p0 + KC * R + c, L - 1);
+        tl.v[c] = load_kv16<NT>(vbase + (int64_t)trow[pv / BS] * block_bytes + (int64_t)(pv % BS) * RB + cv * 16);
       }
     }
   };
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 
   auto row_of = [&](int nl) { return NR >= 4 ? nl * 4 + j : j; };
 
-  auto compute_tile = [&](auto masked_tag, int i, const Tile& tl) {
+  auto compute_tile = [&](auto masked_tag, int i, const TileT& tl) {
     constexpr bool masked = decltype(masked_tag)::value;
     const int tile_p0 = p_begin + (wave + i * NW) * kTile;
 
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
     for (int n = 0; n < NR; ++n) {
       float a = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < KC; ++c) {
         const u32x4 qc = q_chunk(n, c);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -286,13 +291,13 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 
     // ---- P.V on this lane's head_dim slice
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < KC; ++c) {
       float pv[NR];
 #pragma unroll
-      for (int n = 0; n < NR; ++n) pv[n] = p_lds[wave][4 * R + c][n];
+      for (int n = 0; n < NR; ++n) pv[n] = p_lds[wave][KC * R + c][n];
       u32x4 v = tl.v[c];
       if constexpr (masked) {
-        if (tile_p0 + 4 * R + c >= L) v = u32x4{0u, 0u, 0u, 0u};
+        if (tile_p0 + KC * R + c >= L) v = u32x4{0u, 0u, 0u, 0u};
       }
       float vf[E];
 #pragma unroll
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   // path and the wait before each compute leaves the prefetched tiles outstanding.
   if (my_tiles > 0) {
     const int last = my_tiles - 1;
-    Tile ring[PF + 1];
+    TileT ring[PF + 1];
 #pragma unroll
     for (int u = 0; u < PF; ++u) load_tile(min(u, last), BS >= kTile ? phys_of(min(u, last)) : 0, ring[u]);
     int phys_next = BS >= kTile ? phys_of(min(PF, last)) : 0;
@@ -339,14 +344,14 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
     }
   }
 
-  // ---- merge the four V-lane groups, then the waves, then write out or emit the partial
+  // ---- merge the 64/C V-lane groups, then the waves, then write out or emit the partial
 #pragma unroll
   for (int n = 0; n < NR; ++n)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float a = acc[n][e];
-      a += __shfl_xor(a, 16, 64);
-      a += __shfl_xor(a, 32, 64);
+#pragma unroll
+      for (int m = C; m < 64; m <<= 1) a += __shfl_xor(a, m, 64);
       acc[n][e] = a;
     }
 #pragma unroll
@@ -408,33 +413,40 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   }
 }
 
-template <bool BF16, int NR, int BS>
+// Tiles kept in flight ahead of the one being computed: a 32-chunk row (fp32, head_dim 128) makes
+// a tile 64 VGPRs per lane, so its ring keeps one tile ahead to stay at two waves per SIMD.
+template <int C>
+constexpr int prefetch_for() {
+  return C == 32 ? 1 : kPrefetch;
+}
+
+template <bool BF16, int C, int NR, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.B * p.parts * p.row_groups * p.Hkv;
   if (grid == 0) return hipSuccess;
-  decode_valu_kernel<BF16, NR, BS, kWaves, kPrefetch, kQInLds, kNtLoads>
+  decode_valu_kernel<BF16, C, NR, BS, kWaves, prefetch_for<C>(), kQInLds, kNtLoads>
       <<<dim3((unsigned)grid), dim3(kWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <bool BF16, int NR>
+template <bool BF16, int C, int NR>
 hipError_t launch_bs(const DecodeParams& p, hipStream_t stream) {
   switch (p.block_size) {
-    case 4: return launch_t<BF16, NR, 4>(p, stream);
-    case 8: return launch_t<BF16, NR, 8>(p, stream);
-    case 16: return launch_t<BF16, NR, 16>(p, stream);
-    case 32: return launch_t<BF16, NR, 32>(p, stream);
+    case 4: return launch_t<BF16, C, NR, 4>(p, stream);
+    case 8: return launch_t<BF16, C, NR, 8>(p, stream);
+    case 16: return launch_t<BF16, C, NR, 16>(p, stream);
+    case 32: return launch_t<BF16, C, NR, 32>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool BF16>
+template <bool BF16, int C>
 hipError_t launch_nr(const DecodeParams& p, hipStream_t stream) {
   switch (valu_rows_per_group(p.rows)) {
-    case 1: return launch_bs<BF16, 1>(p, stream);
-    case 2: return launch_bs<BF16, 2>(p, stream);
-    case 4: return launch_bs<BF16, 4>(p, stream);
-    default: return launch_bs<BF16, 8>(p, stream);
+    case 1: return launch_bs<BF16, C, 1>(p, stream);
+    case 2: return launch_bs<BF16, C, 2>(p, stream);
+    case 4: return launch_bs<BF16, C, 4>(p, stream);
+    default: return launch_bs<BF16, C, 8>(p, stream);
   }
 }
 
@@ -448,13 +460,15 @@ int valu_rows_per_group(int rows) {
 }
 
 bool valu_supported(const pa_dims& d) {
-  const bool shape = (d.kv_dtype == PA_BF16 && d.head_dim == 128) || (d.kv_dtype == PA_F32 && d.head_dim == 64);
+  const bool dtype = d.kv_dtype == PA_BF16 || d.kv_dtype == PA_F32;
+  const bool head = d.head_dim == 64 || d.head_dim == 128;
   const bool block = d.block_size == 4 || d.block_size == 8 || d.block_size == 16 || d.block_size == 32;
-  return shape && block && d.q_dtype == d.kv_dtype;
+  return dtype && head && block && d.q_dtype == d.kv_dtype;
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
-  return kv_dtype == PA_BF16 ? launch_nr<true>(p, stream) : launch_nr<false>(p, stream);
+  if (kv_dtype == PA_BF16) return p.D == 64 ? launch_nr<true, 8>(p, stream) : launch_nr<true, 16>(p, stream);
+  return p.D == 64 ? launch_nr<false, 16>(p, stream) : launch_nr<false, 32>(p, stream);
 }
 
 }  // namespace pa

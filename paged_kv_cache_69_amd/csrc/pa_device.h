@@ -66,10 +66,9 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
 }
 
-// ---- codes of 8-bit pools, shared by the append and the decode that appends in the same launch, so
-// both decide every code with the same fp32 operations: the scale amax / 127 (int8) or amax / 448
+// ---- codes of 8-bit pools, as the append decides them: the scale amax / 127 (int8) or amax / 448
 // (E4M3), the quotient x / scale (correctly rounded), then round half to even and clip (int8) or the
-// E4M3 rounding below.
+// E4M3 rounding below, every step in fp32.
 __device__ __forceinline__ int quantise(float x, float scale) {
   if (scale == 0.f) return 0;
   return (int)fminf(fmaxf(__builtin_rintf(x / scale), -127.f), 127.f);

@@ -20,8 +20,7 @@ struct DecodeParams {
   void* out;                 // [B, T, Hq, D] (single-pass launches)
   float* part_ml;            // [B*T*Hq, parts, 2]: (m, l) per partition (partitioned launches)
   float* part_acc;           // [B*T*Hq, parts, D]: unnormalised accumulator per partition
-  const float* k_scales;     // int8 pools: [N, Hkv] scale of each (block, kv head); else null
-  const float* v_scales;
+  const float* scales;       // 8-bit pools: [N, Hkv, 2] (K scale, V scale) of each (block, kv head); else null
   const void* k_new;         // fused append: [B, T, Hkv, D] new rows for positions L - T .. L - 1
   const void* v_new;
   float qk_scale_log2;       // scale * log2(e): scores are kept in base-2 exponent units
@@ -33,9 +32,9 @@ struct DecodeParams {
   int32_t part_tokens;       // positions per partition (single pass: >= every length)
   int32_t out_dtype;         // pa_dtype of out
   int32_t partial;           // 1: write (m, l, acc) partials; 0: write normalised out
-  int32_t kv_int8;           // 1: the pools hold 8-bit codes scaled by k_scales / v_scales
+  int32_t kv_int8;           // 1: the pools hold 8-bit codes scaled by `scales`
   int32_t kv_fp8;            // with kv_int8: the codes are E4M3 values (else int8 integers)
-  int32_t append;            // 1: also store k_new / v_new into the pools (MFMA kernel, bf16)
+  int32_t append;            // 1: also store k_new / v_new into the pools (MFMA kernel, bf16 pools)
   int32_t prefix_tokens;     // cascade: positions every sequence shares (0: none)
   int32_t prefix_parts;      // cascade: workspace slots 0 .. prefix_parts-1 hold the prefix's partials
                              // (one per group of mfma_waves() chunks)
@@ -50,7 +49,7 @@ hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_ne
 
 // 8-bit pools (int8 or, with fp8, E4M3 codes): append with per-(block, kv head) scales.
 hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
-                                int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                                int8_t* v_pool, float* scales, const int32_t* block_tables,
                                 const int32_t* positions, bool fp8, hipStream_t stream);
 
 // Rows handled by one VALU workgroup for `rows` query rows per kv head.
@@ -79,9 +78,10 @@ int mfma_lpt_max_seqs();  // largest batch the single pass can order longest fir
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
 
-// Copy-on-write block copies: pairs [n, 2] (source, destination) on the device.
-hipError_t launch_copy_blocks(const pa_dims& d, void* k_pool, void* v_pool, const int32_t* pairs, int32_t num_pairs,
-                              hipStream_t stream);
+// Copy-on-write block copies: pairs [n, 2] (source, destination) on the device; for 8-bit pools the
+// blocks' [Hkv, 2] scales too (scales non-null).
+hipError_t launch_copy_blocks(const pa_dims& d, void* k_pool, void* v_pool, float* scales, const int32_t* pairs,
+                              int32_t num_pairs, hipStream_t stream);
 // PA_CHECK=1: every pair in [0, num_blocks), destinations distinct and never a source.
 int debug_check_copies(const pa_dims* dims, const int32_t* pairs, int32_t num_pairs, hipStream_t stream);
 

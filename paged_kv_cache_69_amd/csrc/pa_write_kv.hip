@@ -60,8 +60,7 @@ struct WriteInt8Params {
   const void* v_new;
   int8_t* k_pool;
   int8_t* v_pool;
-  float* k_scales;
-  float* v_scales;
+  float* scales;  // [N, Hkv, 2]: K scale, V scale of each (block, kv head)
   const int32_t* block_tables;
   const int32_t* positions;
   int32_t T, Hkv, MB, block_size, D;
@@ -85,7 +84,6 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
   {
     const void* src = which ? p.v_new : p.k_new;
     int8_t* pool = which ? p.v_pool : p.k_pool;
-    float* scales = which ? p.v_scales : p.k_scales;
     for (int t = 0; t < p.T;) {
       const int pos0 = p.positions[(int64_t)seq * p.T + t];
       const int first = pos0 % b;
@@ -100,7 +98,7 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
       }
       a = wave_max(a);
       const float cand = a / kCodeMax;
-      float* sp = scales + (int64_t)blk * p.Hkv + kvh;
+      float* sp = p.scales + ((int64_t)blk * p.Hkv + kvh) * 2 + which;
       const float old = first > 0 ? *sp : 0.f;
       const float scale = first > 0 ? fmaxf(old, cand) : cand;
       if (first > 0 && scale > old) {
@@ -137,15 +135,14 @@ __global__ __launch_bounds__(128) void write_kv_int8_kernel(const WriteInt8Param
 }  // namespace
 
 hipError_t launch_write_kv_int8(const pa_dims& d, const void* k_new, const void* v_new, int8_t* k_pool,
-                                int8_t* v_pool, float* k_scales, float* v_scales, const int32_t* block_tables,
+                                int8_t* v_pool, float* scales, const int32_t* block_tables,
                                 const int32_t* positions, bool fp8, hipStream_t stream) {
   WriteInt8Params p;
   p.k_new = k_new;
   p.v_new = v_new;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
-  p.k_scales = k_scales;
-  p.v_scales = v_scales;
+  p.scales = scales;
   p.block_tables = block_tables;
   p.positions = positions;
   p.T = d.q_tokens;

@@ -56,7 +56,7 @@ def test_status_strings_and_version(lib):
 def _dims(**kw):
     base = dict(num_seqs=4, q_tokens=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                 num_blocks=100, max_blocks_per_seq=8, q_dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16,
-                out_dtype=pa.PA_F32, variant=0)
+                out_dtype=pa.PA_F32, variant=0, wave_parts=0)
     base.update(kw)
     return pa.PaDims(*[base[n] for n, _ in pa.PaDims._fields_])
 
@@ -73,7 +73,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails val
     (dict(q_dtype=pa.PA_F32), -2),       # q and KV dtypes differ
     (dict(head_dim=96), -2),             # no kernel for this head_dim
     (dict(block_size=64), -2),
-    (dict(kv_dtype=pa.PA_F32, q_dtype=pa.PA_F32, head_dim=128), -2),
+    (dict(wave_parts=3), -1),
+    (dict(wave_parts=-1), -1),
 ])
 def test_decode_rejects_bad_dims(lib, kw, status):
     d = _dims(**kw)
@@ -125,17 +126,18 @@ def test_partitioned_wave_parts_arithmetic(lib):
 
 
 def test_partitioned_wave_parts_override(lib, monkeypatch):
-    d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
-    f = lambda: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), 32768, 512)  # noqa: E731
-    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "1")
-    assert f() == 1
-    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "2")
-    assert f() == 2
-    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "7")  # not 1 or 2: the usual choice
-    assert f() == 2
-    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "2")
-    d8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=pa.PA_INT8)
-    assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d8), 32768, 512) == 1
+    """pa_dims.wave_parts forces the count for bf16 pools of up to 16 rows per kv head, is ignored where
+    two partitions per wave do not exist, and no environment variable changes anything."""
+    f = lambda d: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), 32768, 512)  # noqa: E731
+    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=1)) == 1
+    assert f(_dims(num_seqs=1, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=2)) == 2
+    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=0)) == 2
+    monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "1")  # the variable of an earlier version: no effect
+    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=0)) == 2
+    for code in (pa.PA_INT8, pa.PA_FP8_E4M3):
+        assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code, wave_parts=2)) == 1
+    assert f(_dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, wave_parts=2)) == 1
+    assert f(_dims(wave_parts=5)) == -1
 
 
 def test_fused_cascade_refuses_missing_rows(lib):

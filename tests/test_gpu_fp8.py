@@ -30,8 +30,11 @@ def _bits(t):
 
 
 def _np(pools):
-    """(k codes uint8, k scales, v codes uint8, v scales) as numpy arrays for the oracle."""
-    return [p.cpu().view(torch.uint8).numpy() if p.dtype == torch.float8_e4m3fn else p.cpu().numpy() for p in pools]
+    """(k codes, v codes, scales [N, Hkv, 2]) -> the oracle's (k codes uint8, k scales, v codes uint8,
+    v scales) as numpy arrays."""
+    kc, vc, sc = [p.cpu().view(torch.uint8).numpy() if p.dtype == torch.float8_e4m3fn else p.cpu().numpy()
+                  for p in pools]
+    return [kc, np.ascontiguousarray(sc[..., 0]), vc, np.ascontiguousarray(sc[..., 1])]
 
 
 def _gpu(*ts):
@@ -39,8 +42,18 @@ def _gpu(*ts):
 
 
 def _write(pa, g):
-    """g = [k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_tables, positions] on the GPU."""
-    pa.write_kv_fp8(g[0], g[1], g[2], g[4], g[3], g[5], g[6], g[7])
+    """g = [k_new, v_new, k_codes, v_codes, scales, block_tables, positions] on the GPU."""
+    pa.write_kv_fp8(*g)
+
+
+def _check_append(g, ref):
+    """Pools and scales after the GPU append (g[2:5]) against the oracle's, bit for bit."""
+    kc, ks, vc, vs = ref
+    assert np.array_equal(_bits(g[2]), kc), "k codes"
+    assert np.array_equal(_bits(g[3]), vc), "v codes"
+    sc = _bits(g[4])
+    assert np.array_equal(sc[..., 0], ks.view(np.int32)), "k scales"
+    assert np.array_equal(sc[..., 1], vs.view(np.int32)), "v scales"
 
 
 def _append_ref(case, pools, k_new, v_new):
@@ -74,9 +87,7 @@ def test_write_kv_fp8_bit_exact(gpu_lib, b, t, dtype, hkv):
     g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
     _write(gpu_lib, g)
     torch.cuda.synchronize()
-    ref = _append_ref(case, pools, case.k_new, case.v_new)
-    for name, got, want in zip(("k codes", "k scales", "v codes", "v scales"), g[2:6], ref):
-        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want), name
+    _check_append(g, _append_ref(case, pools, case.k_new, case.v_new))
 
 
 # ----------------------------------------------------------------------------- decode
@@ -92,13 +103,13 @@ def test_decode_fp8_shapes(gpu_lib, b, hq, hkv, t):
     pools = fp8_pools(case, seed=hq * 7 + t)
     ref = _decode_ref(case, pools)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    kc, ks, vc, vs = _gpu(*pools)
+    kc, vc, sc = _gpu(*pools)
     print(f"[case] fp8 decode b={b} hq={hq} hkv={hkv} T={t}", flush=True)
-    out = gpu_lib.decode_fp8(q, kc, vc, ks, vs, tables, lens, case.scale)
+    out = gpu_lib.decode_fp8(q, kc, vc, sc, tables, lens, case.scale)
     torch.cuda.synchronize()
     assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what="single pass")
     for pt in (32, 48 if 48 % b == 0 else 64):
-        out = gpu_lib.decode_partitioned_fp8(q, kc, vc, ks, vs, tables, lens, case.scale, case.max_seq_len, pt)
+        out = gpu_lib.decode_partitioned_fp8(q, kc, vc, sc, tables, lens, case.scale, case.max_seq_len, pt)
         torch.cuda.synchronize()
         assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.float32, what=f"split {pt}")
 
@@ -108,8 +119,8 @@ def test_decode_fp8_bf16_output(gpu_lib):
     pools = fp8_pools(case, seed=5)
     ref = _decode_ref(case, pools)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    kc, ks, vc, vs = _gpu(*pools)
-    out = gpu_lib.decode_fp8(q, kc, vc, ks, vs, tables, lens, case.scale, out_dtype=torch.bfloat16)
+    kc, vc, sc = _gpu(*pools)
+    out = gpu_lib.decode_fp8(q, kc, vc, sc, tables, lens, case.scale, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_attention_close(out.cpu(), ref, kv_dtype=torch.float8_e4m3fn, out_dtype=torch.bfloat16, what="bf16 out")
 
@@ -121,7 +132,7 @@ def test_append_then_decode_step(gpu_lib):
     g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
     _write(gpu_lib, g)
     q, lens = _gpu(case.q, case.seq_lens)
-    out = gpu_lib.decode_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+    out = gpu_lib.decode_fp8(q, g[2], g[3], g[4], g[5], lens, case.scale)
     torch.cuda.synchronize()
     kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
     ref = oracle.decode_fp8(case.q.float().numpy(), kc, ks, vc, vs, case.block_tables.numpy(),
@@ -133,13 +144,13 @@ def test_decode_fp8_permuted_blocks_bitwise(gpu_lib):
     """Relabelling physical blocks (codes, scales and table entries together) leaves the output
     bit-identical."""
     case = make_case("batch64", num_seqs=8)
-    kc, ks, vc, vs = fp8_pools(case, seed=11)
+    kc, vc, sc = fp8_pools(case, seed=11)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    a = gpu_lib.decode_fp8(q, *_gpu(kc, vc, ks, vs), tables, lens, case.scale)
+    a = gpu_lib.decode_fp8(q, *_gpu(kc, vc, sc), tables, lens, case.scale)
     n = kc.shape[0]
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(4))
     moved = []
-    for x in (kc, vc, ks, vs):
+    for x in (kc, vc, sc):
         raw = x.view(torch.uint8) if x.dtype == torch.float8_e4m3fn else x
         y = torch.empty_like(raw)
         y[perm] = raw
@@ -160,7 +171,7 @@ def test_fp8_unsupported_shapes_are_refused(gpu_lib):
         pools = _gpu(*fp8_pools(case, seed=2))
         q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
         with pytest.raises(gpu_lib.PaError) as err:
-            gpu_lib.decode_fp8(q, pools[0], pools[2], pools[1], pools[3], tables, lens, case.scale)
+            gpu_lib.decode_fp8(q, pools[0], pools[1], pools[2], tables, lens, case.scale)
         assert err.value.status == -2
 
 
@@ -177,14 +188,13 @@ def test_fp8_full_size_sampled(gpu_lib, name, partition_tokens):
     _write(gpu_lib, g)
     q, lens = _gpu(case.q, case.seq_lens)
     if partition_tokens:
-        out = gpu_lib.decode_partitioned_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale, case.max_seq_len,
+        out = gpu_lib.decode_partitioned_fp8(q, g[2], g[3], g[4], g[5], lens, case.scale, case.max_seq_len,
                                               partition_tokens)
     else:
-        out = gpu_lib.decode_fp8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+        out = gpu_lib.decode_fp8(q, g[2], g[3], g[4], g[5], lens, case.scale)
     torch.cuda.synchronize()
     kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
-    for got, want in zip(g[2:6], (kc, ks, vc, vs)):
-        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want)
+    _check_append(g, (kc, ks, vc, vs))
     del g, pools
     got = out.cpu().double().numpy()
     qf = case.q.float().numpy()

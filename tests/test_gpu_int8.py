@@ -32,20 +32,34 @@ def _gpu(*ts):
 
 
 def _write(pa, g):
-    """g = [k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_tables, positions] on the GPU."""
-    pa.write_kv_int8(g[0], g[1], g[2], g[4], g[3], g[5], g[6], g[7])
+    """g = [k_new, v_new, k_codes, v_codes, scales, block_tables, positions] on the GPU."""
+    pa.write_kv_int8(*g)
+
+
+def _split(pools):
+    """(k_codes, v_codes, scales [N, Hkv, 2]) -> the oracle's (k_codes, k_scales, v_codes, v_scales) in numpy."""
+    kc, vc, sc = [p.cpu().numpy() for p in pools]
+    return kc, np.ascontiguousarray(sc[..., 0]), vc, np.ascontiguousarray(sc[..., 1])
 
 
 def _append_ref(case, pools, k_new, v_new):
-    kc, ks, vc, vs = [p.cpu().numpy() for p in pools]
-    return oracle.append_int8(kc, ks, vc, vs, k_new.float().numpy(), v_new.float().numpy(),
+    return oracle.append_int8(*_split(pools), k_new.float().numpy(), v_new.float().numpy(),
                               case.block_tables.numpy(), case.positions.numpy(), case.block_size)
 
 
 def _decode_ref(case, pools):
-    kc, ks, vc, vs = [p.cpu().numpy() for p in pools]
-    return oracle.decode_int8(case.q.float().numpy(), kc, ks, vc, vs, case.block_tables.numpy(),
+    return oracle.decode_int8(case.q.float().numpy(), *_split(pools), case.block_tables.numpy(),
                               case.seq_lens.numpy(), case.scale, case.block_size)
+
+
+def _check_append(g, ref):
+    """Pools and scales after the GPU append (g[2:5]) against the oracle's, bit for bit."""
+    kc, ks, vc, vs = ref
+    assert np.array_equal(_bits(g[2]), kc), "k codes"
+    assert np.array_equal(_bits(g[3]), vc), "v codes"
+    sc = _bits(g[4])
+    assert np.array_equal(sc[..., 0], ks.view(np.int32)), "k scales"
+    assert np.array_equal(sc[..., 1], vs.view(np.int32)), "v scales"
 
 
 # ----------------------------------------------------------------------------- append
@@ -67,9 +81,7 @@ def test_write_kv_int8_bit_exact(gpu_lib, b, t, dtype, hkv):
     g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
     _write(gpu_lib, g)
     torch.cuda.synchronize()
-    ref = _append_ref(case, pools, case.k_new, case.v_new)
-    for name, got, want in zip(("k codes", "k scales", "v codes", "v scales"), g[2:6], ref):
-        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want), name
+    _check_append(g, _append_ref(case, pools, case.k_new, case.v_new))
 
 
 # ----------------------------------------------------------------------------- decode
@@ -85,13 +97,13 @@ def test_decode_int8_shapes(gpu_lib, b, hq, hkv, t):
     pools = int8_pools(case, seed=hq * 7 + t)
     ref = _decode_ref(case, pools)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    kc, ks, vc, vs = _gpu(*pools)
+    kc, vc, sc = _gpu(*pools)
     print(f"[case] int8 decode b={b} hq={hq} hkv={hkv} T={t}", flush=True)
-    out = gpu_lib.decode_int8(q, kc, vc, ks, vs, tables, lens, case.scale)
+    out = gpu_lib.decode_int8(q, kc, vc, sc, tables, lens, case.scale)
     torch.cuda.synchronize()
     assert_attention_close(out.cpu(), ref, kv_dtype=torch.int8, out_dtype=torch.float32, what="single pass")
     for pt in (32, 48 if 48 % b == 0 else 64):
-        out = gpu_lib.decode_partitioned_int8(q, kc, vc, ks, vs, tables, lens, case.scale, case.max_seq_len, pt)
+        out = gpu_lib.decode_partitioned_int8(q, kc, vc, sc, tables, lens, case.scale, case.max_seq_len, pt)
         torch.cuda.synchronize()
         assert_attention_close(out.cpu(), ref, kv_dtype=torch.int8, out_dtype=torch.float32, what=f"split {pt}")
 
@@ -101,8 +113,8 @@ def test_decode_int8_bf16_output(gpu_lib):
     pools = int8_pools(case, seed=5)
     ref = _decode_ref(case, pools)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    kc, ks, vc, vs = _gpu(*pools)
-    out = gpu_lib.decode_int8(q, kc, vc, ks, vs, tables, lens, case.scale, out_dtype=torch.bfloat16)
+    kc, vc, sc = _gpu(*pools)
+    out = gpu_lib.decode_int8(q, kc, vc, sc, tables, lens, case.scale, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_attention_close(out.cpu(), ref, kv_dtype=torch.int8, out_dtype=torch.bfloat16, what="bf16 out")
 
@@ -114,7 +126,7 @@ def test_append_then_decode_step(gpu_lib):
     g = _gpu(case.k_new, case.v_new, *pools, case.block_tables, case.positions)
     _write(gpu_lib, g)
     q, lens = _gpu(case.q, case.seq_lens)
-    out = gpu_lib.decode_int8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+    out = gpu_lib.decode_int8(q, g[2], g[3], g[4], g[5], lens, case.scale)
     torch.cuda.synchronize()
     kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
     ref = oracle.decode_int8(case.q.float().numpy(), kc, ks, vc, vs, case.block_tables.numpy(),
@@ -126,13 +138,13 @@ def test_decode_int8_permuted_blocks_bitwise(gpu_lib):
     """Relabelling physical blocks (codes, scales and table entries together) leaves the output
     bit-identical."""
     case = make_case("batch64", num_seqs=8)
-    kc, ks, vc, vs = int8_pools(case, seed=11)
+    kc, vc, sc = int8_pools(case, seed=11)
     q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
-    a = gpu_lib.decode_int8(q, *_gpu(kc, vc, ks, vs), tables, lens, case.scale)
+    a = gpu_lib.decode_int8(q, *_gpu(kc, vc, sc), tables, lens, case.scale)
     n = kc.shape[0]
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(4))
     moved = []
-    for x in (kc, vc, ks, vs):
+    for x in (kc, vc, sc):
         y = torch.empty_like(x)
         y[perm] = x
         moved.append(y)
@@ -152,7 +164,7 @@ def test_int8_unsupported_shapes_are_refused(gpu_lib):
         pools = _gpu(*int8_pools(case, seed=2))
         q, tables, lens = _gpu(case.q, case.block_tables, case.seq_lens)
         with pytest.raises(gpu_lib.PaError) as err:
-            gpu_lib.decode_int8(q, pools[0], pools[2], pools[1], pools[3], tables, lens, case.scale)
+            gpu_lib.decode_int8(q, pools[0], pools[1], pools[2], tables, lens, case.scale)
         assert err.value.status == -2
 
 
@@ -169,14 +181,13 @@ def test_int8_full_size_sampled(gpu_lib, name, partition_tokens):
     _write(gpu_lib, g)
     q, lens = _gpu(case.q, case.seq_lens)
     if partition_tokens:
-        out = gpu_lib.decode_partitioned_int8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale, case.max_seq_len,
+        out = gpu_lib.decode_partitioned_int8(q, g[2], g[3], g[4], g[5], lens, case.scale, case.max_seq_len,
                                               partition_tokens)
     else:
-        out = gpu_lib.decode_int8(q, g[2], g[4], g[3], g[5], g[6], lens, case.scale)
+        out = gpu_lib.decode_int8(q, g[2], g[3], g[4], g[5], lens, case.scale)
     torch.cuda.synchronize()
     kc, ks, vc, vs = _append_ref(case, pools, case.k_new, case.v_new)
-    for got, want in zip(g[2:6], (kc, ks, vc, vs)):
-        assert np.array_equal(_bits(got), want.view(np.int32) if want.dtype == np.float32 else want)
+    _check_append(g, (kc, ks, vc, vs))
     del g, pools
     got = out.cpu().double().numpy()
     qf = case.q.float().numpy()

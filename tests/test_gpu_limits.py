@@ -107,15 +107,15 @@ def test_int8_pool_past_4gib_bitwise(gpu_lib):
     """int8 pools (and their per-(block, kv head) scales) of 300,000 blocks, 4.9 GB each: the top blocks give
     the small pool's bits, single pass and split."""
     case = make_case("batch64", num_seqs=12)
-    kc, ks, vc, vs = (x.to(DEV) for x in int8_pools(case, seed=31))
+    kc, vc, sc = (x.to(DEV) for x in int8_pools(case, seed=31))
     big_n = 300_000
     assert (big_n - 1000) * kc[0].numel() > 2 ** 32  # every used block starts past 4 GiB
-    (bkc, bks, bvc, bvs), btab = _relabel_high(case, big_n, (kc, ks, vc, vs))
+    (bkc, bvc, bsc), btab = _relabel_high(case, big_n, (kc, vc, sc))
     q, tab, lens = (case.q.to(DEV), case.block_tables.to(DEV), case.seq_lens.to(DEV))
     print("[case] int8 pool past 4 GiB", flush=True)
-    a = gpu_lib.decode_int8(q, kc, vc, ks, vs, tab, lens, case.scale)
-    b = gpu_lib.decode_int8(q, bkc, bvc, bks, bvs, btab, lens, case.scale)
-    pa_ = gpu_lib.decode_partitioned_int8(q, kc, vc, ks, vs, tab, lens, case.scale, case.max_seq_len, 64)
-    pb = gpu_lib.decode_partitioned_int8(q, bkc, bvc, bks, bvs, btab, lens, case.scale, case.max_seq_len, 64)
+    a = gpu_lib.decode_int8(q, kc, vc, sc, tab, lens, case.scale)
+    b = gpu_lib.decode_int8(q, bkc, bvc, bsc, btab, lens, case.scale)
+    pa_ = gpu_lib.decode_partitioned_int8(q, kc, vc, sc, tab, lens, case.scale, case.max_seq_len, 64)
+    pb = gpu_lib.decode_partitioned_int8(q, bkc, bvc, bsc, btab, lens, case.scale, case.max_seq_len, 64)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(pa_, pb)

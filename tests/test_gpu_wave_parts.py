@@ -3,7 +3,7 @@
 When B * Hkv * ceil(max_seq_len / partition_tokens) exceeds the waves the GPU holds at once, each wave of
 the matrix-core split kernel walks two consecutive partitions (pa_decode_partitioned_wave_parts = 2). It
 still writes one partial per partition, each with that partition's own reference maximum, so the merged
-result must be the same bits as with one partition per wave. PA_SPLIT_WAVE_PARTS forces either choice, so
+result must be the same bits as with one partition per wave. pa_dims.wave_parts forces either choice, so
 the same call runs both ways. Both runs also meet the float64 oracle; nothing expected comes from the GPU.
 """
 
@@ -27,14 +27,13 @@ def _gpu(case):
                                                     "seq_lens", "positions")}
 
 
-def _both_ways(pa, g, case, pt, monkeypatch, call):
-    """call() with one, then two partitions per wave (forced), at the case's own max_seq_len."""
+def _both_ways(pa, g, case, pt, call):
+    """call(kp) with one, then two partitions per wave (forced through pa_dims.wave_parts), at the case's
+    own max_seq_len."""
     outs = []
     for kp in (1, 2):
-        monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", str(kp))
-        assert pa.wave_parts(g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt) == kp
-        outs.append(call())
-    monkeypatch.delenv("PA_SPLIT_WAVE_PARTS")
+        assert pa.wave_parts(g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt, force=kp) == kp
+        outs.append(call(kp))
     torch.cuda.synchronize()
     return outs
 
@@ -53,7 +52,7 @@ def _lengths(t):
 
 @pytest.mark.parametrize("b", [4, 8, 16, 32])
 @pytest.mark.parametrize("hq,hkv,t", [(32, 8, 1), (8, 2, 4), (12, 4, 3), (4, 1, 1)])
-def test_two_partitions_per_wave_bitwise(gpu_lib, monkeypatch, b, hq, hkv, t):
+def test_two_partitions_per_wave_bitwise(gpu_lib, b, hq, hkv, t):
     """bf16 pools, separate append and fused append + decode: two partitions per wave give the bits of one
     per wave, and meet the oracle."""
     case = build_case(lengths=_lengths(t), num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=b,
@@ -65,18 +64,19 @@ def test_two_partitions_per_wave_bitwise(gpu_lib, monkeypatch, b, hq, hkv, t):
         print(f"[case] wave parts b={b} hq={hq} hkv={hkv} T={t} pt={pt}", flush=True)
         g = _gpu(case)
         gpu_lib.write_kv(g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"], g["positions"])
-        outs = _both_ways(gpu_lib, g, case, pt, monkeypatch, lambda: gpu_lib.decode_partitioned(
-            g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt))
+        outs = _both_ways(gpu_lib, g, case, pt, lambda kp: gpu_lib.decode_partitioned(
+            g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt,
+            wave_parts=kp))
         fs = []
 
-        def fused_call():
+        def fused_call(kp):
             f = _gpu(case)
             fs.append(f)
             return gpu_lib.write_kv_decode(f["q"], f["k_new"], f["v_new"], f["k_pool"], f["v_pool"],
                                            f["block_tables"], f["seq_lens"], case.scale,
-                                           max_seq_len=case.max_seq_len, partition_tokens=pt)
+                                           max_seq_len=case.max_seq_len, partition_tokens=pt, wave_parts=kp)
 
-        fused = _both_ways(gpu_lib, g, case, pt, monkeypatch, fused_call)
+        fused = _both_ways(gpu_lib, g, case, pt, fused_call)
         for f in fs:
             assert np.array_equal(bits(f["k_pool"]), kp) and np.array_equal(bits(f["v_pool"]), vp)
         assert torch.equal(outs[0], outs[1]), f"two partitions per wave changed the result (pt={pt})"
@@ -86,7 +86,7 @@ def test_two_partitions_per_wave_bitwise(gpu_lib, monkeypatch, b, hq, hkv, t):
                                what=f"two per wave, pt={pt}")
 
 
-def test_two_partitions_per_wave_reference_restarts(gpu_lib, monkeypatch):
+def test_two_partitions_per_wave_reference_restarts(gpu_lib):
     """Scores that grow by about 130 base-2 units per 512-position partition make tiles outrun their
     partition's reference max (set by its first tile) several times inside each partition, the second
     partition of a wave included; each restart runs that partition again from its first tile. The bits
@@ -114,8 +114,9 @@ def test_two_partitions_per_wave_reference_restarts(gpu_lib, monkeypatch):
     g = _gpu(case)
     gpu_lib.write_kv(g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"], g["positions"])
     print("[case] wave parts reference restarts", flush=True)
-    outs = _both_ways(gpu_lib, g, case, pt, monkeypatch, lambda: gpu_lib.decode_partitioned(
-        g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt))
+    outs = _both_ways(gpu_lib, g, case, pt, lambda kp: gpu_lib.decode_partitioned(
+        g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt,
+        wave_parts=kp))
     single = gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])

@@ -227,25 +227,26 @@ def int8_pools(case: Case, *, seed: int | None = None, device=None):
     Codes are round(N(0, 40^2)) clipped to [-127, 127]; each (block, kv head) gets a scale drawn from
     U[0.02, 0.04] (about what max|x| / 127 gives for a block of N(0, 1) values). No quantiser runs
     here: codes and scales are drawn directly. Blocks no table references get NaN scales, so a read
-    of one would show in the output. Returns ``(k_codes, k_scales, v_codes, v_scales)`` on ``device``
-    (the case's pool device by default).
+    of one would show in the output. Returns ``(k_codes, v_codes, scales)`` on ``device`` (the case's
+    pool device by default), ``scales [N, Hkv, 2]`` holding the (K, V) scale pair of each (block, kv
+    head).
     """
     device = torch.device(device) if device is not None else case.k_pool.device
     gen = torch.Generator(device=device).manual_seed(int(seed if seed is not None else 7777))
     n, hkv, b, d = case.k_pool.shape
-    out = []
-    for _ in range(2):
-        codes = torch.empty((n, hkv, b, d), dtype=torch.int8, device=device)
-        flat = codes.view(-1)
+    codes, scales = [], torch.empty((n, hkv, 2), dtype=torch.float32, device=device)
+    for side in range(2):
+        c = torch.empty((n, hkv, b, d), dtype=torch.int8, device=device)
+        flat = c.view(-1)
         for start in range(0, flat.numel(), _FILL_CHUNK):
             m = min(_FILL_CHUNK, flat.numel() - start)
             x = torch.randn(m, generator=gen, dtype=torch.float32, device=device) * 40.0
             flat[start:start + m] = x.round().clamp(-127, 127).to(torch.int8)
-        scales = torch.rand((n, hkv), generator=gen, dtype=torch.float32, device=device) * 0.02 + 0.02
-        if case.unused_blocks is not None and case.unused_blocks.numel():
-            scales[case.unused_blocks.to(device)] = float("nan")
-        out += [codes, scales]
-    return tuple(out)
+        scales[:, :, side] = torch.rand((n, hkv), generator=gen, dtype=torch.float32, device=device) * 0.02 + 0.02
+        codes.append(c)
+    if case.unused_blocks is not None and case.unused_blocks.numel():
+        scales[case.unused_blocks.to(device)] = float("nan")
+    return codes[0], codes[1], scales
 
 
 def fp8_pools(case: Case, *, seed: int | None = None, device=None):
@@ -254,25 +255,26 @@ def fp8_pools(case: Case, *, seed: int | None = None, device=None):
     Codes are N(0, 120^2) draws clipped to +-448 and rounded to E4M3 by torch's float8_e4m3fn cast
     (round to nearest even), as the float pools round N(0, 1) draws to bf16; each (block, kv head)
     gets a scale drawn from U[0.004, 0.008] (about what max|x| / 448 gives for a block of N(0, 1)
-    values). Blocks no table references get NaN scales. Returns ``(k_codes, k_scales, v_codes,
-    v_scales)`` with float8_e4m3fn codes, on ``device`` (the case's pool device by default).
+    values). Blocks no table references get NaN scales. Returns ``(k_codes, v_codes, scales)`` with
+    float8_e4m3fn codes and ``scales [N, Hkv, 2]`` (the (K, V) pair of each (block, kv head)), on
+    ``device`` (the case's pool device by default).
     """
     device = torch.device(device) if device is not None else case.k_pool.device
     gen = torch.Generator(device=device).manual_seed(int(seed if seed is not None else 8888))
     n, hkv, b, d = case.k_pool.shape
-    out = []
-    for _ in range(2):
-        codes = torch.empty((n, hkv, b, d), dtype=torch.float8_e4m3fn, device=device)
-        flat = codes.view(-1)
+    codes, scales = [], torch.empty((n, hkv, 2), dtype=torch.float32, device=device)
+    for side in range(2):
+        c = torch.empty((n, hkv, b, d), dtype=torch.float8_e4m3fn, device=device)
+        flat = c.view(-1)
         for start in range(0, flat.numel(), _FILL_CHUNK):
             m = min(_FILL_CHUNK, flat.numel() - start)
             x = torch.randn(m, generator=gen, dtype=torch.float32, device=device) * 120.0
             flat[start:start + m] = x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-        scales = torch.rand((n, hkv), generator=gen, dtype=torch.float32, device=device) * 0.004 + 0.004
-        if case.unused_blocks is not None and case.unused_blocks.numel():
-            scales[case.unused_blocks.to(device)] = float("nan")
-        out += [codes, scales]
-    return tuple(out)
+        scales[:, :, side] = torch.rand((n, hkv), generator=gen, dtype=torch.float32, device=device) * 0.004 + 0.004
+        codes.append(c)
+    if case.unused_blocks is not None and case.unused_blocks.numel():
+        scales[case.unused_blocks.to(device)] = float("nan")
+    return codes[0], codes[1], scales
 
 
 # ----------------------------------------------------------------------------- paged prefill
