@@ -59,7 +59,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, bad dtype code, workspace too small */
   PA_ERR_UNSUPPORTED = -2, /* valid arguments, but no kernel for this (dtype, head_dim, block, rows) */
   PA_ERR_LAUNCH = -3,      /* the HIP runtime reported an error for the launch */
-  PA_ERR_NO_BLOCKS = -4    /* block manager: the pool has too few free blocks (nothing changed) */
+  PA_ERR_NO_BLOCKS = -4,   /* block manager: the pool has too few free blocks (nothing changed) */
+  PA_ERR_TOO_LARGE = -5    /* pa_decode_partitioned_noalloc: partials beyond its fixed device scratch */
 } pa_status;
 
 /* PA_INT8 and PA_FP8_E4M3 are pool dtypes only: 8-bit codes (int8
@@ -197,6 +198,30 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
  * bf16 pools with T * G <= 16, and this query then returns it. Host-only;
  * returns PA_ERR_INVALID_ARG for invalid dims or sizes. */
 int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);
+
+/* pa_decode_partitioned_noalloc: pa_decode_partitioned with no workspace
+ * argument and no allocation of any kind, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The partials go to a fixed device
+ * scratch array of PA_NOALLOC_SCRATCH_BYTES inside the library: each GPU the
+ * call runs on holds one such array from its first use until the process
+ * ends. The call runs on the current device (the one `stream` belongs to);
+ * its first call there looks up that device's array once.
+ *   Result, arguments and supported shapes: those of pa_decode_partitioned
+ *   (same kernels, so the output is the same bits).
+ *   Limit: pa_decode_partitioned_workspace_bytes(dims, max_seq_len,
+ *   partition_tokens) must not exceed PA_NOALLOC_SCRATCH_BYTES, else
+ *   PA_ERR_TOO_LARGE and nothing is launched.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race; order them, for example on one
+ * stream. The array's contents on entry are irrelevant (each call overwrites
+ * what it reads), and nothing in it needs clearing. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_partitioned_noalloc(const pa_dims* dims, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* seq_lens, float scale, void* out,
+                                  int32_t max_seq_len, int32_t partition_tokens,
+                                  pa_stream_t stream);
 
 /* pa_write_kv_decode: one decode step in one launch: pa_write_kv of the T new
  * tokens at each sequence's last T positions (positions[i][t] = seq_lens[i] -

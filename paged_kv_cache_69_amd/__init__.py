@@ -12,6 +12,8 @@ Entry points, with the same names as the C ABI:
 * :func:`decode_partitioned`: split-context decode plus its merge pass
   (``pa_decode_partitioned``).
 * :func:`workspace_bytes`: workspace size for :func:`decode_partitioned`.
+* :func:`decode_partitioned_noalloc`: the same with the library's fixed device scratch instead of a
+  workspace, for callers that cannot allocate (``pa_decode_partitioned_noalloc``).
 * :func:`write_kv_decode`: append + decode in one launch (``pa_write_kv_decode``,
   ``pa_write_kv_decode_partitioned``).
 * :func:`decode_cascade`: decode with a shared prefix attended once (``pa_decode_cascade``).
@@ -32,6 +34,7 @@ import os
 from ._build import LIB_PATH
 
 PA_F32, PA_BF16, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 EXPORTS = (
     "pa_write_kv",
@@ -39,6 +42,7 @@ EXPORTS = (
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
     "pa_decode_partitioned_wave_parts",
+    "pa_decode_partitioned_noalloc",
     "pa_decode_cascade_workspace_bytes",
     "pa_decode_cascade",
     "pa_write_kv_decode_cascade",
@@ -129,6 +133,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_decode_partitioned_noalloc.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P]
+    lib.pa_decode_partitioned_noalloc.restype = ctypes.c_int
     lib.pa_decode_cascade_workspace_bytes.argtypes = [dims_p, _I32, _I32, _I32]
     lib.pa_decode_cascade_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode_cascade.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32, _P,
@@ -310,6 +316,26 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     _check(lib, "pa_decode_partitioned", st)
+    return out
+
+
+def decode_partitioned_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
+                               partition_tokens: int, out, *, variant: int = VARIANT_AUTO, wave_parts: int = 0,
+                               stream=None):
+    """``pa_decode_partitioned_noalloc``: split-context decode + merge with the partials in the library's
+    fixed device scratch (no workspace, no allocation). ``out`` must be given: nothing is allocated here
+    either. Calls that overlap on one GPU race on the scratch."""
+    import torch
+
+    lib = load_library()
+    dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out)
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
+    _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
+    st = lib.pa_decode_partitioned_noalloc(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                           block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                           int(max_seq_len), int(partition_tokens), _stream_handle(stream, dev))
+    _check(lib, "pa_decode_partitioned_noalloc", st)
     return out
 
 

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -296,6 +297,32 @@ static int cascade_entry(const pa_dims* dims, bool append, const void* q, const 
 }
 
 
+// ---- the fixed device scratch of pa_decode_partitioned_noalloc. In host code `scratch` names a host-side
+// stand-in, not device memory: the array's device address on a GPU comes from hipGetSymbolAddress with that
+// device current, once per device, and only that address is handed to kernels.
+constexpr size_t kNoallocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up on the first call on the device.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int pa_abi_version(void) { return kAbiVersion; }
@@ -307,6 +334,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
+    case PA_ERR_TOO_LARGE: return "the partials exceed the fixed device scratch of pa_decode_partitioned_noalloc (32 MiB)";
     default: return "unknown status";
   }
 }
@@ -354,6 +382,22 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
                           size_t workspace_bytes, pa_stream_t stream) {
   return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out,
                       max_seq_len, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_partitioned_noalloc(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                                  int32_t max_seq_len, int32_t partition_tokens, pa_stream_t stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  const size_t need = pa_decode_partitioned_workspace_bytes(dims, max_seq_len, partition_tokens);
+  if (need == 0) return PA_ERR_INVALID_ARG;
+  if (need > kNoallocScratchBytes) return PA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != PA_OK) return st;
+  return decode_entry(dims, false, true, q, k_pool, v_pool, nullptr, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, ws, kNoallocScratchBytes, stream);
 }
 
 int pa_write_kv_decode(const pa_dims* dims, const void* q, const void* k_new, const void* v_new, void* k_pool,
