@@ -22,8 +22,16 @@ duration and to the 8 TB/s HBM peak; its `traffic` is the HBM bytes one call
 moved as rocprofv3's FETCH_SIZE + WRITE_SIZE counters read them (scaled by
 what the same counters read for a copy kernel of known size), taken from the
 summary under profiles/ when that summary was made with the libpa.so now
-built, else null. `cpu_baseline` is the float64 oracle on this host's cores,
-over a bounded sample of the same workload.
+built, else null. `roofline` also relates the call to two figures measured in
+the same run with libpa_probe.so: `stream_gbps`, the best rate a plain
+streaming-read kernel reaches over 2 GiB (`frac_of_stream` = achieved /
+stream_gbps), and `floor_us`, the duration of a launch that makes only the
+dependent loads in front of each decode workgroup's first K/V tile (length and
+table entry together, then the tile) over the same cold replicas;
+`model_us` = floor_us + bytes / stream_gbps. `cpu_baseline` is the float64
+oracle on this host's cores (sequences spread over a thread pool, BLAS on
+one BLAS thread per worker), over a bounded sample of the same workload, with a
+one-thread figure beside it.
 
 Two helper modes turn rocprofv3 output into those profiles/ summaries:
 ``--summarize-pmc FETCH_DIR WRITE_DIR BENCH_LOG`` and ``--summarize-stats DIR``.
@@ -52,6 +60,7 @@ HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
 REPLICAS = 0  # --replicas N: that many input copies instead of enough for a cold cache (a warm-cache run)
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
+STREAM_BYTES = 2 << 30  # the streaming-read probe reads this much per launch (far past every cache)
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Launch configuration per workload: partition_tokens None = single-pass decode; fused = the step is
@@ -349,15 +358,136 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
         torch.cuda.synchronize()
         t0, t1 = e0, time.perf_counter()
     call_ms = ev0.elapsed_time(ev1) / steps
+    floor = time_first_tile(reps, case, steps) if graphs and case.block_size * case.k_pool.shape[3] * \
+        case.k_pool.element_size() <= 16384 else None
     del reps
     torch.cuda.empty_cache()
-    return (t1 - t0) / steps, call_ms, n_rep
+    return (t1 - t0) / steps, call_ms, n_rep, floor
+
+
+def probe_library():
+    """libpa_probe.so (the measurement probes), loaded once with its signatures declared."""
+    import ctypes
+
+    global _PROBE
+    if _PROBE is None:
+        from paged_kv_cache_69_amd._build import PROBE_LIB_PATH
+
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: run __graft_entry__.build() first")
+        lib = ctypes.CDLL(PROBE_LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        lib.pa_probe_stream_read.argtypes = [P, ctypes.c_size_t, I32, I32, P, P]
+        lib.pa_probe_stream_read.restype = ctypes.c_int
+        lib.pa_probe_first_tile.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, P]
+        lib.pa_probe_first_tile.restype = ctypes.c_int
+        _PROBE = lib
+    return _PROBE
+
+
+_PROBE = None
+_STREAM = None
+
+
+def calibrate_stream(runs: int = 5):
+    """The best rate (GB/s) the streaming-read probe reaches over STREAM_BYTES, over launch shapes of 2048
+    to 8192 workgroups and 4 or 8 loads in flight per thread; each shape's figure is the average of
+    ``runs`` launches between HIP events on the stream they run on. Measured once per process."""
+    import ctypes
+
+    import torch
+
+    global _STREAM
+    if _STREAM is not None:
+        return _STREAM
+    lib = probe_library()
+    buf = torch.empty(STREAM_BYTES // 4, dtype=torch.int32, device="cuda:0").random_(generator=torch.Generator(
+        device="cuda:0").manual_seed(5))
+    best = (0.0, None)
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    for wg in (2048, 4096, 8192):
+        out = torch.empty(wg, dtype=torch.int32, device="cuda:0")
+        for unroll in (4, 8):
+            if lib.pa_probe_stream_read(buf.data_ptr(), STREAM_BYTES, wg, unroll, out.data_ptr(), h):
+                raise RuntimeError("pa_probe_stream_read failed")
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(runs):
+                lib.pa_probe_stream_read(buf.data_ptr(), STREAM_BYTES, wg, unroll, out.data_ptr(), h)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            gbps = STREAM_BYTES / (ev0.elapsed_time(ev1) / runs * 1e-3) / 1e9
+            if gbps > best[0]:
+                best = (gbps, {"workgroups": wg, "loads_in_flight_per_thread": unroll})
+    del buf
+    torch.cuda.empty_cache()
+    _STREAM = {"stream_gbps": round(best[0], 1), "stream_launch": best[1], "stream_bytes": STREAM_BYTES}
+    return _STREAM
+
+
+def time_first_tile(reps, case, steps):
+    """Average duration (us) of the first-tile probe over the decode call's own replicas, launched and
+    timed like the decode calls (one graph of ``steps`` launches, replicas rotating, HIP events around
+    it): the loads a decode workgroup waits for before its first tile, with nothing else. Both forms:
+    length and table entry issued together (as the kernels do), and length -> table -> tile."""
+    import ctypes
+
+    import torch
+
+    lib = probe_library()
+    b, hkv = case.q.shape[0], case.k_pool.shape[1]
+    n, _, bs, d = case.k_pool.shape
+    row_bytes = d * case.k_pool.element_size()
+    out = torch.empty(b * hkv, dtype=torch.int32, device="cuda:0")
+    res = {}
+    for dependent in (0, 1):
+        def launch(r, h):
+            t = r.t
+            st = lib.pa_probe_first_tile(t["k_pool"].data_ptr(), t["v_pool"].data_ptr(), t["block_tables"].data_ptr(),
+                                         t["seq_lens"].data_ptr(), b, hkv, case.block_tables.shape[1], n, bs,
+                                         row_bytes, dependent, out.data_ptr(), h)
+            if st:
+                raise RuntimeError(f"pa_probe_first_tile: {st}")
+        stream = torch.cuda.current_stream()
+        for s in range(len(reps)):
+            launch(reps[s], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for s in range(steps):
+                    launch(reps[s % len(reps)], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        stream.wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        res["floor_dependent_us" if dependent else "floor_us"] = round(ev0.elapsed_time(ev1) / steps * 1e3, 3)
+        del g
+    return res
+
+
+def host_cores() -> int:
+    """Cores this process may use: the affinity mask, capped by OMP_NUM_THREADS when the host sets it."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() and int(env) > 0 else max(1, n)
 
 
 def cpu_baseline(case, budget_s: float):
-    """The float64 oracle (KV write + decode) on this host, one thread, on a bounded sample of the
-    workload: the first n sequences, n grown until one pass takes about ``budget_s`` or covers the
-    whole batch; a pass shorter than the budget is repeated until the budget is spent."""
+    """The float64 oracle (KV write + decode) on this host, over a bounded sample of the workload: the
+    first n sequences, n grown until one pass takes about ``budget_s`` or covers the whole batch, and a
+    pass shorter than the budget repeated until the budget is spent. Measured twice: on every core (the
+    KV write, then one oracle decode per sequence spread over a thread pool of that many workers, one
+    BLAS thread each; numpy drops the GIL in its gathers and products), and on one thread."""
+    import concurrent.futures as cf
+
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -371,35 +501,60 @@ def cpu_baseline(case, budget_s: float):
 
     b = case.q.shape[0]
     kp_all, vp_all = npbits(case.k_pool), npbits(case.v_pool)
+    q_all = case.q.float().numpy()
+    tables_all, lens_all = case.block_tables.numpy(), case.seq_lens.numpy()
 
-    def one_pass(n):
+    def one_pass(n, pool):
         sl = slice(0, n)
         kp, vp = oracle.write_kv(kp_all, vp_all, npbits(case.k_new[sl]), npbits(case.v_new[sl]),
-                                 case.block_tables[sl].numpy(), case.positions[sl].numpy(), case.block_size)
+                                 tables_all[sl], case.positions[sl].numpy(), case.block_size)
         as_f = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).float().numpy()) \
             if kp.dtype == np.uint16 else (lambda a: a.view(np.float32))
-        oracle.decode(case.q[sl].float().numpy(), as_f(kp), as_f(vp), case.block_tables[sl].numpy(),
-                      case.seq_lens[sl].numpy(), case.scale, case.block_size)
+        kf, vf = as_f(kp), as_f(vp)
 
-    with threadpool_limits(limits=1):
-        n = 1
-        while True:
-            t0 = time.perf_counter()
-            one_pass(n)
-            dt = time.perf_counter() - t0
-            if dt >= budget_s or n >= b:
-                break
-            n = min(b, max(n + 1, int(n * min(8.0, 1.2 * budget_s / max(dt, 1e-3)))))
-        passes, total = 1, dt
-        while total < budget_s:
-            t0 = time.perf_counter()
-            one_pass(n)
-            total += time.perf_counter() - t0
-            passes += 1
-    tokens = n * case.q.shape[1] * passes
-    return {"value": round(tokens / total, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"KV write + float64 decode of the first {n} of {b} sequences "
-                      f"({int(case.seq_lens[:n].sum())} positions) x {passes} pass(es), one thread, {total:.1f} s"}
+        def seq(i):
+            return oracle.decode(q_all[i:i + 1], kf, vf, tables_all[i:i + 1], lens_all[i:i + 1], case.scale,
+                                 case.block_size)
+
+        if pool is None:
+            for i in range(n):
+                seq(i)
+        else:
+            list(pool.map(seq, range(n)))
+
+    def timed(cores):
+        pool = cf.ThreadPoolExecutor(max_workers=cores) if cores > 1 else None
+        try:
+            # one BLAS thread per worker: the workers already use every core (BLAS threads on top of
+            # them oversubscribe the host; the products are small)
+            with threadpool_limits(limits=1):
+                n = 1
+                while True:
+                    t0 = time.perf_counter()
+                    one_pass(n, pool)
+                    dt = time.perf_counter() - t0
+                    if dt >= budget_s or n >= b:
+                        break
+                    n = min(b, max(n + 1, int(n * min(8.0, 1.2 * budget_s / max(dt, 1e-3)))))
+                passes, total = 1, dt
+                while total < budget_s:
+                    t0 = time.perf_counter()
+                    one_pass(n, pool)
+                    total += time.perf_counter() - t0
+                    passes += 1
+        finally:
+            if pool is not None:
+                pool.shutdown()
+        tokens = n * case.q.shape[1] * passes
+        return round(tokens / total, 2), (f"KV write + float64 decode of the first {n} of {b} sequences "
+                                          f"({int(case.seq_lens[:n].sum())} positions) x {passes} pass(es), "
+                                          f"{cores} thread(s), {total:.1f} s")
+
+    cores = host_cores()
+    multi, multi_sample = timed(cores)
+    single, single_sample = timed(1)
+    return {"value": multi, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": multi_sample,
+            "single_thread": {"value": single, "cores": 1, "sample": single_sample}}
 
 
 def calibrate_copy(n_runs: int = 3):
@@ -631,6 +786,19 @@ def run_copy_workload(pa, name, steps, warmup, graphs=True):
     return res
 
 
+def stream_terms(achieved_gbps, bytes_per_launch, launch_us, floor):
+    """The call against the two measured bounds: the streaming-read rate and the first-tile floor."""
+    out = {}
+    if _STREAM is not None:
+        out.update(stream_gbps=_STREAM["stream_gbps"], frac_of_stream=round(achieved_gbps / _STREAM["stream_gbps"], 4))
+    if floor:
+        out.update(floor)
+        if _STREAM is not None:
+            model = floor["floor_us"] + bytes_per_launch / (_STREAM["stream_gbps"] * 1e3)
+            out.update(model_us=round(model, 3), over_model=round(launch_us / model, 4))
+    return out
+
+
 def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graphs=True, fused=True):
     import torch
 
@@ -652,8 +820,8 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
                and rows <= 32)
     fused = fused and spec.get("fused", False) and variant != 1 and mfma_ok
     cascade = spec.get("cascade", 0) if variant != 1 else 0
-    sec_per_step, dur_ms, n_rep = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant, graphs,
-                                              fused, cascade)
+    sec_per_step, dur_ms, n_rep, floor = measure_gpu(pa, case, spec["partition_tokens"], steps, warmup, variant,
+                                                     graphs, fused, cascade)
     # a cascade reads each shared block once: count every physical block once
     algo = unique_bytes(case) if cascade else algorithmic_bytes(case)
     if fused:  # the call also reads the new rows and stores them into the pools
@@ -679,7 +847,7 @@ def run_workload(pa, name, steps, warmup, with_cpu, cpu_budget, variant=0, graph
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": kernel, "bytes_per_launch": algo, "avg_launch_us": round(dur_ms * 1e3, 3),
-                     "launches_timed": steps},
+                     "launches_timed": steps, **stream_terms(achieved, algo, dur_ms * 1e3, floor)},
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": b, "q_tokens": t,
                    "kv_positions": case.kv_tokens(), "max_seq_len": case.max_seq_len,
                    "partition_tokens": spec["partition_tokens"], "replicas": n_rep,
@@ -838,13 +1006,17 @@ def main(argv=None):
     ap.add_argument("--secondary", default="long,prefix,spec,batch64_int8,long_int8,batch64_fp8,long_fp8,prefill,"
                                            "cow_copy",
                     help="comma-separated workloads also measured and reported under 'secondary' ('' for none)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for each cpu_baseline leg (every core, then one thread)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 vector-ALU kernel, 2 MFMA kernel")
     ap.add_argument("--no-fused", action="store_true",
                     help="time the step as separate pa_write_kv and decode calls on every workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for counter calibration)")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read calibration")
+    ap.add_argument("--cpu-secondary", default="long",
+                    help="comma-separated secondary workloads that also get a cpu_baseline ('' for none)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eagerly launched steps only (for counter-collection runs; not a headline number)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"))
@@ -880,6 +1052,8 @@ def main(argv=None):
     pa.load_library()
     if args.calibrate_copy:
         calibrate_copy()
+    if not args.no_stream:
+        calibrate_stream()
     main_res = run_workload(pa, args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_budget,
                             args.variant, not args.no_graph, not args.no_fused)
     line = {
@@ -902,13 +1076,17 @@ def main(argv=None):
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
+    if _STREAM is not None:
+        line["stream_calibration"] = _STREAM
     secondary = {}
+    cpu_secondary = {c for c in args.cpu_secondary.split(",") if c} if not args.no_cpu else set()
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = run_workload(pa, name, args.steps, args.warmup, False, 0, args.variant, not args.no_graph,
-                         not args.no_fused)
+        r = run_workload(pa, name, args.steps, args.warmup, name in cpu_secondary, args.cpu_budget, args.variant,
+                         not args.no_graph, not args.no_fused)
         secondary[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 6),
                            "achieved_gbps": round(r["achieved_gbps"], 1), "roofline": r["roofline"],
-                           "config": r["config"], **{k: r[k] for k in ("unique_bytes", "logical_bytes", "achieved_gbps_logical") if k in r}}
+                           "config": r["config"], **{k: r[k] for k in ("unique_bytes", "logical_bytes",
+                                                                     "achieved_gbps_logical", "cpu_baseline") if k in r}}
     if secondary:
         line["secondary"] = secondary
     print(json.dumps(line), flush=True)

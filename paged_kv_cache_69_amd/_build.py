@@ -10,6 +10,7 @@ import subprocess
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libpa_probe.so")  # the benchmark's measurement probes
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 HIP_FLAGS = [
@@ -36,8 +37,8 @@ def hipcc() -> str:
     return exe
 
 
-def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(PKG_DIR, "csrc", "*.hip")))
+def sources(folder: str = "csrc") -> list[str]:
+    return sorted(glob.glob(os.path.join(PKG_DIR, folder, "*.hip")))
 
 
 _NOISE = "packed-fp32-ops' is not a recognized feature"
@@ -51,29 +52,36 @@ def _run(cmd: list[str]) -> str:
     return log
 
 
+def _build_lib(folder: str, lib_path: str, logs: list, ex) -> None:
+    inc = ["-I", os.path.join(ROOT, "include")]
+    jobs = []
+    for src in sources(folder):
+        obj = os.path.join(OBJ_DIR, folder + "_" + os.path.basename(src) + ".o")
+        flags = FILE_FLAGS.get(os.path.basename(src), [])
+        jobs.append((obj, [hipcc(), *HIP_FLAGS, *flags, *inc, "-c", src, "-o", obj]))
+    logs += list(ex.map(lambda j: _run(j[1]), jobs))
+    tmp = lib_path + ".tmp"
+    logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]))
+    os.replace(tmp, lib_path)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source to an object (in parallel), link them into
-    ``paged_kv_cache_69_amd/libpa.so``; return its path."""
+    """Compile every HIP source to an object (in parallel) and link them: csrc/ into
+    ``paged_kv_cache_69_amd/libpa.so`` (the decode library) and probe/ into ``libpa_probe.so`` (the
+    benchmark's measurement probes); return the decode library's path."""
     from concurrent.futures import ThreadPoolExecutor
 
-    inc = ["-I", os.path.join(ROOT, "include")]
     # a fixed object directory: the paths hipcc records stay the same from build to build, so the
     # library is byte-reproducible (its hash identifies the code a profile was taken from)
     os.makedirs(OBJ_DIR, exist_ok=True)
-    jobs = []
-    for src in sources():
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-        flags = FILE_FLAGS.get(os.path.basename(src), [])
-        jobs.append((obj, [hipcc(), *HIP_FLAGS, *flags, *inc, "-c", src, "-o", obj]))
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        logs = list(ex.map(lambda j: _run(j[1]), jobs))
-    tmp = LIB_PATH + ".tmp"
-    logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]))
+    logs: list = []
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        _build_lib("csrc", LIB_PATH, logs, ex)
+        _build_lib("probe", PROBE_LIB_PATH, logs, ex)
     if verbose:
         for log in logs:
             if log.strip():
                 print(log)
-    os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 

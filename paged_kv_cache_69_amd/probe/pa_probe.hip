@@ -1,0 +1,111 @@
+// Measurement probes of libpa_probe.so (declared in include/pa_probe.h): a streaming-read kernel, the
+// ceiling HBM reads reach on this GPU, and the dependent loads in front of a decode workgroup's first
+// tile, the latency floor of a decode launch. Neither is part of the decode path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// XOR of a workgroup's per-thread values, written by thread 0 (256 threads, 4 waves).
+__device__ __forceinline__ void store_xor(uint32_t x, uint32_t* dst) {
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) *dst = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+// Consecutive threads read consecutive 16-byte chunks; each thread takes U chunks one grid-stride apart
+// per step, all in flight before any is used.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16, uint32_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  store_xor(fold(acc), out + blockIdx.x);
+}
+
+struct ChainParams {
+  const char* k_pool;
+  const char* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t hkv, mb, nblocks, bs, row_bytes, dependent;
+  uint32_t* out;
+};
+
+__global__ __launch_bounds__(256) void first_tile_kernel(const ChainParams p) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvh = blockIdx.x % p.hkv, seq = blockIdx.x / p.hkv;
+  const int32_t* row = p.tables + (int64_t)seq * p.mb;
+  const int L = p.lens[seq];
+  int j;
+  if (p.dependent) {
+    j = min(min(w, max(0, (L + p.bs - 1) / p.bs - 1)), p.mb - 1);  // the index needs the length first
+  } else {
+    j = min(w, p.mb - 1);  // clamped to the row: issued with the length
+  }
+  const int blk = (int)min((uint32_t)row[j], (uint32_t)(p.nblocks - 1));
+  const int tile = p.bs * p.row_bytes;
+  const int64_t off = ((int64_t)blk * p.hkv + kvh) * tile;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int b = lane * 16; b < tile; b += 64 * 16) {
+    acc ^= *reinterpret_cast<const u32x4*>(p.k_pool + off + b);
+    acc ^= *reinterpret_cast<const u32x4*>(p.v_pool + off + b);
+  }
+  store_xor(fold(acc) ^ (uint32_t)L, p.out + blockIdx.x);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, uint32_t* out,
+                         pa_probe_stream_t stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0) return -1;
+  if (workgroups < 1) return -1;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n16 = (int64_t)(bytes / 16);
+  (void)hipGetLastError();
+  switch (unroll) {
+    case 1: stream_read_kernel<1><<<dim3(workgroups), dim3(256), 0, s>>>((const u32x4*)src, n16, out); break;
+    case 2: stream_read_kernel<2><<<dim3(workgroups), dim3(256), 0, s>>>((const u32x4*)src, n16, out); break;
+    case 4: stream_read_kernel<4><<<dim3(workgroups), dim3(256), 0, s>>>((const u32x4*)src, n16, out); break;
+    case 8: stream_read_kernel<8><<<dim3(workgroups), dim3(256), 0, s>>>((const u32x4*)src, n16, out); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int pa_probe_first_tile(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks, int32_t num_blocks,
+                        int32_t block_size, int32_t row_bytes, int32_t dependent, uint32_t* out,
+                        pa_probe_stream_t stream) {
+  if (!k_pool || !v_pool || !block_tables || !seq_lens || !out) return -1;
+  if (num_seqs < 1 || num_kv_heads < 1 || max_blocks < 1 || num_blocks < 1 || block_size < 1 || row_bytes < 16 ||
+      row_bytes % 16 != 0 || (int64_t)block_size * row_bytes > 16384)
+    return -1;
+  ChainParams p = {static_cast<const char*>(k_pool), static_cast<const char*>(v_pool), block_tables, seq_lens,
+                   num_kv_heads, max_blocks, num_blocks, block_size, row_bytes, dependent ? 1 : 0, out};
+  (void)hipGetLastError();
+  first_tile_kernel<<<dim3((unsigned)((int64_t)num_seqs * num_kv_heads)), dim3(256), 0,
+                      reinterpret_cast<hipStream_t>(stream)>>>(p);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // extern "C"
