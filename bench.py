@@ -59,6 +59,7 @@ METRIC = "paged decode attention: tokens/s and achieved HBM GB/s (% of peak), 1 
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
 REPLICAS = 0  # --replicas N: that many input copies instead of enough for a cold cache (a warm-cache run)
+SPLIT_SCHEDULE = 0  # --split-schedule N: pa_dims.split_schedule of split calls (0: the library's choice)
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
 STREAM_BYTES = 2 << 30  # the streaming-read probe reads this much per launch (far past every cache)
 PROFILES = os.path.join(ROOT, "profiles")
@@ -190,7 +191,7 @@ class Replica:
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device=src["q"].device)
         self.lib = pa.load_library()
         self.dims = pa.make_dims(self.t["q"], self.t["k_pool"], self.t["block_tables"], out_dtype=torch.float32,
-                                 variant=variant)
+                                 variant=variant, split_schedule=SPLIT_SCHEDULE)
         kd = case.k_pool.shape
         self.int8 = "scales" in src
         code = pa.dtype_code(case.k_new.dtype)
@@ -206,8 +207,9 @@ class Replica:
                 n = pa.cascade_workspace_bytes(self.t["q"], self.t["k_pool"], self.t["block_tables"], cascade,
                                                self.max_len, partition_tokens)
             else:
-                n = pa.workspace_bytes(self.t["q"], self.t["k_pool"], self.t["block_tables"], self.max_len,
-                                       partition_tokens)
+                n = pa.workspace_bytes(self.t["q"], self.t["k_pool"].view(torch.int8) if self.int8 else
+                                       self.t["k_pool"], self.t["block_tables"], self.max_len, partition_tokens,
+                                       split_schedule=SPLIT_SCHEDULE)
             self.ws = torch.empty(n, dtype=torch.uint8, device=src["q"].device)
         p = {k: v.data_ptr() for k, v in self.t.items()}
         scales = (p["scales"],) if self.int8 else ()
@@ -1024,6 +1026,9 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=0,
                     help="input copies to rotate over (default: enough to miss every cache; 1: warm)")
     ap.add_argument("--summarize-stats", nargs="+", metavar="DIR COMMAND [BENCH_LOG]")
+    ap.add_argument("--split-schedule", type=int, default=0,
+                    help="pa_dims.split_schedule of the split calls: 0 the library's choice, 1 one partition per "
+                         "wave, 2 two per wave, 3 balanced ranges")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.workload), end="")
@@ -1039,8 +1044,9 @@ def main(argv=None):
               "GPU and needs no collectives: its (sequence, kv head) units split across GPUs with no exchange.",
               file=sys.stderr)
         return 2
-    global REPLICAS
+    global REPLICAS, SPLIT_SCHEDULE
     REPLICAS = max(0, args.replicas)
+    SPLIT_SCHEDULE = args.split_schedule
 
     import torch
 

@@ -77,6 +77,26 @@ typedef enum {
   PA_VARIANT_MFMA = 2  /* matrix-core kernel: bf16, 16 or 32 query rows per kv head */
 } pa_variant;
 
+/* Split-context schedules (pa_dims.split_schedule). Every schedule gives the same partials, each with
+ * its own reference maximum, so the merged output agrees to rounding; ONE_PER_WAVE and TWO_PER_WAVE
+ * give the same bits.
+ *   PA_SPLIT_ONE_PER_WAVE: one wave per partition.
+ *   PA_SPLIT_TWO_PER_WAVE: a wave walks two consecutive partitions of one sequence (bf16 pools,
+ *     T * G <= 16; elsewhere one per wave).
+ *   PA_SPLIT_BALANCED: for each kv head the tiles of all sequences form one list, cut into equal
+ *     ranges, one per wave, with one wave per SIMD of the GPU; a partition that a range boundary
+ *     cuts leaves two partials, which the merge adds like any others. Every wave then streams the
+ *     same number of tiles whatever the spread of lengths; it is opt-in (the automatic choice never
+ *     takes it: it measured slower on the long-context workloads). Needs bf16 or 8-bit pools,
+ *     D = 128, b in {16, 32}, T * G <= 16, B <= 1024 and B * T * G * 256 <= 48 KiB
+ *     (PA_ERR_UNSUPPORTED otherwise); the workspace then holds two slots per partition. */
+typedef enum {
+  PA_SPLIT_AUTO = 0,
+  PA_SPLIT_ONE_PER_WAVE = 1,
+  PA_SPLIT_TWO_PER_WAVE = 2,
+  PA_SPLIT_BALANCED = 3
+} pa_split_schedule;
+
 /* Problem dimensions.
  * B = num_seqs; T = q_tokens, the new tokens per sequence, which are causal
  * among themselves; Hq = num_q_heads; Hkv = num_kv_heads; G = Hq / Hkv is the
@@ -96,11 +116,10 @@ typedef struct {
   int32_t kv_dtype;  /* pa_dtype of the pools; must equal q_dtype */
   int32_t out_dtype; /* pa_dtype of out */
   int32_t variant;   /* pa_variant */
-  int32_t wave_parts; /* split calls on the matrix-core kernel: consecutive partitions per wave.
-                         0 lets the library choose (pa_decode_partitioned_wave_parts); 1 or 2 forces
-                         that count where two are possible (bf16 pools, T * G <= 16) and is ignored
-                         elsewhere. Any other value: PA_ERR_INVALID_ARG. The results are the same
-                         bits for every value. */
+  int32_t split_schedule; /* pa_split_schedule: how split calls on the matrix-core kernels share
+                             out the partitions. PA_SPLIT_AUTO (0) lets the library choose
+                             (pa_decode_partitioned_schedule); the others force a schedule and are
+                             ignored by the vector-ALU kernel. Any other value: PA_ERR_INVALID_ARG. */
 } pa_dims;
 
 /* pa_write_kv: the KV-append scatter.
@@ -151,8 +170,9 @@ int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void
               pa_stream_t stream);
 
 /* Bytes of device workspace pa_decode_partitioned needs for these dims:
- * B * T * Hq * P * (D + 2) * 4 plus alignment, with
- * P = ceil(max_seq_len / partition_tokens). Returns 0 for invalid
+ * B * T * Hq * S * (D + 2) * 4 plus alignment, with S = 2P slots per row when
+ * dims->split_schedule asks for balanced ranges the dims allow (else S = P),
+ * and P = ceil(max_seq_len / partition_tokens). Returns 0 for invalid
  * arguments. */
 size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
                                              int32_t partition_tokens);
@@ -178,26 +198,23 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
  * Other arguments and the supported shapes are as for pa_decode. Two calls
  * that share one workspace must be ordered by the caller, for example by
  * using the same stream: calls that overlap on one workspace race. On the
- * matrix-core kernel one wave may walk several consecutive partitions (see
- * pa_decode_partitioned_wave_parts); it still writes one partial per
- * partition, each with its own reference maximum, so the result is the same
- * bits either way. */
+ * matrix-core kernels the partitions are shared out to waves by a schedule
+ * (pa_dims.split_schedule, pa_decode_partitioned_schedule). */
 int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables,
                           const int32_t* seq_lens, float scale, void* out, int32_t max_seq_len,
                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
 
-/* pa_decode_partitioned_wave_parts: the number of consecutive partitions (1
- * or 2) that one wave of the matrix-core kernel walks in a split call with
- * these arguments (pa_decode_partitioned, pa_write_kv_decode_partitioned).
- * It is 2 for bf16 pools when T * G <= 16 and B * Hkv * ceil(max_seq_len /
- * partition_tokens) exceeds the 2048 split waves the GPU holds at once, so
- * that long-context batches run in one round of waves; 8-bit pools keep one
- * partition per wave. dims->wave_parts = 1 or 2 overrides that choice for
- * bf16 pools with T * G <= 16, and this query then returns it. Host-only;
- * returns PA_ERR_INVALID_ARG for invalid dims or sizes. */
-int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);
+/* pa_decode_partitioned_schedule: the pa_split_schedule (1, 2 or 3) a split
+ * call with these arguments runs on the matrix-core kernels. With
+ * PA_SPLIT_AUTO it is TWO_PER_WAVE for bf16 pools with T * G <= 16 when one
+ * partition per wave would need more than the 2048 waves the GPU holds at
+ * once (B * Hkv * ceil(max_seq_len / partition_tokens) > 2048), else
+ * ONE_PER_WAVE. A forced schedule is returned as the call would run it
+ * (PA_ERR_UNSUPPORTED for a balanced schedule the dims do not allow).
+ * Host-only; PA_ERR_INVALID_ARG for invalid dims or sizes. */
+int pa_decode_partitioned_schedule(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);
 
 /* pa_decode_partitioned_noalloc: pa_decode_partitioned with no workspace
  * argument and no allocation of any kind, for callers that cannot allocate

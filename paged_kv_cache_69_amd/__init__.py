@@ -36,12 +36,13 @@ from ._build import LIB_PATH
 PA_F32, PA_BF16, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+SPLIT_AUTO, SPLIT_ONE_PER_WAVE, SPLIT_TWO_PER_WAVE, SPLIT_BALANCED = 0, 1, 2, 3  # pa_split_schedule
 EXPORTS = (
     "pa_write_kv",
     "pa_decode",
     "pa_decode_partitioned_workspace_bytes",
     "pa_decode_partitioned",
-    "pa_decode_partitioned_wave_parts",
+    "pa_decode_partitioned_schedule",
     "pa_decode_partitioned_noalloc",
     "pa_decode_cascade_workspace_bytes",
     "pa_decode_cascade",
@@ -84,7 +85,7 @@ EXPORTS = (
 ABI_VERSION = 2
 
 _DIM_FIELDS = ("num_seqs", "q_tokens", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
-               "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "variant", "wave_parts")
+               "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "variant", "split_schedule")
 
 
 class PaDims(ctypes.Structure):
@@ -128,8 +129,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode_partitioned_workspace_bytes.argtypes = [dims_p, _I32, _I32]
     lib.pa_decode_partitioned_workspace_bytes.restype = ctypes.c_size_t
-    lib.pa_decode_partitioned_wave_parts.argtypes = [dims_p, _I32, _I32]
-    lib.pa_decode_partitioned_wave_parts.restype = ctypes.c_int
+    lib.pa_decode_partitioned_schedule.argtypes = [dims_p, _I32, _I32]
+    lib.pa_decode_partitioned_schedule.restype = ctypes.c_int
     lib.pa_decode_partitioned.argtypes = [dims_p, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _P,
                                           ctypes.c_size_t, _P]
     lib.pa_decode_partitioned.restype = ctypes.c_int
@@ -219,7 +220,8 @@ def _check_tensors(**tensors):
     return dev
 
 
-def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT_AUTO, wave_parts: int = 0) -> PaDims:
+def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT_AUTO,
+              split_schedule: int = SPLIT_AUTO) -> PaDims:
     """Dims for q ``[B, T, Hq, D]``, pools ``[N, Hkv, b, D]`` and tables ``[B, MB]``."""
     _require(q.dim() == 4 and k_pool.dim() == 4 and block_tables.dim() == 2, "bad tensor ranks")
     b, t, hq, d = q.shape
@@ -227,7 +229,7 @@ def make_dims(q, k_pool, block_tables, *, out_dtype=None, variant: int = VARIANT
     _require(d == d2, "head_dim of q and pools differ")
     _require(block_tables.shape[0] == b, "block_tables rows != num_seqs")
     return PaDims(b, t, hq, hkv, d, bs, n, block_tables.shape[1], dtype_code(q.dtype), dtype_code(k_pool.dtype),
-                  dtype_code(out_dtype if out_dtype is not None else q.dtype), int(variant), int(wave_parts))
+                  dtype_code(out_dtype if out_dtype is not None else q.dtype), int(variant), int(split_schedule))
 
 
 def write_kv(k_new, v_new, k_pool, v_pool, block_tables, positions, *, stream=None):
@@ -271,46 +273,50 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, *,
 
 
 def workspace_bytes(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int,
-                    *, variant: int = VARIANT_AUTO) -> int:
-    """``pa_decode_partitioned_workspace_bytes`` for these tensors."""
+                    *, variant: int = VARIANT_AUTO, split_schedule: int = SPLIT_AUTO) -> int:
+    """``pa_decode_partitioned_workspace_bytes`` for these tensors (twice the slots when
+    ``split_schedule`` asks for balanced ranges)."""
     lib = load_library()
-    dims = make_dims(q, k_pool, block_tables, variant=variant)
+    dims = make_dims(q, k_pool, block_tables, variant=variant, split_schedule=split_schedule)
     n = lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
     if n == 0:
         raise PaError("pa_decode_partitioned_workspace_bytes", -1, "invalid argument")
     return int(n)
 
 
-def wave_parts(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int, *, force: int = 0) -> int:
-    """``pa_decode_partitioned_wave_parts``: consecutive partitions per wave of the matrix-core split kernel
-    (``force`` = 1 or 2 is ``pa_dims.wave_parts``)."""
+def split_schedule(q, k_pool, block_tables, max_seq_len: int, partition_tokens: int, *,
+                   force: int = SPLIT_AUTO) -> int:
+    """``pa_decode_partitioned_schedule``: the split schedule (1 one partition per wave, 2 two, 3 balanced
+    ranges) a split call with these tensors runs on the matrix-core kernels (``force`` is
+    ``pa_dims.split_schedule``)."""
     lib = load_library()
-    dims = make_dims(q, k_pool, block_tables, wave_parts=force)
-    n = lib.pa_decode_partitioned_wave_parts(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
+    dims = make_dims(q, k_pool, block_tables, split_schedule=force)
+    n = lib.pa_decode_partitioned_schedule(ctypes.byref(dims), int(max_seq_len), int(partition_tokens))
     if n < 0:
-        raise PaError("pa_decode_partitioned_wave_parts", n, "invalid argument")
+        raise PaError("pa_decode_partitioned_schedule", n, "invalid argument" if n == -1 else "unsupported")
     return int(n)
 
 
 def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
                        partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
-                       variant: int = VARIANT_AUTO, wave_parts: int = 0, stream=None):
+                       variant: int = VARIANT_AUTO, split_schedule: int = SPLIT_AUTO, stream=None):
     """``pa_decode_partitioned``: split-context decode + merge. ``workspace`` is a uint8 device tensor
-    of at least :func:`workspace_bytes` bytes (allocated here if omitted); ``wave_parts`` is
-    ``pa_dims.wave_parts`` (0: the library's choice)."""
+    of at least :func:`workspace_bytes` bytes (allocated here if omitted); ``split_schedule`` is
+    ``pa_dims.split_schedule`` (0: the library's choice)."""
     import torch
 
     lib = load_library()
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant)
+    need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant,
+                           split_schedule=split_schedule)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out,
                          workspace=workspace)
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, split_schedule=split_schedule)
     st = lib.pa_decode_partitioned(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                    block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                    int(max_seq_len), int(partition_tokens), workspace.data_ptr(),
@@ -320,8 +326,8 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale: float, 
 
 
 def decode_partitioned_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
-                               partition_tokens: int, out, *, variant: int = VARIANT_AUTO, wave_parts: int = 0,
-                               stream=None):
+                               partition_tokens: int, out, *, variant: int = VARIANT_AUTO,
+                               split_schedule: int = SPLIT_AUTO, stream=None):
     """``pa_decode_partitioned_noalloc``: split-context decode + merge with the partials in the library's
     fixed device scratch (no workspace, no allocation). ``out`` must be given: nothing is allocated here
     either. Calls that overlap on one GPU race on the scratch."""
@@ -331,7 +337,7 @@ def decode_partitioned_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale:
     dev = _check_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, out=out)
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, split_schedule=split_schedule)
     st = lib.pa_decode_partitioned_noalloc(ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                            block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                            int(max_seq_len), int(partition_tokens), _stream_handle(stream, dev))
@@ -408,7 +414,7 @@ def write_kv_decode_cascade(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
 
 def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, *,
                     max_seq_len: int | None = None, partition_tokens: int | None = None, workspace=None,
-                    out_dtype=None, variant: int = VARIANT_AUTO, wave_parts: int = 0, stream=None):
+                    out_dtype=None, variant: int = VARIANT_AUTO, split_schedule: int = SPLIT_AUTO, stream=None):
     """``pa_write_kv_decode`` (or ``pa_write_kv_decode_partitioned`` when ``partition_tokens`` is
     given): append ``k_new``/``v_new [B, T, Hkv, D]`` at each sequence's last T positions and decode,
     in one launch. Returns ``out``."""
@@ -421,7 +427,8 @@ def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, sca
                    seq_lens=seq_lens, out=out)
     split = partition_tokens is not None
     if split:
-        need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant)
+        need = workspace_bytes(q, k_pool, block_tables, max_seq_len, partition_tokens, variant=variant,
+                               split_schedule=split_schedule)
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         tensors["workspace"] = workspace
@@ -429,7 +436,7 @@ def write_kv_decode(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, sca
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape and k_new.shape == v_new.shape, "shape mismatch")
     _require(k_new.dtype == q.dtype and k_pool.dtype == q.dtype, "q, new rows and pools must share a dtype")
-    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, wave_parts=wave_parts)
+    dims = make_dims(q, k_pool, block_tables, out_dtype=out.dtype, variant=variant, split_schedule=split_schedule)
     args = [ctypes.byref(dims), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
             v_pool.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
     if split:
@@ -486,7 +493,8 @@ def _write_kv_q8(fmt, k_new, v_new, k_pool, v_pool, scales, block_tables, positi
     _check(lib, func, st)
 
 
-def _decode_q8(fmt, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream, split=None):
+def _decode_q8(fmt, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream, split=None,
+               split_schedule=SPLIT_AUTO):
     import torch
 
     lib = load_library()
@@ -498,14 +506,15 @@ def _decode_q8(fmt, q, k_pool, v_pool, scales, block_tables, seq_lens, scale, ou
     if split is not None:
         max_seq_len, partition_tokens, workspace = split
         if workspace is None:
-            need = workspace_bytes(q, k_pool.view(torch.int8), block_tables, max_seq_len, partition_tokens)
+            need = workspace_bytes(q, k_pool.view(torch.int8), block_tables, max_seq_len, partition_tokens,
+                                   split_schedule=split_schedule)
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         tensors["workspace"] = workspace
     dev = _check_tensors(**tensors)
     _check_scales(k_pool, scales)
     _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables/seq_lens must be int32")
     _require(out.shape == q.shape and k_pool.shape == v_pool.shape, "shape mismatch")
-    dims = make_dims(q, k_pool.view(torch.int8), block_tables, out_dtype=out.dtype)
+    dims = make_dims(q, k_pool.view(torch.int8), block_tables, out_dtype=out.dtype, split_schedule=split_schedule)
     dims.kv_dtype = kv_code
     args = [ctypes.byref(dims), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), scales.data_ptr(),
             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr()]
@@ -533,10 +542,11 @@ def decode_int8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float,
 
 
 def decode_partitioned_int8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, max_seq_len: int,
-                            partition_tokens: int, out=None, workspace=None, *, out_dtype=None, stream=None):
+                            partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                            split_schedule: int = SPLIT_AUTO, stream=None):
     """``pa_decode_partitioned_int8``: split-context decode + merge over int8 pools."""
     return _decode_q8("int8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream,
-                      (max_seq_len, partition_tokens, workspace))
+                      (max_seq_len, partition_tokens, workspace), split_schedule)
 
 
 def write_kv_fp8(k_new, v_new, k_pool, v_pool, scales, block_tables, positions, *, stream=None):
@@ -551,10 +561,11 @@ def decode_fp8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, 
 
 
 def decode_partitioned_fp8(q, k_pool, v_pool, scales, block_tables, seq_lens, scale: float, max_seq_len: int,
-                           partition_tokens: int, out=None, workspace=None, *, out_dtype=None, stream=None):
+                           partition_tokens: int, out=None, workspace=None, *, out_dtype=None,
+                           split_schedule: int = SPLIT_AUTO, stream=None):
     """``pa_decode_partitioned_fp8``: split-context decode + merge over E4M3 pools."""
     return _decode_q8("fp8", q, k_pool, v_pool, scales, block_tables, seq_lens, scale, out, out_dtype, stream,
-                      (max_seq_len, partition_tokens, workspace))
+                      (max_seq_len, partition_tokens, workspace), split_schedule)
 
 
 # ----------------------------------------------------------------------------- paged prefill

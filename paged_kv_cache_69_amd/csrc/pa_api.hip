@@ -36,7 +36,7 @@ int check_shape(const pa_dims* d) {
     return PA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (d->variant < PA_VARIANT_AUTO || d->variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
-  if (d->wave_parts < 0 || d->wave_parts > 2) return PA_ERR_INVALID_ARG;
+  if (d->split_schedule < PA_SPLIT_AUTO || d->split_schedule > PA_SPLIT_BALANCED) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -112,6 +112,7 @@ DecodeParams base_params(const pa_dims* d, const void* q, const void* k_pool, co
   p.num_blocks = d->num_blocks;
   p.rows = p.T * p.G;
   p.out_dtype = d->out_dtype;
+  p.slots_per_part = 1;
   return p;
 }
 
@@ -127,7 +128,7 @@ int launch_attention(const pa_dims* d, int variant, DecodeParams& p, hipStream_t
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace split: (m, l) pairs first, then the accumulators, each 256-byte aligned.
+// Workspace split: (m, l) pairs first, then the accumulators, each 256-byte aligned. `parts` slots per row.
 void workspace_layout(const pa_dims* d, int32_t parts, size_t* ml_bytes, size_t* acc_bytes) {
   const size_t rows = (size_t)d->num_seqs * d->q_tokens * d->num_q_heads;
   *ml_bytes = align256(rows * (size_t)parts * 2 * sizeof(float));
@@ -163,16 +164,29 @@ int32_t cascade_parts(const pa_dims* d, int32_t prefix_tokens, int32_t max_seq_l
   return cascade_prefix_slots(d, prefix_tokens) + (max_seq_len - prefix_tokens + partition_tokens - 1) / partition_tokens;
 }
 
-// Consecutive partitions per wave of the matrix-core split kernel: two once one partition per wave
-// would need more waves than the GPU holds at once (B * Hkv * parts bounds the waves from above), for
-// bf16 pools and 16 query rows per kv head (T * G <= 16). 8-bit tiles are half the bytes, so those
-// kernels need every wave they can get in flight and keep one partition per wave. dims->wave_parts
-// = 1 or 2 forces the count (the results are the same bits either way).
-int32_t split_wave_parts(const pa_dims* d, int32_t parts) {
+// Workspace slots per partition: two for a call that asks for balanced ranges (they cut a partition into
+// at most two pieces), one otherwise. A function of the dims alone, like the size.
+int32_t slots_per_part(const pa_dims* d) {
+  return d->split_schedule == PA_SPLIT_BALANCED && pa::balanced_supported(*d) ? 2 : 1;
+}
+
+// The split schedule of the matrix-core kernels (pa_split_schedule), or PA_ERR_UNSUPPORTED for a forced
+// balanced schedule the dims do not allow. Automatic choice: two consecutive partitions per wave once one
+// per wave would need more waves than the GPU holds at once (B * Hkv * parts bounds the waves from above),
+// for bf16 pools and 16 query rows per kv head; else one. 8-bit tiles are half the bytes, so those kernels
+// keep one partition per wave and every wave they can get in flight. Balanced ranges are never chosen
+// automatically: on the long-context workloads they measured slower than these schedules.
+int32_t split_schedule(const pa_dims* d, int32_t parts) {
   const bool rows16 = d->q_tokens * (d->num_q_heads / d->num_kv_heads) <= 16;
-  if (!rows16 || d->kv_dtype != PA_BF16) return 1;
-  if (d->wave_parts == 1 || d->wave_parts == 2) return d->wave_parts;
-  return (int64_t)d->num_seqs * d->num_kv_heads * parts > kResidentSplitWaves ? 2 : 1;
+  const bool two_ok = rows16 && d->kv_dtype == PA_BF16;
+  const bool big = (int64_t)d->num_seqs * d->num_kv_heads * parts > kResidentSplitWaves;
+  switch (d->split_schedule) {
+    case PA_SPLIT_BALANCED: return pa::balanced_supported(*d) ? PA_SPLIT_BALANCED : PA_ERR_UNSUPPORTED;
+    case PA_SPLIT_ONE_PER_WAVE: return PA_SPLIT_ONE_PER_WAVE;
+    case PA_SPLIT_TWO_PER_WAVE: return two_ok ? PA_SPLIT_TWO_PER_WAVE : PA_SPLIT_ONE_PER_WAVE;
+    default:
+      return big && two_ok ? PA_SPLIT_TWO_PER_WAVE : PA_SPLIT_ONE_PER_WAVE;
+  }
 }
 
 // Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
@@ -231,15 +245,25 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
     p.lpt = variant == PA_VARIANT_MFMA && dims->num_seqs >= kLptMinSeqs && dims->num_seqs <= pa::mfma_lpt_max_seqs();
     return launch_attention(dims, variant, p, s);
   }
+  const int32_t slots = parts * slots_per_part(dims);  // the workspace's slots per row
   size_t ml_bytes = 0, acc_bytes = 0;
-  workspace_layout(dims, parts, &ml_bytes, &acc_bytes);
-  p.parts = parts;
+  workspace_layout(dims, slots, &ml_bytes, &acc_bytes);
+  const int32_t schedule = variant == PA_VARIANT_MFMA ? split_schedule(dims, parts) : PA_SPLIT_ONE_PER_WAVE;
+  if (schedule < 0) return schedule;
   p.part_tokens = partition_tokens;
   p.partial = 1;
-  p.wave_parts = variant == PA_VARIANT_MFMA ? split_wave_parts(dims, parts) : 1;
   p.part_ml = static_cast<float*>(workspace);
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
-  st = launch_attention(dims, variant, p, s);
+  if (schedule == PA_SPLIT_BALANCED) {
+    p.parts = slots;
+    p.slots_per_part = 2;
+    discard_stale_error();
+    st = launch_status(pa::launch_balanced(p, s));
+  } else {
+    p.parts = parts;  // one slot per partition (the workspace rows are `parts` slots apart, the rest unused)
+    p.wave_parts = schedule == PA_SPLIT_TWO_PER_WAVE ? 2 : 1;
+    st = launch_attention(dims, variant, p, s);
+  }
   if (st != PA_OK) return st;
   return launch_status(pa::launch_merge_partials(p, s));
 }
@@ -367,13 +391,13 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
   if (check_shape(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return 0;
   const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
   size_t ml = 0, acc = 0;
-  workspace_layout(dims, parts, &ml, &acc);
+  workspace_layout(dims, parts * slots_per_part(dims), &ml, &acc);
   return ml + acc;
 }
 
-int pa_decode_partitioned_wave_parts(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens) {
+int pa_decode_partitioned_schedule(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens) {
   if (check_shape(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return PA_ERR_INVALID_ARG;
-  return split_wave_parts(dims, (max_seq_len + partition_tokens - 1) / partition_tokens);
+  return split_schedule(dims, (max_seq_len + partition_tokens - 1) / partition_tokens);
 }
 
 int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool, const void* v_pool,

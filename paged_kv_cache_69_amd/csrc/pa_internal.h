@@ -41,6 +41,7 @@ struct DecodeParams {
   int32_t prefix_part_tokens;  // cascade: positions of the prefix per chunk (one wave's share)
   int32_t lpt;               // single pass on the MFMA kernel: sequences dealt longest first
   int32_t wave_parts;        // split launches on the MFMA kernel: consecutive partitions per wave (<= 1: one)
+  int32_t slots_per_part;    // split launches: workspace slots per partition (2: balanced ranges, else 1)
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,
@@ -77,6 +78,11 @@ int mfma_waves();  // waves per MFMA workgroup (prefix chunks merged into one ca
 int mfma_lpt_max_seqs();  // largest batch the single pass can order longest first
 
 hipError_t launch_merge_partials(const DecodeParams& p, hipStream_t stream);
+
+// Split context with balanced wave ranges (pa_decode_balanced.hip): bf16 or 8-bit pools, head_dim 128,
+// b in {16, 32}, T * G <= 16, up to 1024 sequences whose q rows of one kv head fit 48 KiB of LDS.
+bool balanced_supported(const pa_dims& d);
+hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream);
 
 // Copy-on-write block copies: pairs [n, 2] (source, destination) on the device; for 8-bit pools the
 // blocks' [Hkv, 2] scales too (scales non-null).

@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
   }
   const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
   // slots written: the shared prefix's (cascade), then one per partition of the sequence's own positions
-  const int own = max(0, (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens);
+  // (two per partition after balanced ranges: the partition's two pieces, or its partial and an empty pair)
+  const int own = max(0, (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens) * p.slots_per_part;
   const int nparts = row_raw < rows && L > 0 ? min(p.parts, p.prefix_parts + own) : 0;
 
   // M = max m_k over partitions with l_k > 0, then l = sum l_k 2^(m_k - M)

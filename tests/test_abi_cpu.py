@@ -56,7 +56,7 @@ def test_status_strings_and_version(lib):
 def _dims(**kw):
     base = dict(num_seqs=4, q_tokens=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                 num_blocks=100, max_blocks_per_seq=8, q_dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16,
-                out_dtype=pa.PA_F32, variant=0, wave_parts=0)
+                out_dtype=pa.PA_F32, variant=0, split_schedule=0)
     base.update(kw)
     return pa.PaDims(*[base[n] for n, _ in pa.PaDims._fields_])
 
@@ -73,8 +73,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails val
     (dict(q_dtype=pa.PA_F32), -2),       # q and KV dtypes differ
     (dict(head_dim=96), -2),             # no kernel for this head_dim
     (dict(block_size=64), -2),
-    (dict(wave_parts=3), -1),
-    (dict(wave_parts=-1), -1),
+    (dict(split_schedule=4), -1),
+    (dict(split_schedule=-1), -1),
 ])
 def test_decode_rejects_bad_dims(lib, kw, status):
     d = _dims(**kw)
@@ -98,46 +98,61 @@ def test_empty_batch_is_a_no_op(lib):
 
 
 def test_partitioned_workspace_arithmetic(lib):
-    d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
-    # rows = 16*32 = 512; parts = ceil(32768 / 512) = 64
-    ml = 512 * 64 * 2 * 4
-    acc = 512 * 64 * 128 * 4
+    """rows = 16 * 32 = 512; P = ceil(32768 / 512) = 64 partitions: one slot per partition, two when the call
+    asks for balanced ranges (which these dims allow); 32 query rows per kv head allow none: one."""
     align = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 32768, 512) == align(ml) + align(acc)
+    for sched, slots in ((0, 64), (2, 64), (3, 128)):
+        d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=sched)
+        want = align(512 * slots * 2 * 4) + align(512 * slots * 128 * 4)
+        assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 32768, 512) == want
+    d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, split_schedule=3)
+    rows32 = 16 * 4 * 64
+    want32 = align(rows32 * 64 * 2 * 4) + align(rows32 * 64 * 128 * 4)
+    assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d32), 32768, 512) == want32
+    d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
     assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 0, 512) == 0
     assert lib.pa_decode_partitioned_workspace_bytes(None, 10, 512) == 0
 
 
-def test_partitioned_wave_parts_arithmetic(lib):
-    """Two partitions per split wave once B * Hkv * ceil(max_seq_len / partition_tokens) > 2048."""
+def test_partitioned_schedule_choice(lib):
+    """PA_SPLIT_AUTO: two partitions per wave once B * Hkv * ceil(max_seq_len / partition_tokens) > 2048
+    (bf16 pools, <= 16 rows per kv head), else one; balanced ranges only when asked for."""
     d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
     assert d.num_kv_heads == 8
-    f = lambda msl, pt: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), msl, pt)  # noqa: E731
-    assert f(32768, 512) == 2            # 16 * 8 * 64 = 8192 partitions
-    assert f(16 * 512, 512) == 1         # 16 * 8 * 16 = 2048: one round already
-    assert f(16 * 512 + 1, 512) == 2     # 17 partitions per sequence
-    assert f(0, 512) == -1 and f(100, 0) == -1
-    assert lib.pa_decode_partitioned_wave_parts(None, 100, 512) == -1
-    d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128)  # 32 rows per kv head: one partition
-    assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d32), 32768, 512) == 1
+    f = lambda dd, msl, pt: lib.pa_decode_partitioned_schedule(ctypes.byref(dd), msl, pt)  # noqa: E731
+    assert f(d, 32768, 512) == pa.SPLIT_TWO_PER_WAVE      # 16 * 8 * 64 = 8192 partitions
+    assert f(d, 16 * 512, 512) == pa.SPLIT_ONE_PER_WAVE  # 16 * 8 * 16 = 2048: one round already
+    assert f(d, 16 * 512 + 1, 512) == pa.SPLIT_TWO_PER_WAVE
+    assert f(d, 0, 512) == -1 and f(d, 100, 0) == -1
+    assert lib.pa_decode_partitioned_schedule(None, 100, 512) == -1
+    d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128)  # 32 rows per kv head
+    assert f(d32, 32768, 512) == pa.SPLIT_ONE_PER_WAVE
     for code in (pa.PA_INT8, pa.PA_FP8_E4M3):  # 8-bit pools: one partition per wave
         d8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code)
-        assert lib.pa_decode_partitioned_wave_parts(ctypes.byref(d8), 32768, 512) == 1
+        assert f(d8, 32768, 512) == pa.SPLIT_ONE_PER_WAVE
+    big_b = _dims(num_seqs=1100, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3)  # too many to stage
+    assert f(big_b, 4096, 512) == -2
+    d_b8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, block_size=8, split_schedule=3)
+    assert f(d_b8, 32768, 512) == -2
 
 
-def test_partitioned_wave_parts_override(lib, monkeypatch):
-    """pa_dims.wave_parts forces the count for bf16 pools of up to 16 rows per kv head, is ignored where
-    two partitions per wave do not exist, and no environment variable changes anything."""
-    f = lambda d: lib.pa_decode_partitioned_wave_parts(ctypes.byref(d), 32768, 512)  # noqa: E731
-    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=1)) == 1
-    assert f(_dims(num_seqs=1, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=2)) == 2
-    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=0)) == 2
+def test_partitioned_schedule_override(lib, monkeypatch):
+    """pa_dims.split_schedule forces a schedule; two per wave falls back to one where it does not exist; a
+    forced balanced schedule the dims do not allow is PA_ERR_UNSUPPORTED; no environment variable changes
+    anything."""
+    f = lambda d: lib.pa_decode_partitioned_schedule(ctypes.byref(d), 32768, 512)  # noqa: E731
+    base = dict(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
+    assert f(_dims(**base, split_schedule=1)) == 1
+    assert f(_dims(**base, split_schedule=2)) == 2
+    assert f(_dims(**base, split_schedule=3)) == 3
+    assert f(_dims(num_seqs=1, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3)) == 3
     monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "1")  # the variable of an earlier version: no effect
-    assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, wave_parts=0)) == 2
+    assert f(_dims(**base, split_schedule=0)) == 2
     for code in (pa.PA_INT8, pa.PA_FP8_E4M3):
-        assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code, wave_parts=2)) == 1
-    assert f(_dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, wave_parts=2)) == 1
-    assert f(_dims(wave_parts=5)) == -1
+        assert f(_dims(**base, kv_dtype=code, split_schedule=2)) == 1
+    assert f(_dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, split_schedule=2)) == 1
+    assert f(_dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, split_schedule=3)) == -2
+    assert f(_dims(split_schedule=5)) == -1
 
 
 def test_fused_cascade_refuses_missing_rows(lib):

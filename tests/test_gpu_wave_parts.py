@@ -1,9 +1,9 @@
 """Split decode with two consecutive partitions per wave, on the GPU.
 
 When B * Hkv * ceil(max_seq_len / partition_tokens) exceeds the waves the GPU holds at once, each wave of
-the matrix-core split kernel walks two consecutive partitions (pa_decode_partitioned_wave_parts = 2). It
+the matrix-core split kernel walks two consecutive partitions (pa_decode_partitioned_schedule = 2). It
 still writes one partial per partition, each with that partition's own reference maximum, so the merged
-result must be the same bits as with one partition per wave. pa_dims.wave_parts forces either choice, so
+result must be the same bits as with one partition per wave. pa_dims.split_schedule forces either choice, so
 the same call runs both ways. Both runs also meet the float64 oracle; nothing expected comes from the GPU.
 """
 
@@ -28,11 +28,11 @@ def _gpu(case):
 
 
 def _both_ways(pa, g, case, pt, call):
-    """call(kp) with one, then two partitions per wave (forced through pa_dims.wave_parts), at the case's
+    """call(kp) with one, then two partitions per wave (forced through pa_dims.split_schedule), at the case's
     own max_seq_len."""
     outs = []
     for kp in (1, 2):
-        assert pa.wave_parts(g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt, force=kp) == kp
+        assert pa.split_schedule(g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt, force=kp) == kp
         outs.append(call(kp))
     torch.cuda.synchronize()
     return outs
@@ -66,7 +66,7 @@ def test_two_partitions_per_wave_bitwise(gpu_lib, b, hq, hkv, t):
         gpu_lib.write_kv(g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"], g["positions"])
         outs = _both_ways(gpu_lib, g, case, pt, lambda kp: gpu_lib.decode_partitioned(
             g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt,
-            wave_parts=kp))
+            split_schedule=kp))
         fs = []
 
         def fused_call(kp):
@@ -74,7 +74,7 @@ def test_two_partitions_per_wave_bitwise(gpu_lib, b, hq, hkv, t):
             fs.append(f)
             return gpu_lib.write_kv_decode(f["q"], f["k_new"], f["v_new"], f["k_pool"], f["v_pool"],
                                            f["block_tables"], f["seq_lens"], case.scale,
-                                           max_seq_len=case.max_seq_len, partition_tokens=pt, wave_parts=kp)
+                                           max_seq_len=case.max_seq_len, partition_tokens=pt, split_schedule=kp)
 
         fused = _both_ways(gpu_lib, g, case, pt, fused_call)
         for f in fs:
@@ -116,7 +116,7 @@ def test_two_partitions_per_wave_reference_restarts(gpu_lib):
     print("[case] wave parts reference restarts", flush=True)
     outs = _both_ways(gpu_lib, g, case, pt, lambda kp: gpu_lib.decode_partitioned(
         g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale, case.max_seq_len, pt,
-        wave_parts=kp))
+        split_schedule=kp))
     single = gpu_lib.decode(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
