@@ -59,6 +59,7 @@ METRIC = "paged decode attention: tokens/s and achieved HBM GB/s (% of peak), 1 
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
 REPLICAS = 0  # --replicas N: that many input copies instead of enough for a cold cache (a warm-cache run)
+PAGED_PROBE = True  # --no-paged-probe: skip the paged-read probe sweep
 SPLIT_SCHEDULE = 0  # --split-schedule N: pa_dims.split_schedule of split calls (0: the library's choice)
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
 STREAM_BYTES = 2 << 30  # the streaming-read probe reads this much per launch (far past every cache)
@@ -362,6 +363,8 @@ def measure_gpu(pa, case, partition_tokens, steps, warmup, variant=0, graphs=Tru
     call_ms = ev0.elapsed_time(ev1) / steps
     floor = time_first_tile(reps, case, steps) if graphs and case.block_size * case.k_pool.shape[3] * \
         case.k_pool.element_size() <= 16384 else None
+    if floor is not None and PAGED_PROBE:
+        floor.update(time_paged_read(reps, case, steps))
     del reps
     torch.cuda.empty_cache()
     return (t1 - t0) / steps, call_ms, n_rep, floor
@@ -383,6 +386,8 @@ def probe_library():
         lib.pa_probe_stream_read.restype = ctypes.c_int
         lib.pa_probe_first_tile.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, P]
         lib.pa_probe_first_tile.restype = ctypes.c_int
+        lib.pa_probe_paged_read.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P]
+        lib.pa_probe_paged_read.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
 
@@ -428,13 +433,42 @@ def calibrate_stream(runs: int = 5):
     return _STREAM
 
 
+def _graph_us(launch, reps, steps):
+    """Average duration (us) of ``launch(replica, stream_handle)`` over one graph of ``steps`` launches with
+    the replicas rotating, between HIP events on the stream the graph runs on (after one warm replay)."""
+    import ctypes
+
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for s in range(len(reps)):
+        launch(reps[s], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for s in range(steps):
+                launch(reps[s % len(reps)], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    stream.wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / steps * 1e3
+    del g
+    return us
+
+
 def time_first_tile(reps, case, steps):
     """Average duration (us) of the first-tile probe over the decode call's own replicas, launched and
     timed like the decode calls (one graph of ``steps`` launches, replicas rotating, HIP events around
     it): the loads a decode workgroup waits for before its first tile, with nothing else. Both forms:
     length and table entry issued together (as the kernels do), and length -> table -> tile."""
-    import ctypes
-
     import torch
 
     lib = probe_library()
@@ -451,28 +485,43 @@ def time_first_tile(reps, case, steps):
                                          row_bytes, dependent, out.data_ptr(), h)
             if st:
                 raise RuntimeError(f"pa_probe_first_tile: {st}")
-        stream = torch.cuda.current_stream()
-        for s in range(len(reps)):
-            launch(reps[s], ctypes.c_void_p(stream.cuda_stream))
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for s in range(steps):
-                    launch(reps[s % len(reps)], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        stream.wait_stream(side)
-        g.replay()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        res["floor_dependent_us" if dependent else "floor_us"] = round(ev0.elapsed_time(ev1) / steps * 1e3, 3)
-        del g
+        res["floor_dependent_us" if dependent else "floor_us"] = round(_graph_us(launch, reps, steps), 3)
     return res
+
+
+def time_paged_read(reps, case, steps):
+    """The paged-read probe over the decode call's own replicas and tables (every K/V block the call
+    reads, no arithmetic), timed like the decode calls, at its best over launch shapes: 16 or 64 blocks
+    per wave, 1, 2 or 4 blocks in flight per wave, plain or nontemporal loads. Returns the rate (GB/s)
+    of the best shape and that shape, or {} when the block is not 1, 2, 4 or 8 KiB per kv head."""
+    import torch
+
+    lib = probe_library()
+    b, hkv = case.q.shape[0], case.k_pool.shape[1]
+    n, _, bs, d = case.k_pool.shape
+    mb = case.block_tables.shape[1]
+    row_bytes = d * case.k_pool.element_size()
+    if bs * row_bytes not in (1024, 2048, 4096, 8192):
+        return {}
+    blocks = int(((case.seq_lens.cpu().long() + bs - 1) // bs).clamp(max=mb).sum())
+    nbytes = blocks * hkv * 2 * bs * row_bytes
+    best = (0.0, None)
+    for bpw in (16, 64):
+        groups = (mb + 4 * bpw - 1) // (4 * bpw)
+        out = torch.empty(b * groups * hkv, dtype=torch.int32, device="cuda:0")
+        for unroll in (1, 2, 4):
+            for nt in (0, 1):
+                def launch(r, h):
+                    t = r.t
+                    st = lib.pa_probe_paged_read(t["k_pool"].data_ptr(), t["v_pool"].data_ptr(),
+                                                 t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(), b, hkv, mb,
+                                                 n, bs, row_bytes, bpw, unroll, nt, out.data_ptr(), h)
+                    if st:
+                        raise RuntimeError(f"pa_probe_paged_read: {st}")
+                gbps = nbytes / (_graph_us(launch, reps, steps) * 1e-6) / 1e9
+                if gbps > best[0]:
+                    best = (gbps, {"blocks_per_wave": bpw, "blocks_in_flight_per_wave": unroll, "nontemporal": nt})
+    return {"paged_read_gbps": round(best[0], 1), "paged_read_launch": best[1], "paged_read_bytes": nbytes}
 
 
 def host_cores() -> int:
@@ -789,7 +838,9 @@ def run_copy_workload(pa, name, steps, warmup, graphs=True):
 
 
 def stream_terms(achieved_gbps, bytes_per_launch, launch_us, floor):
-    """The call against the two measured bounds: the streaming-read rate and the first-tile floor."""
+    """The call against the measured bounds: the streaming-read rate, the paged-read rate of its own
+    tables, and the first-tile floor. model_us = floor + bytes / stream rate; paged_model_us = floor +
+    bytes / paged-read rate."""
     out = {}
     if _STREAM is not None:
         out.update(stream_gbps=_STREAM["stream_gbps"], frac_of_stream=round(achieved_gbps / _STREAM["stream_gbps"], 4))
@@ -798,6 +849,10 @@ def stream_terms(achieved_gbps, bytes_per_launch, launch_us, floor):
         if _STREAM is not None:
             model = floor["floor_us"] + bytes_per_launch / (_STREAM["stream_gbps"] * 1e3)
             out.update(model_us=round(model, 3), over_model=round(launch_us / model, 4))
+        if floor.get("paged_read_gbps"):
+            pm = floor["floor_us"] + bytes_per_launch / (floor["paged_read_gbps"] * 1e3)
+            out.update(frac_of_paged_read=round(achieved_gbps / floor["paged_read_gbps"], 4),
+                       paged_model_us=round(pm, 3), over_paged_model=round(launch_us / pm, 4))
     return out
 
 
@@ -1017,6 +1072,7 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for counter calibration)")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read calibration")
+    ap.add_argument("--no-paged-probe", action="store_true", help="skip the paged-read probe sweep")
     ap.add_argument("--cpu-secondary", default="long",
                     help="comma-separated secondary workloads that also get a cpu_baseline ('' for none)")
     ap.add_argument("--no-graph", action="store_true",
@@ -1044,9 +1100,10 @@ def main(argv=None):
               "GPU and needs no collectives: its (sequence, kv head) units split across GPUs with no exchange.",
               file=sys.stderr)
         return 2
-    global REPLICAS, SPLIT_SCHEDULE
+    global REPLICAS, SPLIT_SCHEDULE, PAGED_PROBE
     REPLICAS = max(0, args.replicas)
     SPLIT_SCHEDULE = args.split_schedule
+    PAGED_PROBE = not args.no_paged_probe
 
     import torch
 

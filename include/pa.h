@@ -84,12 +84,13 @@ typedef enum {
  *   PA_SPLIT_TWO_PER_WAVE: a wave walks two consecutive partitions of one sequence (bf16 pools,
  *     T * G <= 16; elsewhere one per wave).
  *   PA_SPLIT_BALANCED: for each kv head the tiles of all sequences form one list, cut into equal
- *     ranges, one per wave, with one wave per SIMD of the GPU; a partition that a range boundary
- *     cuts leaves two partials, which the merge adds like any others. Every wave then streams the
- *     same number of tiles whatever the spread of lengths; it is opt-in (the automatic choice never
- *     takes it: it measured slower on the long-context workloads). Needs bf16 or 8-bit pools,
- *     D = 128, b in {16, 32}, T * G <= 16, B <= 1024 and B * T * G * 256 <= 48 KiB
- *     (PA_ERR_UNSUPPORTED otherwise); the workspace then holds two slots per partition. */
+ *     ranges (each at least one partition long), one per pair of waves, one pair per SIMD of the
+ *     GPU; the two waves of a pair share their range from its two ends, so they end together
+ *     whatever their relative speed. Each wave leaves one partial per sequence it touched, which the
+ *     merge adds like any others (so the last bits of the output may change from call to call).
+ *     Needs bf16 or 8-bit pools, D = 128, b in {16, 32}, T * G <= 16,
+ *     B <= 1024 and B * T * G * 256 <= 48 KiB (PA_ERR_UNSUPPORTED otherwise); the workspace then
+ *     holds 2P + 2 slots per row and B int32 slot counts. */
 typedef enum {
   PA_SPLIT_AUTO = 0,
   PA_SPLIT_ONE_PER_WAVE = 1,
@@ -170,8 +171,9 @@ int pa_decode(const pa_dims* dims, const void* q, const void* k_pool, const void
               pa_stream_t stream);
 
 /* Bytes of device workspace pa_decode_partitioned needs for these dims:
- * B * T * Hq * S * (D + 2) * 4 plus alignment, with S = 2P slots per row when
- * dims->split_schedule asks for balanced ranges the dims allow (else S = P),
+ * B * T * Hq * S * (D + 2) * 4 plus alignment, with S = 2P + 2 slots per row
+ * and B * 4 more bytes when the call runs balanced ranges (the schedule
+ * pa_decode_partitioned_schedule returns for these arguments), else S = P,
  * and P = ceil(max_seq_len / partition_tokens). Returns 0 for invalid
  * arguments. */
 size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_seq_len,
@@ -208,10 +210,14 @@ int pa_decode_partitioned(const pa_dims* dims, const void* q, const void* k_pool
 
 /* pa_decode_partitioned_schedule: the pa_split_schedule (1, 2 or 3) a split
  * call with these arguments runs on the matrix-core kernels. With
- * PA_SPLIT_AUTO it is TWO_PER_WAVE for bf16 pools with T * G <= 16 when one
- * partition per wave would need more than the 2048 waves the GPU holds at
- * once (B * Hkv * ceil(max_seq_len / partition_tokens) > 2048), else
- * ONE_PER_WAVE. A forced schedule is returned as the call would run it
+ * PA_SPLIT_AUTO, when one partition per wave would need more than the 2048
+ * waves the GPU holds at once (B * Hkv * ceil(max_seq_len /
+ * partition_tokens) > 2048), it is BALANCED where the dims allow it, else
+ * TWO_PER_WAVE for bf16 pools with T * G <= 16; ONE_PER_WAVE otherwise.
+ * Balanced calls may differ from one call to the next in the last bits of
+ * the output (each pair of waves splits its range where their timing puts
+ * the meeting point); ONE_PER_WAVE and TWO_PER_WAVE give the same bits on
+ * every call. A forced schedule is returned as the call would run it
  * (PA_ERR_UNSUPPORTED for a balanced schedule the dims do not allow).
  * Host-only; PA_ERR_INVALID_ARG for invalid dims or sizes. */
 int pa_decode_partitioned_schedule(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens);

@@ -1,8 +1,9 @@
 /*
  * pa_probe.h: C ABI of libpa_probe.so, the measurement probes the benchmark runs beside the decode
- * step. They are not part of the decode path: they measure the two numbers that bound it on the GPU
- * at hand, the rate at which HBM streams reads and the latency of the dependent loads a decode
- * workgroup makes before its first K/V tile arrives. [P3] "Asynchronous KV Cache Prefetching",
+ * step. They are not part of the decode path: they measure the numbers that bound it on the GPU at
+ * hand, the rate at which HBM streams reads (sequentially, and in the decode's own pattern of blocks
+ * through the tables) and the latency of the dependent loads a decode workgroup makes before its
+ * first K/V tile arrives. [P3] "Asynchronous KV Cache Prefetching",
  * sections 2.2 and 3.2, names both: decode attention streams the cache at memory speed, and the
  * block-table lookup in front of each block's load is exposed latency.
  *
@@ -42,6 +43,22 @@ int pa_probe_first_tile(const void* k_pool, const void* v_pool, const int32_t* b
                         int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks, int32_t num_blocks,
                         int32_t block_size, int32_t row_bytes, int32_t dependent, uint32_t* out,
                         pa_probe_stream_t stream);
+
+/* pa_probe_paged_read: every K and V block a decode call over these tables reads, and nothing else:
+ * for each (sequence i, kv head h), blocks 0 .. ceil(seq_lens[i] / block_size) - 1 of row i of
+ * block_tables (ids clamped to the pool), each block_size rows of row_bytes bytes of head h in pools
+ * laid out [num_blocks, num_kv_heads, block_size, row_bytes]; block_size * row_bytes must be 1, 2, 4
+ * or 8 KiB. A workgroup of 4 waves takes 4 * blocks_per_wave consecutive blocks of one (sequence,
+ * kv head), blocks_per_wave per wave, with `unroll` (1, 2 or 4) blocks' loads in flight per wave per
+ * step; `nontemporal` = 1 issues them as nontemporal loads. Each workgroup writes the XOR of what it
+ * read to out[] (one uint32 per workgroup: num_seqs * ceil(max_blocks / (4 * blocks_per_wave)) *
+ * num_kv_heads entries). It is the decode's byte stream without the attention, so its rate is the
+ * ceiling of that access pattern: 4 KiB pieces at the places the tables name, not one sequential
+ * sweep. */
+int pa_probe_paged_read(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks, int32_t num_blocks,
+                        int32_t block_size, int32_t row_bytes, int32_t blocks_per_wave, int32_t unroll,
+                        int32_t nontemporal, uint32_t* out, pa_probe_stream_t stream);
 
 #ifdef __cplusplus
 }

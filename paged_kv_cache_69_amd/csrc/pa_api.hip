@@ -112,7 +112,7 @@ DecodeParams base_params(const pa_dims* d, const void* q, const void* k_pool, co
   p.num_blocks = d->num_blocks;
   p.rows = p.T * p.G;
   p.out_dtype = d->out_dtype;
-  p.slots_per_part = 1;
+  p.slot_counts = nullptr;
   return p;
 }
 
@@ -164,18 +164,13 @@ int32_t cascade_parts(const pa_dims* d, int32_t prefix_tokens, int32_t max_seq_l
   return cascade_prefix_slots(d, prefix_tokens) + (max_seq_len - prefix_tokens + partition_tokens - 1) / partition_tokens;
 }
 
-// Workspace slots per partition: two for a call that asks for balanced ranges (they cut a partition into
-// at most two pieces), one otherwise. A function of the dims alone, like the size.
-int32_t slots_per_part(const pa_dims* d) {
-  return d->split_schedule == PA_SPLIT_BALANCED && pa::balanced_supported(*d) ? 2 : 1;
-}
 
 // The split schedule of the matrix-core kernels (pa_split_schedule), or PA_ERR_UNSUPPORTED for a forced
-// balanced schedule the dims do not allow. Automatic choice: two consecutive partitions per wave once one
-// per wave would need more waves than the GPU holds at once (B * Hkv * parts bounds the waves from above),
-// for bf16 pools and 16 query rows per kv head; else one. 8-bit tiles are half the bytes, so those kernels
-// keep one partition per wave and every wave they can get in flight. Balanced ranges are never chosen
-// automatically: on the long-context workloads they measured slower than these schedules.
+// balanced schedule the dims do not allow. Automatic choice, once one partition per wave would need more
+// waves than the GPU holds at once (B * Hkv * parts bounds the waves from above): balanced ranges where
+// the dims allow them (on the long-context workloads they end every SIMD's work together), else two
+// consecutive partitions per wave for bf16 pools and 16 query rows per kv head; one partition per wave
+// otherwise, and for 8-bit pools (half the bytes per tile: every wave they can get in flight).
 int32_t split_schedule(const pa_dims* d, int32_t parts) {
   const bool rows16 = d->q_tokens * (d->num_q_heads / d->num_kv_heads) <= 16;
   const bool two_ok = rows16 && d->kv_dtype == PA_BF16;
@@ -185,8 +180,21 @@ int32_t split_schedule(const pa_dims* d, int32_t parts) {
     case PA_SPLIT_ONE_PER_WAVE: return PA_SPLIT_ONE_PER_WAVE;
     case PA_SPLIT_TWO_PER_WAVE: return two_ok ? PA_SPLIT_TWO_PER_WAVE : PA_SPLIT_ONE_PER_WAVE;
     default:
+      if (big && pa::balanced_supported(*d)) return PA_SPLIT_BALANCED;
       return big && two_ok ? PA_SPLIT_TWO_PER_WAVE : PA_SPLIT_ONE_PER_WAVE;
   }
+}
+
+// Workspace of a split call with `parts` partitions per row: the slots per row, and the bytes of the
+// (m, l) pairs, the accumulators and the per-sequence slot counts, in that order. Balanced ranges are
+// at least one partition long, so a sequence meets at most parts + 1 of them, each with a slot per
+// wave of its pair: 2 parts + 2 slots, and the counts (one int32 per sequence) the merge reads.
+int32_t split_layout(const pa_dims* d, int32_t parts, size_t* ml, size_t* acc, size_t* counts) {
+  const bool bal = split_schedule(d, parts) == PA_SPLIT_BALANCED;
+  const int32_t slots = bal ? 2 * parts + 2 : parts;
+  workspace_layout(d, slots, ml, acc);
+  *counts = bal ? align256((size_t)d->num_seqs * sizeof(int32_t)) : 0;
+  return slots;
 }
 
 // Every decode entry point: argument checks, kernel choice, the attention launch and, for a split
@@ -245,9 +253,8 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
     p.lpt = variant == PA_VARIANT_MFMA && dims->num_seqs >= kLptMinSeqs && dims->num_seqs <= pa::mfma_lpt_max_seqs();
     return launch_attention(dims, variant, p, s);
   }
-  const int32_t slots = parts * slots_per_part(dims);  // the workspace's slots per row
-  size_t ml_bytes = 0, acc_bytes = 0;
-  workspace_layout(dims, slots, &ml_bytes, &acc_bytes);
+  size_t ml_bytes = 0, acc_bytes = 0, count_bytes = 0;
+  const int32_t slots = split_layout(dims, parts, &ml_bytes, &acc_bytes, &count_bytes);  // slots per row
   const int32_t schedule = variant == PA_VARIANT_MFMA ? split_schedule(dims, parts) : PA_SPLIT_ONE_PER_WAVE;
   if (schedule < 0) return schedule;
   p.part_tokens = partition_tokens;
@@ -256,7 +263,7 @@ int decode_entry(const pa_dims* dims, bool int8, bool split, const void* q, cons
   p.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
   if (schedule == PA_SPLIT_BALANCED) {
     p.parts = slots;
-    p.slots_per_part = 2;
+    p.slot_counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ml_bytes + acc_bytes);
     discard_stale_error();
     st = launch_status(pa::launch_balanced(p, s));
   } else {
@@ -390,9 +397,9 @@ size_t pa_decode_partitioned_workspace_bytes(const pa_dims* dims, int32_t max_se
                                              int32_t partition_tokens) {
   if (check_shape(dims) != PA_OK || max_seq_len < 1 || partition_tokens < 1) return 0;
   const int32_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
-  size_t ml = 0, acc = 0;
-  workspace_layout(dims, parts * slots_per_part(dims), &ml, &acc);
-  return ml + acc;
+  size_t ml = 0, acc = 0, counts = 0;
+  split_layout(dims, parts, &ml, &acc, &counts);
+  return ml + acc + counts;
 }
 
 int pa_decode_partitioned_schedule(const pa_dims* dims, int32_t max_seq_len, int32_t partition_tokens) {

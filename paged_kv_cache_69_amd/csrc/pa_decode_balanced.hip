@@ -1,24 +1,31 @@
-// Split-context decode with balanced wave ranges, on the matrix cores (gfx950 MFMA), head_dim 128,
+// Split-context decode over balanced, paired ranges, on the matrix cores (gfx950 MFMA), head_dim 128,
 // bf16 or 8-bit (int8, E4M3) pools, up to 16 query rows per kv head.
 //
 // It computes what pa_decode_partitioned computes ([P1] "25. Paged attention and prefix caching",
-// section "Attention that reads through the table": long contexts are cut into partitions whose
-// partial results a second pass merges; [P5] "Chapter 7 Paged KV Cache and Memory Management",
-// section 4.2: the exact merge of (m, l, acc) partials) with a different division of the work:
+// section "Attention that reads through the table": long contexts are cut into pieces whose partial
+// results a second pass merges; [P5] "Chapter 7 Paged KV Cache and Memory Management", section 4.2:
+// the exact merge of (m, l, acc) partials) with a division of the work that keeps every SIMD busy
+// to the end:
 //  * The 16-position tiles of every sequence, for one kv head, are taken as one list (sequence 0's
-//    tiles, then sequence 1's, ...), and the list is cut into R equal contiguous ranges, one per
-//    wave. Every wave therefore streams the same number of tiles, however the lengths are spread.
-//    The launch has one wave per SIMD (one round), and each wave keeps PF tiles in flight in
-//    registers, so the bytes in flight per SIMD do not depend on another wave's progress.
-//  * A range never holds less than one partition (R <= tiles / partition tiles), so a partition is
-//    cut by at most one range boundary. Its first piece goes to workspace slot 2k of the row, its
-//    second piece to slot 2k + 1; a partition that one wave walks whole writes its partial to slot
-//    2k and an empty (m = -inf, l = 0) pair to slot 2k + 1. The merge kernel combines the 2P slots
-//    of each row exactly as it combines P partitions.
-//  * Each piece has its own reference max and restarts itself when a score outruns it by 2^64, as in
-//    the other matrix-core kernels, so every slot holds what a wave of its own would have written.
+//    tiles, then sequence 1's, ...), cut into R equal contiguous ranges (R <= tiles / partition
+//    tiles, so a range is at least one partition long), one per pair of waves.
+//  * A workgroup is 8 waves, 4 pairs (w, w + 4), and its LDS keeps it alone on its CU, two waves per
+//    SIMD. Of two waves on one SIMD the older one is served first and streams several times faster
+//    while both run, so ranges fixed per wave end at very different times. Here the two waves of a
+//    pair share their range instead: one takes tiles from the front and the other from the back,
+//    through one 64-bit LDS word (front, back) that both update with an atomic add, and they meet
+//    wherever their speeds put them, so both end within a few tiles of each other.
+//  * A wave's tiles of one sequence form one piece with its own (m, l, acc). Its partial goes to
+//    workspace slot 2 (r - r0) + side of each of the sequence's rows, r the pair's range, r0 the
+//    range holding the sequence's first tile, side 0 for the front wave and 1 for the back wave. At
+//    the end each wave marks the slots of the sequences of its range that it did not touch as empty
+//    (m = -inf, l = 0), and the kernel writes each sequence's slot count for the merge kernel, which
+//    combines the slots of each row exactly.
+//  * A piece's first tile sets each row's reference max; a later score more than 2^64 above it
+//    raises the reference and rescales that row's l and accumulator by 2^(old - new) (rare: scores
+//    that climb by more than 64 base-2 units; o = acc / l does not depend on the reference).
 //  * The workgroup stages the tile prefix sums of the batch, the lengths and the q rows of its kv
-//    head in LDS before any wave starts; a wave crossing into the next sequence takes that
+//    head in LDS before any wave starts; a wave crossing into another sequence takes that
 //    sequence's q operand from there.
 // The per-tile arithmetic (S^T = K Q^T on the matrix cores, masking, probabilities split into bf16 hi
 // and lo parts, V through a swizzled LDS tile and transposed reads, P.V on the matrix cores) and the
@@ -32,32 +39,33 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kBalWaves = 4;  // waves per workgroup
-#ifndef PA_BAL_WAVES_PER_SIMD
-#define PA_BAL_WAVES_PER_SIMD 1
-#endif
+constexpr int kBalWaves = 8;  // waves per workgroup: pairs (w, w + 4)
+constexpr int kBalPairs = kBalWaves / 2;
 #ifndef PA_BAL_PREFETCH
-#define PA_BAL_PREFETCH 6
+#define PA_BAL_PREFETCH 2
 #endif
 #ifndef PA_BAL_Q8_PREFETCH
-#define PA_BAL_Q8_PREFETCH 10
+#define PA_BAL_Q8_PREFETCH 4
 #endif
-constexpr int kBalWavesPerSimd = PA_BAL_WAVES_PER_SIMD;
 constexpr int kBalPrefetch = PA_BAL_PREFETCH;      // bf16 tiles in flight ahead of the one computed
 constexpr int kBalQ8Prefetch = PA_BAL_Q8_PREFETCH;  // 8-bit tiles are half the registers
 constexpr int kBalMaxSeqs = 1024;
+constexpr int kBalSeqsPerThread = kBalMaxSeqs / (kBalWaves * 64);
 constexpr int kBalQBytes = 48 * 1024;  // q rows of the batch for one kv head: B * rows * 256 bytes at most
 
 struct BalLds {
-  char vt[kBalWaves][kTileBytes];  // per-wave V tile
-  int pre[kBalMaxSeqs + 1];        // pre[s]: tiles of the sequences before s
+  char vt[kBalWaves][kTileBytes];        // per-wave V tile
+  int pre[kBalMaxSeqs + 1];              // pre[s]: tiles of the sequences before s
   int len[kBalMaxSeqs];
   int wsum[kBalWaves];
-  char q[kBalQBytes];              // [B][rows][256 B]: q rows of this kv head, bf16 as stored
+  unsigned long long cursor[kBalPairs];  // per pair: next front tile (low word), back end (high word)
+  char q[kBalQBytes];                    // [B][rows][256 B]: q rows of this kv head, bf16 as stored
 };
+// more than half of a CU's 160 KiB: one workgroup per CU, so a pair's two waves share a SIMD
+static_assert(sizeof(BalLds) > 80 * 1024, "the workgroup must hold a CU alone");
 
 template <int BS, bool Q8, bool F8, bool AP, int PF>
-__global__ __launch_bounds__(kBalWaves * 64) __attribute__((amdgpu_waves_per_eu(kBalWavesPerSimd)))
+__global__ __launch_bounds__(kBalWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void balanced_kernel(const DecodeParams p) {
   static_assert(BS >= kTile, "a tile lies inside one block");
   static_assert(!(Q8 && AP), "8-bit pools append with the separate append kernel");
@@ -69,30 +77,26 @@ void balanced_kernel(const DecodeParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave % kBalPairs, side = wave / kBalPairs;  // side 0 walks forward, 1 backward
   const int g = lane >> 4, c16 = lane & 15;
   const int kvh = blockIdx.x % p.Hkv;
-  const int W = (int)(gridDim.x / p.Hkv) * kBalWaves;  // waves per kv head
-  const int r = (int)(blockIdx.x / p.Hkv) * kBalWaves + wave;
+  const int W = (int)(gridDim.x / p.Hkv) * kBalPairs;  // pairs per kv head
+  const int r = (int)(blockIdx.x / p.Hkv) * kBalPairs + pair;
   const int T = p.T, B = p.B, rows = p.rows;
   const int pt = p.part_tokens / kTile;  // tiles per partition
 
   // ---- lengths, tile prefix sums and this kv head's q rows into LDS (the whole workgroup)
   {
-    int loc[4], sum = 0;
+    int loc[kBalSeqsPerThread], sum = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = 4 * tid + k;
+    for (int k = 0; k < kBalSeqsPerThread; ++k) {
+      const int s = kBalSeqsPerThread * tid + k;
       const int L = s < B ? (int)read_only(p.seq_lens)[s] : 0;
       loc[k] = L > 0 ? (L + kTile - 1) / kTile : 0;
       if (s < B) sh.len[s] = L;
       sum += loc[k];
     }
-    int incl = sum;  // inclusive scan over the wave, then over the waves
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
+    const int incl = wave_inclusive_sum(sum);  // over the wave, then over the waves
     if (lane == 63) sh.wsum[wave] = incl;
     for (int idx = tid; idx < B * rows * 16; idx += kBalWaves * 64) {
       const int s = idx / (rows * 16), n = (idx / 16) % rows, c = idx % 16;
@@ -105,8 +109,8 @@ void balanced_kernel(const DecodeParams p) {
     for (int w = 0; w < wave; ++w) base += sh.wsum[w];
     int run_sum = base + incl - sum;  // exclusive prefix of this thread's first sequence
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = 4 * tid + k;
+    for (int k = 0; k < kBalSeqsPerThread; ++k) {
+      const int s = kBalSeqsPerThread * tid + k;
       if (s <= B) sh.pre[s] = run_sum;
       run_sum += loc[k];
     }
@@ -115,32 +119,51 @@ void balanced_kernel(const DecodeParams p) {
   }
   const int N = sh.pre[B];
   const int R = min(W, max(1, N / pt));
-  if (r >= R) return;  // no barrier below this point
-  const int t0 = (int)((int64_t)r * N / R), t1 = (int)((int64_t)(r + 1) * N / R);
-  if (t1 <= t0) return;
-
+  // range of tile t < N: the largest r with floor(r N / R) <= t
+  auto range_of = [&](int t) { return (int)(((int64_t)(t + 1) * R - 1) / N); };
   auto pre_at = [&](int s) { return __builtin_amdgcn_readfirstlane(sh.pre[s]); };
   auto len_at = [&](int s) { return __builtin_amdgcn_readfirstlane(sh.len[s]); };
+
+  // slot counts for the merge, one per sequence (every kv head has the same ranges): written once
+  if (blockIdx.x == 0) {
+    for (int s = tid; s < B; s += kBalWaves * 64) {
+      const int a = sh.pre[s], b = sh.pre[s + 1];
+      p.slot_counts[s] = b > a ? 2 * (range_of(b - 1) - range_of(a) + 1) : 0;
+    }
+  }
+  const int t0 = r < R ? (int)((int64_t)r * N / R) : 0;
+  const int t1 = r < R ? (int)((int64_t)(r + 1) * N / R) : 0;
+  if (side == 0 && lane == 0)
+    sh.cursor[pair] = (unsigned long long)(uint32_t)t0 | ((unsigned long long)(uint32_t)t1 << 32);
+  __syncthreads();
+  if (t1 <= t0) return;  // no barrier below this point
+
   // sequence of tile t: the largest s with pre[s] <= t (empty sequences are passed over)
-  int s_first = 0;
-  {
+  auto seq_of = [&](int t) {
     int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pre_at(mid) <= t0) lo = mid; else hi = mid;
+      if (pre_at(mid) <= t) lo = mid; else hi = mid;
     }
-    s_first = lo;
-  }
-  struct Cursor {
-    int s, beg, end, L;  // sequence, its tiles [beg, end) in the list, its length
+    return lo;
   };
-  auto advance = [&](Cursor& c, int t) {
-    while (t >= c.end) {
-      ++c.s;
-      c.beg = c.end;
-      c.end = pre_at(c.s + 1);
-      c.L = len_at(c.s);
-    }
+
+  // The next tile of this wave from the pair's shared word, or -1 once the two ends have met. The
+  // front wave adds 1 to the low word and takes the old front; the back wave adds -1 to the high
+  // word and takes the old back - 1; a tile is taken when the old front < the old back, compared as
+  // signed words (the back may pass below 0 after the last take). Each wave stops at its first
+  // miss, so the front wave's tiles are [t0, m) and the back wave's [m, t1) for one m.
+  auto grab_issue = [&]() -> uint64_t {
+    uint64_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&sh.cursor[pair], side == 0 ? 1ull : 0xFFFFFFFF00000000ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    return old;
+  };
+  auto grab_take = [&](uint64_t old) -> int {
+    const int f = __builtin_amdgcn_readfirstlane((int)(uint32_t)old);
+    const int b = __builtin_amdgcn_readfirstlane((int)(uint32_t)(old >> 32));
+    return f < b ? (side == 0 ? f : b - 1) : -1;
   };
 
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kKvRow;
@@ -149,7 +172,7 @@ void balanced_kernel(const DecodeParams p) {
   lds_char* vt = (lds_char*)sh.vt[wave];
 
   struct Meta {
-    int s, j, L, blk;
+    int t, s, j, L, blk;  // t < 0: no tile
     float ks, vs;
   };
   struct TileRegs {
@@ -159,16 +182,31 @@ void balanced_kernel(const DecodeParams p) {
   const uint32_t k_lane_off = Q8 ? c16 * kD + 32 * g : c16 * kRowBytes + g * 16;
   const uint32_t v_lane_off = Q8 ? (lane >> 2) * kD + 32 * (lane & 3) : lane * 16;
 
-  // Block id and scales of tile t of the load cursor's sequence, then its loads.
-  auto meta_of = [&](const Cursor& c, int t) -> Meta {
+  // Block id and scales of tile t; the lookup cursor only moves one way (forward or backward).
+  int lk_s = seq_of(side == 0 ? t0 : t1 - 1);
+  int lk_beg = pre_at(lk_s), lk_end = pre_at(lk_s + 1);
+  auto meta_of = [&](int t) -> Meta {
     Meta m;
-    m.s = c.s;
-    m.j = t - c.beg;
-    m.L = c.L;
-    const auto* trow = read_only(p.block_tables + (int64_t)c.s * p.MB);
+    m.t = t;
+    m.s = m.j = m.L = m.blk = 0;
+    m.ks = m.vs = 1.f;
+    if (t < 0) return m;
+    while (t >= lk_end) {
+      ++lk_s;
+      lk_beg = lk_end;
+      lk_end = pre_at(lk_s + 1);
+    }
+    while (t < lk_beg) {
+      --lk_s;
+      lk_end = lk_beg;
+      lk_beg = pre_at(lk_s);
+    }
+    m.s = lk_s;
+    m.j = t - lk_beg;
+    m.L = len_at(lk_s);
+    const auto* trow = read_only(p.block_tables + (int64_t)lk_s * p.MB);
     // the id is clamped into the pool: a table entry past the length is never used for the result
     m.blk = (int)min((uint32_t)trow[min(m.j * kTile / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-    m.ks = m.vs = 1.f;
     if constexpr (Q8) {
       const f32x2 sc = read_only(reinterpret_cast<const f32x2*>(p.scales))[(int64_t)m.blk * p.Hkv + kvh];
       m.ks = sc[0];
@@ -211,7 +249,7 @@ void balanced_kernel(const DecodeParams p) {
     }
   };
 
-  // ---- the compute cursor's sequence: q operand, row limits
+  // ---- the computed piece's sequence: q operand, row limits
   int cs = -1, L_c = 0, vis_all = 0, row_lim = -1, row_tok = 0;
   u32x4 qb[4];
   float qsum = 0.f, qk_mul = p.qk_scale_log2;
@@ -277,6 +315,8 @@ void balanced_kernel(const DecodeParams p) {
   f32x4 acc[8];
   bool have_ref = false;
   auto clear = [&]() {
+    m_ref = kNegInf;
+    have_ref = false;
     l_part = 0.f;
     vcorr = 0.f;
 #pragma unroll
@@ -320,11 +360,27 @@ void balanced_kernel(const DecodeParams p) {
     }
     return c;
   };
-  auto raise_ref = [&](const f32x4& s) {
+  // the row max of s, on every lane of the row's column c16
+  auto row_max = [&](const f32x4& s) {
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    m_ref = fmaxf(m_ref, mx);
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  };
+  // A score above the reference by more than 2^64: the row's reference becomes its max, and l, the V
+  // offset weight and the accumulator row are rescaled by 2^(old - new) (accumulator row 4g + e of a
+  // lane takes the factor of lane 4g + e, whose column c16 is that row).
+  auto rescale = [&](const f32x4& s) {
+    const float m_new = fmaxf(m_ref, row_max(s));
+    const float f = exp2_fast(m_ref - m_new);
+    l_part *= f;
+    vcorr *= f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float fe = __shfl(f, 4 * g + e, 64);
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) acc[jb][e] *= fe;
+    }
+    m_ref = m_new;
   };
   // P.V of one tile: probabilities split into bf16 hi + lo parts, V through the swizzled LDS tile.
   auto accumulate = [&](bool masked, int tile_p0, const f32x4& s, const TileRegs& tr, float vscale) {
@@ -374,10 +430,12 @@ void balanced_kernel(const DecodeParams p) {
     wave_lds_order();
   };
 
-  // The partial of the piece [seg_i0, i_end) of sequence cs: slot 2k (the piece starts its partition)
-  // or 2k + 1; a piece that is its whole partition also marks slot 2k + 1 empty.
-  int seg_i0 = t0, seg_j0 = 0;
-  auto flush = [&](int i_end) {
+  auto out_row = [&](int s, int n) -> int64_t { return (int64_t)(s * T + n / p.G) * p.Hq + kvh * p.G + n % p.G; };
+  // slot of sequence s for this range and side; past the workspace's slots (lengths beyond the
+  // call's max_seq_len) nothing is written
+  auto slot_of = [&](int s) { return 2 * (r - range_of(pre_at(s))) + side; };
+  // This wave's partial of sequence cs (its piece) into the sequence's slot for this range and side.
+  auto flush = [&]() {
     if constexpr (Q8 && !F8) {  // remove the V offset: accumulator row 4g + e held 128 * sum(scaled P)
       float tot = vcorr;
       tot += __shfl_xor(tot, 16, 64);
@@ -389,119 +447,124 @@ void balanced_kernel(const DecodeParams p) {
         for (int jb = 0; jb < 8; ++jb) acc[jb][e] -= ce;
       }
     }
-    const int k = seg_j0 / pt;
-    const bool starts = seg_j0 % pt == 0;
-    const int j_last = i_end - 1 - pre_at(cs);
-    const int ntiles = pre_at(cs + 1) - pre_at(cs);
-    const bool whole = starts && ((j_last + 1) % pt == 0 || j_last + 1 == ntiles);
-    const int slot = 2 * k + (starts ? 0 : 1);
-    auto out_row = [&](int n) -> int64_t { return (int64_t)(cs * T + n / p.G) * p.Hq + kvh * p.G + n % p.G; };
+    const int slot = slot_of(cs);
+    if (slot >= p.parts) return;
     float l = l_part;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (g == 0 && present) {
-      const int64_t pi = out_row(c16) * p.parts + slot;
-      *reinterpret_cast<f32x2*>(p.part_ml + pi * 2) = f32x2{m_ref, l};
-      if (whole) *reinterpret_cast<f32x2*>(p.part_ml + (pi + 1) * 2) = f32x2{kNegInf, 0.f};
-    }
+    if (g == 0 && present)
+      *reinterpret_cast<f32x2*>(p.part_ml + (out_row(cs, c16) * p.parts + slot) * 2) = f32x2{m_ref, l};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int na = 4 * g + e;
       if (na < rows) {
-        float* dst = p.part_acc + (out_row(na) * p.parts + slot) * kD + c16;
+        float* dst = p.part_acc + (out_row(cs, na) * p.parts + slot) * kD + c16;
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb) dst[16 * jb] = acc[jb][e];
       }
     }
   };
 
-  const int last = t1 - 1;
-  // Tiles [ib, t1) of the current piece onwards. Returns -1 when done, or the first tile of the piece
-  // to run again when a score outran the reference (raised by then).
-  auto run = [&](int ib) -> int {
-    ib = __builtin_amdgcn_readfirstlane(ib);
-    clear();
+  // ---- the pipeline: loads run PF tiles ahead of the tile computed, block ids one tile before their
+  // loads, and grabs one tile before that. Past this wave's last tile the loads re-read its last
+  // tile, so every step issues the same loads.
+  int lo_tile = INT32_MAX, hi_tile = -1;  // this wave's part of the range, as it is taken
+  {
     TileRegs ring[NBUF];
     Meta meta[NBUF];
-    Cursor lc = {cs, pre_at(cs), pre_at(cs + 1), L_c};
+    meta[0] = meta_of(grab_take(grab_issue()));
+    if (meta[0].t >= 0) {
+      Meta last_valid = meta[0];
+      load_tile(meta[0], ring[0]);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int ti = min(ib + u, last);
-      advance(lc, ti);
-      meta[u] = meta_of(lc, ti);
-      load_tile(meta[u], ring[u]);
-    }
-    // block ids (and scales) are fetched one tile before the loads that need them
-    advance(lc, min(ib + PF, last));
-    Meta m_next = meta_of(lc, min(ib + PF, last));
-    int again = -1;
-    for (int i0 = ib; i0 < t1 && again < 0; i0 += NBUF) {
+      for (int u = 1; u < PF; ++u) {
+        meta[u] = meta_of(meta[u - 1].t >= 0 ? grab_take(grab_issue()) : -1);
+        if (meta[u].t >= 0) last_valid = meta[u];
+        load_tile(last_valid, ring[u]);
+      }
+      Meta m_next = meta_of(meta[PF - 1].t >= 0 ? grab_take(grab_issue()) : -1);
+      int t_pending = m_next.t >= 0 ? grab_take(grab_issue()) : -1;
+      for (bool more = true; more;) {
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int i = i0 + u;
-        if (i < t1 && again < 0) {
-          const Meta m = meta[u];
-          {
-            meta[(u + PF) % NBUF] = m_next;
-            load_tile(m_next, ring[(u + PF) % NBUF]);
-            const int ti = min(i + PF + 1, last);
-            advance(lc, ti);
-            m_next = meta_of(lc, ti);
-          }
-          if (i != seg_i0 && (m.s != cs || m.j % pt == 0)) {  // a new piece starts at tile i
-            flush(i);
-            if (m.s != cs) switch_seq(m.s);
-            seg_i0 = i;
-            seg_j0 = m.j;
-            m_ref = kNegInf;
-            have_ref = false;
-            clear();
-          }
-          const int tile_p0 = m.j * kTile;
-          const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
-          const f32x4 s = scores(masked, tile_p0, ring[u], m.ks);
-          if (!have_ref) {
-            raise_ref(s);
-            have_ref = true;
-          } else {
-            bool over = false;
+        for (int u = 0; u < NBUF; ++u) {
+          if (more) {
+            const Meta m = meta[u];
+            if (m.t < 0) {
+              more = false;
+            } else {
+              // the loads PF tiles ahead, the block ids of the tile after, the grab of the one after that
+              if (m_next.t >= 0) last_valid = m_next;
+              meta[(u + PF) % NBUF] = m_next;
+              load_tile(last_valid, ring[(u + PF) % NBUF]);
+              m_next = meta_of(t_pending);
+              const bool grab_live = t_pending >= 0;
+              const uint64_t raw = grab_live ? grab_issue() : 0ull;
+
+              lo_tile = min(lo_tile, m.t);
+              hi_tile = max(hi_tile, m.t);
+              if (m.s != cs) {  // a new piece: this wave's tiles of another sequence
+                if (cs >= 0) flush();
+                switch_seq(m.s);
+                clear();
+              }
+              const int tile_p0 = m.j * kTile;
+              const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
+              const f32x4 s = scores(masked, tile_p0, ring[u], m.ks);
+              if (!have_ref) {
+                m_ref = row_max(s);  // the piece's first tile sets the reference
+                have_ref = true;
+              } else {
+                bool over = false;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) over |= s[e] > m_ref + kRefSlack;
-            if (__builtin_expect(__any(over), 0)) {
-              raise_ref(s);
-              again = seg_i0;
+                for (int e = 0; e < 4; ++e) over |= s[e] > m_ref + kRefSlack;
+                if (__builtin_expect(__any(over), 0)) rescale(s);
+              }
+              accumulate(masked, tile_p0, s, ring[u], m.vs);
+              t_pending = grab_live ? grab_take(raw) : -1;
             }
           }
-          accumulate(masked, tile_p0, s, ring[u], m.vs);
         }
       }
+      flush();
     }
-    return again;
-  };
-
-  switch_seq(s_first);
-  seg_i0 = t0;
-  seg_j0 = t0 - pre_at(s_first);
-  for (int from = t0; (from = run(from)) >= 0;) {
   }
-  flush(t1);
+
+  // ---- empty slots: the sequences of the range that this wave's part does not touch. The front
+  // part is [t0, hi_tile], the back part [lo_tile, t1 - 1].
+  {
+    int skip_lo = seq_of(t0), skip_hi = seq_of(t1 - 1);
+    if (hi_tile >= 0) {
+      if (side == 0)
+        skip_lo = seq_of(hi_tile) + 1;  // the sequences after the front part's last
+      else
+        skip_hi = seq_of(lo_tile) - 1;  // the sequences before the back part's first
+    }
+    for (int s = skip_lo; s <= skip_hi; ++s) {
+      if (pre_at(s + 1) == pre_at(s)) continue;  // an empty sequence has no slots
+      const int slot = slot_of(s);
+      if (slot < p.parts && g == 0 && present)
+        *reinterpret_cast<f32x2*>(p.part_ml + (out_row(s, c16) * p.parts + slot) * 2) = f32x2{kNegInf, 0.f};
+    }
+  }
 
   if constexpr (AP) {
     // the new rows (positions L - T .. L - 1) whose tiles this wave walked go to their pool slots
-    for (int s = s_first; s < B && pre_at(s) < t1; ++s) {
-      const int L = len_at(s);
-      const auto* trow = read_only(p.block_tables + (int64_t)s * p.MB);
-      for (int t = max(0, T - L); t < T; ++t) {
-        const int pos = L - T + t;
-        const int tile = pre_at(s) + pos / kTile;
-        if (tile < t0 || tile >= t1) continue;
-        const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
-        if (lane < 32) {
-          const int which = lane >> 4, chunk = lane & 15;
-          const int64_t dst = (int64_t)blk * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
-          const char* src = static_cast<const char*>(which ? p.v_new : p.k_new) +
-                            ((int64_t)(s * T + t) * p.Hkv + kvh) * kRowBytes + chunk * 16;
-          *reinterpret_cast<u32x4*>(const_cast<char*>(which ? vbase : kbase) + dst) = load16(src);
+    if (hi_tile >= 0) {
+      for (int s = seq_of(lo_tile); s < B && pre_at(s) <= hi_tile; ++s) {
+        const int L = len_at(s);
+        const auto* trow = read_only(p.block_tables + (int64_t)s * p.MB);
+        for (int t = max(0, T - L); t < T; ++t) {
+          const int pos = L - T + t;
+          const int tile = pre_at(s) + pos / kTile;
+          if (tile < lo_tile || tile > hi_tile) continue;
+          const int blk = (int)min((uint32_t)trow[min(pos / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+          if (lane < 32) {
+            const int which = lane >> 4, chunk = lane & 15;
+            const int64_t dst = (int64_t)blk * block_bytes + (int64_t)(pos % BS) * kRowBytes + chunk * 16;
+            const char* src = static_cast<const char*>(which ? p.v_new : p.k_new) +
+                              ((int64_t)(s * T + t) * p.Hkv + kvh) * kRowBytes + chunk * 16;
+            *reinterpret_cast<u32x4*>(const_cast<char*>(which ? vbase : kbase) + dst) = load16(src);
+          }
         }
       }
     }
@@ -524,6 +587,19 @@ hipError_t launch_q(const DecodeParams& p, int grid, hipStream_t stream) {
   }
 }
 
+// Compute units of the current device (one workgroup each), read once per device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 
 bool balanced_supported(const pa_dims& d) {
@@ -534,14 +610,11 @@ bool balanced_supported(const pa_dims& d) {
          d.num_seqs <= kBalMaxSeqs && (int64_t)d.num_seqs * rows * kRowBytes <= kBalQBytes;
 }
 
-int balanced_waves() { return 1024 * kBalWavesPerSimd; }
-
 hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
-  // one wave per SIMD of the chip (256 CUs x 4 SIMDs) per resident round, shared out over the kv heads
-  const int per_head = max(kBalWaves, balanced_waves() / p.Hkv / kBalWaves * kBalWaves);
-  const int grid = p.Hkv * (per_head / kBalWaves);
-  if (p.append && p.kv_int8) return hipErrorInvalidValue;
+  if (!p.slot_counts || (p.append && p.kv_int8)) return hipErrorInvalidValue;
+  // one workgroup (4 pairs) per CU, shared out over the kv heads; at least one per kv head
+  const int grid = p.Hkv * max(1, device_cus() / p.Hkv);
   if (p.kv_int8)
     return p.kv_fp8 ? launch_q<true, true, false>(p, grid, stream) : launch_q<true, false, false>(p, grid, stream);
   return p.append ? launch_q<false, false, true>(p, grid, stream) : launch_q<false, false, false>(p, grid, stream);

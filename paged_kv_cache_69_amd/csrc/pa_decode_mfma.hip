@@ -207,11 +207,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   const int g = lane >> 4;    // 16-lane group
   const int c16 = lane & 15;  // column inside the group
 
-  // Single pass: block = seq * Hkv + kvh. Split context: block = (seq * groups + cg) * Hkv + kvh, wave w
-  // owning partition cg * NW + w of the sequence's own partitions (the slots after the prefix_parts
-  // prefix slots). Cascade prefix items: `seq` is a group of ROWS query rows over all sequences and
-  // the wave owns prefix partition cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks
-  // are dealt round-robin to the 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
+  // Single pass: block = seq * Hkv + kvh. Split context: block = j * Hkv + kvh, where j counts the
+  // (sequence, group cg) pairs that hold work (see below), wave w owning item cg * NW + w of the
+  // sequence's own partitions (the slots after the prefix_parts prefix slots). Cascade prefix items:
+  // `seq` is a group of ROWS query rows over all sequences and the wave owns prefix partition
+  // cg * NW + w. Consecutive blocks are consecutive kv heads, and blocks are dealt round-robin to the
+  // 8 XCDs, so with Hkv = 8 one kv head's blocks share an L2.
   int bid = block;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
@@ -223,12 +224,26 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
                          : CASCADE ? (p.prefix_tokens + p.prefix_part_tokens - 1) / p.prefix_part_tokens
                                    : (p.parts - p.prefix_parts + KP - 1) / KP;
   const int groups = WAVE_ITEMS ? (item_parts + NW - 1) / NW : 1;
-  const int cg = bid % groups;
+  int cg = bid % groups;
+  int seq = bid / groups;
+  int L_item = 0;  // split items: the sequence's length, found with it
+  if constexpr (WAVE_ITEMS && !CASCADE) {
+    // Split items are packed: workgroup index j (per kv head) is the j-th (sequence, group of NW
+    // items) that holds work, sequence by sequence, and the grid's bound on their number leaves
+    // only its tail empty. The dispatcher deals an XCD's workgroups to its shader engines in strict
+    // rotation and waits when the next one's engine is full, so empty workgroups spread through the
+    // grid would pile the real ones onto some engines while others idle.
+    const int pt = p.part_tokens, pre = p.prefix_tokens, cap = p.parts - p.prefix_parts;
+    auto count = [&](int len) {  // capped at the workspace's partitions, like the grid's bound
+      const int own_parts = min(cap, max(0, (len - pre + pt - 1) / pt));
+      return ((own_parts + KP - 1) / KP + NW - 1) / NW;
+    };
+    if (!find_item(p.seq_lens, p.B, bid, count, seq, cg, L_item)) return;
+  }
   // Longest first (p.lpt, single pass): when the grid takes several rounds of workgroups, the j-th
   // workgroup of each kv head takes the sequence of length rank j (ties by index), so the rounds end
   // with the short sequences and the last workgroups to start are the quickest to finish. The ranking
   // reads every length once through LDS, past the V tiles' part of it.
-  int seq = bid / groups;
   if constexpr (!WAVE_ITEMS && !CASCADE) {
     if (p.lpt) {
       int* lens = reinterpret_cast<int*>(lds + NW * kTileBytes);  // [kLptMaxSeqs], then the winner
@@ -376,7 +391,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     return ids;
   };
   const TileIds ids0 = ids_of(0);
-  const int L = CASCADE ? p.prefix_tokens : read_only(p.seq_lens)[seq];  // prefix items: every prefix position is visible
+  // prefix items: every prefix position is visible
+  const int L = CASCADE ? p.prefix_tokens : WAVE_ITEMS ? L_item : read_only(p.seq_lens)[seq];
   // an empty split partition's wave leaves (the merge never reads its slot); a prefix item's wave with
   // no chunk stays for the workgroup's merge, with nothing to add
   if (WAVE_ITEMS && !CASCADE && (part_local >= item_parts || p_begin >= L)) return;

@@ -56,6 +56,46 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele through lane shuffles).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Item `item` of a list in which sequence s (s < B, in order) owns count(L_s) consecutive items, L_s =
+// lens[s]: sets seq, the item's rank inside its sequence and L, all wave-uniform, and returns false
+// when the list has fewer than item + 1 items. One lens entry per lane, 64 sequences per step, the
+// next step's lengths loaded while this step's counts are summed.
+template <typename Count>
+__device__ __forceinline__ bool find_item(const int32_t* lens, int B, int item, Count count, int& seq, int& rank,
+                                          int& L) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  int len = lane < B ? lens[lane] : 0;
+  for (int base = 0; base < B; base += 64) {
+    const int next = base + 64 + lane < B ? lens[base + 64 + lane] : 0;
+    const int c = base + lane < B ? count(len) : 0;
+    const int incl = wave_inclusive_sum(c);
+    const int excl = incl - c;
+    const uint64_t hit = __ballot(c > 0 && item >= carry + excl && item < carry + incl);
+    if (hit) {
+      const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      seq = base + l;
+      rank = __builtin_amdgcn_readfirstlane(item - carry - __shfl(excl, l, 64));
+      L = __builtin_amdgcn_readfirstlane(__shfl(len, l, 64));
+      return true;
+    }
+    carry += __shfl(incl, 63, 64);
+    len = next;
+  }
+  return false;
+}
+
 // Raw buffer descriptor for `bytes` bytes at a wave-uniform `base` (gfx9 format word 0x00020000).
 // Loads through it take a 32-bit lane offset, so no 64-bit vector address is formed per load, and
 // any offset at or past `bytes` reads zeros instead of touching memory.

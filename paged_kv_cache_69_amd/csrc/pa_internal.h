@@ -41,7 +41,8 @@ struct DecodeParams {
   int32_t prefix_part_tokens;  // cascade: positions of the prefix per chunk (one wave's share)
   int32_t lpt;               // single pass on the MFMA kernel: sequences dealt longest first
   int32_t wave_parts;        // split launches on the MFMA kernel: consecutive partitions per wave (<= 1: one)
-  int32_t slots_per_part;    // split launches: workspace slots per partition (2: balanced ranges, else 1)
+  int32_t* slot_counts;      // balanced ranges: [B] slots each sequence's rows use (the merge reads them);
+                             // null otherwise (one slot per partition)
 };
 
 hipError_t launch_write_kv(const pa_dims& d, const void* k_new, const void* v_new, void* k_pool,

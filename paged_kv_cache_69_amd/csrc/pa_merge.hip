@@ -59,10 +59,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Dec
     v[j] = ml[k];
     a[j] = *reinterpret_cast<const f32x4*>(acc + (int64_t)k * D);
   }
-  const int L = p.seq_lens[row / ((int64_t)p.T * p.Hq)];
-  // slots written: the shared prefix's (cascade), then one per partition of the sequence's own positions
-  // (two per partition after balanced ranges: the partition's two pieces, or its partial and an empty pair)
-  const int own = max(0, (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens) * p.slots_per_part;
+  const int64_t seq = row / ((int64_t)p.T * p.Hq);
+  const int L = p.seq_lens[seq];
+  // slots written: the shared prefix's (cascade), then one per partition of the sequence's own positions,
+  // or, after balanced ranges, the count that kernel wrote for the sequence
+  const int own = p.slot_counts ? p.slot_counts[seq] : max(0, (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens);
   const int nparts = row_raw < rows && L > 0 ? min(p.parts, p.prefix_parts + own) : 0;
 
   // M = max m_k over partitions with l_k > 0, then l = sum l_k 2^(m_k - M)
@@ -141,6 +142,9 @@ hipError_t launch_d(const DecodeParams& p, int64_t rows, hipStream_t stream) {
   // Rows per workgroup: a row's threads load up to 8 partitions per slot in one go, so one wave per row
   // (2 slots for D = 128) covers 16 partitions; more partitions get more of the workgroup.
   constexpr int LPC = D / 4;
+  // balanced ranges: the workspace rows hold 2P + 2 slots, but a row uses about two per range of its
+  // sequence; two rows per workgroup prefetch 32 slots each and loop past that
+  if (p.slot_counts) return launch_rpw<D, 2>(p, rows, stream);
   if (p.parts * LPC > 8 * kMergeThreads) return launch_rpw<D, 1>(p, rows, stream);
   if (p.parts * LPC > 4 * kMergeThreads) return launch_rpw<D, 2>(p, rows, stream);
   return launch_rpw<D, 4>(p, rows, stream);

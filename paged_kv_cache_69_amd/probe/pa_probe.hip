@@ -1,6 +1,8 @@
 // Measurement probes of libpa_probe.so (declared in include/pa_probe.h): a streaming-read kernel, the
-// ceiling HBM reads reach on this GPU, and the dependent loads in front of a decode workgroup's first
-// tile, the latency floor of a decode launch. Neither is part of the decode path.
+// ceiling HBM reads reach on this GPU; a paged read of every K/V block a decode call reads, through the
+// same block tables with no arithmetic, the ceiling of that access pattern; and the dependent loads in
+// front of a decode workgroup's first tile, the latency floor of a decode launch. None of them is part
+// of the decode path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,6 +73,82 @@ __global__ __launch_bounds__(256) void first_tile_kernel(const ChainParams p) {
   store_xor(fold(acc) ^ (uint32_t)L, p.out + blockIdx.x);
 }
 
+struct PagedParams {
+  const char* k_pool;
+  const char* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t hkv, mb, nblocks, bs, blocks_per_wave, groups;
+  uint32_t* out;
+};
+
+template <int NT>
+__device__ __forceinline__ u32x4 load_policy(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+// One workgroup of 4 waves per (sequence, group of 4 * blocks_per_wave blocks, kv head), the kv head
+// fastest; wave w reads blocks [j0, j0 + blocks_per_wave) of its group, U blocks (K and V rows of its
+// kv head, NL 16-byte loads per lane each) in flight per step, through the table. A wave past the
+// sequence's last block leaves. Each wave folds what it read into the workgroup's XOR.
+template <int U, int NL, int NT>
+__global__ __launch_bounds__(256) void paged_read_kernel(const PagedParams p) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bid = blockIdx.x;
+  const int kvh = bid % p.hkv;
+  bid /= p.hkv;
+  const int grp = bid % p.groups, seq = bid / p.groups;
+  const int32_t* row = p.tables + (int64_t)seq * p.mb;
+  const int nb = min((p.lens[seq] + p.bs - 1) / p.bs, p.mb);
+  const int j0 = (grp * 4 + w) * p.blocks_per_wave, j1 = min(nb, j0 + p.blocks_per_wave);
+  const int64_t tile = (int64_t)NL * 1024;  // bytes of one block's rows of one kv head
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int j = j0; j < j1; j += U) {
+    u32x4 v[U][2 * NL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = (int)min((uint32_t)row[min(j + u, j1 - 1)], (uint32_t)(p.nblocks - 1));
+      const int64_t off = ((int64_t)blk * p.hkv + kvh) * tile + lane * 16;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        v[u][l] = load_policy<NT>(reinterpret_cast<const u32x4*>(p.k_pool + off + l * 1024));
+        v[u][NL + l] = load_policy<NT>(reinterpret_cast<const u32x4*>(p.v_pool + off + l * 1024));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j + u < j1) {
+#pragma unroll
+        for (int l = 0; l < 2 * NL; ++l) acc ^= v[u][l];
+      }
+  }
+  store_xor(fold(acc), p.out + blockIdx.x);
+}
+
+template <int U, int NT>
+hipError_t launch_paged_u(const PagedParams& p, int nl, dim3 grid, hipStream_t s) {
+  switch (nl) {
+    case 1: paged_read_kernel<U, 1, NT><<<grid, dim3(256), 0, s>>>(p); break;
+    case 2: paged_read_kernel<U, 2, NT><<<grid, dim3(256), 0, s>>>(p); break;
+    case 4: paged_read_kernel<U, 4, NT><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: paged_read_kernel<U, 8, NT><<<grid, dim3(256), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_paged(const PagedParams& p, int nl, int unroll, dim3 grid, hipStream_t s) {
+  switch (unroll) {
+    case 1: return launch_paged_u<1, NT>(p, nl, grid, s);
+    case 2: return launch_paged_u<2, NT>(p, nl, grid, s);
+    case 4: return launch_paged_u<4, NT>(p, nl, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +184,30 @@ int pa_probe_first_tile(const void* k_pool, const void* v_pool, const int32_t* b
   first_tile_kernel<<<dim3((unsigned)((int64_t)num_seqs * num_kv_heads)), dim3(256), 0,
                       reinterpret_cast<hipStream_t>(stream)>>>(p);
   return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int pa_probe_paged_read(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks, int32_t num_blocks,
+                        int32_t block_size, int32_t row_bytes, int32_t blocks_per_wave, int32_t unroll,
+                        int32_t nontemporal, uint32_t* out, pa_probe_stream_t stream) {
+  if (!k_pool || !v_pool || !block_tables || !seq_lens || !out) return -1;
+  if (num_seqs < 1 || num_kv_heads < 1 || max_blocks < 1 || num_blocks < 1 || block_size < 1 || row_bytes < 1 ||
+      blocks_per_wave < 1)
+    return -1;
+  const int64_t block_bytes = (int64_t)block_size * row_bytes;  // one block's rows of one kv head
+  const int nl = (int)(block_bytes / 1024);
+  if (block_bytes % 1024 != 0 || (nl != 1 && nl != 2 && nl != 4 && nl != 8)) return -1;
+  const int32_t groups = (int32_t)(((int64_t)max_blocks + 4 * blocks_per_wave - 1) / (4 * blocks_per_wave));
+  const int64_t grid = (int64_t)num_seqs * groups * num_kv_heads;
+  if (grid > INT32_MAX) return -1;
+  const PagedParams p = {static_cast<const char*>(k_pool), static_cast<const char*>(v_pool), block_tables, seq_lens,
+                         num_kv_heads, max_blocks, num_blocks, block_size, blocks_per_wave, groups, out};
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const hipError_t e = nontemporal ? launch_paged<1>(p, nl, unroll, dim3((unsigned)grid), s)
+                                   : launch_paged<0>(p, nl, unroll, dim3((unsigned)grid), s);
+  if (e == hipErrorInvalidValue) return -1;
+  return e == hipSuccess ? 0 : -3;
 }
 
 }  // extern "C"

@@ -98,38 +98,46 @@ def test_empty_batch_is_a_no_op(lib):
 
 
 def test_partitioned_workspace_arithmetic(lib):
-    """rows = 16 * 32 = 512; P = ceil(32768 / 512) = 64 partitions: one slot per partition, two when the call
-    asks for balanced ranges (which these dims allow); 32 query rows per kv head allow none: one."""
+    """rows = 16 * 32 = 512; P = ceil(32768 / 512) = 64 partitions: 2P + 2 slots and 16 int32 slot counts when
+    the call runs balanced ranges (asked for, or chosen: 16 * 8 * 64 > 2048 partitions), one slot per
+    partition otherwise; 32 query rows per kv head allow no balanced ranges: one slot per partition."""
     align = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    for sched, slots in ((0, 64), (2, 64), (3, 128)):
+    for sched, slots, counts in ((0, 130, align(16 * 4)), (1, 64, 0), (2, 64, 0), (3, 130, align(16 * 4))):
         d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=sched)
-        want = align(512 * slots * 2 * 4) + align(512 * slots * 128 * 4)
+        want = align(512 * slots * 2 * 4) + align(512 * slots * 128 * 4) + counts
         assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 32768, 512) == want
     d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, split_schedule=3)
     rows32 = 16 * 4 * 64
     want32 = align(rows32 * 64 * 2 * 4) + align(rows32 * 64 * 128 * 4)
     assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d32), 32768, 512) == want32
     d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
+    # a small split (16 * 8 * 16 = 2048 partitions, one resident round) keeps one slot per partition
+    assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 16 * 512, 512) == \
+        align(512 * 16 * 2 * 4) + align(512 * 16 * 128 * 4)
     assert lib.pa_decode_partitioned_workspace_bytes(ctypes.byref(d), 0, 512) == 0
     assert lib.pa_decode_partitioned_workspace_bytes(None, 10, 512) == 0
 
 
 def test_partitioned_schedule_choice(lib):
-    """PA_SPLIT_AUTO: two partitions per wave once B * Hkv * ceil(max_seq_len / partition_tokens) > 2048
-    (bf16 pools, <= 16 rows per kv head), else one; balanced ranges only when asked for."""
+    """PA_SPLIT_AUTO, once B * Hkv * ceil(max_seq_len / partition_tokens) > 2048: balanced ranges where the
+    dims allow them, else two partitions per wave (bf16 pools, <= 16 rows per kv head); one otherwise."""
     d = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128)
     assert d.num_kv_heads == 8
     f = lambda dd, msl, pt: lib.pa_decode_partitioned_schedule(ctypes.byref(dd), msl, pt)  # noqa: E731
-    assert f(d, 32768, 512) == pa.SPLIT_TWO_PER_WAVE      # 16 * 8 * 64 = 8192 partitions
+    assert f(d, 32768, 512) == pa.SPLIT_BALANCED      # 16 * 8 * 64 = 8192 partitions
     assert f(d, 16 * 512, 512) == pa.SPLIT_ONE_PER_WAVE  # 16 * 8 * 16 = 2048: one round already
-    assert f(d, 16 * 512 + 1, 512) == pa.SPLIT_TWO_PER_WAVE
+    assert f(d, 16 * 512 + 1, 512) == pa.SPLIT_BALANCED
+    d_b8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, block_size=8)  # b = 8: no balanced
+    assert f(d_b8, 32768, 512) == pa.SPLIT_TWO_PER_WAVE
     assert f(d, 0, 512) == -1 and f(d, 100, 0) == -1
     assert lib.pa_decode_partitioned_schedule(None, 100, 512) == -1
     d32 = _dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128)  # 32 rows per kv head
     assert f(d32, 32768, 512) == pa.SPLIT_ONE_PER_WAVE
-    for code in (pa.PA_INT8, pa.PA_FP8_E4M3):  # 8-bit pools: one partition per wave
+    for code in (pa.PA_INT8, pa.PA_FP8_E4M3):  # 8-bit pools: balanced, else one partition per wave
         d8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code)
-        assert f(d8, 32768, 512) == pa.SPLIT_ONE_PER_WAVE
+        assert f(d8, 32768, 512) == pa.SPLIT_BALANCED
+        assert f(_dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, kv_dtype=code, block_size=8),
+                 32768, 512) == pa.SPLIT_ONE_PER_WAVE
     big_b = _dims(num_seqs=1100, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3)  # too many to stage
     assert f(big_b, 4096, 512) == -2
     d_b8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, block_size=8, split_schedule=3)
@@ -147,7 +155,7 @@ def test_partitioned_schedule_override(lib, monkeypatch):
     assert f(_dims(**base, split_schedule=3)) == 3
     assert f(_dims(num_seqs=1, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3)) == 3
     monkeypatch.setenv("PA_SPLIT_WAVE_PARTS", "1")  # the variable of an earlier version: no effect
-    assert f(_dims(**base, split_schedule=0)) == 2
+    assert f(_dims(**base, split_schedule=0)) == 3
     for code in (pa.PA_INT8, pa.PA_FP8_E4M3):
         assert f(_dims(**base, kv_dtype=code, split_schedule=2)) == 1
     assert f(_dims(num_seqs=16, q_tokens=4, num_q_heads=64, head_dim=128, split_schedule=2)) == 1

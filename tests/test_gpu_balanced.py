@@ -1,12 +1,15 @@
 """The balanced split schedule (pa_dims.split_schedule = PA_SPLIT_BALANCED) against the float64 oracle, on
 the GPU.
 
-The tiles of every sequence of one kv head form one list cut into equal ranges, one per wave, so ranges
-cross sequences and cut partitions in two; each piece leaves its own partial (slot 2k or 2k + 1 of its
-partition) and a partition walked whole marks slot 2k + 1 empty. The workspace is filled beforehand with
+The tiles of every sequence of one kv head form one list cut into equal ranges, one per pair of waves,
+so ranges cross sequences; the two waves of a pair share their range from its two ends, each leaves
+one partial per sequence it touched (slot 2 (range - first range of the sequence) + side), and marks
+the slots of the range's other sequences empty. The workspace is filled beforehand with
 partials that look valid (m = 0, l = 1, acc = 1e6), so a slot the kernel failed to write would show in
 the output. Every case meets the oracle at the bar of its pool type; the fused append under this
-schedule equals the separate append followed by the same decode, bit for bit.
+schedule writes the pools bit for bit like the separate append, and its output meets the oracle too
+(the two waves of a pair meet where their timing puts them, so the pieces, and the rounding of their
+probabilities, may differ from call to call).
 """
 
 from __future__ import annotations
@@ -32,7 +35,7 @@ def _poisoned_workspace(pa, q, k_pool, tables, max_len, pt):
     f.fill_(1.0e6)
     rows = q.shape[0] * q.shape[1] * q.shape[2]
     parts = -(-max_len // pt)
-    ml = f[: rows * 2 * parts * 2].view(-1, 2)
+    ml = f[: rows * (2 * parts + 2) * 2].view(-1, 2)
     ml[:, 0] = 0.0
     ml[:, 1] = 1.0
     return ws
@@ -77,7 +80,9 @@ def test_balanced_bf16(gpu_lib, b, hq, hkv, t, pt):
                                     split_schedule=BAL)
     torch.cuda.synchronize()
     assert np.array_equal(bits(f["k_pool"]), kp) and np.array_equal(bits(f["v_pool"]), vp)
-    assert torch.equal(fused, out)
+    # the pair's meeting point follows the waves' timing, so the two calls may cut the pieces (and round
+    # their probabilities, relative to each piece's own reference) differently: each meets the oracle
+    assert_attention_close(fused.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what=f"fused pt={pt}")
 
 
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])

@@ -386,21 +386,22 @@ def test_full_size_sampled(gpu_lib, name, partitioned, variant):
 
 # ----------------------------------------------------------------------------- fused append + decode
 
-def _fused_vs_separate(pa, case, *, partition_tokens=None, variant_sep=MFMA):
+def _fused_vs_separate(pa, case, *, partition_tokens=None, variant_sep=MFMA, split_schedule=0):
     """Run pa_write_kv + decode and pa_write_kv_decode on copies of the same inputs; return both
     (pools, out) so callers can require bit identity."""
     a = _to_gpu(case)
     pa.write_kv(a["k_new"], a["v_new"], a["k_pool"], a["v_pool"], a["block_tables"], a["positions"])
     if partition_tokens:
         out_a = pa.decode_partitioned(a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["seq_lens"], case.scale,
-                                      case.max_seq_len, partition_tokens, variant=variant_sep)
+                                      case.max_seq_len, partition_tokens, variant=variant_sep,
+                                      split_schedule=split_schedule)
     else:
         out_a = pa.decode(a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["seq_lens"], case.scale,
                           variant=variant_sep)
     b = _to_gpu(case)
     out_b = pa.write_kv_decode(b["q"], b["k_new"], b["v_new"], b["k_pool"], b["v_pool"], b["block_tables"],
                                b["seq_lens"], case.scale, max_seq_len=case.max_seq_len if partition_tokens else None,
-                               partition_tokens=partition_tokens)
+                               partition_tokens=partition_tokens, split_schedule=split_schedule)
     torch.cuda.synchronize()
     return a, out_a, b, out_b
 
@@ -426,15 +427,24 @@ def test_fused_append_decode_bitwise(gpu_lib, b, hq, hkv, t):
                            out_dtype=torch.float32, what="fused")
 
 
-@pytest.mark.parametrize("name,pt", [("batch64", None), ("long", 512), ("spec", None)])
-def test_fused_append_decode_full_size_bitwise(gpu_lib, name, pt):
-    """Full workload sizes: the fused step equals the two separate calls bit for bit."""
+@pytest.mark.parametrize("name,pt,sched", [("batch64", None, 0), ("long", 512, 2), ("long", 512, 0), ("spec", None, 0)])
+def test_fused_append_decode_full_size_bitwise(gpu_lib, name, pt, sched):
+    """Full workload sizes: the fused step writes the pools bit for bit like the separate append, and its
+    output equals the separate decode's bit for bit on the schedules that give the same bits on every
+    call (single pass; long with two partitions per wave). Long under the library's choice runs balanced
+    ranges, whose pairs of waves meet where their timing puts them: there both outputs agree to well
+    inside the bf16 bar (every row of that call meets the oracle in the full-row tests)."""
     case = make_case(name, pool_device=DEV)
-    print(f"[case] fused full {name}", flush=True)
-    a, out_a, g, out_b = _fused_vs_separate(gpu_lib, case, partition_tokens=pt)
+    print(f"[case] fused full {name} schedule={sched}", flush=True)
+    a, out_a, g, out_b = _fused_vs_separate(gpu_lib, case, partition_tokens=pt, split_schedule=sched)
     assert torch.equal(a["k_pool"].view(torch.int16), g["k_pool"].view(torch.int16))
     assert torch.equal(a["v_pool"].view(torch.int16), g["v_pool"].view(torch.int16))
-    assert torch.equal(out_a, out_b)
+    if pt and sched == 0:
+        assert gpu_lib.split_schedule(case.q, case.k_pool, case.block_tables, case.max_seq_len, pt) == \
+            gpu_lib.SPLIT_BALANCED
+        assert (out_a - out_b).abs().max().item() < 1e-4
+    else:
+        assert torch.equal(out_a, out_b)
 
 
 def test_fused_append_decode_refuses_unsupported(gpu_lib):

@@ -25,7 +25,7 @@ def _declared():
 
 def test_probe_library_exports_every_declared_function():
     lib = bench.probe_library()
-    assert _declared() == ["pa_probe_first_tile", "pa_probe_stream_read"]
+    assert _declared() == ["pa_probe_first_tile", "pa_probe_paged_read", "pa_probe_stream_read"]
     for name in _declared():
         assert hasattr(lib, name), name
 
@@ -38,6 +38,11 @@ def test_probe_arguments_rejected_without_a_launch():
     assert lib.pa_probe_stream_read(fake, 1024, 0, 4, out, None) == -1
     assert lib.pa_probe_first_tile(fake, fake, fake, fake, 4, 8, 4, 10, 16, 100, 0, out, None) == -1  # row bytes
     assert lib.pa_probe_first_tile(fake, fake, fake, fake, 4, 8, 4, 10, 64, 512, 0, out, None) == -1  # tile > 16 KiB
+    # paged read: a block of 16 rows of 100 bytes is not 1, 2, 4 or 8 KiB; no such unroll; no blocks per wave
+    assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 16, 100, 16, 2, 0, out, None) == -1
+    assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 16, 256, 16, 3, 0, out, None) == -1
+    assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 16, 256, 0, 2, 0, out, None) == -1
+    assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 64, 256, 16, 2, 0, out, None) == -1  # 16 KiB
 
 
 def test_stream_terms_model():
@@ -48,6 +53,11 @@ def test_stream_terms_model():
         bench._STREAM = None
     assert t["frac_of_stream"] == 0.5 and t["floor_us"] == 5.0
     assert t["model_us"] == pytest.approx(5.0 + 10.0) and t["over_model"] == pytest.approx(1.0)
+    assert "frac_of_paged_read" not in t
+    # with the paged-read rate: 50 MB at 4000 GB/s is 12.5 us, plus the 5 us floor
+    t = bench.stream_terms(2500.0, 50_000_000, 35.0, {"floor_us": 5.0, "paged_read_gbps": 4000.0})
+    assert "frac_of_stream" not in t and t["frac_of_paged_read"] == 0.625
+    assert t["paged_model_us"] == pytest.approx(17.5) and t["over_paged_model"] == pytest.approx(2.0)
 
 
 def _xor(t):
@@ -95,3 +105,35 @@ def test_first_tile_reads_each_workgroups_first_blocks(gpu_lib, dependent):
                 blk = min(int(case.block_tables[i, j]) & 0xFFFFFFFF, n - 1)
                 want ^= _xor(case.k_pool[blk, h_]) ^ _xor(case.v_pool[blk, h_]) ^ (L & 0xFFFFFFFF)
             assert (int(out[i * hkv + h_]) & 0xFFFFFFFF) == want, (i, h_)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("bpw,unroll,nt", [(1, 1, 0), (3, 2, 1), (16, 4, 0)])
+def test_paged_read_reads_every_block_once(gpu_lib, bpw, unroll, nt):
+    """Each workgroup's XOR is the XOR of the K and V rows of exactly its blocks: blocks
+    [4 * bpw * grp, 4 * bpw * (grp + 1)) of its sequence, cut at ceil(L / b)."""
+    from workloads import make_case
+
+    case = make_case("batch64", num_seqs=7)
+    lib = bench.probe_library()
+    n, hkv, bs, d = case.k_pool.shape
+    mb = case.block_tables.shape[1]
+    groups = -(-mb // (4 * bpw))
+    g = {k: getattr(case, k).to("cuda:0") for k in ("k_pool", "v_pool", "block_tables", "seq_lens")}
+    out = torch.zeros(7 * groups * hkv, dtype=torch.int32, device="cuda:0")
+    print(f"[case] paged read bpw={bpw} unroll={unroll} nt={nt}", flush=True)
+    h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.pa_probe_paged_read(g["k_pool"].data_ptr(), g["v_pool"].data_ptr(), g["block_tables"].data_ptr(),
+                                   g["seq_lens"].data_ptr(), 7, hkv, mb, n, bs, d * 2, bpw, unroll, nt,
+                                   out.data_ptr(), h) == 0
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for i in range(7):
+        nb = min(-(-int(case.seq_lens[i]) // bs), mb)
+        for grp in range(groups):
+            for h_ in range(hkv):
+                want = 0
+                for j in range(4 * bpw * grp, min(nb, 4 * bpw * (grp + 1))):
+                    blk = min(int(case.block_tables[i, j]) & 0xFFFFFFFF, n - 1)
+                    want ^= _xor(case.k_pool[blk, h_]) ^ _xor(case.v_pool[blk, h_])
+                assert (int(got[(i * groups + grp) * hkv + h_]) & 0xFFFFFFFF) == want, (i, grp, h_)
