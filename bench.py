@@ -491,8 +491,8 @@ def time_first_tile(reps, case, steps):
 
 def time_paged_read(reps, case, steps):
     """The paged-read probe over the decode call's own replicas and tables (every K/V block the call
-    reads, no arithmetic), timed like the decode calls, at its best over launch shapes: 16 or 64 blocks
-    per wave, 1, 2 or 4 blocks in flight per wave, plain or nontemporal loads. Returns the rate (GB/s)
+    reads, no arithmetic), timed like the decode calls, at its best over launch shapes: 1, 4, 16 or 64
+    blocks per wave, 1, 2 or 4 blocks in flight per wave, plain or nontemporal loads. Returns the rate (GB/s)
     of the best shape and that shape, or {} when the block is not 1, 2, 4 or 8 KiB per kv head."""
     import torch
 
@@ -506,7 +506,7 @@ def time_paged_read(reps, case, steps):
     blocks = int(((case.seq_lens.cpu().long() + bs - 1) // bs).clamp(max=mb).sum())
     nbytes = blocks * hkv * 2 * bs * row_bytes
     best = (0.0, None)
-    for bpw in (16, 64):
+    for bpw in (1, 4, 16, 64):
         groups = (mb + 4 * bpw - 1) // (4 * bpw)
         out = torch.empty(b * groups * hkv, dtype=torch.int32, device="cuda:0")
         for unroll in (1, 2, 4):
