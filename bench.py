@@ -965,16 +965,16 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_log: str, workload: str)
     w_fac = CALIBRATION_BYTES / (cw[0] * 1024.0)
     kernels = sorted({k[1] for k in med
                       if k[1].startswith("void decode_") or "merge_partials" in k[1] or "prefill_mfma" in k[1]
-                      or "copy_blocks" in k[1] or "cascade_kernel" in k[1]})
+                      or "copy_blocks" in k[1] or "cascade_kernel" in k[1] or "balanced_kernel" in k[1]})
     lines = [f"# HBM traffic of one decode call, workload {workload}",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by",
              f"# what it reads for a copy kernel that reads and writes {CALIBRATION_BYTES} bytes.",
              "# commands (from the repository root; the summary itself comes from",
              "#   python bench.py --summarize-pmc /tmp/pa_prof/pmc_fetch_W /tmp/pa_prof/pmc_write_W <bench log> --workload W):",
              f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/pa_prof/pmc_fetch_{workload} -o run -- "
-             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
+             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --no-stream --no-paged-probe --steps 20 --warmup 5 --calibrate-copy",
              f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/pa_prof/pmc_write_{workload} -o run -- "
-             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --steps 20 --warmup 5 --calibrate-copy",
+             f"python3 bench.py --workload {workload} --secondary '' --no-cpu --no-graph --no-stream --no-paged-probe --steps 20 --warmup 5 --calibrate-copy",
              f"workload = {workload}",
              f"library_sha256 = {library_sha256()}",
              f"copy_fetch_kib = {cf[0]:.1f}",
@@ -1005,7 +1005,7 @@ def summarize_l2(directory: str, workload: str, command: str) -> str:
     med = {k: statistics.median(v) for k, v in per.items()}
     kernels = sorted({k[1] for k in med
                       if k[1].startswith("void decode_") or "merge_partials" in k[1] or "cascade_kernel" in k[1]
-                      or "prefill_mfma" in k[1]})
+                      or "prefill_mfma" in k[1] or "balanced_kernel" in k[1]})
     lines = [f"# L2 (TCC) hits and misses of one decode call, workload {workload} (median over dispatches)",
              f"# command (from the repository root): {command}",
              f"workload = {workload}", f"library_sha256 = {library_sha256()}"]
@@ -1014,6 +1014,47 @@ def summarize_l2(directory: str, workload: str, command: str) -> str:
         rate = hit / (hit + miss) if hit + miss else 0.0
         lines += [f"kernel_{i} = {k}", f"kernel_{i}_tcc_hit = {hit:.0f}", f"kernel_{i}_tcc_miss = {miss:.0f}",
                   f"kernel_{i}_l2_hit_rate = {rate:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
+SIMDS = 1024  # 256 compute units x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs' instances
+
+
+def summarize_counters(directories: list, workload: str, commands: list) -> str:
+    """Per-kernel medians (over dispatches) of the SQ / GRBM counters of one or more ``rocprofv3 --pmc``
+    runs of ``bench.py --workload W``, with the derived shares: matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES
+    / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), LDS bank conflicts per LDS instruction, instructions per
+    wave. GRBM_GUI_ACTIVE counts GPU-busy cycles once per XCD and rocprofv3 sums the instances, so one
+    XCD's share is the kernel's elapsed cycles."""
+    per = {}
+    for directory in directories:
+        for r in _pmc_rows(directory):
+            per.setdefault((_short(r["Kernel_Name"]), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+    kernels = sorted({k[0] for k in med if k[0].startswith("void decode_") or "merge_partials" in k[0]
+                      or "prefill_mfma" in k[0] or "balanced_kernel" in k[0] or "cascade_kernel" in k[0]
+                      or "copy_blocks" in k[0]})
+    lines = [f"# SQ / GRBM counters of one call, workload {workload} (median over dispatches)"]
+    lines += [f"# command (from the repository root): {c}" for c in commands]
+    lines += [f"workload = {workload}", f"library_sha256 = {library_sha256()}"]
+    for i, k in enumerate(kernels):
+        lines.append(f"kernel_{i} = {k}")
+        names = sorted({c for (kk, c) in med if kk == k})
+        for c in names:
+            lines.append(f"kernel_{i}_{c} = {med[(k, c)]:.0f}")
+        get = lambda c: med.get((k, c))  # noqa: E731
+        if get("SQ_VALU_MFMA_BUSY_CYCLES") is not None and get("GRBM_GUI_ACTIVE"):
+            lines.append(f"kernel_{i}_elapsed_cycles = {get('GRBM_GUI_ACTIVE') / XCDS:.0f}")
+            lines.append(f"kernel_{i}_mfma_busy_frac = "
+                         f"{get('SQ_VALU_MFMA_BUSY_CYCLES') / (get('GRBM_GUI_ACTIVE') / XCDS * SIMDS):.4f}")
+        if get("SQ_LDS_BANK_CONFLICT") is not None and get("SQ_INSTS_LDS"):
+            lines.append(f"kernel_{i}_lds_bank_conflict_cycles_per_lds_inst = "
+                         f"{get('SQ_LDS_BANK_CONFLICT') / get('SQ_INSTS_LDS'):.3f}")
+        if get("SQ_WAVES"):
+            for c in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+                if get(c) is not None:
+                    lines.append(f"kernel_{i}_{c}_per_wave = {get(c) / get('SQ_WAVES'):.1f}")
     return "\n".join(lines) + "\n"
 
 
@@ -1082,6 +1123,8 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=0,
                     help="input copies to rotate over (default: enough to miss every cache; 1: warm)")
     ap.add_argument("--summarize-stats", nargs="+", metavar="DIR COMMAND [BENCH_LOG]")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR:COMMAND",
+                    help="counter runs of --workload W, each given as its output folder and command joined by '::'")
     ap.add_argument("--split-schedule", type=int, default=0,
                     help="pa_dims.split_schedule of the split calls: 0 the library's choice, 1 one partition per "
                          "wave, 2 two per wave, 3 balanced ranges")
@@ -1094,6 +1137,10 @@ def main(argv=None):
         return 0
     if args.summarize_stats:
         print(summarize_stats(*args.summarize_stats), end="")
+        return
+    if args.summarize_counters:
+        pairs = [x.split("::", 1) for x in args.summarize_counters]
+        print(summarize_counters([d for d, _ in pairs], args.workload, [c for _, c in pairs]), end="")
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode step runs on one "

@@ -70,7 +70,6 @@ void balanced_kernel(const DecodeParams p) {
   static_assert(BS >= kTile, "a tile lies inside one block");
   static_assert(!(Q8 && AP), "8-bit pools append with the separate append kernel");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;
-  constexpr int kKvTile = kTile * kKvRow;
   constexpr int NBUF = PF + 1;
   __shared__ __attribute__((aligned(16))) BalLds sh;
 
@@ -217,8 +216,10 @@ void balanced_kernel(const DecodeParams p) {
   auto load_tile = [&](const Meta& m, TileRegs& tr) {
     const int tile_p0 = m.j * kTile;
     const int64_t boff = (int64_t)m.blk * block_bytes + (int64_t)(tile_p0 % BS) * kKvRow;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, kKvTile);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, kKvTile);
+    // the descriptors end at the sequence's length: rows past it read as zeros, fetching nothing
+    const int bytes = min(kTile, m.L - tile_p0) * kKvRow;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, bytes);
     if constexpr (Q8) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) tr.k[c] = buffer_load16(kr, k_lane_off + 16 * c);

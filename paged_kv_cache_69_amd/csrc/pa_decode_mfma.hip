@@ -26,6 +26,8 @@
 //    gives each lane 4 positions of one head_dim column, the B operand.
 //  * Tiles inside one block are read through a buffer descriptor built per
 //    tile in SGPRs plus a fixed lane offset: no per-tile vector address math.
+//    The descriptor of a sequence's last tile ends at its length, so the rows
+//    past it are never fetched (they read as zeros and are masked anyway).
 //  * Softmax reference: a wave's first tile sets each row's reference max m.
 //    Later tiles use p = 2^(x - m) with x in base-2 units. If a score ever
 //    exceeds m by more than 2^64, the wave restarts its range with the larger
@@ -197,7 +199,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   static_assert(!(Q8 && APPEND), "8-bit pools append with the separate append kernel");
   static_assert(!F8 || Q8, "FP8 pools are 8-bit pools");
   constexpr int kKvRow = Q8 ? kD : kRowBytes;  // bytes of one K or V row in the pool
-  constexpr int kKvTile = kTile * kKvRow;
   constexpr int ROWS = 16 * MT;
   constexpr int NBUF = PF + 1;
   constexpr bool kLdsMerge = !WAVE_ITEMS || CASCADE;  // the waves' (m, l, acc) meet in LDS at the end
@@ -444,8 +445,11 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
     const int tile_p0 = tile_p0_of(i);
     if constexpr (BS >= kTile) {
       const int64_t boff = (int64_t)ids.b[0] * block_bytes + (int64_t)(tile_p0 % BS) * kKvRow;
-      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, kKvTile);
-      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, kKvTile);
+      // the descriptors end at the sequence's length: rows past it read as zeros and cost no memory
+      // traffic (they are masked out of the result in any case)
+      const int bytes = min(kTile, L - tile_p0) * kKvRow;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, bytes);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, bytes);
       if constexpr (Q8) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) tr.k[c] = buffer_load16(kr, k_lane_off + 16 * c);
