@@ -213,11 +213,13 @@ void balanced_kernel(const DecodeParams p) {
     }
     return m;
   };
-  auto load_tile = [&](const Meta& m, TileRegs& tr) {
+  // `live` false: a load past the wave's last tile (every step issues the same loads); its empty
+  // descriptors fetch nothing.
+  auto load_tile = [&](const Meta& m, TileRegs& tr, bool live) {
     const int tile_p0 = m.j * kTile;
     const int64_t boff = (int64_t)m.blk * block_bytes + (int64_t)(tile_p0 % BS) * kKvRow;
     // the descriptors end at the sequence's length: rows past it read as zeros, fetching nothing
-    const int bytes = min(kTile, m.L - tile_p0) * kKvRow;
+    const int bytes = live ? min(kTile, m.L - tile_p0) * kKvRow : 0;
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, bytes);
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, bytes);
     if constexpr (Q8) {
@@ -467,8 +469,8 @@ void balanced_kernel(const DecodeParams p) {
   };
 
   // ---- the pipeline: loads run PF tiles ahead of the tile computed, block ids one tile before their
-  // loads, and grabs one tile before that. Past this wave's last tile the loads re-read its last
-  // tile, so every step issues the same loads.
+  // loads, and grabs one tile before that. Past this wave's last tile every step still issues the same
+  // loads, through empty descriptors that fetch nothing.
   int lo_tile = INT32_MAX, hi_tile = -1;  // this wave's part of the range, as it is taken
   {
     TileRegs ring[NBUF];
@@ -476,12 +478,12 @@ void balanced_kernel(const DecodeParams p) {
     meta[0] = meta_of(grab_take(grab_issue()));
     if (meta[0].t >= 0) {
       Meta last_valid = meta[0];
-      load_tile(meta[0], ring[0]);
+      load_tile(meta[0], ring[0], true);
 #pragma unroll
       for (int u = 1; u < PF; ++u) {
         meta[u] = meta_of(meta[u - 1].t >= 0 ? grab_take(grab_issue()) : -1);
         if (meta[u].t >= 0) last_valid = meta[u];
-        load_tile(last_valid, ring[u]);
+        load_tile(last_valid, ring[u], meta[u].t >= 0);
       }
       Meta m_next = meta_of(meta[PF - 1].t >= 0 ? grab_take(grab_issue()) : -1);
       int t_pending = m_next.t >= 0 ? grab_take(grab_issue()) : -1;
@@ -496,7 +498,7 @@ void balanced_kernel(const DecodeParams p) {
               // the loads PF tiles ahead, the block ids of the tile after, the grab of the one after that
               if (m_next.t >= 0) last_valid = m_next;
               meta[(u + PF) % NBUF] = m_next;
-              load_tile(last_valid, ring[(u + PF) % NBUF]);
+              load_tile(last_valid, ring[(u + PF) % NBUF], m_next.t >= 0);
               m_next = meta_of(t_pending);
               const bool grab_live = t_pending >= 0;
               const uint64_t raw = grab_live ? grab_issue() : 0ull;

@@ -35,8 +35,9 @@
 //    by MFMAs. 2^64 headroom keeps l and acc far inside fp32 range, and
 //    o = acc / l does not depend on the reference ([P5] section 4.2).
 //  * Loads run PF tiles ahead. Every iteration issues the same 8 vector loads
-//    (past the end it re-reads the wave's last tile), so the compiler's wait
-//    before a tile is used leaves the younger tiles' loads in flight.
+//    (past the wave's last tile through empty descriptors, which fetch nothing),
+//    so the compiler's wait before a tile is used leaves the younger tiles'
+//    loads in flight.
 // Masked tail tiles (positions >= L, causal limits when T > 1, absent padded
 // rows) select -inf scores and zero the V rows past L before they are stored
 // to LDS, so garbage in unwritten slots never reaches the result.
@@ -441,13 +442,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
   };
   const uint32_t k_lane_off = Q8 ? c16 * kD + 32 * g : c16 * kRowBytes + g * 16;
   const uint32_t v_lane_off = Q8 ? (lane >> 2) * kD + 32 * (lane & 3) : lane * 16;
-  auto load_tile = [&](int i, const TileIds& ids, TileRegs& tr) {
+  // `live` false: a load past the wave's last tile, issued only so that every step issues the same
+  // loads; its descriptors are empty, so it fetches nothing and reads zeros.
+  auto load_tile = [&](int i, const TileIds& ids, TileRegs& tr, bool live) {
     const int tile_p0 = tile_p0_of(i);
     if constexpr (BS >= kTile) {
       const int64_t boff = (int64_t)ids.b[0] * block_bytes + (int64_t)(tile_p0 % BS) * kKvRow;
       // the descriptors end at the sequence's length: rows past it read as zeros and cost no memory
       // traffic (they are masked out of the result in any case)
-      const int bytes = min(kTile, L - tile_p0) * kKvRow;
+      const int bytes = live ? min(kTile, L - tile_p0) * kKvRow : 0;
       const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + boff, bytes);
       const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + boff, bytes);
       if constexpr (Q8) {
@@ -678,7 +681,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       cur[u] = ib + u == 0 ? ids0 : ids_of(min(ib + u, last));
-      load_tile(min(ib + u, last), cur[u], ring[u]);
+      load_tile(min(ib + u, last), cur[u], ring[u], ib + u <= last);
     }
     TileIds ids_next = ids_of(min(ib + PF, last));
     int again = -1;
@@ -690,7 +693,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
         if (i < my_tiles && again < 0) {
           const TileIds ids = ids_next;
           ids_next = ids_of(min(i + PF + 1, last));
-          load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF]);
+          load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF], i + PF <= last);
           const TileIds ids_cur = cur[u];  // the scales of tile i
           cur[(u + PF) % NBUF] = ids;
           const int tile_p0 = tile_p0_of(i);
