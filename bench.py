@@ -1083,7 +1083,7 @@ def summarize_stats(directory: str, command: str, bench_log: str | None = None) 
         for name, v in per.items():
             stats.append((name, len(v), sum(v) / len(v), min(v), max(v), 100.0 * sum(v) / total))
     stats.sort(key=lambda r: -r[5])
-    out = ["# rocprofv3 --kernel-trace --stats summary", f"# command: {command}",
+    out = ["# rocprofv3 --kernel-trace --stats summary", f"# command: {command}", f"# library_sha256 = {library_sha256()}",
            f"{'kernel':80s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     for name, calls, avg, mn, mx, pct in stats:
         out.append(f"{name[:80]:80s} {calls:7d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {pct:6.2f}")
