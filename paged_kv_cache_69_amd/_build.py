@@ -11,6 +11,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libpa_probe.so")  # the benchmark's measurement probes
+TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libpa_timeline.so")  # per-wave timelines (built on request)
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 HIP_FLAGS = [
@@ -52,13 +53,13 @@ def _run(cmd: list[str]) -> str:
     return log
 
 
-def _build_lib(folder: str, lib_path: str, logs: list, ex) -> None:
+def _build_lib(folder: str, lib_path: str, logs: list, ex, defines=(), tag: str = "") -> None:
     inc = ["-I", os.path.join(ROOT, "include")]
     jobs = []
     for src in sources(folder):
-        obj = os.path.join(OBJ_DIR, folder + "_" + os.path.basename(src) + ".o")
+        obj = os.path.join(OBJ_DIR, tag + folder + "_" + os.path.basename(src) + ".o")
         flags = FILE_FLAGS.get(os.path.basename(src), [])
-        jobs.append((obj, [hipcc(), *HIP_FLAGS, *flags, *inc, "-c", src, "-o", obj]))
+        jobs.append((obj, [hipcc(), *HIP_FLAGS, *flags, *defines, *inc, "-c", src, "-o", obj]))
     logs += list(ex.map(lambda j: _run(j[1]), jobs))
     tmp = lib_path + ".tmp"
     logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]))
@@ -85,5 +86,23 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_timeline(verbose: bool = False) -> str:
+    """The measurement build: csrc/ with PA_TIMELINE=1 into ``libpa_timeline.so`` (the decode kernels
+    also record a per-wave timeline; include/pa_timeline.h). Not part of build()."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    logs: list = []
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        _build_lib("csrc", TIMELINE_LIB_PATH, logs, ex, defines=("-DPA_TIMELINE=1",), tag="timeline_")
+    if verbose:
+        for log in logs:
+            if log.strip():
+                print(log)
+    return TIMELINE_LIB_PATH
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+
+    print(build_timeline(verbose=True) if "--timeline" in sys.argv[1:] else build(verbose=True))

@@ -600,3 +600,20 @@ int pa_prefill(const pa_dims* dims, const void* q, const void* k_pool, const voi
 }
 
 }  // extern "C"
+
+#if PA_TIMELINE
+#include "pa_wave_timeline.h"
+#include "pa_timeline.h"
+
+extern "C" int pa_timeline_read(int32_t family, void* host, size_t bytes) {
+  if (!host) return -1;
+  if (family == PA_TIMELINE_MFMA) return pa::timeline_read_mfma(host, bytes);
+  if (family == PA_TIMELINE_BALANCED) return pa::timeline_read_balanced(host, bytes);
+  return -1;
+}
+
+extern "C" int pa_timeline_clear(void) {
+  const int a = pa::timeline_clear_mfma();
+  return a != 0 ? a : pa::timeline_clear_balanced();
+}
+#endif

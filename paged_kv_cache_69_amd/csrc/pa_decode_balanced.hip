@@ -33,6 +33,9 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma_tile.h"
+#include "pa_wave_timeline.h"
+
+PA_TIMELINE_BUFFER(balanced)
 
 namespace pa {
 namespace {
@@ -72,6 +75,8 @@ void balanced_kernel(const DecodeParams p) {
   constexpr int kKvRow = Q8 ? kD : kRowBytes;
   constexpr int NBUF = PF + 1;
   __shared__ __attribute__((aligned(16))) BalLds sh;
+  WaveTimeline tl;
+  tl.begin();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,17 +157,22 @@ void balanced_kernel(const DecodeParams p) {
   // word and takes the old back - 1; a tile is taken when the old front < the old back, compared as
   // signed words (the back may pass below 0 after the last take). Each wave stops at its first
   // miss, so the front wave's tiles are [t0, m) and the back wave's [m, t1) for one m.
-  auto grab_issue = [&]() -> uint64_t {
+  // A wave may also take k tiles at once: the front wave adds k and takes [f, min(f + k, b)), the back
+  // wave subtracts k from the high word and takes [max(f, b - k), b); in either order the two takes
+  // are disjoint and each wave's tiles stay contiguous from its end of the range.
+  auto grab_issue = [&](int k = 1) -> uint64_t {
     uint64_t old = 0;
     if (lane == 0)
-      old = __hip_atomic_fetch_add(&sh.cursor[pair], side == 0 ? 1ull : 0xFFFFFFFF00000000ull, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __hip_atomic_fetch_add(&sh.cursor[pair], side == 0 ? (uint64_t)k : (uint64_t)(-(int64_t)k) << 32,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return old;
   };
-  auto grab_take = [&](uint64_t old) -> int {
+  // the i-th tile (in this wave's order) of a take of k >= i + 1 tiles, or -1
+  auto grab_take = [&](uint64_t old, int i = 0) -> int {
     const int f = __builtin_amdgcn_readfirstlane((int)(uint32_t)old);
     const int b = __builtin_amdgcn_readfirstlane((int)(uint32_t)(old >> 32));
-    return f < b ? (side == 0 ? f : b - 1) : -1;
+    const int t = side == 0 ? f + i : b - 1 - i;
+    return t >= f && t < b ? t : -1;
   };
 
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kKvRow;
@@ -181,28 +191,35 @@ void balanced_kernel(const DecodeParams p) {
   const uint32_t k_lane_off = Q8 ? c16 * kD + 32 * g : c16 * kRowBytes + g * 16;
   const uint32_t v_lane_off = Q8 ? (lane >> 2) * kD + 32 * (lane & 3) : lane * 16;
 
-  // Block id and scales of tile t; the lookup cursor only moves one way (forward or backward).
+  // Block id and scales of tile t; the lookup cursor only moves one way (forward or backward). The
+  // cursor keeps its sequence's bounds and length in registers, so a lookup inside the same sequence
+  // reads no LDS: an LDS read there would wait for the table loads still in flight (LDS and scalar
+  // loads share one counter, and scalar loads complete out of order), and the block-id loads of
+  // consecutive tiles would then go out one after another instead of together.
   int lk_s = seq_of(side == 0 ? t0 : t1 - 1);
-  int lk_beg = pre_at(lk_s), lk_end = pre_at(lk_s + 1);
+  int lk_beg = pre_at(lk_s), lk_end = pre_at(lk_s + 1), lk_len = len_at(lk_s);
   auto meta_of = [&](int t) -> Meta {
     Meta m;
     m.t = t;
     m.s = m.j = m.L = m.blk = 0;
     m.ks = m.vs = 1.f;
     if (t < 0) return m;
-    while (t >= lk_end) {
-      ++lk_s;
-      lk_beg = lk_end;
-      lk_end = pre_at(lk_s + 1);
-    }
-    while (t < lk_beg) {
-      --lk_s;
-      lk_end = lk_beg;
-      lk_beg = pre_at(lk_s);
+    if (t >= lk_end || t < lk_beg) {
+      while (t >= lk_end) {
+        ++lk_s;
+        lk_beg = lk_end;
+        lk_end = pre_at(lk_s + 1);
+      }
+      while (t < lk_beg) {
+        --lk_s;
+        lk_end = lk_beg;
+        lk_beg = pre_at(lk_s);
+      }
+      lk_len = len_at(lk_s);
     }
     m.s = lk_s;
     m.j = t - lk_beg;
-    m.L = len_at(lk_s);
+    m.L = lk_len;
     const auto* trow = read_only(p.block_tables + (int64_t)lk_s * p.MB);
     // the id is clamped into the pool: a table entry past the length is never used for the result
     m.blk = (int)min((uint32_t)trow[min(m.j * kTile / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
@@ -475,18 +492,20 @@ void balanced_kernel(const DecodeParams p) {
   {
     TileRegs ring[NBUF];
     Meta meta[NBUF];
-    meta[0] = meta_of(grab_take(grab_issue()));
+    // the prologue's tiles in one take: the PF loaded ahead, the next block ids and the pending grab;
+    // their block-id lookups then go out together
+    const uint64_t first = grab_issue(PF + 2);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) meta[u] = meta_of(grab_take(first, u));
     if (meta[0].t >= 0) {
       Meta last_valid = meta[0];
-      load_tile(meta[0], ring[0], true);
 #pragma unroll
-      for (int u = 1; u < PF; ++u) {
-        meta[u] = meta_of(meta[u - 1].t >= 0 ? grab_take(grab_issue()) : -1);
+      for (int u = 0; u < PF; ++u) {
         if (meta[u].t >= 0) last_valid = meta[u];
         load_tile(last_valid, ring[u], meta[u].t >= 0);
       }
-      Meta m_next = meta_of(meta[PF - 1].t >= 0 ? grab_take(grab_issue()) : -1);
-      int t_pending = m_next.t >= 0 ? grab_take(grab_issue()) : -1;
+      Meta m_next = meta_of(grab_take(first, PF));
+      int t_pending = grab_take(first, PF + 1);
       for (bool more = true; more;) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -503,6 +522,7 @@ void balanced_kernel(const DecodeParams p) {
               const bool grab_live = t_pending >= 0;
               const uint64_t raw = grab_live ? grab_issue() : 0ull;
 
+              tl.first_tile();
               lo_tile = min(lo_tile, m.t);
               hi_tile = max(hi_tile, m.t);
               if (m.s != cs) {  // a new piece: this wave's tiles of another sequence
@@ -531,6 +551,7 @@ void balanced_kernel(const DecodeParams p) {
       flush();
     }
   }
+  tl.end_loop(hi_tile >= lo_tile ? hi_tile - lo_tile + 1 : 0);
 
   // ---- empty slots: the sequences of the range that this wave's part does not touch. The front
   // part is [t0, hi_tile], the back part [lo_tile, t1 - 1].
@@ -572,6 +593,7 @@ void balanced_kernel(const DecodeParams p) {
       }
     }
   }
+  PA_TIMELINE_STORE(tl, blockIdx.x * kBalWaves + wave);
 }
 
 template <int BS, bool Q8, bool F8, bool AP>

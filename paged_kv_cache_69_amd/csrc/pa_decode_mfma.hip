@@ -110,6 +110,9 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma_tile.h"
+#include "pa_wave_timeline.h"
+
+PA_TIMELINE_BUFFER(mfma)
 
 namespace pa {
 namespace {
@@ -193,7 +196,7 @@ constexpr int decode_lds_bytes() {
 // its place among the cascade launch's blocks of the same kind).
 template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8,
           bool MULTI = false>
-__device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, int block) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, int block, WaveTimeline& tl) {
   static_assert(!MULTI || (WAVE_ITEMS && !CASCADE && !Q8), "two partitions per wave are for bf16 split items");
   static_assert(!CASCADE || (WAVE_ITEMS && !Q8 && !APPEND), "prefix items are split-context bf16 items");
   static_assert(!Q8 || BS >= kTile, "int8 pools need a tile inside one block");
@@ -696,6 +699,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
           load_tile(min(i + PF, last), ids, ring[(u + PF) % NBUF], i + PF <= last);
           const TileIds ids_cur = cur[u];  // the scales of tile i
           cur[(u + PF) % NBUF] = ids;
+          tl.first_tile();
           const int tile_p0 = tile_p0_of(i);
           const bool masked = !rows_all_present || tile_p0 + kTile > vis_all;
           const float kscale = ids_cur.ks, vscale = ids_cur.vs;
@@ -786,6 +790,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 
   for (int from = 0; (from = run(from)) >= 0;) {
   }
+  tl.end_loop(my_tiles);
   if constexpr (APPEND && !Q8 && !CASCADE) {
     if (late_dst >= 0) {
       const bool v_half = (lane >> 4) & 1;
@@ -905,7 +910,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, char* lds, in
 template <int MT, int BS, int NW, int PF, bool WAVE_ITEMS, bool Q8, bool APPEND, bool CASCADE, bool F8, bool MULTI>
 __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void decode_mfma_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<MT, NW, WAVE_ITEMS, CASCADE, MULTI>()];
-  decode_body<MT, BS, NW, PF, WAVE_ITEMS, Q8, APPEND, CASCADE, F8, MULTI>(p, lds, blockIdx.x);
+  WaveTimeline tl;
+  tl.begin();
+  decode_body<MT, BS, NW, PF, WAVE_ITEMS, Q8, APPEND, CASCADE, F8, MULTI>(p, lds, blockIdx.x, tl);
+  PA_TIMELINE_STORE(tl, blockIdx.x * NW + (threadIdx.x >> 6));
 }
 
 // Cascade in one launch: the shared prefix's items (32 rows of many sequences per wave, L2-bound) and
@@ -922,10 +930,13 @@ void cascade_kernel(const DecodeParams p, int pre_runs, int suf_runs) {
   const int both = min(pre_runs, suf_runs);
   const bool prefix = run < 2 * both ? (run & 1) == 0 : pre_runs > suf_runs;
   const int idx = (run < 2 * both ? run / 2 : both + (run - 2 * both)) * p.Hkv + r;
+  WaveTimeline tl;
+  tl.begin();
   if (prefix)
-    decode_body<2, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, true, false>(p, lds, idx);
+    decode_body<2, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, false, true, false>(p, lds, idx, tl);
   else
-    decode_body<MT, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, AP, false, false>(p, lds, idx);
+    decode_body<MT, BS, kMfmaWaves, kMfmaSplitPrefetch, true, false, AP, false, false>(p, lds, idx, tl);
+  PA_TIMELINE_STORE(tl, blockIdx.x * kMfmaWaves + (threadIdx.x >> 6));
 }
 
 template <int MT, int BS, bool WI, bool Q8, bool AP, bool CAS = false, bool F8 = false>

@@ -261,3 +261,27 @@ def test_library_binds_to_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_timeline_entry_points_only_in_the_timeline_build():
+    """libpa.so exports no timeline entry point (the records exist only in the measurement build); the
+    timeline build, when present, exports the two that include/pa_timeline.h declares and the whole
+    decode ABI besides."""
+    import re
+    import subprocess
+
+    from paged_kv_cache_69_amd._build import LIB_PATH, TIMELINE_LIB_PATH
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+        return {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+
+    assert not any(s.startswith("pa_timeline") for s in exported(LIB_PATH))
+    if not os.path.exists(TIMELINE_LIB_PATH):
+        pytest.skip("timeline build not present (python -m paged_kv_cache_69_amd._build --timeline)")
+    header = open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa_timeline.h")).read()
+    declared = set(re.findall(r"\b(pa_timeline_[a-z]+)\s*\(", re.sub(r"/\*.*?\*/", "", header, flags=re.S)))
+    assert declared == {"pa_timeline_read", "pa_timeline_clear"}
+    syms = exported(TIMELINE_LIB_PATH)
+    assert declared <= syms
+    assert {s for s in exported(LIB_PATH) if s.startswith("pa_")} <= syms
