@@ -24,9 +24,13 @@
 //  * A piece's first tile sets each row's reference max; a later score more than 2^64 above it
 //    raises the reference and rescales that row's l and accumulator by 2^(old - new) (rare: scores
 //    that climb by more than 64 base-2 units; o = acc / l does not depend on the reference).
-//  * The workgroup stages the tile prefix sums of the batch, the lengths and the q rows of its kv
-//    head in LDS before any wave starts; a wave crossing into another sequence takes that
-//    sequence's q operand from there.
+//  * The q rows of the workgroup's kv head go to LDS; a wave crossing into another sequence takes
+//    that sequence's q operand from there. Up to 63 sequences (with their q rows in four 16-byte
+//    pieces per thread), every wave scans the lengths itself in registers, lane s holding sequence
+//    s, and its first tiles are fixed without the shared word (the front wave takes up to PF + 2
+//    from the front, the back wave up to PF + 2 from the back, halves of shorter ranges), so its
+//    first block-id lookups and tile loads go out before the workgroup's one barrier, behind which
+//    the q rows and the shared words are stored. Larger batches stage the prefix sums in LDS first.
 // The per-tile arithmetic (S^T = K Q^T on the matrix cores, masking, probabilities split into bf16 hi
 // and lo parts, V through a swizzled LDS tile and transposed reads, P.V on the matrix cores) and the
 // 8-bit widenings are those of the other matrix-core kernels (pa_mfma_tile.h).
@@ -55,6 +59,7 @@ constexpr int kBalQ8Prefetch = PA_BAL_Q8_PREFETCH;  // 8-bit tiles are half the 
 constexpr int kBalMaxSeqs = 1024;
 constexpr int kBalSeqsPerThread = kBalMaxSeqs / (kBalWaves * 64);
 constexpr int kBalQBytes = 48 * 1024;  // q rows of the batch for one kv head: B * rows * 256 bytes at most
+constexpr int kBalQRegs = 4;            // small batches: 16-byte pieces of q per thread held in registers
 
 struct BalLds {
   char vt[kBalWaves][kTileBytes];        // per-wave V tile
@@ -89,8 +94,27 @@ void balanced_kernel(const DecodeParams p) {
   const int T = p.T, B = p.B, rows = p.rows;
   const int pt = p.part_tokens / kTile;  // tiles per partition
 
-  // ---- lengths, tile prefix sums and this kv head's q rows into LDS (the whole workgroup)
-  {
+  // ---- lengths and tile prefix sums: in registers for small batches (lane s: sequence s's length
+  // and first tile), else in LDS
+  auto q_src = [&](int idx) {  // 16-byte piece idx of the kv head's q rows, [B][rows][16]
+    const int s = idx / (rows * 16), n = (idx / 16) % rows, c = idx % 16;
+    return static_cast<const char*>(p.q) + ((int64_t)(s * T + n / p.G) * p.Hq + kvh * p.G + n % p.G) * kRowBytes +
+           c * 16;
+  };
+  const int q_pieces = B * rows * 16;
+  const bool small = B < 64 && q_pieces <= kBalQRegs * kBalWaves * 64;
+  int r_len = 0, r_pre = 0;
+  u32x4 qreg[kBalQRegs];
+  if (small) {
+    r_len = lane < B ? (int)read_only(p.seq_lens)[lane] : 0;
+#pragma unroll
+    for (int i = 0; i < kBalQRegs; ++i) {
+      const int idx = tid + i * kBalWaves * 64;
+      if (idx < q_pieces) qreg[i] = load16(q_src(idx));
+    }
+    const int cnt = r_len > 0 ? (r_len + kTile - 1) / kTile : 0;
+    r_pre = wave_inclusive_sum(cnt) - cnt;  // lanes B..63 hold the total
+  } else {
     int loc[kBalSeqsPerThread], sum = 0;
 #pragma unroll
     for (int k = 0; k < kBalSeqsPerThread; ++k) {
@@ -102,12 +126,8 @@ void balanced_kernel(const DecodeParams p) {
     }
     const int incl = wave_inclusive_sum(sum);  // over the wave, then over the waves
     if (lane == 63) sh.wsum[wave] = incl;
-    for (int idx = tid; idx < B * rows * 16; idx += kBalWaves * 64) {
-      const int s = idx / (rows * 16), n = (idx / 16) % rows, c = idx % 16;
-      const char* src = static_cast<const char*>(p.q) +
-                        ((int64_t)(s * T + n / p.G) * p.Hq + kvh * p.G + n % p.G) * kRowBytes + c * 16;
-      *reinterpret_cast<u32x4*>(sh.q + (s * rows + n) * kRowBytes + c * 16) = load16(src);
-    }
+    for (int idx = tid; idx < q_pieces; idx += kBalWaves * 64)
+      *reinterpret_cast<u32x4*>(sh.q + idx * 16) = load16(q_src(idx));
     __syncthreads();
     int base = 0;
     for (int w = 0; w < wave; ++w) base += sh.wsum[w];
@@ -121,29 +141,23 @@ void balanced_kernel(const DecodeParams p) {
     if (tid == kBalWaves * 64 - 1 && B == kBalMaxSeqs) sh.pre[B] = run_sum;
     __syncthreads();
   }
-  const int N = sh.pre[B];
+  // pre[s] (s <= B) and the length of sequence s < B, wave-uniform
+  auto pre_at = [&](int s) {
+    return small ? __builtin_amdgcn_readlane(r_pre, s) : __builtin_amdgcn_readfirstlane(sh.pre[s]);
+  };
+  auto len_at = [&](int s) {
+    return small ? __builtin_amdgcn_readlane(r_len, s) : __builtin_amdgcn_readfirstlane(sh.len[s]);
+  };
+  const int N = pre_at(B);
   const int R = min(W, max(1, N / pt));
   // range of tile t < N: the largest r with floor(r N / R) <= t
   auto range_of = [&](int t) { return (int)(((int64_t)(t + 1) * R - 1) / N); };
-  auto pre_at = [&](int s) { return __builtin_amdgcn_readfirstlane(sh.pre[s]); };
-  auto len_at = [&](int s) { return __builtin_amdgcn_readfirstlane(sh.len[s]); };
-
-  // slot counts for the merge, one per sequence (every kv head has the same ranges): written once
-  if (blockIdx.x == 0) {
-    for (int s = tid; s < B; s += kBalWaves * 64) {
-      const int a = sh.pre[s], b = sh.pre[s + 1];
-      p.slot_counts[s] = b > a ? 2 * (range_of(b - 1) - range_of(a) + 1) : 0;
-    }
-  }
-  const int t0 = r < R ? (int)((int64_t)r * N / R) : 0;
-  const int t1 = r < R ? (int)((int64_t)(r + 1) * N / R) : 0;
-  if (side == 0 && lane == 0)
-    sh.cursor[pair] = (unsigned long long)(uint32_t)t0 | ((unsigned long long)(uint32_t)t1 << 32);
-  __syncthreads();
-  if (t1 <= t0) return;  // no barrier below this point
-
   // sequence of tile t: the largest s with pre[s] <= t (empty sequences are passed over)
   auto seq_of = [&](int t) {
+    if (small) {
+      const uint64_t at_or_before = __ballot(lane < B && r_pre <= t);
+      return __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(at_or_before));
+    }
     int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -152,29 +166,35 @@ void balanced_kernel(const DecodeParams p) {
     return lo;
   };
 
-  // The next tile of this wave from the pair's shared word, or -1 once the two ends have met. The
-  // front wave adds 1 to the low word and takes the old front; the back wave adds -1 to the high
-  // word and takes the old back - 1; a tile is taken when the old front < the old back, compared as
-  // signed words (the back may pass below 0 after the last take). Each wave stops at its first
-  // miss, so the front wave's tiles are [t0, m) and the back wave's [m, t1) for one m.
-  // A wave may also take k tiles at once: the front wave adds k and takes [f, min(f + k, b)), the back
-  // wave subtracts k from the high word and takes [max(f, b - k), b); in either order the two takes
-  // are disjoint and each wave's tiles stay contiguous from its end of the range.
-  auto grab_issue = [&](int k = 1) -> uint64_t {
+  const int t0 = r < R ? (int)((int64_t)r * N / R) : 0;
+  const int t1 = r < R ? (int)((int64_t)(r + 1) * N / R) : 0;
+  // the first tiles of each wave, fixed: up to PF + 2 from its end, the halves of a shorter range
+  constexpr int kFirst = PF + 2;
+  const int n_range = t1 - t0;
+  const int k_front = min(kFirst, (n_range + 1) / 2), k_back = min(kFirst, n_range - k_front);
+  auto first_take = [&](int i) {
+    return side == 0 ? (i < k_front ? t0 + i : -1) : (i < k_back ? t1 - 1 - i : -1);
+  };
+
+  // The next tile of this wave from the pair's shared word (front, back), which starts past both first
+  // takes, or -1 once the two ends have met. The front wave adds 1 to the low word and takes the old
+  // front; the back wave adds -1 to the high word and takes the old back - 1; a tile is taken when the
+  // old front < the old back, compared as signed words (the back may pass below 0 after the last take).
+  // Each wave stops at its first miss, so the front wave's tiles are [t0, m) and the back wave's
+  // [m, t1) for one m.
+  auto grab_issue = [&]() -> uint64_t {
     uint64_t old = 0;
     if (lane == 0)
-      old = __hip_atomic_fetch_add(&sh.cursor[pair], side == 0 ? (uint64_t)k : (uint64_t)(-(int64_t)k) << 32,
+      old = __hip_atomic_fetch_add(&sh.cursor[pair], side == 0 ? (uint64_t)1 : (uint64_t)(-(int64_t)1) << 32,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return old;
   };
-  // the i-th tile (in this wave's order) of a take of k >= i + 1 tiles, or -1
-  auto grab_take = [&](uint64_t old, int i = 0) -> int {
+  auto grab_take = [&](uint64_t old) -> int {
     const int f = __builtin_amdgcn_readfirstlane((int)(uint32_t)old);
     const int b = __builtin_amdgcn_readfirstlane((int)(uint32_t)(old >> 32));
-    const int t = side == 0 ? f + i : b - 1 - i;
+    const int t = side == 0 ? f : b - 1;
     return t >= f && t < b ? t : -1;
   };
-
   const int64_t block_bytes = (int64_t)p.Hkv * BS * kKvRow;
   const char* kbase = static_cast<const char*>(p.k_pool) + (int64_t)kvh * BS * kKvRow;
   const char* vbase = static_cast<const char*>(p.v_pool) + (int64_t)kvh * BS * kKvRow;
@@ -196,8 +216,13 @@ void balanced_kernel(const DecodeParams p) {
   // reads no LDS: an LDS read there would wait for the table loads still in flight (LDS and scalar
   // loads share one counter, and scalar loads complete out of order), and the block-id loads of
   // consecutive tiles would then go out one after another instead of together.
-  int lk_s = seq_of(side == 0 ? t0 : t1 - 1);
-  int lk_beg = pre_at(lk_s), lk_end = pre_at(lk_s + 1), lk_len = len_at(lk_s);
+  int lk_s = 0, lk_beg = 0, lk_end = 0, lk_len = 0;
+  if (first_take(0) >= 0) {
+    lk_s = seq_of(first_take(0));
+    lk_beg = pre_at(lk_s);
+    lk_end = pre_at(lk_s + 1);
+    lk_len = len_at(lk_s);
+  }
   auto meta_of = [&](int t) -> Meta {
     Meta m;
     m.t = t;
@@ -492,20 +517,48 @@ void balanced_kernel(const DecodeParams p) {
   {
     TileRegs ring[NBUF];
     Meta meta[NBUF];
-    // the prologue's tiles in one take: the PF loaded ahead, the next block ids and the pending grab;
-    // their block-id lookups then go out together
-    const uint64_t first = grab_issue(PF + 2);
+    // the first takes: the PF tiles loaded ahead, the next block ids and the pending tile; their
+    // block-id lookups go out together, before the workgroup's barrier
 #pragma unroll
-    for (int u = 0; u < PF; ++u) meta[u] = meta_of(grab_take(first, u));
+    for (int u = 0; u < PF; ++u) meta[u] = meta_of(first_take(u));
+    Meta last_valid = meta[0];
     if (meta[0].t >= 0) {
-      Meta last_valid = meta[0];
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (meta[u].t >= 0) last_valid = meta[u];
         load_tile(last_valid, ring[u], meta[u].t >= 0);
       }
-      Meta m_next = meta_of(grab_take(first, PF));
-      int t_pending = grab_take(first, PF + 1);
+    }
+    Meta m_next = meta_of(first_take(PF));
+    int t_pending = first_take(PF + 1);
+
+    // q rows (small batches), the pairs' shared words and the merge's slot counts; then the one barrier
+    if (small) {
+#pragma unroll
+      for (int i = 0; i < kBalQRegs; ++i) {
+        const int idx = tid + i * kBalWaves * 64;
+        if (idx < q_pieces) *reinterpret_cast<u32x4*>(sh.q + idx * 16) = qreg[i];
+      }
+    }
+    if (side == 0 && lane == 0)
+      sh.cursor[pair] = (unsigned long long)(uint32_t)(t0 + k_front) |
+                        ((unsigned long long)(uint32_t)(t1 - k_back) << 32);
+    // slot counts for the merge, one per sequence (every kv head has the same ranges): written once
+    if (blockIdx.x == 0) {
+      if (small) {
+        // pre[s + 1] from lane s + 1, read with every lane active (lane B <= 63 holds the total)
+        const int a = r_pre, b = __shfl_down(r_pre, 1, 64);
+        if (wave == 0 && lane < B) p.slot_counts[lane] = b > a ? 2 * (range_of(b - 1) - range_of(a) + 1) : 0;
+      } else {
+        for (int s = tid; s < B; s += kBalWaves * 64) {
+          const int a = sh.pre[s], b = sh.pre[s + 1];
+          p.slot_counts[s] = b > a ? 2 * (range_of(b - 1) - range_of(a) + 1) : 0;
+        }
+      }
+    }
+    __syncthreads();  // no barrier below this point
+
+    if (meta[0].t >= 0) {
       for (bool more = true; more;) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -551,6 +604,7 @@ void balanced_kernel(const DecodeParams p) {
       flush();
     }
   }
+  if (n_range <= 0) return;  // a range past the last (more pairs than ranges)
   tl.end_loop(hi_tile >= lo_tile ? hi_tile - lo_tile + 1 : 0);
 
   // ---- empty slots: the sequences of the range that this wave's part does not touch. The front
