@@ -52,10 +52,13 @@ constexpr int kBalPairs = kBalWaves / 2;
 #define PA_BAL_PREFETCH 2
 #endif
 #ifndef PA_BAL_Q8_PREFETCH
-#define PA_BAL_Q8_PREFETCH 4
+#define PA_BAL_Q8_PREFETCH 2
 #endif
-constexpr int kBalPrefetch = PA_BAL_PREFETCH;      // bf16 tiles in flight ahead of the one computed
-constexpr int kBalQ8Prefetch = PA_BAL_Q8_PREFETCH;  // 8-bit tiles are half the registers
+constexpr int kBalPrefetch = PA_BAL_PREFETCH;  // bf16 tiles in flight ahead of the one computed
+// 8-bit tiles are half the registers, but running them further ahead measured slower (long_int8 96.7 us
+// at 4 ahead against 90.5 at 2 and 89.9 at 1): the deeper ring's block ids and scales spill the
+// tile loop's scalar registers
+constexpr int kBalQ8Prefetch = PA_BAL_Q8_PREFETCH;
 constexpr int kBalMaxSeqs = 1024;
 constexpr int kBalSeqsPerThread = kBalMaxSeqs / (kBalWaves * 64);
 constexpr int kBalQBytes = 48 * 1024;  // q rows of the batch for one kv head: B * rows * 256 bytes at most
