@@ -140,6 +140,11 @@ def test_partitioned_schedule_choice(lib):
                  32768, 512) == pa.SPLIT_ONE_PER_WAVE
     big_b = _dims(num_seqs=1100, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3)  # too many to stage
     assert f(big_b, 4096, 512) == -2
+    # q rows staged in 48 KiB of LDS: 48 sequences of 4 rows (256 bytes each) fit, 49 do not, and the
+    # automatic choice then takes two partitions per wave
+    assert f(_dims(num_seqs=48, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3), 32768, 512) == 3
+    assert f(_dims(num_seqs=49, q_tokens=1, num_q_heads=32, head_dim=128, split_schedule=3), 32768, 512) == -2
+    assert f(_dims(num_seqs=49, q_tokens=1, num_q_heads=32, head_dim=128), 32768, 512) == pa.SPLIT_TWO_PER_WAVE
     d_b8 = _dims(num_seqs=16, q_tokens=1, num_q_heads=32, head_dim=128, block_size=8, split_schedule=3)
     assert f(d_b8, 32768, 512) == -2
 

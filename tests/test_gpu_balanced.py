@@ -157,3 +157,37 @@ def test_balanced_fewer_tiles_than_waves(gpu_lib):
         torch.cuda.synchronize()
         assert_attention_close(out.cpu(), _oracle_bf16(case, kp, vp), kv_dtype=torch.bfloat16,
                                out_dtype=torch.float32, what=f"{lengths}")
+
+
+@pytest.mark.parametrize("nseq", [1, 2, 32, 33, 48])
+def test_balanced_scan_paths(gpu_lib, nseq):
+    """Both ways the kernel finds its ranges: up to 63 sequences whose q rows fit four 16-byte pieces per
+    thread (32 sequences of 4 rows here) scan the lengths in registers and fix each wave's first takes; 33
+    and more scan in LDS, up to 48 (their q rows fill the 48 KiB the workgroup stages them in). Random lengths (a one-position sequence among them) at partitions of 64 tokens, the
+    fused append and the plain decode, poisoned workspaces, against the oracle."""
+    rng = np.random.default_rng(1400 + nseq)
+    lengths = [int(x) for x in rng.integers(1, 700, size=nseq)]
+    if nseq > 2:
+        lengths[1] = 1  # a one-position sequence among long ones
+    case = build_case(lengths=lengths, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_tokens=1,
+                      dtype=torch.bfloat16, seed=1400 + nseq, pool_slack=0.2)
+    poison_case(case)
+    kp, vp = oracle_after_write(case)
+    ref = _oracle_bf16(case, kp, vp)
+    pt = 64
+    print(f"[case] balanced scan paths B={nseq}", flush=True)
+    g = {k: getattr(case, k).to(DEV, copy=True) for k in ("q", "k_new", "v_new", "k_pool", "v_pool", "block_tables",
+                                                         "seq_lens", "positions")}
+    assert gpu_lib.split_schedule(g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt, force=BAL) == BAL
+    ws = _poisoned_workspace(gpu_lib, g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt)
+    fused = gpu_lib.write_kv_decode(g["q"], g["k_new"], g["v_new"], g["k_pool"], g["v_pool"], g["block_tables"],
+                                    g["seq_lens"], case.scale, max_seq_len=case.max_seq_len, partition_tokens=pt,
+                                    workspace=ws, split_schedule=BAL)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(g["k_pool"]), kp) and np.array_equal(bits(g["v_pool"]), vp)
+    assert_attention_close(fused.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what="fused")
+    ws = _poisoned_workspace(gpu_lib, g["q"], g["k_pool"], g["block_tables"], case.max_seq_len, pt)
+    out = gpu_lib.decode_partitioned(g["q"], g["k_pool"], g["v_pool"], g["block_tables"], g["seq_lens"], case.scale,
+                                     case.max_seq_len, pt, workspace=ws, split_schedule=BAL)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what="decode")
