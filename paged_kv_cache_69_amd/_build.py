@@ -66,10 +66,11 @@ def _build_lib(folder: str, lib_path: str, logs: list, ex, defines=(), tag: str 
     os.replace(tmp, lib_path)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, timeline: bool = True) -> str:
     """Compile every HIP source to an object (in parallel) and link them: csrc/ into
     ``paged_kv_cache_69_amd/libpa.so`` (the decode library) and probe/ into ``libpa_probe.so`` (the
-    benchmark's measurement probes); return the decode library's path."""
+    benchmark's measurement probes) and, with ``timeline``, csrc/ again with PA_TIMELINE=1 into
+    ``libpa_timeline.so`` (the per-wave timeline build); return the decode library's path."""
     from concurrent.futures import ThreadPoolExecutor
 
     # a fixed object directory: the paths hipcc records stay the same from build to build, so the
@@ -79,6 +80,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=8) as ex:
         _build_lib("csrc", LIB_PATH, logs, ex)
         _build_lib("probe", PROBE_LIB_PATH, logs, ex)
+        if timeline:
+            _build_lib("csrc", TIMELINE_LIB_PATH, logs, ex, defines=("-DPA_TIMELINE=1",), tag="timeline_")
     if verbose:
         for log in logs:
             if log.strip():
@@ -88,7 +91,7 @@ def build(verbose: bool = False) -> str:
 
 def build_timeline(verbose: bool = False) -> str:
     """The measurement build: csrc/ with PA_TIMELINE=1 into ``libpa_timeline.so`` (the decode kernels
-    also record a per-wave timeline; include/pa_timeline.h). Not part of build()."""
+    also record a per-wave timeline; include/pa_timeline.h) alone."""
     from concurrent.futures import ThreadPoolExecutor
 
     os.makedirs(OBJ_DIR, exist_ok=True)
