@@ -16,10 +16,15 @@
 //    q rows are the resident B operand of S^T = K Q^T, as in the decode
 //    kernel.
 //  * Positions go in tiles of 32. The whole workgroup loads a tile's K and V
-//    (8 KiB each) from the pool into LDS, one tile ahead of the one being
-//    computed (double buffer, one barrier per tile). Each thread loads 16-byte
-//    chunks of two positions and looks up their block itself, so any block
-//    size works.
+//    (8 KiB each) from the pool straight into LDS, two tiles ahead of the one
+//    whose scores are computed (four buffers, one barrier per tile). Each
+//    thread loads 16-byte chunks of two positions; the block ids come from the
+//    table one step before the loads are issued, and for b < 16 a lane picks
+//    its own position's block, so any block size works.
+//  * The LDS operand reads of a tile run one stretch of work ahead of the
+//    MFMAs that use them (the next tile's K and half of this tile's V behind
+//    the softmax, the other half of V behind the scores), kept there by
+//    scheduling fences: the matrix cores otherwise wait on LDS latency.
 //  * K sits in LDS as [position][256 B] with its 16-byte chunks XOR-swizzled
 //    by position, so the A operand reads (16 positions x the same chunk) hit
 //    16 different bank groups.
@@ -106,6 +111,11 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Keeps the compiler's scheduler from moving any instruction across it: the LDS operand reads of the
+// tile loop then stay one stretch of work ahead of the MFMAs that consume them (left to itself, the
+// scheduler moves each read down to its first use, and the MFMA waits for the LDS).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Workgroup barrier with no implied wait for outstanding memory operations; the memory clobber keeps
 // the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -187,14 +197,32 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
   const int lc_k = (lane & 15) ^ (tq & 15);              // K chunk this lane's LDS chunk holds
   const int lc_v = (lane & 15) ^ ((tq & 7) << 1);        // V chunk (32-byte blocks swizzled)
   constexpr int kHalfBlocks = BS >= 16 ? 1 : 16 / BS;    // blocks one half spans
-  auto issue = [&](lds_char* buf, int tile) {
+  const uint32_t lane_k = (uint32_t)(tq * kRowBytes + lc_k * 16);  // this lane's chunk within a half
+  const uint32_t lane_v = (uint32_t)(tq * kRowBytes + lc_v * 16);
+  // Block ids of a tile's two 16-position halves (b >= 16), read one step before the tile's loads
+  // are issued so that the issue does not wait for the table; the index is clamped to the table row.
+  auto fetch_blocks = [&](int tile, int (&nb)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      nb[h] = trow[min((tile * kKT + 16 * h) / BS, p.MB - 1)];  // clamped to the pool where used
+  };
+  auto issue = [&](lds_char* buf, int tile, const int (&nb)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int p0 = tile * kKT + 16 * h;
       // block of this lane's row (scalar table loads; a lane selects among them for b < 16)
       int64_t row_off;
       if constexpr (BS >= 16) {
-        const int blk = (int)min((uint32_t)trow[min(p0 / BS, p.MB - 1)], (uint32_t)(p.num_blocks - 1));
+        const int blk = (int)min((uint32_t)nb[h], (uint32_t)(p.num_blocks - 1));
+        const int64_t base_off = (int64_t)blk * block_bytes + (int64_t)(p0 % BS) * kRowBytes;
+        if (p0 + 16 <= L) {
+          // every row of the half is below the length: a scalar base plus this lane's fixed offset
+          __builtin_amdgcn_global_load_lds((const void*)(kbase + base_off + lane_k),
+                                           (lds_void*)(buf + (4 * h + wave) * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(vbase + base_off + lane_v),
+                                           (lds_void*)(buf + (8 + 4 * h + wave) * 1024), 16, 0, 0);
+          continue;
+        }
         row_off = (int64_t)blk * block_bytes + (int64_t)(p0 % BS + tq) * kRowBytes;
       } else {
         int ids[kHalfBlocks];
@@ -233,24 +261,29 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) acc[mt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K operands of a tile: position c16 (+16 for half 1), chunk 4kc + g.
+  auto read_k = [&](const lds_char* buf, u32x4 (&ka)[4][2]) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      ka[kc][0] = *(const lds_u32x4*)(buf + rd_k[kc]);
+      ka[kc][1] = *(const lds_u32x4*)(buf + kKBytes / 2 + rd_k[kc]);
+    }
+  };
   // Raw S^T of a tile for both 16-position halves: lane (g, c16) holds positions 16h + 4g + e of
-  // row c16 + 16 mt.
-  auto scores = [&](const lds_char* buf, f32x4 (&s)[2][2]) {
+  // row c16 + 16 mt. Four independent accumulation chains, interleaved, so no MFMA waits for the one
+  // before it.
+  auto scores = [&](const u32x4 (&ka)[4][2], f32x4 (&s)[2][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) s[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // four independent accumulation chains, interleaved, so no MFMA waits for the one before it
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const u32x4 ka0 = *(const lds_u32x4*)(buf + rd_k[kc]);
-      const u32x4 ka1 = *(const lds_u32x4*)(buf + kKBytes / 2 + rd_k[kc]);
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        s[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka0), as_bf16x8(qb[mt][kc]), s[0][mt], 0, 0, 0);
-        s[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka1), as_bf16x8(qb[mt][kc]), s[1][mt], 0, 0, 0);
+        s[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc][0]), as_bf16x8(qb[mt][kc]), s[0][mt], 0, 0, 0);
+        s[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kc][1]), as_bf16x8(qb[mt][kc]), s[1][mt], 0, 0, 0);
       }
-    }
   };
   // Softmax and P.V of a tile whose raw scores are s and whose V rows are in buf.
   // Mask, reference check and (rarely) rescale for a tile whose raw scores are s.
@@ -293,6 +326,12 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
       }
     }
   };
+  // The bf16 pairs (-1, 0) and (0, -1), materialised in registers: as an operand of the packed-bf16
+  // dot product the compiler encodes the first as the inline constant -1.0, and the results were
+  // then wrong (the products did not use that pair).
+  uint32_t neg_lo, neg_hi;
+  asm("v_mov_b32 %0, 0xbf80" : "=v"(neg_lo));
+  asm("v_mov_b32 %0, 0xbf800000" : "=v"(neg_hi));
   // P of a tile (hi and lo operands) and its row sums.
   auto probs = [&](const f32x4 (&s)[2][2], u32x4 (&a_hi)[2], u32x4 (&a_lo)[2]) {
     // P = 2^(c s - m), masked positions exactly 0. Split P = hi + lo: hi is P truncated to bf16 (its
@@ -311,50 +350,60 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t u0 = __float_as_uint(pr[2 * w]), u1 = __float_as_uint(pr[2 * w + 1]);
-        a_hi[mt][w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-        a_lo[mt][w] = cvt_pk_bf16(pr[2 * w] - __uint_as_float(u0 & 0xffff0000u),
-                                  pr[2 * w + 1] - __uint_as_float(u1 & 0xffff0000u));
+        const uint32_t hp = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        a_hi[mt][w] = hp;
+        // P - hi, exact, as one packed-bf16 dot product each: (hi0, hi1) . (-1, 0) + P0 and
+        // (hi0, hi1) . (0, -1) + P1 (the products are exact in fp32 and so is the difference)
+        a_lo[mt][w] = cvt_pk_bf16(dot2_bf16(hp, neg_lo, pr[2 * w]), dot2_bf16(hp, neg_hi, pr[2 * w + 1]));
       }
     }
   };
-  // P.V of a tile whose V rows are in buf.
-  auto pv = [&](const lds_char* buf, const u32x4 (&a_hi)[2], const u32x4 (&a_lo)[2]) {
-    // Two head_dim blocks at a time: their hi MFMAs for both row tiles, then their lo MFMAs, so an
-    // accumulator's two updates are four instructions apart.
+  // V operands (transposed reads) of head_dim blocks jb0 .. jb0+3 of a tile.
+  auto read_v = [&](const lds_char* buf, int jb0, u32x4 (&bv)[4]) {
 #pragma unroll
-    for (int jb = 0; jb < 8; jb += 2) {
-      u32x4 bv[2];
+    for (int j = 0; j < 4; ++j) {
+      const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + rd_v[jb0 + j]));
+      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kKBytes / 2 + rd_v[jb0 + j]));
+      const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
+      bv[j] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+    }
+  };
+  // P.V of head_dim blocks jb0 .. jb0+3. Two blocks at a time: their hi MFMAs for both row tiles, then
+  // their lo MFMAs, so an accumulator's two updates are four instructions apart.
+  auto pv = [&](const u32x4 (&bv)[4], int jb0, const u32x4 (&a_hi)[2], const u32x4 (&a_lo)[2]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + rd_v[jb + j]));
-        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + kKBytes / 2 + rd_v[jb + j]));
-        const uint64_t w0 = __builtin_bit_cast(uint64_t, b0), w1 = __builtin_bit_cast(uint64_t, b1);
-        bv[j] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
-      }
+    for (int j0 = 0; j0 < 4; j0 += 2) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[mt][jb + j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi[mt]), as_bf16x8(bv[j]), acc[mt][jb + j], 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = j0; j < j0 + 2; ++j)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          acc[mt][jb + j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo[mt]), as_bf16x8(bv[j]), acc[mt][jb + j], 0, 0, 0);
+          acc[mt][jb0 + j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi[mt]), as_bf16x8(bv[j]), acc[mt][jb0 + j], 0, 0, 0);
+#pragma unroll
+      for (int j = j0; j < j0 + 2; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt][jb0 + j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo[mt]), as_bf16x8(bv[j]), acc[mt][jb0 + j], 0, 0, 0);
     }
   };
 
   // Software pipeline, step i: wait for this wave's loads of tile i+1 (tile i+2 may stay in flight),
-  // barrier (every wave's part of tile i+1 is in LDS, and every wave is done with tile i-1), issue
-  // tile i+3 into the buffer tile i-1 used, then the scores of tile i+1 on the matrix cores while
-  // the vector ALUs run the softmax of tile i, whose P.V follows. Unrolled by four so that each
-  // buffer is a fixed LDS object.
+  // barrier (every wave's part of tile i+1 is in LDS, and every wave is done with tile i-1); the LDS
+  // reads of tile i+1's K operands and of half of tile i's V operands; issue tile i+3 into the buffer
+  // tile i-1 used (and read the table for tile i+4); the mask and reference check of tile i; then,
+  // fenced apart so that each group of LDS reads has a stretch of work to hide behind: tile i's P on
+  // the vector ALUs, tile i+1's scores, the other half of the V reads, and tile i's P.V. Unrolled by
+  // four so that each buffer is a fixed LDS object.
   lds_char* const bufs[4] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+  int nb[2] = {0, 0};
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (t < ntiles) issue(bufs[t], t);
+  for (int t = 0; t < 3; ++t) {
+    if constexpr (BS >= 16) fetch_blocks(min(t, ntiles - 1), nb);
+    if (t < ntiles) issue(bufs[t], t, nb);
+  }
+  if constexpr (BS >= 16) fetch_blocks(min(3, ntiles - 1), nb);
+  // tile 0 in LDS: the loads of tiles 1 and 2 may stay in flight
   if (ntiles > 2)
     wait_vmem<8>();
   else if (ntiles > 1)
@@ -363,7 +412,16 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
     wait_vmem<0>();
   lds_barrier();
   f32x4 s_a[2][2], s_b[2][2];
-  scores(bufs[0], s_a);
+  {
+    u32x4 ka[4][2];
+    read_k(bufs[0], ka);
+    scores(ka, s_a);
+  }
+  // Every scalar value the loop reads (the kernel arguments above all) is in its register before the
+  // loop starts: otherwise the wait for such a load lands inside the loop, where it would also wait
+  // for every LDS read in flight, on every step.
+  asm volatile("" ::"s"(c));  // the scale's load is issued above this point
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   for (int i0 = 0; i0 < ntiles; i0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -371,22 +429,33 @@ __global__ __launch_bounds__(kNW * 64) void prefill_mfma_kernel(const PrefillPar
       if (i < ntiles) {
         f32x4(&s_cur)[2][2] = (u & 1) ? s_b : s_a;
         f32x4(&s_next)[2][2] = (u & 1) ? s_a : s_b;
+        u32x4 ka[4][2], bv0[4], bv1[4], a_hi[2], a_lo[2];
         if (i + 1 < ntiles) {
           if (i + 2 < ntiles)
             wait_vmem<4>();
           else
             wait_vmem<0>();
           lds_barrier();
-          if (i + 3 < ntiles) issue(bufs[(u + 3) & 3], i + 3);
+        }
+        // Past the last tile the K reads and scores use a stale buffer and are never used; tiles past
+        // a wave's rows are fully masked and add nothing.
+        read_k(bufs[(u + 1) & 3], ka);
+        read_v(bufs[u], 0, bv0);
+        if (i + 1 < ntiles) {
+          if (i + 3 < ntiles) issue(bufs[(u + 3) & 3], i + 3, nb);
+          if constexpr (BS >= 16) fetch_blocks(min(i + 4, ntiles - 1), nb);
         }
         head(i, s_cur);
-        // One branch-free stretch: the next tile's scores on the matrix cores, this tile's P on the
-        // vector ALUs, then this tile's P.V. Past the last tile the scores read a stale buffer and
-        // are never used; tiles past a wave's rows are fully masked and add nothing.
-        scores(bufs[(u + 1) & 3], s_next);
-        u32x4 a_hi[2], a_lo[2];
-        probs(s_cur, a_hi, a_lo);
-        pv(bufs[u], a_hi, a_lo);
+        sched_fence();
+        probs(s_cur, a_hi, a_lo);  // behind it: the K reads and the first V reads
+        sched_fence();
+        scores(ka, s_next);
+        sched_fence();
+        read_v(bufs[u], 4, bv1);
+        sched_fence();
+        pv(bv0, 0, a_hi, a_lo);  // behind it (and the scores): the second V reads
+        sched_fence();
+        pv(bv1, 4, a_hi, a_lo);
       }
     }
   }
