@@ -28,7 +28,10 @@ streaming-read kernel reaches over 2 GiB (`frac_of_stream` = achieved /
 stream_gbps), and `floor_us`, the duration of a launch that makes only the
 dependent loads in front of each decode workgroup's first K/V tile (length and
 table entry together, then the tile) over the same cold replicas;
-`model_us` = floor_us + bytes / stream_gbps. `cpu_baseline` is the float64
+`model_us` = floor_us + bytes / stream_gbps. The prefill line's roofline (the
+bf16 matrix peak) carries `measured_mfma_tflops`, the rate a register-only MFMA
+loop of the same instruction reaches on this GPU in the same run, and
+`frac_of_measured_mfma`. `cpu_baseline` is the float64
 oracle on this host's cores (sequences spread over a thread pool, BLAS on
 one BLAS thread per worker), over a bounded sample of the same workload, with a
 one-thread figure beside it.
@@ -60,6 +63,7 @@ HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30  # replicas rotate over at least this much memory
 REPLICAS = 0  # --replicas N: that many input copies instead of enough for a cold cache (a warm-cache run)
 PAGED_PROBE = True  # --no-paged-probe: skip the paged-read probe sweep
+MFMA_PROBE = True  # --no-mfma-probe: skip the matrix-rate probe of the prefill line
 SPLIT_SCHEDULE = 0  # --split-schedule N: pa_dims.split_schedule of split calls (0: the library's choice)
 CALIBRATION_BYTES = 512 << 20  # the copy kernel that calibrates the traffic counters reads and writes this much
 STREAM_BYTES = 2 << 30  # the streaming-read probe reads this much per launch (far past every cache)
@@ -388,12 +392,15 @@ def probe_library():
         lib.pa_probe_first_tile.restype = ctypes.c_int
         lib.pa_probe_paged_read.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P]
         lib.pa_probe_paged_read.restype = ctypes.c_int
+        lib.pa_probe_mfma.argtypes = [I32, I32, I32, P, P]
+        lib.pa_probe_mfma.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
 
 
 _PROBE = None
 _STREAM = None
+_MFMA = None
 
 
 def calibrate_stream(runs: int = 5):
@@ -431,6 +438,44 @@ def calibrate_stream(runs: int = 5):
     torch.cuda.empty_cache()
     _STREAM = {"stream_gbps": round(best[0], 1), "stream_launch": best[1], "stream_bytes": STREAM_BYTES}
     return _STREAM
+
+
+def calibrate_mfma(runs: int = 3, iters: int = 4000):
+    """The bf16 matrix rate (TFLOP/s) this GPU sustains: pa_probe_mfma with 2 and 4 waves per SIMD
+    (512 and 1024 workgroups), best of the two, alone and with 2 fp32 FMAs after each MFMA (about the
+    prefill kernel's ratio of other vector instructions to MFMAs); each figure the average of ``runs``
+    launches between HIP events on the stream they run on. Measured once per process."""
+    import ctypes
+
+    import torch
+
+    global _MFMA
+    if _MFMA is not None:
+        return _MFMA
+    lib = probe_library()
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for nv in (0, 2):
+        best = (0.0, None)
+        for wg in (512, 1024):
+            out = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
+            if lib.pa_probe_mfma(wg, 100, nv, out.data_ptr(), h):
+                raise RuntimeError("pa_probe_mfma failed")
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(runs):
+                lib.pa_probe_mfma(wg, iters, nv, out.data_ptr(), h)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            flops = wg * 4 * iters * 8 * 16384
+            tflops = flops / (ev0.elapsed_time(ev1) / runs * 1e-3) / 1e12
+            if tflops > best[0]:
+                best = (tflops, wg // 256)
+        res["mfma_tflops" if nv == 0 else "mfma_tflops_2fma"] = round(best[0], 1)
+        res["waves_per_simd" if nv == 0 else "waves_per_simd_2fma"] = best[1]
+    _MFMA = res
+    return _MFMA
 
 
 def _graph_us(launch, reps, steps):
@@ -735,6 +780,7 @@ def run_prefill_workload(pa, name, steps, warmup, graphs=True):
     flops = prefill_flops(case)
     tflops = flops / (call_ms * 1e-3) / 1e12
     tokens = sum(case.chunks)
+    mfma = calibrate_mfma() if MFMA_PROBE else None
     res = {
         "tokens_per_s": tokens / sec_per_step,
         "ms_per_step": sec_per_step * 1e3,
@@ -744,7 +790,10 @@ def run_prefill_workload(pa, name, steps, warmup, graphs=True):
                      "traffic": traffic_from_profiles(name),
                      "kernel": "prefill_mfma_kernel (one pa_prefill call)", "flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": prefill_algorithmic_bytes(case),
-                     "avg_launch_us": round(call_ms * 1e3, 3), "launches_timed": steps},
+                     "avg_launch_us": round(call_ms * 1e3, 3), "launches_timed": steps,
+                     **({"measured_mfma_tflops": mfma["mfma_tflops"],
+                         "frac_of_measured_mfma": round(tflops / mfma["mfma_tflops"], 4),
+                         "measured_mfma_tflops_2fma": mfma["mfma_tflops_2fma"]} if mfma else {})},
         "config": {"workload": f"{name}: {spec['desc']}", "num_seqs": len(case.chunks), "chunk_tokens": tokens,
                    "histories": sum(case.histories), "replicas": n_rep,
                    "step": "pa_write_kv_varlen call + pa_prefill call"},
@@ -1114,6 +1163,7 @@ def main(argv=None):
                     help="first run a copy kernel of known size (for counter calibration)")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read calibration")
     ap.add_argument("--no-paged-probe", action="store_true", help="skip the paged-read probe sweep")
+    ap.add_argument("--no-mfma-probe", action="store_true", help="skip the matrix-rate probe of the prefill line")
     ap.add_argument("--cpu-secondary", default="long",
                     help="comma-separated secondary workloads that also get a cpu_baseline ('' for none)")
     ap.add_argument("--no-graph", action="store_true",
@@ -1147,10 +1197,11 @@ def main(argv=None):
               "GPU and needs no collectives: its (sequence, kv head) units split across GPUs with no exchange.",
               file=sys.stderr)
         return 2
-    global REPLICAS, SPLIT_SCHEDULE, PAGED_PROBE
+    global REPLICAS, SPLIT_SCHEDULE, PAGED_PROBE, MFMA_PROBE
     REPLICAS = max(0, args.replicas)
     SPLIT_SCHEDULE = args.split_schedule
     PAGED_PROBE = not args.no_paged_probe
+    MFMA_PROBE = not args.no_mfma_probe
 
     import torch
 

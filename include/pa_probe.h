@@ -5,7 +5,9 @@
  * through the tables) and the latency of the dependent loads a decode workgroup makes before its
  * first K/V tile arrives. [P3] "Asynchronous KV Cache Prefetching",
  * sections 2.2 and 3.2, names both: decode attention streams the cache at memory speed, and the
- * block-table lookup in front of each block's load is exposed latency.
+ * block-table lookup in front of each block's load is exposed latency. The fourth, the MFMA rate,
+ * is the matching ceiling for the prefill, whose roofline is the matrix peak ([P1] "25. Paged
+ * attention and prefix caching", stretch exercise 4: a block of queries makes it a dense contraction).
  *
  * Every pointer is device memory owned by the caller; each call enqueues one kernel on `stream` and
  * returns 0, or -1 for an invalid argument, -3 when the launch fails.
@@ -59,6 +61,14 @@ int pa_probe_paged_read(const void* k_pool, const void* v_pool, const int32_t* b
                         int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks, int32_t num_blocks,
                         int32_t block_size, int32_t row_bytes, int32_t blocks_per_wave, int32_t unroll,
                         int32_t nontemporal, uint32_t* out, pa_probe_stream_t stream);
+
+/* pa_probe_mfma: the bf16 matrix rate, with no memory traffic. `workgroups` workgroups of 256 threads
+ * (4 waves); each wave runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 (16384 flops
+ * each) into 8 accumulators, each MFMA followed by `valu_per_mfma` (0, 2 or 4) independent fp32 FMAs
+ * on other registers, in that order. With 256 * w workgroups every SIMD holds w waves. Each thread
+ * writes one float of what it computed to out[workgroup * 256 + thread] (workgroups * 256 floats), so
+ * no instruction can be dropped. Flops per call: workgroups * 4 * iters * 8 * 16384. */
+int pa_probe_mfma(int32_t workgroups, int32_t iters, int32_t valu_per_mfma, float* out, pa_probe_stream_t stream);
 
 #ifdef __cplusplus
 }

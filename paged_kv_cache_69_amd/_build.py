@@ -28,6 +28,9 @@ HIP_FLAGS = [
 # back on every tile, so that file uses the VGPR form of the MFMA instructions.
 FILE_FLAGS = {
     "pa_prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the matrix-rate probe measures what the prefill kernel's form of the instruction sustains; in the
+    # AGPR form its fenced loop would also copy every accumulator after each MFMA
+    "pa_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

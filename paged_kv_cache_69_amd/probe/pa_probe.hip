@@ -1,8 +1,9 @@
 // Measurement probes of libpa_probe.so (declared in include/pa_probe.h): a streaming-read kernel, the
 // ceiling HBM reads reach on this GPU; a paged read of every K/V block a decode call reads, through the
-// same block tables with no arithmetic, the ceiling of that access pattern; and the dependent loads in
-// front of a decode workgroup's first tile, the latency floor of a decode launch. None of them is part
-// of the decode path.
+// same block tables with no arithmetic, the ceiling of that access pattern; the dependent loads in
+// front of a decode workgroup's first tile, the latency floor of a decode launch; and a register-only
+// MFMA loop, the bf16 matrix rate this GPU sustains, alone and with vector-ALU work beside it. None of
+// them is part of the decode path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,6 +12,8 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
@@ -149,6 +152,41 @@ hipError_t launch_paged(const PagedParams& p, int nl, int unroll, dim3 grid, hip
   }
 }
 
+// Each wave: `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 into 8 accumulators, each MFMA
+// followed by NV independent fp32 FMAs; scheduling fences keep that order. Operands come from the lane
+// index, so the loop touches no memory; every thread stores one float made of all it computed.
+template <int NV>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int32_t iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(lane + i));
+    b[i] = (__bf16)(0.002f * (float)(lane - i));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.01f * (float)lane + (float)k;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[(j * NV + k) & 7] = fmaf(v[(j * NV + k) & 7], 0.9999f, 0.5f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) t += v[k];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +246,19 @@ int pa_probe_paged_read(const void* k_pool, const void* v_pool, const int32_t* b
                                    : launch_paged<0>(p, nl, unroll, dim3((unsigned)grid), s);
   if (e == hipErrorInvalidValue) return -1;
   return e == hipSuccess ? 0 : -3;
+}
+
+int pa_probe_mfma(int32_t workgroups, int32_t iters, int32_t valu_per_mfma, float* out, pa_probe_stream_t stream) {
+  if (!out || workgroups < 1 || iters < 1) return -1;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (valu_per_mfma) {
+    case 0: mfma_rate_kernel<0><<<dim3(workgroups), dim3(256), 0, s>>>(iters, out); break;
+    case 2: mfma_rate_kernel<2><<<dim3(workgroups), dim3(256), 0, s>>>(iters, out); break;
+    case 4: mfma_rate_kernel<4><<<dim3(workgroups), dim3(256), 0, s>>>(iters, out); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
 """libpa_probe.so, the benchmark's measurement probes: on the CPU, the library loads and exports what
 include/pa_probe.h declares, and rejects bad arguments before any launch; on the GPU, each probe reads
-exactly the bytes it states (the XOR it writes equals torch's XOR of the same words), and the stream
-figures bench.py derives from the probes are consistent."""
+exactly the bytes it states (the XOR it writes equals torch's XOR of the same words), the MFMA probe
+computes what its header states, and the stream figures bench.py derives from the probes are
+consistent."""
 
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ def _declared():
 
 def test_probe_library_exports_every_declared_function():
     lib = bench.probe_library()
-    assert _declared() == ["pa_probe_first_tile", "pa_probe_paged_read", "pa_probe_stream_read"]
+    assert _declared() == ["pa_probe_first_tile", "pa_probe_mfma", "pa_probe_paged_read", "pa_probe_stream_read"]
     for name in _declared():
         assert hasattr(lib, name), name
 
@@ -43,6 +44,11 @@ def test_probe_arguments_rejected_without_a_launch():
     assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 16, 256, 16, 3, 0, out, None) == -1
     assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 16, 256, 0, 2, 0, out, None) == -1
     assert lib.pa_probe_paged_read(fake, fake, fake, fake, 4, 8, 4, 10, 64, 256, 16, 2, 0, out, None) == -1  # 16 KiB
+    # MFMA rate: no workgroups, no rounds, no such number of FMAs per MFMA, no output
+    assert lib.pa_probe_mfma(0, 10, 0, out, None) == -1
+    assert lib.pa_probe_mfma(4, 0, 0, out, None) == -1
+    assert lib.pa_probe_mfma(4, 10, 3, out, None) == -1
+    assert lib.pa_probe_mfma(4, 10, 0, None, None) == -1
 
 
 def test_stream_terms_model():
@@ -137,3 +143,43 @@ def test_paged_read_reads_every_block_once(gpu_lib, bpw, unroll, nt):
                     blk = min(int(case.block_tables[i, j]) & 0xFFFFFFFF, n - 1)
                     want ^= _xor(case.k_pool[blk, h_]) ^ _xor(case.v_pool[blk, h_])
                 assert (int(got[(i * groups + grp) * hkv + h_]) & 0xFFFFFFFF) == want, (i, grp, h_)
+
+
+def _mfma_probe_expected(iters: int, nv: int) -> np.ndarray:
+    """What every workgroup of pa_probe_mfma writes, thread by thread, in float64: the operands are
+    A[r][k] = bf16(0.001 (lane + k % 8)) held by lane r + 16 (k // 8), B[k][c] = bf16(0.002 (lane - k % 8))
+    held by lane c + 16 (k // 8); lane (g, c) keeps D[4g + e][c] of D = A B, e < 4, in each of its 8
+    accumulators, iters times; its 8 FMA chains start at 0.01 lane + k and take nv steps per round each
+    (v <- 0.9999 v + 0.5)."""
+    def bf16(x):
+        return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+    k = np.arange(32)
+    A = np.stack([bf16(0.001 * (r + 16 * (k // 8) + k % 8)) for r in range(16)])        # [16, 32]
+    B = np.stack([bf16(0.002 * (c + 16 * (k // 8) - k % 8)) for c in range(16)], axis=1)  # [32, 16]
+    D = A @ B
+    out = np.zeros(256)
+    for t in range(256):
+        lane = t % 64
+        g, c = lane // 16, lane % 16
+        acc = 8 * iters * sum(D[4 * g + e, c] for e in range(4))
+        steps = nv * iters
+        v = sum(5000.0 + (0.01 * lane + kk - 5000.0) * 0.9999 ** steps for kk in range(8))
+        out[t] = acc + v
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nv", [0, 2, 4])
+def test_mfma_probe_computes_what_it_states(gpu_lib, nv):
+    lib = bench.probe_library()
+    wg, iters = 300, 7
+    out = torch.full((wg * 256,), float("nan"), dtype=torch.float32, device="cuda:0")
+    print(f"[case] mfma probe nv={nv}", flush=True)
+    h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.pa_probe_mfma(wg, iters, nv, out.data_ptr(), h) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(wg, 256).astype(np.float64)
+    assert np.isfinite(got).all()
+    assert (got == got[0]).all()  # every workgroup computes the same
+    np.testing.assert_allclose(got[0], _mfma_probe_expected(iters, nv), rtol=1e-5)
