@@ -1073,8 +1073,11 @@ XCDS = 8      # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs' instances
 def summarize_counters(directories: list, workload: str, commands: list) -> str:
     """Per-kernel medians (over dispatches) of the SQ / GRBM counters of one or more ``rocprofv3 --pmc``
     runs of ``bench.py --workload W``, with the derived shares: matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES
-    / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), LDS bank conflicts per LDS instruction, instructions per
-    wave. GRBM_GUI_ACTIVE counts GPU-busy cycles once per XCD and rocprofv3 sums the instances, so one
+    / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); vector-ALU busy = 4 x SQ_ACTIVE_INST_VALU (quad-cycles,
+    summed over waves) over the same SIMD-cycles; matrix/vector co-execution =
+    SQ_VALU_MFMA_COEXEC_CYCLES over them; a wave's time issuing, waiting to issue, and waiting on its
+    counters or a barrier (SQ_ACTIVE_INST_ANY, SQ_WAIT_INST_ANY, SQ_WAIT_ANY over SQ_WAVE_CYCLES); LDS
+    bank conflicts per LDS instruction; instructions per wave (SQ_INSTS_VALU counts the MFMAs too). GRBM_GUI_ACTIVE counts GPU-busy cycles once per XCD and rocprofv3 sums the instances, so one
     XCD's share is the kernel's elapsed cycles."""
     per = {}
     for directory in directories:
@@ -1097,6 +1100,18 @@ def summarize_counters(directories: list, workload: str, commands: list) -> str:
             lines.append(f"kernel_{i}_elapsed_cycles = {get('GRBM_GUI_ACTIVE') / XCDS:.0f}")
             lines.append(f"kernel_{i}_mfma_busy_frac = "
                          f"{get('SQ_VALU_MFMA_BUSY_CYCLES') / (get('GRBM_GUI_ACTIVE') / XCDS * SIMDS):.4f}")
+        el = get("GRBM_GUI_ACTIVE") / XCDS if get("GRBM_GUI_ACTIVE") else None
+        if el and get("SQ_ACTIVE_INST_VALU") is not None:
+            # quad-cycles summed over waves; one SIMD issues one VALU instruction at a time
+            lines.append(f"kernel_{i}_valu_busy_frac = {4 * get('SQ_ACTIVE_INST_VALU') / (el * SIMDS):.4f}")
+        if el and get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
+            lines.append(f"kernel_{i}_valu_mfma_coexec_frac = "
+                         f"{get('SQ_VALU_MFMA_COEXEC_CYCLES') / (el * SIMDS):.4f}")
+        if get("SQ_WAVE_CYCLES"):
+            for c, n in (("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_WAIT_INST_ANY", "waiting_to_issue"),
+                         ("SQ_WAIT_ANY", "waiting_on_counters_or_barrier")):
+                if get(c) is not None:
+                    lines.append(f"kernel_{i}_wave_time_{n} = {get(c) / get('SQ_WAVE_CYCLES'):.4f}")
         if get("SQ_LDS_BANK_CONFLICT") is not None and get("SQ_INSTS_LDS"):
             lines.append(f"kernel_{i}_lds_bank_conflict_cycles_per_lds_inst = "
                          f"{get('SQ_LDS_BANK_CONFLICT') / get('SQ_INSTS_LDS'):.3f}")
