@@ -122,3 +122,42 @@ def test_two_partitions_per_wave_reference_restarts(gpu_lib):
     assert torch.equal(outs[0], outs[1])
     for what, out in (("split", outs[1]), ("single pass", single)):
         assert_attention_close(out.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what=what)
+
+
+@pytest.mark.parametrize("t", [1, 4])
+def test_fused_single_pass_short_wave_restarts(gpu_lib, t):
+    """Fused append + single pass on sequences of 2 to 16 tiles, so every wave has at most four tiles and
+    computes its first tile before it asks for its second. K points along head_dim 0 with a value that
+    climbs about 2.6 per position (about 2 base-2 units of score per position), so a wave's later tiles
+    outrun the reference its first tile set and it runs again from its first tile. The fused call gives the
+    bits of the separate append + single pass, and both meet the oracle."""
+    lengths = [max(t, x) for x in (20, 100, 180, 200, 250, 256)]
+    case = build_case(lengths=lengths, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, q_tokens=t,
+                      dtype=torch.bfloat16, seed=7300 + t, pool_slack=0.1)
+
+    def ramp(pos):
+        return float(torch.tensor(2.6 * pos).to(torch.bfloat16))
+
+    for i, L in enumerate(lengths):
+        for pos in range(L - t):
+            phys = int(case.block_tables[i, pos // 16])
+            case.k_pool[phys, :, pos % 16] = 0.0
+            case.k_pool[phys, :, pos % 16, 0] = ramp(pos)
+        for j in range(t):
+            case.k_new[i, j] = 0.0
+            case.k_new[i, j, :, 0] = ramp(L - t + j)
+    case.q[..., 0] = (6.0 + 0.1 * case.q[..., 0].float()).to(torch.bfloat16)
+    kp, vp = oracle_after_write(case)
+    ref = _oracle_decode(case, kp, vp)
+    f, s = _gpu(case), _gpu(case)
+    print(f"[case] fused single pass short-wave restarts T={t}", flush=True)
+    fused = gpu_lib.write_kv_decode(f["q"], f["k_new"], f["v_new"], f["k_pool"], f["v_pool"], f["block_tables"],
+                                    f["seq_lens"], case.scale)
+    gpu_lib.write_kv(s["k_new"], s["v_new"], s["k_pool"], s["v_pool"], s["block_tables"], s["positions"])
+    separate = gpu_lib.decode(s["q"], s["k_pool"], s["v_pool"], s["block_tables"], s["seq_lens"], case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, separate)
+    for g in (f, s):  # bit patterns: the pools' unused slots hold NaN
+        assert np.array_equal(bits(g["k_pool"]), kp) and np.array_equal(bits(g["v_pool"]), vp)
+    for what, out in (("fused", fused), ("separate", separate)):
+        assert_attention_close(out.cpu(), ref, kv_dtype=torch.bfloat16, out_dtype=torch.float32, what=what)
